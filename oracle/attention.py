@@ -1,0 +1,279 @@
+"""Oracle: tree-masked attention, forward and backward, with RoPE at depth positions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The method computes exactly (up to rounding order) a result with a plain
+definition: "Tree Training" §3.1 Eq. 6 (forward equivalence) and the "Trie
+packing" page ("identical initial representations plus identical visible
+contexts produce identical layer outputs") say that every packed token's
+attention output equals the one it gets in an ordinary causal forward pass
+over any single root-to-leaf sequence that contains it. So the main oracle
+here unpacks every root-to-leaf path, runs textbook causal attention on it
+(S = QK^T / sqrt(d) with a causal mask, the "Trie packing" page, Step 3), and
+maps the rows back. RoPE is applied to q and k at each token's position on
+its path ("Trie packing" Step 1, "Tree Training" §3.2 Eq. 9), in the
+rotate-half convention with base theta (the pages name RoPE but fix neither
+convention nor base; this reading is listed in the design doc).
+
+Everything is float64. bf16 inputs are widened exactly.
+
+Conventions: q [T, Hq, d], k and v [T, Hkv, d]; query head h uses kv head
+h // (Hq // Hkv); LSE is the natural-log row log-sum-exp of the scaled scores,
+laid out [Hq, T].
+
+Other formulations kept for cross-checks and for sampled checks at full size:
+  forward_dense   packed formulation with a brute-force dense visibility mask
+  forward_rows    one query row at a time over its ancestor chain
+  backward_rows_dq, backward_keys   gradients for sampled rows / keys
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .pack import leaf_paths, path_counts_through, ancestors_or_self, children_lists
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def rope_angles(positions, d, theta):
+    """angle[n, k] = position_n * theta^(-2k/d), k < d/2, in float64."""
+    k = np.arange(d // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * k / d)
+    return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope(x, positions, theta):
+    """Rotate-half RoPE. x [L, H, d] (float64); positions [L]."""
+    d = x.shape[-1]
+    ang = rope_angles(positions, d, theta)
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rope_transpose(g, positions, theta):
+    """Gradient through RoPE: apply the inverse (= transposed) rotation."""
+    d = g.shape[-1]
+    ang = rope_angles(positions, d, theta)
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    g1, g2 = g[..., : d // 2], g[..., d // 2:]
+    return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
+
+
+def _causal_fwd(qr, kr, vv, scale):
+    """Textbook causal attention on one sequence, one head. qr, kr, vv [L, d]."""
+    L = qr.shape[0]
+    S = (qr @ kr.T) * scale
+    S[np.triu_indices(L, 1)] = -np.inf
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    P = E / l
+    return P @ vv, (m + np.log(l))[:, 0], P
+
+
+def forward_branches(q, k, v, par, pos, scale=None, theta=10000.0, check_agree=True):
+    """Per-branch forward. Returns (O [T,Hq,d], LSE [Hq,T]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    O = np.full((T, Hq, d), np.nan)
+    LSE = np.full((Hq, T), np.nan)
+    seen = np.zeros(T, dtype=bool)
+    for p in leaf_paths(par):
+        L = len(p)
+        if not np.array_equal(np.asarray(pos)[p], np.arange(L)):
+            raise AssertionError("depth positions differ from path offsets")
+        qr = rope(q[p], np.arange(L), theta)
+        kr = rope(k[p], np.arange(L), theta)
+        for h in range(Hq):
+            o, lse, _ = _causal_fwd(qr[:, h], kr[:, h // G], v[p, h // G], scale)
+            new = ~seen[p]
+            if check_agree and (~new).any():
+                old = O[p[~new], h]
+                if np.max(np.abs(old - o[~new])) > 1e-9:
+                    raise AssertionError("branches disagree on a shared token")
+            O[p[new], h] = o[new]
+            LSE[h, p[new]] = lse[new]
+        seen[p] = True
+    return O, LSE
+
+
+def backward_branches(q, k, v, do, par, pos, scale=None, theta=10000.0):
+    """Per-branch backward of sum_i <dO_i, O_i>. Returns dq, dk, dv (float64).
+
+    The upstream gradient of a token is split evenly over the c_i leaf paths
+    through it; any split that sums to dO_i gives the same total, because
+    every path through i contains all of i's visible keys. Per path the
+    textbook attention backward runs (the "Trie packing" page, "Same chain
+    rule": ordinary matrix backward, masked edges contribute zero), then the
+    inverse RoPE rotation, then a scatter-add back to the packed rows, which
+    also sums dK and dV over the query heads of a kv group.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    c = path_counts_through(par).astype(np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for p in leaf_paths(par):
+        L = len(p)
+        ar = np.arange(L)
+        qr = rope(q[p], ar, theta)
+        kr = rope(k[p], ar, theta)
+        dqr = np.zeros((L, Hq, d))
+        dkr = np.zeros((L, Hkv, d))
+        for h in range(Hq):
+            hk = h // G
+            o, _, P = _causal_fwd(qr[:, h], kr[:, hk], v[p, hk], scale)
+            dop = do[p, h] / c[p][:, None]
+            dv[p, hk] += P.T @ dop
+            dP = dop @ v[p, hk].T
+            D = np.sum(dop * o, axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dqr[:, h] += (dS @ kr[:, hk]) * scale
+            dkr[:, hk] += (dS.T @ qr[:, h]) * scale
+        dq[p] += rope_transpose(dqr, ar, theta)
+        dk[p] += rope_transpose(dkr, ar, theta)
+    return dq, dk, dv
+
+
+def forward_dense(q, k, v, vis, pos, scale=None, theta=10000.0):
+    """Packed formulation: S = QK^T * scale + M with M = 0 where vis, -inf
+    elsewhere ("Trie packing" Step 3). Tiny inputs only."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    qr = rope(q, pos, theta)
+    kr = rope(k, pos, theta)
+    O = np.zeros((T, Hq, d))
+    LSE = np.zeros((Hq, T))
+    for h in range(Hq):
+        S = (qr[:, h] @ kr[:, h // G].T) * scale
+        S = np.where(vis, S, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        l = E.sum(axis=1, keepdims=True)
+        O[:, h] = (E / l) @ v[:, h // G]
+        LSE[h] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def _row(qi, kc, vc, scale):
+    """One query row against its visible keys (already rotated)."""
+    s = (kc @ qi) * scale
+    m = s.max()
+    e = np.exp(s - m)
+    l = e.sum()
+    p = e / l
+    return p @ vc, m + np.log(l), p
+
+
+def forward_rows(q, k, v, par, rows, heads=None, scale=None, theta=10000.0):
+    """Attention for selected query rows, each over its ancestor-or-self chain.
+
+    Positions are the offsets along the chain (the token's depth). Returns
+    O [len(rows), len(heads), d] and LSE [len(heads), len(rows)].
+    """
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    heads = list(range(Hq)) if heads is None else list(heads)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    O = np.zeros((len(rows), len(heads), d))
+    LSE = np.zeros((len(heads), len(rows)))
+    for a, i in enumerate(rows):
+        chain = ancestors_or_self(par, int(i))
+        L = len(chain)
+        qi = rope(_f64(q[i:i + 1]), [L - 1], theta)[0]
+        kc = rope(_f64(k[chain]), np.arange(L), theta)
+        vc = _f64(v[chain])
+        for b, h in enumerate(heads):
+            o, lse, _ = _row(qi[h], kc[:, h // G], vc[:, h // G], scale)
+            O[a, b] = o
+            LSE[b, a] = lse
+    return O, LSE
+
+
+def backward_rows_dq(q, k, v, do, par, rows, heads=None, scale=None, theta=10000.0):
+    """dQ for selected rows: it depends only on the row's own chain.
+
+    dq'_i = scale * sum_j dS_ij k'_j with dS_ij = P_ij (dO_i.v_j - dO_i.O_i),
+    then the inverse rotation at the row's depth.
+    """
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    heads = list(range(Hq)) if heads is None else list(heads)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((len(rows), len(heads), d))
+    for a, i in enumerate(rows):
+        chain = ancestors_or_self(par, int(i))
+        L = len(chain)
+        qi = rope(_f64(q[i:i + 1]), [L - 1], theta)[0]
+        kc = rope(_f64(k[chain]), np.arange(L), theta)
+        vc = _f64(v[chain])
+        for b, h in enumerate(heads):
+            hk = h // G
+            o, _, p = _row(qi[h], kc[:, hk], vc[:, hk], scale)
+            doi = _f64(do[i, h])
+            ds = p * (vc[:, hk] @ doi - doi @ o)
+            g = (ds @ kc[:, hk]) * scale
+            out[a, b] = rope_transpose(g[None, None, :], [L - 1], theta)[0, 0]
+    return out
+
+
+def subtree_rows(par, j):
+    """Token j and all its descendants, from the parent links alone."""
+    ch = children_lists(par)
+    out, stack = [], [int(j)]
+    while stack:
+        x = stack.pop()
+        out.append(x)
+        stack.extend(ch[x])
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def backward_keys(q, k, v, do, par, keys, kv_heads=None, scale=None, theta=10000.0):
+    """dK and dV for selected keys: sums over the key's descendants-or-self.
+
+    dV_j = sum_{h in group} sum_i P_ij dO_i ;  dk'_j = scale * sum dS_ij q'_i,
+    then the inverse rotation at the key's depth. Returns (dk, dv) of shape
+    [len(keys), len(kv_heads), d].
+    """
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    dk = np.zeros((len(keys), len(kv_heads), d))
+    dv = np.zeros((len(keys), len(kv_heads), d))
+    for a, j in enumerate(keys):
+        j = int(j)
+        depth_j = len(ancestors_or_self(par, j)) - 1
+        acc_k = np.zeros((len(kv_heads), d))
+        for i in subtree_rows(par, j):
+            chain = ancestors_or_self(par, int(i))
+            L = len(chain)
+            where_j = depth_j  # j sits at offset depth_j of every chain through it
+            qi = rope(_f64(q[i:i + 1]), [L - 1], theta)[0]
+            kc = rope(_f64(k[chain]), np.arange(L), theta)
+            vc = _f64(v[chain])
+            for b, hk in enumerate(kv_heads):
+                for h in range(hk * G, (hk + 1) * G):
+                    o, _, p = _row(qi[h], kc[:, hk], vc[:, hk], scale)
+                    doi = _f64(do[i, h])
+                    dv[a, b] += p[where_j] * doi
+                    ds_ij = p[where_j] * (vc[where_j, hk] @ doi - doi @ o)
+                    acc_k[b] += ds_ij * qi[h] * scale
+        dk[a] = rope_transpose(acc_k[None], [depth_j], theta)[0]
+    return dk, dv
