@@ -1,0 +1,197 @@
+"""Benchmark of the tree-attention hot path on one MI355X.
+
+A step is one pass of the device hot path over one packed batch: RoPE at
+depth positions + tile plan, tree-masked forward, and backward (dQ, dK, dV),
+through the C ABI. Inputs (q, k, v, dO and the packer's pos / subtree_end)
+are resident in HBM before the timed region. Reported value: visible-pair
+TFLOP/s, 14 * d * P * Hq per step (forward 4, backward 10), P = sum(pos + 1).
+
+Also reported on the same line: the host packer's time (not in the step),
+the tile classification, tree_logprob on 16384 bf16 rows x 151936 vocab with
+every row referenced 3 times (its own timed leg, HBM GB/s), per-kernel HIP
+event timings, the roofline of the dominant kernel and the CPU oracle timed
+on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload multistep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-attn fwd+bwd visible-pair TFLOP/s and % bf16 MFMA peak; packed tokens/s"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0
+
+DESCR = {
+    "short": "short-prompt groups: 8 trees x (256-token prompt + 4 branches x 128), T=6144, 32q/8kv, d=128, bf16",
+    "multistep": "long prompt, multi-step: 4 trees x (1024-token prompt + 8 trajectories x 2 steps "
+                 "[256 resp; +256 tool +256 resp]), T=28672, 32q/8kv, d=128, bf16",
+    "agentic": "random agentic tree, depth<=6, branching U{1,2,3}, segments U{64..1024}, T=32768, 64q/8kv, d=128, bf16",
+    "agentic_l": "random agentic tree, depth<=10, T=131072, 64q/8kv, d=128, bf16",
+}
+
+# algorithmic FLOPs per visible pair and query head, per kernel group, in units of d
+KERNEL_FLOPS = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
+
+
+def cpu_baseline(seqs, groups, cfg):
+    """The float64 oracle (per-branch fwd + bwd) on tree 0 and kv group 0."""
+    import numpy as np
+
+    import workloads
+    from oracle import attention as OA
+    from oracle import pack as OP
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    po = OP.pack(seqs, groups)
+    ts, te = int(po["tree_start"][0]), int(po["tree_start"][1])
+    par = po["par"][ts:te].copy()
+    par[par >= 0] -= ts
+    G = cfg["Hq"] // cfg["Hkv"]
+    q, k, v, do = workloads.dense_inputs(te - ts, G, 1, cfg["d"], "bf16", 77)
+    f = lambda t: t.float().numpy()
+    t0 = time.perf_counter()
+    OA.forward_branches(f(q), f(k), f(v), par, po["pos"][ts:te], check_agree=False)
+    OA.backward_branches(f(q), f(k), f(v), f(do), par, po["pos"][ts:te])
+    dt = time.perf_counter() - t0
+    P = int((po["pos"][ts:te] + 1).sum())
+    flops = 14.0 * cfg["d"] * P * G
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"tree 0 ({te - ts} tokens) x kv group 0 ({G} q heads), fwd+bwd, float64 NumPy, "
+                      f"{dt:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="multistep", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-logprob", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding is a design "
+              "note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_packed_attention_amd as ta
+    import workloads
+
+    dev = torch.device("cuda:0")
+    cfg = workloads.WORKLOADS[args.workload]
+    seqs, groups = workloads.sequences(args.workload)
+    t0 = time.perf_counter()
+    p = ta.tree_pack(seqs, groups)
+    pack_ms = (time.perf_counter() - t0) * 1e3
+    T, Hq, Hkv, d = p["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    P = int((p["pos"].astype(np.int64) + 1).sum())
+    flops = 14.0 * d * P * Hq
+    full, partial, empty, causal = ta.tree_tile_stats(p["subtree_end"], T, 128, 64)
+    print(f"[bench] {args.workload}: T={T} P={P} tiles full/partial/empty={full}/{partial}/{empty}", flush=True)
+
+    q, k, v, do = workloads.dense_inputs(T, Hq, Hkv, d, "bf16", cfg["seed"], device=dev)
+    pos = torch.from_numpy(p["pos"]).to(dev)
+    se = torch.from_numpy(p["subtree_end"]).to(dev)
+    ws = ta.attn_workspace(T, Hq, Hkv, d, True, dev)
+
+    def step():
+        o, lse, _ = ta.tree_attn_fwd(q, k, v, pos, se, workspace=ws)
+        return ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws, reuse_prep=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ta.tree_attn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kern = ta.tree_attn_profile_read()
+    ta.tree_attn_profile_enable(False)
+    ms_step = dt / args.steps * 1e3
+    value = flops * args.steps / dt / 1e12
+    print(f"[bench] attention step {ms_step:.3f} ms, {value:.1f} TFLOP/s", flush=True)
+
+    kernel_ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in kern.items()}
+    dom = max((n for n in kernel_ms if n in KERNEL_FLOPS), key=lambda n: kernel_ms[n])
+    achieved = KERNEL_FLOPS[dom] * d * P * Hq / (kernel_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": KERNEL_FLOPS[dom] * d * P * Hq}
+
+    lp = None
+    if not args.no_logprob:
+        del ws
+        torch.cuda.empty_cache()
+        R, V = 16384, 151936
+        src, tgt, w = workloads.repeated_rows_entries(R, V, 3, 5)
+        z = workloads.logits_input(R, V, "bf16", 5, device=dev)
+        s_t = torch.as_tensor(src, device=dev)
+        t_t = torch.as_tensor(tgt, device=dev)
+        w_t = torch.as_tensor(w, device=dev)
+        lws = torch.empty(ta.library().tree_logprob_workspace_bytes(R, len(src)), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            ta.tree_logprob(z, s_t, t_t, w_t, workspace=lws)
+        torch.cuda.synchronize()
+        ta.tree_attn_profile_enable(True)
+        n_lp = max(3, args.steps // 2)
+        t0 = time.perf_counter()
+        for _ in range(n_lp):
+            ta.tree_logprob(z, s_t, t_t, w_t, workspace=lws)
+        torch.cuda.synchronize()
+        lp_dt = (time.perf_counter() - t0) / n_lp
+        lk = ta.tree_attn_profile_read()
+        ta.tree_attn_profile_enable(False)
+        M = len(src)
+        alg = 2.0 * R * V * 2 + 12.0 * M + 4.0 * R
+        rows_ms = lk["lp_rows"][0] / lk["lp_rows"][1]
+        lp = {"workload": "16384 bf16 rows x 151936 vocab, M=49152 (each row 3x), fused fwd+bwd",
+              "ms": round(lp_dt * 1e3, 4), "gbps": round(alg / lp_dt / 1e9, 1),
+              "row_kernel_ms": round(rows_ms, 4), "row_kernel_gbps": round(2.0 * R * V * 2 / (rows_ms * 1e-3) / 1e9, 1),
+              "hbm_peak_gbps": PEAK_HBM_GBPS,
+              "kernel_ms": {n: round(tot / max(c, 1), 4) for n, (tot, c) in lk.items()}}
+        print(f"[bench] tree_logprob {lp['ms']:.3f} ms, {lp['gbps']:.0f} GB/s", flush=True)
+        del z
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline ...", flush=True)
+        cpu = cpu_baseline(seqs, groups, cfg)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": DESCR[args.workload], "T": T, "visible_pairs": P, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "trees": p["n_trees"], "fwd_bwd_flop": flops},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "packed_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "tiles_128x64": {"full": full, "partial": partial, "empty": empty, "causal": causal,
+                         "skip": round(empty / causal, 4)},
+        "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
+        "pack_ms_host": round(pack_ms, 2),
+        "roofline": roofline, "tree_logprob": lp, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

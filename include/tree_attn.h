@@ -1,0 +1,222 @@
+/*
+ * tree_attn.h - C ABI of the MI355X (gfx950) tree-packed attention library.
+ *
+ * Branching token sequences that share prefixes are merged into one prefix
+ * tree and laid out in depth-first (preorder) order, every tree token once
+ * ("Tree Training", §3.1 Eq. 8; the "Trie packing" page, Step 1; the Claw-R1
+ * "Prefix Tree Merge" page, section 1). Each packed token attends only to its
+ * ancestors and itself ("Trie packing" Step 2; "Tree Training" §3.2, Attention
+ * Mask), and takes RoPE at its depth on its own path ("Trie packing" Step 1;
+ * "Tree Training" §3.2 Eq. 9). In preorder the descendants of token j are
+ * exactly the packed indices in (j, subtree_end[j]), so the mask is the O(T)
+ * rule: key j is visible to query i  iff  j <= i < subtree_end[j].
+ *
+ * Conventions for every entry point
+ *   - Return value: TA_OK (0) or a negative TA_E* code. No C++ exception
+ *     crosses this boundary. tree_attn_last_error() returns a thread-local
+ *     message for the last failure on the calling thread.
+ *   - All arguments are validated on the host before any HIP call; a rejected
+ *     call touches no memory and launches nothing.
+ *   - Nothing is allocated and nothing is freed: every buffer is owned by the
+ *     caller. Device entry points are asynchronous on `stream` (a hipStream_t
+ *     passed as void*, NULL = the default stream) and do not synchronize.
+ *   - Device tensors are contiguous and token-major: q, o, dout, dq are
+ *     [T][Hq][d]; k, v, dk, dv are [T][Hkv][d]; lse is [Hq][T] float32.
+ *     Query head h uses kv head h / (Hq / Hkv).
+ *   - The library keeps no state besides the error string and the opt-in
+ *     profiling table below: calls on different streams with separate
+ *     workspaces may run concurrently.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TA_OK = 0,
+  TA_EINVAL = -1,       /* bad argument: null pointer, bad size or offsets */
+  TA_ECAPACITY = -2,    /* an output capacity is too small; sizes reported */
+  TA_EUNSUPPORTED = -3, /* valid but unsupported shape (e.g. head dim) */
+  TA_EHIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+typedef enum { TA_BF16 = 0, TA_F32 = 1 } ta_dtype;
+
+/* tree_attn_bwd flag: the workspace still holds what tree_attn_fwd put there
+ * for the same q, k, pos, subtree_end, T, heads, d and rope_theta, so the
+ * RoPE and tile-plan pass is skipped. */
+enum { TA_REUSE_PREP = 1 };
+
+/* Thread-local text of the last error ("" if none). Never NULL. */
+const char* tree_attn_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * tree_pack  (HOST)
+ *
+ * Packs token sequences into DFS-serialized prefix trees, one tree per group.
+ * Follows the "Trie packing" page (shared prefixes, depth positions), "Tree
+ * Training" §3.1 (Eq. 2-4: g_t paths through t, weight g_t / K; Eq. 8: DFS
+ * serialization; Eq. 9: positions) and the "Prefix Tree Merge" page, section
+ * 1 (insert, compress single-child chains, preorder ranges).
+ *
+ * Readings fixed here: children are visited in first-insertion order; a new
+ * node (chunk) starts at a tree root, below a fork, and after a token where
+ * an input sequence ends; K is the number of input sequences of the group and
+ * g the number of input sequences containing the token; groups become trees
+ * in order of first appearance; positions restart at 0 in each tree; all
+ * ends are exclusive.
+ *
+ * Inputs (host memory, caller-owned, read only):
+ *   tokens        [seq_offsets[n_seqs]] token ids, any int32 value
+ *   seq_offsets   [n_seqs + 1] int64, seq_offsets[0] == 0, strictly
+ *                 increasing (an empty sequence is TA_EINVAL)
+ *   n_seqs        >= 1
+ *   group_of_seq  [n_seqs] group label per sequence, or NULL (one tree)
+ *   cap_T         capacity of the per-token outputs (T <= seq_offsets[n_seqs])
+ *   cap_nodes     capacity of the per-node outputs (n_nodes <= T)
+ * Outputs (host memory, caller-owned; any may be NULL to skip it):
+ *   packed_ids [T]  token id;    pos [T] depth on its path;
+ *   subtree_end [T] one past its last descendant;  parent [T] (-1 at a root);
+ *   path_count [T]  g;  weight [T] float32 g / K (IEEE round-to-nearest);
+ *   occ_map [seq_offsets[n_seqs]]  packed index of every input token;
+ *   node_start, node_end (exclusive), node_parent (-1 at a root),
+ *   node_subtree_end  [n_nodes];
+ *   tree_start [n_trees + 1] (capacity n_seqs + 1 always suffices);
+ *   sizes  T, n_nodes, n_trees (always filled when non-NULL and the inputs
+ *          are valid, also on TA_ECAPACITY).
+ * Errors: TA_EINVAL (bad inputs), TA_ECAPACITY (cap_T < T or
+ * cap_nodes < n_nodes; nothing but `sizes` is written).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t T;
+  int32_t n_nodes;
+  int32_t n_trees;
+} ta_pack_sizes;
+
+int tree_pack(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+              const int32_t* group_of_seq, int32_t cap_T, int32_t cap_nodes,
+              int32_t* packed_ids, int32_t* pos, int32_t* subtree_end, int32_t* parent,
+              int32_t* path_count, float* weight, int32_t* occ_map,
+              int32_t* node_start, int32_t* node_end, int32_t* node_parent,
+              int32_t* node_subtree_end, int32_t* tree_start, ta_pack_sizes* sizes);
+
+/* ------------------------------------------------------------------------
+ * Tree-masked attention (DEVICE)
+ *
+ * Forward ("Trie packing" Step 3: S = Q K^T / sqrt(d) + M_tree, M_tree = 0
+ * where visible, -inf elsewhere; "Tree Training" §3.2):
+ *   q'_i = R(pos_i) q_i,  k'_j = R(pos_j) k_j        (RoPE, rotate-half)
+ *   S_ij = scale * q'_i . k'_j   for visible pairs  (j <= i < subtree_end[j])
+ *   o_i  = sum_j softmax_j(S_ij) v_j;  lse_i = ln sum_j exp(S_ij)
+ * RoPE: angle(p, k) = p * rope_theta^(-2k/d) rotates dims (k, k + d/2);
+ * rope_theta == 0 disables RoPE. scale <= 0 selects 1/sqrt(d).
+ *
+ * Backward (the "Trie packing" page, "Same chain rule", Step 3: ordinary
+ * attention backward, masked edges contribute nothing; a shared key / value
+ * row collects the gradients of all its descendants):
+ *   dv_j = sum_i P_ij do_i;  dS_ij = P_ij (do_i . v_j - do_i . o_i)
+ *   dq_i = R(pos_i)^T scale sum_j dS_ij k'_j;  dk_j = R(pos_j)^T scale sum_i dS_ij q'_i
+ * with dk and dv summed over the query heads of a kv group. All gradient
+ * accumulation is float32 ("Tree Training" App. B.5); dq, dk, dv are written
+ * once, in the tensor dtype. The result is bitwise reproducible.
+ *
+ * dt: TA_BF16 or TA_F32 for q, k, v, o, dout, dq, dk, dv (TA_F32 inputs are
+ * rounded to bf16 for the matrix products; accumulation stays float32).
+ * d must be 16, 64 or 128 (else TA_EUNSUPPORTED). 1 <= T <= 2^22,
+ * Hq % Hkv == 0, Hq <= 256.
+ * pos, subtree_end: device int32 [T] as produced by tree_pack (a forest of
+ * trees is fine; subtree ends must satisfy i < subtree_end[i] <= T).
+ * workspace: device memory of at least tree_attn_workspace_bytes(...) bytes,
+ * 256-byte aligned; contents are scratch between calls except under
+ * TA_REUSE_PREP.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_EHIP (launch failure).
+ * ---------------------------------------------------------------------- */
+size_t tree_attn_workspace_bytes(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t with_bwd);
+
+int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dtype dt,
+                  int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                  const int32_t* pos, const int32_t* subtree_end,
+                  float softmax_scale, float rope_theta,
+                  void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, ta_dtype dt, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                  const int32_t* pos, const int32_t* subtree_end,
+                  float softmax_scale, float rope_theta, int32_t flags,
+                  void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_logprob  (DEVICE)
+ *
+ * Per-occurrence log-probabilities gathered from shared logit rows, weighted
+ * loss, and the gradient scatter-added into the shared rows (the "Trie
+ * packing" page, "Share logits, preserve every prediction" and "Combine
+ * gradients at the shared logits"; "Tree Training" §3.1 Eq. 4 and §3.2 Loss
+ * Weights):
+ *   lse_r   = ln sum_v exp z[r, v]
+ *   logp_m  = z[src_m, tgt_m] - lse[src_m]
+ *   loss    = -sum_m w_m logp_m
+ *   dlogits[r, :] = grad_scale * sum_{m: src_m = r} w_m (softmax(z_r) - e_{tgt_m})
+ * Rows no entry references get dlogits = 0.
+ *
+ * logits [R][V] (dt TA_BF16 or TA_F32), row-major, device.
+ * src_row, target: device int32 [M]; weight: device float32 [M].
+ * logp [M] float32 (required). row_lse [R] float32 or NULL. loss: device
+ * float32 scalar or NULL. dlogits [R][V] in dt, or NULL for forward only.
+ * An entry with src_row outside [0, R) or target outside [0, V) gets
+ * logp = NaN, contributes NaN to loss, and nothing to dlogits.
+ * The loss and dlogits are summed in a fixed order: bitwise reproducible.
+ * workspace: >= tree_logprob_workspace_bytes(R, M) bytes, 256-byte aligned.
+ * Limits: 1 <= R < 2^31, 1 <= V < 2^31, 0 <= M < 2^31 - 1.
+ * Errors: TA_EINVAL, TA_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t tree_logprob_workspace_bytes(int64_t R, int64_t M);
+
+int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V,
+                 const int32_t* src_row, const int32_t* target, const float* weight, int64_t M,
+                 float* logp, float* row_lse, float* loss,
+                 void* dlogits, float grad_scale,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_tile_stats  (HOST)
+ *
+ * Counts of (query-tile, key-tile) pairs under the tile classification the
+ * kernels use, from a host copy of subtree_end. Tiles are BQ rows x BK keys;
+ * key columns past T are padding that is never visible; only causal tiles
+ * (first key <= last real row) are counted. With i0/i1 the first/one-past-
+ * last real row and j0/j1 = j0 + BK the key range of a tile:
+ *   empty   max(subtree_end over its keys) <= i0
+ *   full    j1 - 1 <= i0 and min(subtree_end over its keys, padding = 0) >= i1
+ *   partial otherwise
+ * An empty tile holds no visible pair and a full tile only visible pairs.
+ * Errors: TA_EINVAL.
+ * ---------------------------------------------------------------------- */
+int tree_tile_stats(const int32_t* subtree_end, int32_t T, int32_t BQ, int32_t BK,
+                    int64_t* full, int64_t* partial, int64_t* empty, int64_t* causal);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (HOST control; for benchmarks and tracing)
+ *
+ * tree_attn_profile_enable(1) clears the table and starts bracketing every
+ * kernel group the library launches (RoPE prep, tile plan, forward, row
+ * dots, dQ, dK/dV, log-prob CSR / rows / loss) with HIP events on the
+ * caller's stream; (0) stops. tree_attn_profile_read(idx, ...) waits for the
+ * recorded events and returns the idx-th kernel group's name, total time in
+ * milliseconds and launch count (TA_EINVAL past the last entry). The table
+ * is process-wide and guarded by a mutex; timings of calls that overlap on
+ * several streams are not meaningful.
+ * ---------------------------------------------------------------------- */
+int tree_attn_profile_enable(int32_t on);
+int tree_attn_profile_read(int32_t idx, char* name, int32_t name_cap, double* total_ms, int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -247,7 +247,8 @@ def backward_keys(q, k, v, do, par, keys, kv_heads=None, scale=None, theta=10000
     """dK and dV for selected keys: sums over the key's descendants-or-self.
 
     dV_j = sum_{h in group} sum_i P_ij dO_i ;  dk'_j = scale * sum dS_ij q'_i,
-    then the inverse rotation at the key's depth. Returns (dk, dv) of shape
+    then the inverse rotation at the key's depth. Every row's softmax runs
+    over its own ancestor chain. Returns (dk, dv) of shape
     [len(keys), len(kv_heads), d].
     """
     T, Hq, d = q.shape
@@ -259,21 +260,32 @@ def backward_keys(q, k, v, do, par, keys, kv_heads=None, scale=None, theta=10000
     dv = np.zeros((len(keys), len(kv_heads), d))
     for a, j in enumerate(keys):
         j = int(j)
-        depth_j = len(ancestors_or_self(par, j)) - 1
+        above = ancestors_or_self(par, j)          # root .. j
+        depth_j = len(above) - 1
+        sub = subtree_rows(par, j)                 # j and its descendants
+        # rotate every row that any chain below j uses, once
+        rows = np.concatenate([above[:-1], sub])
+        depth = {int(x): n for n, x in enumerate(above)}
+        for x in sub:
+            x = int(x)
+            if x != j:
+                depth[x] = depth[int(par[x])] + 1
+        dpos = np.array([depth[int(x)] for x in rows], dtype=np.float64)
+        slot = {int(x): n for n, x in enumerate(rows)}
+        kr = rope(_f64(k[rows]), dpos, theta)
+        vv = _f64(v[rows])
         acc_k = np.zeros((len(kv_heads), d))
-        for i in subtree_rows(par, j):
-            chain = ancestors_or_self(par, int(i))
-            L = len(chain)
-            where_j = depth_j  # j sits at offset depth_j of every chain through it
-            qi = rope(_f64(q[i:i + 1]), [L - 1], theta)[0]
-            kc = rope(_f64(k[chain]), np.arange(L), theta)
-            vc = _f64(v[chain])
+        for i in sub:
+            i = int(i)
+            chain = [slot[int(x)] for x in ancestors_or_self(par, i)]
+            qi = rope(_f64(q[i:i + 1]), [depth[i]], theta)[0]
+            kc, vc = kr[chain], vv[chain]
             for b, hk in enumerate(kv_heads):
                 for h in range(hk * G, (hk + 1) * G):
                     o, _, p = _row(qi[h], kc[:, hk], vc[:, hk], scale)
                     doi = _f64(do[i, h])
-                    dv[a, b] += p[where_j] * doi
-                    ds_ij = p[where_j] * (vc[where_j, hk] @ doi - doi @ o)
+                    dv[a, b] += p[depth_j] * doi
+                    ds_ij = p[depth_j] * (vc[depth_j, hk] @ doi - doi @ o)
                     acc_k[b] += ds_ij * qi[h] * scale
         dk[a] = rope_transpose(acc_k[None], [depth_j], theta)[0]
     return dk, dv

@@ -1,0 +1,320 @@
+"""Python binding of libtreeattn.so, the MI355X (gfx950) tree-packed attention library.
+
+Argument marshalling only: every step runs in the library (the host packer
+and the HIP kernels). PyTorch supplies device memory and the current stream.
+The names follow the C ABI in include/tree_attn.h:
+
+  tree_pack(seqs, groups=None)                     host packer -> dict of numpy arrays
+  tree_tile_stats(subtree_end, T, BQ, BK)          host tile classification counts
+  tree_attn_fwd(q, k, v, pos, subtree_end, ...)    -> (o, lse)
+  tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, ...) -> (dq, dk, dv)
+  tree_logprob(logits, src_row, target, weight, ...) -> (logp, row_lse, loss, dlogits)
+  TreeAttention                                    torch.autograd.Function over fwd/bwd
+
+The library must be built first (python tree_packed_attention_amd/build.py);
+importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
+
+TA_OK, TA_EINVAL, TA_ECAPACITY, TA_EUNSUPPORTED, TA_EHIP = 0, -1, -2, -3, -4
+TA_BF16, TA_F32 = 0, 1
+TA_REUSE_PREP = 1
+
+EXPORTS = (
+    "tree_attn_last_error",
+    "tree_pack",
+    "tree_attn_workspace_bytes",
+    "tree_attn_fwd",
+    "tree_attn_bwd",
+    "tree_logprob_workspace_bytes",
+    "tree_logprob",
+    "tree_tile_stats",
+    "tree_attn_profile_enable",
+    "tree_attn_profile_read",
+)
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python tree_packed_attention_amd/build.py` "
+        "(there is no fallback implementation)"
+    )
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class PackSizes(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("n_nodes", ctypes.c_int32), ("n_trees", ctypes.c_int32)]
+
+
+_lib.tree_attn_last_error.restype = ctypes.c_char_p
+_lib.tree_attn_last_error.argtypes = []
+_lib.tree_pack.restype = ctypes.c_int
+_lib.tree_pack.argtypes = [_p, _p, _i32, _p, _i32, _i32] + [_p] * 12 + [ctypes.POINTER(PackSizes)]
+_lib.tree_attn_workspace_bytes.restype = _sz
+_lib.tree_attn_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.tree_attn_fwd.restype = ctypes.c_int
+_lib.tree_attn_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _f32, _f32,
+                               _p, _p, _p, _sz, _p]
+_lib.tree_attn_bwd.restype = ctypes.c_int
+_lib.tree_attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _f32, _f32,
+                               _i32, _p, _p, _p, _p, _sz, _p]
+_lib.tree_logprob_workspace_bytes.restype = _sz
+_lib.tree_logprob_workspace_bytes.argtypes = [_i64, _i64]
+_lib.tree_logprob.restype = ctypes.c_int
+_lib.tree_logprob.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _f32, _p, _sz, _p]
+_lib.tree_tile_stats.restype = ctypes.c_int
+_lib.tree_tile_stats.argtypes = [_p, _i32, _i32, _i32] + [ctypes.POINTER(ctypes.c_int64)] * 4
+_lib.tree_attn_profile_enable.restype = ctypes.c_int
+_lib.tree_attn_profile_enable.argtypes = [_i32]
+_lib.tree_attn_profile_read.restype = ctypes.c_int
+_lib.tree_attn_profile_read.argtypes = [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
+
+
+def library():
+    """The loaded ctypes handle (for tests of the raw ABI)."""
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.tree_attn_last_error().decode()
+
+
+def _check(rc):
+    if rc != TA_OK:
+        raise TreeAttnError(rc, last_error())
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------- host
+
+
+def tree_pack(seqs, groups=None):
+    """Packs sequences (iterables of ints) into DFS-serialized prefix trees.
+
+    Returns a dict of int32 / float32 numpy arrays: ids, pos, subtree_end,
+    parent, path_count, weight, occ_map (flat) and seq_offsets, node_start,
+    node_end, node_parent, node_subtree_end, tree_start; plus T, n_nodes,
+    n_trees.
+    """
+    lens = [len(s) for s in seqs]
+    offsets = np.zeros(len(seqs) + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(lens)
+    flat = np.zeros(max(int(offsets[-1]), 1), dtype=np.int32)
+    if offsets[-1] > 0:
+        flat[: offsets[-1]] = np.concatenate([np.asarray(s, dtype=np.int64) for s in seqs]).astype(np.int32)
+    grp = None if groups is None else np.ascontiguousarray(groups, dtype=np.int32)
+    total = int(offsets[-1])
+    cap = max(total, 1)
+    out = {k: np.zeros(cap, dtype=np.int32) for k in
+           ("ids", "pos", "subtree_end", "parent", "path_count", "node_start", "node_end", "node_parent",
+            "node_subtree_end")}
+    out["weight"] = np.zeros(cap, dtype=np.float32)
+    out["occ_map"] = np.zeros(cap, dtype=np.int32)
+    out["tree_start"] = np.zeros(len(seqs) + 1, dtype=np.int32)
+    sizes = PackSizes()
+    rc = _lib.tree_pack(_np_ptr(flat), _np_ptr(offsets), len(seqs), _np_ptr(grp), cap, cap,
+                        _np_ptr(out["ids"]), _np_ptr(out["pos"]), _np_ptr(out["subtree_end"]),
+                        _np_ptr(out["parent"]), _np_ptr(out["path_count"]), _np_ptr(out["weight"]),
+                        _np_ptr(out["occ_map"]), _np_ptr(out["node_start"]), _np_ptr(out["node_end"]),
+                        _np_ptr(out["node_parent"]), _np_ptr(out["node_subtree_end"]), _np_ptr(out["tree_start"]),
+                        ctypes.byref(sizes))
+    _check(rc)
+    T, N, R = sizes.T, sizes.n_nodes, sizes.n_trees
+    for key in ("ids", "pos", "subtree_end", "parent", "path_count", "weight"):
+        out[key] = out[key][:T].copy()
+    for key in ("node_start", "node_end", "node_parent", "node_subtree_end"):
+        out[key] = out[key][:N].copy()
+    out["occ_map"] = out["occ_map"][:total].copy()
+    out["tree_start"] = out["tree_start"][: R + 1].copy()
+    out["seq_offsets"] = offsets
+    out.update(T=T, n_nodes=N, n_trees=R)
+    return out
+
+
+def tree_tile_stats(subtree_end, T, BQ, BK):
+    se = np.ascontiguousarray(subtree_end, dtype=np.int32)
+    vals = [ctypes.c_int64() for _ in range(4)]
+    _check(_lib.tree_tile_stats(_np_ptr(se), int(T), int(BQ), int(BK), *[ctypes.byref(v) for v in vals]))
+    return tuple(v.value for v in vals)  # full, partial, empty, causal
+
+
+def tree_attn_profile_enable(on=True):
+    _check(_lib.tree_attn_profile_enable(1 if on else 0))
+
+
+def tree_attn_profile_read():
+    """{kernel group: (total_ms, launches)} recorded since profiling was enabled."""
+    out = {}
+    idx = 0
+    buf = ctypes.create_string_buffer(64)
+    while True:
+        ms, cnt = ctypes.c_double(), ctypes.c_int64()
+        if _lib.tree_attn_profile_read(idx, buf, 64, ctypes.byref(ms), ctypes.byref(cnt)) != TA_OK:
+            return out
+        out[buf.value.decode()] = (ms.value, cnt.value)
+        idx += 1
+
+
+# ---------------------------------------------------------------------------- device
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TA_BF16
+    if t.dtype == torch.float32:
+        return TA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_ptr(t, name, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def attn_workspace(T, Hq, Hkv, d, with_bwd, device):
+    nbytes = _lib.tree_attn_workspace_bytes(T, Hq, Hkv, d, 1 if with_bwd else 0)
+    return _torch().empty(max(nbytes, 256), dtype=_torch().uint8, device=device)
+
+
+def tree_attn_fwd(q, k, v, pos, subtree_end, softmax_scale=0.0, rope_theta=10000.0, workspace=None,
+                  with_bwd_workspace=False):
+    """q [T,Hq,d], k/v [T,Hkv,d] (bf16 or f32, same dtype) -> (o [T,Hq,d], lse [Hq,T] f32).
+
+    Returns (o, lse, workspace); pass the workspace to tree_attn_bwd with
+    reuse_prep=True to skip the RoPE and tile-plan pass there.
+    """
+    torch = _torch()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if workspace is None:
+        workspace = attn_workspace(T, Hq, Hkv, d, with_bwd_workspace, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(Hq, T, dtype=torch.float32, device=dev)
+    rc = _lib.tree_attn_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev), _dt(q),
+                            T, Hq, Hkv, d, _dev_ptr(pos, "pos", torch.int32, dev),
+                            _dev_ptr(subtree_end, "subtree_end", torch.int32, dev), float(softmax_scale),
+                            float(rope_theta), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"),
+                            _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return o, lse, workspace
+
+
+def tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, softmax_scale=0.0, rope_theta=10000.0,
+                  workspace=None, reuse_prep=False):
+    """Gradients (dq, dk, dv) of sum(o * dout); dk/dv summed over each kv group."""
+    torch = _torch()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if workspace is None:
+        if reuse_prep:
+            raise ValueError("reuse_prep needs the forward's workspace")
+        workspace = attn_workspace(T, Hq, Hkv, d, True, dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    rc = _lib.tree_attn_bwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev),
+                            _dev_ptr(o, "o", q.dtype, dev), _dev_ptr(lse, "lse", torch.float32, dev),
+                            _dev_ptr(dout, "dout", q.dtype, dev), _dt(q), T, Hq, Hkv, d,
+                            _dev_ptr(pos, "pos", torch.int32, dev),
+                            _dev_ptr(subtree_end, "subtree_end", torch.int32, dev), float(softmax_scale),
+                            float(rope_theta), TA_REUSE_PREP if reuse_prep else 0, _dev_ptr(dq, "dq"),
+                            _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), _dev_ptr(workspace, "workspace"),
+                            workspace.numel(), _stream(dev))
+    _check(rc)
+    return dq, dk, dv
+
+
+def tree_logprob(logits, src_row, target, weight, grad_scale=1.0, with_grad=True, with_row_lse=True,
+                 workspace=None):
+    """Returns (logp [M] f32, row_lse [R] f32 or None, loss [] f32, dlogits [R,V] or None)."""
+    torch = _torch()
+    R, V = logits.shape
+    M = src_row.numel()
+    dev = logits.device
+    if workspace is None:
+        nbytes = _lib.tree_logprob_workspace_bytes(R, M)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    logp = torch.empty(max(M, 1), dtype=torch.float32, device=dev)
+    row_lse = torch.empty(R, dtype=torch.float32, device=dev) if with_row_lse else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dlogits = torch.empty_like(logits) if with_grad else None
+    null = ctypes.c_void_p(None)
+    rc = _lib.tree_logprob(_dev_ptr(logits, "logits"), _dt(logits), R, V,
+                           _dev_ptr(src_row, "src_row", torch.int32, dev) if M else null,
+                           _dev_ptr(target, "target", torch.int32, dev) if M else null,
+                           _dev_ptr(weight, "weight", torch.float32, dev) if M else null, M,
+                           _dev_ptr(logp, "logp"), _dev_ptr(row_lse, "row_lse") if with_row_lse else null,
+                           _dev_ptr(loss, "loss"), _dev_ptr(dlogits, "dlogits") if with_grad else null,
+                           float(grad_scale), _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return logp[:M], row_lse, loss, dlogits
+
+
+def _make_autograd():
+    torch = _torch()
+
+    class _TreeAttention(torch.autograd.Function):
+        """o = TreeAttention.apply(q, k, v, pos, subtree_end, scale, theta)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, pos, subtree_end, softmax_scale=0.0, rope_theta=10000.0):
+            o, lse, ws = tree_attn_fwd(q, k, v, pos, subtree_end, softmax_scale, rope_theta,
+                                       with_bwd_workspace=True)
+            ctx.save_for_backward(q, k, v, o, lse, pos, subtree_end)
+            ctx.ws = ws
+            ctx.cfg = (softmax_scale, rope_theta)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse, pos, se = ctx.saved_tensors
+            dq, dk, dv = tree_attn_bwd(q, k, v, o, lse, do.contiguous(), pos, se, *ctx.cfg, workspace=ctx.ws,
+                                       reuse_prep=True)
+            ctx.ws = None
+            return dq, dk, dv, None, None, None, None
+
+    return _TreeAttention
+
+
+TreeAttention = _make_autograd()

@@ -1,0 +1,394 @@
+// tree_logprob for gfx950: per-occurrence log-probabilities on shared logit
+// rows, weighted loss, and the gradient scatter-added into the shared rows.
+//
+// The "Trie packing" page ("Share logits, preserve every prediction",
+// "Combine gradients at the shared logits"): a row predicts the token after
+// its node, several occurrences can read one row, and their gradients
+// (p - e_y) add on that row. "Tree Training" §3.1 Eq. 4 / §3.2 Loss Weights:
+// each occurrence carries its weight (g_t / K for the branch-averaged loss).
+//
+// Pipeline (all on the caller's stream):
+//   1. count entries per source row (invalid entries get logp = NaN here)
+//   2. exclusive scan -> CSR row pointers
+//   3. scatter entry ids into their row's CSR range
+//   4. one workgroup per row: read the row once into registers, row max and
+//      sum of exponentials, lse; rank-sort the row's entry ids so every sum
+//      runs in entry order; logp for the row's entries; W_r = sum of weights;
+//      dlogits = s * W_r * softmax(z_r), then the target columns get
+//      s * (W_r p_t - sum of the weights aiming at t)
+//   5. loss = -sum_m w_m logp_m in entry order (one workgroup)
+// The row is read from HBM once and dlogits written once. Sums run in a
+// fixed order, so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ta_device.h"
+#include "profile.h"
+#include "ta_error.h"
+#include "tree_attn.h"
+
+namespace ta {
+namespace {
+
+constexpr int kRowThreads = 1024;
+
+__global__ void lp_zero_kernel(int* __restrict__ a, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = 0;
+}
+
+__device__ __forceinline__ bool entry_ok(int s, int t, int64_t R, int64_t V) {
+  return s >= 0 && (int64_t)s < R && t >= 0 && (int64_t)t < V;
+}
+
+__global__ void lp_count_kernel(const int* __restrict__ src, const int* __restrict__ tgt, int64_t M, int64_t R,
+                                int64_t V, int* __restrict__ cnt, float* __restrict__ logp) {
+  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  const int s = src[m], t = tgt[m];
+  if (entry_ok(s, t, R, V))
+    atomicAdd(&cnt[s], 1);
+  else
+    logp[m] = __builtin_nanf("");
+}
+
+template <typename Tv, typename Op>
+__device__ Tv block_reduce(Tv v, Op op, Tv* red) {
+  // fixed-order reduction: lanes by xor tree, then waves in index order
+  for (int o = 32; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o));
+  const int wv = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  Tv r = red[0];
+  for (int i = 1; i < nw; ++i) r = op(r, red[i]);
+  return r;
+}
+
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct SumOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct ISumOp {
+  __device__ int operator()(int a, int b) const { return a + b; }
+};
+
+// Exclusive scan of cnt[0..R) into ptr[0..R], one workgroup.
+__global__ __launch_bounds__(1024) void lp_scan_kernel(const int* __restrict__ cnt, int64_t R, int* __restrict__ ptr) {
+  __shared__ int red[16];
+  __shared__ int wave_off[16];
+  const int tid = threadIdx.x;
+  const int64_t per = (R + blockDim.x - 1) / blockDim.x;
+  const int64_t b = tid * per;
+  const int64_t e = b + per < R ? b + per : R;
+  int local = 0;
+  for (int64_t i = b; i < e; ++i) local += cnt[i];
+  // inclusive scan of per-thread sums across the workgroup
+  int x = local;
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[wv] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+      wave_off[i] = acc;
+      acc += red[i];
+    }
+  }
+  __syncthreads();
+  int run = wave_off[wv] + x - local;
+  for (int64_t i = b; i < e; ++i) {
+    ptr[i] = run;
+    run += cnt[i];
+  }
+  if (tid == (int)blockDim.x - 1) ptr[R] = wave_off[wv] + x;
+}
+
+__global__ void lp_fill_kernel(const int* __restrict__ src, const int* __restrict__ tgt, int64_t M, int64_t R,
+                               int64_t V, const int* __restrict__ ptr, int* __restrict__ fill, int* __restrict__ ids) {
+  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  const int s = src[m], t = tgt[m];
+  if (!entry_ok(s, t, R, V)) return;
+  const int slot = ptr[s] + atomicAdd(&fill[s], 1);
+  ids[slot] = (int)m;
+}
+
+template <typename T>
+struct Vec16;  // 16 bytes of logits
+template <>
+struct Vec16<bf16> {
+  static constexpr int N = 8;
+  typedef bf16x8 type;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  typedef f32x4 type;
+};
+
+// Rows of the CSR range [beg, beg + n): rank-sort the ids (all distinct) into
+// `sorted`, then logp, W_r and the per-target corrections in entry order.
+template <typename T>
+__device__ void row_entries(const T* __restrict__ row, int beg, int n, const int* __restrict__ ids,
+                            int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w,
+                            float lse, float* __restrict__ logp, float* red, float* W_out) {
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int id = ids[beg + e];
+    int rank = 0;
+    for (int f = 0; f < n; ++f) rank += ids[beg + f] < id;
+    sorted[beg + rank] = id;
+  }
+  __syncthreads();
+  float ws = 0.0f;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int m = sorted[beg + e];
+    logp[m] = to_f32(row[tgt[m]]) - lse;
+    ws += w[m];
+  }
+  *W_out = block_reduce(ws, SumOp(), red);
+}
+
+template <typename T>
+__device__ void row_corrections(const T* __restrict__ row, int beg, int n, const int* __restrict__ sorted,
+                                const int* __restrict__ tgt, const float* __restrict__ w, float lse, float W,
+                                float gs, T* __restrict__ drow) {
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int t = tgt[sorted[beg + e]];
+    bool first = true;
+    for (int f = 0; f < e; ++f) first = first && (tgt[sorted[beg + f]] != t);
+    if (!first) continue;
+    float tot = 0.0f;
+    for (int f = e; f < n; ++f) {
+      const int m = sorted[beg + f];
+      if (tgt[m] == t) tot += w[m];
+    }
+    const float p = __builtin_amdgcn_exp2f((to_f32(row[t]) - lse) * kLog2e);
+    drow[t] = from_f32<T>(gs * (W * p) - gs * tot);
+  }
+}
+
+// Row kernel with the row held in registers: NV 16-byte vectors per thread.
+template <typename T, int NV>
+__global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
+    const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
+    int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w, float* __restrict__ logp,
+    float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
+  typedef typename Vec16<T>::type vec;
+  constexpr int EPV = Vec16<T>::N;
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const int beg = ptr[r], n = ptr[r + 1] - beg;
+  if (n == 0 && !need_all_rows) return;
+  const T* row = logits + r * V;
+  const int64_t nvec = V / EPV;
+  vec x[NV];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
+    if (vi < nvec) {
+      x[k] = reinterpret_cast<const vec*>(row)[vi];
+#pragma unroll
+      for (int s = 0; s < EPV; ++s) mx = fmaxf(mx, to_f32(x[k][s]));
+    }
+  }
+  mx = block_reduce(mx, MaxOp(), red);
+  float se = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
+    if (vi < nvec) {
+#pragma unroll
+      for (int s = 0; s < EPV; ++s) se += __builtin_amdgcn_exp2f((to_f32(x[k][s]) - mx) * kLog2e);
+    }
+  }
+  se = block_reduce(se, SumOp(), red);
+  const float lse = mx + logf(se);
+  if (row_lse != nullptr && threadIdx.x == 0) row_lse[r] = lse;
+  float W = 0.0f;
+  row_entries(row, beg, n, ids, sorted, tgt, w, lse, logp, red, &W);
+  if (dlogits == nullptr) return;
+  T* drow = dlogits + r * V;
+  const float sw = gs * W;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
+    if (vi < nvec) {
+      vec g;
+#pragma unroll
+      for (int s = 0; s < EPV; ++s)
+        g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
+      reinterpret_cast<vec*>(drow)[vi] = g;
+    }
+  }
+  __syncthreads();
+  row_corrections(row, beg, n, sorted, tgt, w, lse, W, gs, drow);
+}
+
+// Row kernel for any V and alignment: streams the row twice (the second
+// read is served by the caches).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void lp_row_stream_kernel(
+    const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
+    int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w, float* __restrict__ logp,
+    float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const int beg = ptr[r], n = ptr[r + 1] - beg;
+  if (n == 0 && !need_all_rows) return;
+  const T* row = logits + r * V;
+  float m = -__builtin_inff(), s = 0.0f;
+  for (int64_t c = threadIdx.x; c < V; c += blockDim.x) {
+    const float x = to_f32(row[c]);
+    if (x > m) {
+      s = s * __builtin_amdgcn_exp2f((m - x) * kLog2e) + 1.0f;
+      m = x;
+    } else {
+      s += __builtin_amdgcn_exp2f((x - m) * kLog2e);
+    }
+  }
+  const float gm = block_reduce(m, MaxOp(), red);
+  float sc = (m == -__builtin_inff()) ? 0.0f : s * __builtin_amdgcn_exp2f((m - gm) * kLog2e);
+  sc = block_reduce(sc, SumOp(), red);
+  const float lse = gm + logf(sc);
+  if (row_lse != nullptr && threadIdx.x == 0) row_lse[r] = lse;
+  float W = 0.0f;
+  row_entries(row, beg, n, ids, sorted, tgt, w, lse, logp, red, &W);
+  if (dlogits == nullptr) return;
+  T* drow = dlogits + r * V;
+  const float sw = gs * W;
+  for (int64_t c = threadIdx.x; c < V; c += blockDim.x)
+    drow[c] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(row[c]) - lse) * kLog2e));
+  __syncthreads();
+  row_corrections(row, beg, n, sorted, tgt, w, lse, W, gs, drow);
+}
+
+__global__ __launch_bounds__(1024) void lp_loss_kernel(const float* __restrict__ logp, const float* __restrict__ w,
+                                                       int64_t M, float* __restrict__ loss) {
+  __shared__ float red[16];
+  float acc = 0.0f;
+  for (int64_t m = threadIdx.x; m < M; m += blockDim.x) acc += w[m] * logp[m];
+  acc = block_reduce(acc, SumOp(), red);
+  if (threadIdx.x == 0) *loss = -acc;
+}
+
+struct LpLayout {
+  size_t off_cnt, off_ptr, off_fill, off_ids, off_sorted, total;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+LpLayout lp_layout(int64_t R, int64_t M) {
+  LpLayout L{};
+  size_t o = 0;
+  L.off_cnt = o;
+  o = al256(o + (size_t)R * 4);
+  L.off_ptr = o;
+  o = al256(o + (size_t)(R + 1) * 4);
+  L.off_fill = o;
+  o = al256(o + (size_t)R * 4);
+  L.off_ids = o;
+  o = al256(o + (size_t)(M > 0 ? M : 1) * 4);
+  L.off_sorted = o;
+  o = al256(o + (size_t)(M > 0 ? M : 1) * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T, int NV>
+void launch_reg(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const float* w,
+                float* logp, float* row_lse, void* dlogits, float gs, int need_all, hipStream_t st) {
+  hipLaunchKernelGGL((lp_row_reg_kernel<T, NV>), dim3((unsigned)R), dim3(kRowThreads), 0, st,
+                     static_cast<const T*>(logits), V, reinterpret_cast<const int*>(ws + L.off_ptr),
+                     reinterpret_cast<const int*>(ws + L.off_ids), reinterpret_cast<int*>(ws + L.off_sorted), tgt, w,
+                     logp, row_lse, static_cast<T*>(dlogits), gs, need_all);
+}
+
+template <typename T>
+void launch_rows(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const float* w,
+                 float* logp, float* row_lse, void* dlogits, float gs, hipStream_t st) {
+  constexpr int EPV = 16 / sizeof(T);
+  const int need_all = (row_lse != nullptr || dlogits != nullptr) ? 1 : 0;
+  const bool aligned = (V * (int64_t)sizeof(T)) % 16 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
+                       (dlogits == nullptr || reinterpret_cast<uintptr_t>(dlogits) % 16 == 0);
+  const int64_t nvec_per_thread = (V / EPV + kRowThreads - 1) / kRowThreads;
+  if (aligned && nvec_per_thread <= 20) {
+    if (nvec_per_thread <= 1) return launch_reg<T, 1>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nvec_per_thread <= 2) return launch_reg<T, 2>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nvec_per_thread <= 4) return launch_reg<T, 4>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nvec_per_thread <= 8) return launch_reg<T, 8>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nvec_per_thread <= 12) return launch_reg<T, 12>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nvec_per_thread <= 16) return launch_reg<T, 16>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    return launch_reg<T, 20>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+  }
+  hipLaunchKernelGGL(lp_row_stream_kernel<T>, dim3((unsigned)R), dim3(kRowThreads), 0, st,
+                     static_cast<const T*>(logits), V, reinterpret_cast<const int*>(ws + L.off_ptr),
+                     reinterpret_cast<const int*>(ws + L.off_ids), reinterpret_cast<int*>(ws + L.off_sorted), tgt, w,
+                     logp, row_lse, static_cast<T*>(dlogits), gs, need_all);
+}
+
+}  // namespace
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" size_t tree_logprob_workspace_bytes(int64_t R, int64_t M) {
+  if (R < 1 || M < 0) return 0;
+  return lp_layout(R, M).total;
+}
+
+extern "C" int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
+                            const int32_t* target, const float* weight, int64_t M, float* logp, float* row_lse,
+                            float* loss, void* dlogits, float grad_scale, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  clear_error();
+  if (R < 1 || R >= INT32_MAX || V < 1 || V >= INT32_MAX || M < 0 || M >= INT32_MAX - 1)
+    return fail(TA_EINVAL, "tree_logprob: need 1 <= R, V < 2^31 and 0 <= M < 2^31-1 (R=%lld V=%lld M=%lld)",
+                (long long)R, (long long)V, (long long)M);
+  if (!logits || !workspace || (M > 0 && (!src_row || !target || !weight || !logp)))
+    return fail(TA_EINVAL, "tree_logprob: NULL pointer argument");
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_logprob: bad dtype %d", (int)dt);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TA_EINVAL, "tree_logprob: workspace must be 256-byte aligned");
+  const LpLayout L = lp_layout(R, M);
+  if (ws_bytes < L.total)
+    return fail(TA_EINVAL, "tree_logprob: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int* cnt = reinterpret_cast<int*>(ws + L.off_cnt);
+  int* fill = reinterpret_cast<int*>(ws + L.off_fill);
+  {
+  ProfScope ps("lp_csr", st);
+  hipLaunchKernelGGL(lp_zero_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, cnt, R);
+  hipLaunchKernelGGL(lp_zero_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, fill, R);
+  if (M > 0)
+    hipLaunchKernelGGL(lp_count_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, src_row, target, M, R, V,
+                       cnt, logp);
+  hipLaunchKernelGGL(lp_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, R, reinterpret_cast<int*>(ws + L.off_ptr));
+  if (M > 0)
+    hipLaunchKernelGGL(lp_fill_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, src_row, target, M, R, V,
+                       reinterpret_cast<const int*>(ws + L.off_ptr), fill, reinterpret_cast<int*>(ws + L.off_ids));
+  }
+  {
+  ProfScope ps("lp_rows", st);
+  if (dt == TA_BF16)
+    launch_rows<bf16>(R, logits, V, ws, L, target, weight, logp, row_lse, dlogits, grad_scale, st);
+  else
+    launch_rows<float>(R, logits, V, ws, L, target, weight, logp, row_lse, dlogits, grad_scale, st);
+  }
+  if (loss != nullptr) {
+    ProfScope ps("lp_loss", st);
+    hipLaunchKernelGGL(lp_loss_kernel, dim3(1), dim3(1024), 0, st, logp, weight, M, loss);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TA_EHIP, "tree_logprob: kernel launch failed: %s", hipGetErrorString(e));
+  return TA_OK;
+}

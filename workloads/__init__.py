@@ -129,8 +129,24 @@ def random_tree_structure(seed, max_depth, budget, seg_lo=64, seg_hi=1024, max_t
     raise RuntimeError("no tree reached the budget")
 
 
-def _random_tree_sequences(seed, max_depth, budget):
-    children, lengths, accepted = random_tree_structure(seed, max_depth, budget)
+def random_tree(seed, max_depth, budget, seg_lo=64, seg_hi=1024):
+    """Sequences of one random tree from random_tree_structure (DFS leaf order)."""
+    seqs, groups, _ = _random_tree_sequences(seed, max_depth, budget, seg_lo, seg_hi)
+    return seqs, groups
+
+
+def random_forest(seed, budgets, max_depth=4, seg_lo=8, seg_hi=120):
+    """Several random trees, one group each, for multi-tile tests."""
+    seqs, groups = [], []
+    for t, b in enumerate(budgets):
+        s, _ = random_tree(seed * 101 + t, max_depth, b, seg_lo, seg_hi)
+        seqs += s
+        groups += [t] * len(s)
+    return seqs, groups
+
+
+def _random_tree_sequences(seed, max_depth, budget, seg_lo=64, seg_hi=1024):
+    children, lengths, accepted = random_tree_structure(seed, max_depth, budget, seg_lo, seg_hi)
     rng = np.random.default_rng(accepted + 7919)
     segs = [None] * len(lengths)
     segs[0] = _segment(rng, lengths[0])
