@@ -54,6 +54,10 @@ if not os.path.exists(LIB_PATH):
         "(there is no fallback implementation)"
     )
 
+# torch ships its own HIP runtime under the same soname; loading torch first
+# makes the library bind to that one runtime instead of a second copy.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _p, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 

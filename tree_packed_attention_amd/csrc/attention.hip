@@ -154,23 +154,6 @@ __global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm
   if (lane == 0) counts[qt] = n;
 }
 
-// D_i = sum_d dO_i[d] * O_i[d] per (head, row); rows past T get 0.
-template <typename Tio>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const Tio* __restrict__ o, const Tio* __restrict__ dout,
-                                                         int T, int Tp, int Hq, int D, float* __restrict__ dd) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)Tp * Hq) return;
-  const int i = (int)(idx / Hq);
-  const int h = (int)(idx % Hq);
-  float acc = 0.0f;
-  if (i < T) {
-    const Tio* a = o + ((size_t)i * Hq + h) * D;
-    const Tio* b = dout + ((size_t)i * Hq + h) * D;
-    for (int c = 0; c < D; ++c) acc += to_f32(a[c]) * to_f32(b[c]);
-  }
-  dd[(size_t)h * Tp + i] = acc;
-}
-
 // Loads 8 elements [c, c+8) of a caller row; zero past the row end or for
 // rows past T.
 template <typename Tio>
@@ -311,7 +294,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 
 // ------------------------------------------------------------------------
 // Backward dQ. Same shape as the forward: a workgroup owns 128 query rows of
-// one head and loops over their non-empty key tiles.
+// one head and loops over their non-empty key tiles. It first forms
+// D_i = dO_i . O_i from the dO operand registers it holds anyway and stores
+// it for the dK/dV kernel.
 //   S^T = K' Q'^T,  P^T = exp2(S^T * scale*log2e - lse*log2e)
 //   dP^T = V dO^T,  dS^T = P^T (dP^T - D)
 //   dQ'^T += K'^T dS^T  (A operand read transposed from the K' tile)
@@ -319,10 +304,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 template <int DP, typename Tio>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const Tio* __restrict__ v,
-    const Tio* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dd,
-    const int* __restrict__ se, const int* __restrict__ counts, const int* __restrict__ lists,
-    const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nq, int nk, float sl2,
-    float scale, Tio* __restrict__ dq) {
+    const Tio* __restrict__ o, const Tio* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ dd, const int* __restrict__ se, const int* __restrict__ counts,
+    const int* __restrict__ lists, const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nq,
+    int nk, float sl2, float scale, Tio* __restrict__ dq) {
   constexpr int D = DP == 32 ? 16 : DP;
   constexpr int BK = kFwdBK;
   constexpr int KS = DP / 16;
@@ -345,17 +330,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const bool qok = qrow < T;
 
   bf16x8 qop[KS], dop[KS];
+  float dval = 0.0f;
   {
     const bf16* qb = qr + ((size_t)h * Tp + qrow) * DP + 8 * lg;
-    const Tio* db = dout + ((size_t)(qok ? qrow : 0) * Hq + h) * D;
+    const size_t roff = ((size_t)(qok ? qrow : 0) * Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qop[s] = load8(qb + 16 * s);
-      dop[s] = load_row8(db, qok, 16 * s + 8 * lg, D);
+      dop[s] = load_row8(dout + roff, qok, 16 * s + 8 * lg, D);
+      const bf16x8 ov = load_row8(o + roff, qok, 16 * s + 8 * lg, D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dval += (float)dop[s][e] * (float)ov[e];
     }
   }
+  dval += __shfl_xor(dval, 32);
+  if (lg == 0) dd[(size_t)h * Tp + qrow] = dval;
   const float lse2 = qok ? lse[(size_t)h * T + qrow] * kLog2e : 0.0f;
-  const float dval = dd[(size_t)h * Tp + qrow];
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -704,19 +694,12 @@ int run_fwd(const AttnLayout& L, const void* v, const int* se, float sl2, void* 
 template <int DP, typename Tio>
 int run_bwd(const AttnLayout& L, const void* v, const void* o, const float* lse, const void* dout, const int* se,
             float sl2, float scale, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
-  const int64_t n = (int64_t)L.Tp * L.Hq;
-  {
-  ProfScope ps("bwd_rowdot", st);
-  hipLaunchKernelGGL(bwd_rowdot_kernel<Tio>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const Tio*>(o), static_cast<const Tio*>(dout), L.T, L.Tp, L.Hq, L.D,
-                     reinterpret_cast<float*>(ws + L.off_dd));
-  }
   {
   ProfScope ps("attn_bwd_dq", st);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st,
                      reinterpret_cast<const bf16*>(ws + L.off_qr), reinterpret_cast<const bf16*>(ws + L.off_kr),
-                     static_cast<const Tio*>(v), static_cast<const Tio*>(dout), lse,
-                     reinterpret_cast<const float*>(ws + L.off_dd), se,
+                     static_cast<const Tio*>(v), static_cast<const Tio*>(o), static_cast<const Tio*>(dout), lse,
+                     reinterpret_cast<float*>(ws + L.off_dd), se,
                      reinterpret_cast<const int*>(ws + L.off_qcount), reinterpret_cast<const int*>(ws + L.off_qlist),
                      reinterpret_cast<const float2*>(ws + L.off_cs), L.T, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64,
                      sl2, scale, static_cast<Tio*>(dq));
