@@ -81,6 +81,8 @@ def main():
     ap.add_argument("--workload", default="multistep", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run a plain device copy of this many bytes (calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding is a design "
@@ -94,6 +96,14 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.copy_bytes > 0:
+        a = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_bytes} bytes x 3", flush=True)
+        del a, b
     cfg = workloads.WORKLOADS[args.workload]
     seqs, groups = workloads.sequences(args.workload)
     t0 = time.perf_counter()

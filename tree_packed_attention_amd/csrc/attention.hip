@@ -7,62 +7,126 @@
 // "Tree Training" §3.2 (attend iff j <= i and both lie on one root-to-leaf
 // path), expressed with O(T) metadata instead of a (T, T) mask.
 //
-// Layouts (all tiles staged in LDS in natural row-major order):
+// Layouts:
 //   q, o, dout, dq  [T][Hq][D] (caller, bf16 or f32)
 //   k, v, dk, dv    [T][Hkv][D]
 //   lse             [Hq][T] f32
-// workspace:
-//   qr [Hq][Tp][DP], kr [Hkv][Tp][DP]  bf16, RoPE applied, rows >= T and
-//                                       columns >= D zero (DP = max(D, 32))
+// workspace (Tp = T rounded up to 128, DP = max(D, 32); padding is zero):
+//   qr [Hq][Tp][DP], kr, vr [Hkv][Tp][DP]  bf16; q, k rotated by RoPE
+//   sep [Tp]                             subtree ends, 0 past T
 //   cs [Tp][D/2] float2                  cos / sin of every token's angles
-//   kmm64 [nk64] int2, kmm128 [nk128]   min / max subtree end per key tile
-//   qcount [nq], qlist [nq][nk64]       non-empty key tiles per query tile
-//                                       (2 * tile + full flag), ascending
-//   dd [Hq][Tp] f32                      rowsum(dO * O) for the backward
+//   kmm64 [nk64], kmm128 [nk128] int2    min / max subtree end per key tile
+//   qcount, qorder [nq]; qlist [nq][nk64] non-empty 64-key tiles per 128-row
+//                                        query tile (2 * tile + full flag);
+//                                        qorder = query tiles, heaviest first
+//   kwork, korder [nk128]                dK/dV work per 128-key tile, order
+//   dd, l2 [Hq][Tp] f32                  rowsum(dO * O) and lse * log2(e)
+//   dor [Hq][Tp][DP] bf16                dO, head-major (written by dQ pass)
 //
 // Products use v_mfma_f32_32x32x16_bf16 with float32 accumulation. The
 // forward and dQ kernels work on S^T (keys x queries): each lane then owns
 // one query column, so softmax statistics reduce inside the lane plus one
 // exchange with the lane 32 away, and the probabilities feed the next MFMA
-// as its B operand without any data movement (key rows are fed to the first
-// MFMA in bit-2/bit-3 swapped order so the C layout matches the B layout).
+// as its B operand without any data movement (the key rows of a tile sit in
+// LDS in bit-2/bit-3 swapped order so that the C layout of the first product
+// matches the B layout of the second).
+//
+// Tiles move HBM -> LDS with global_load_lds_dwordx4 (no register staging),
+// double buffered: the loads for tile i+1 are in flight while tile i is
+// computed. Each 64-row tile is stored without padding; 16-byte chunk c of
+// row r sits at chunk c ^ swz(r), which keeps both the 16-byte operand reads
+// (8 consecutive rows, one chunk) and the transposing 8-byte reads (4
+// consecutive rows, two adjacent chunks) free of bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include <climits>
 #include <cstdint>
 
-#include "ta_device.h"
 #include "profile.h"
+#include "ta_device.h"
 #include "ta_error.h"
 #include "tree_attn.h"
 
 namespace ta {
 namespace {
 
-constexpr int kFwdBQ = 128;   // query rows per forward / dQ workgroup (4 waves x 32)
-constexpr int kFwdBK = 64;    // keys per forward / dQ iteration
-constexpr int kBwdBK = 128;   // keys per dK/dV workgroup (4 waves x 32)
-constexpr int kBwdBQ = 64;    // query rows per dK/dV iteration
+constexpr int kFwdBQ = 128;  // query rows per forward / dQ workgroup (4 waves x 32)
+constexpr int kFwdBK = 64;   // keys per forward / dQ iteration
+constexpr int kBwdBK = 128;  // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kBwdBQ = 64;   // query rows per dK/dV iteration
 constexpr float kNegInf = -__builtin_inff();
+// Lazy rescaling: the running maximum used as the softmax reference is only
+// raised when a tile's maximum exceeds it by more than 2^8 (log2 units), so
+// probabilities stay <= 256 and the O accumulator is rarely touched.
+constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ int perm_row(int r) { return (r & ~31) | swap23(r & 31); }
 
-// Key (or query) index, inside a 64-row tile, of C register i of M-block mb
-// for lane group lg, when the A operand rows were fed in swap23 order.
+// Key (or query) index inside a 64-row tile of C register i of M-block mb
+// for lane group lg, when the A operand rows were fed in perm_row order.
 __device__ __forceinline__ int c_row(int mb, int i, int lg) {
   return 32 * mb + 16 * (i >> 3) + 8 * lg + 4 * ((i >> 2) & 1) + (i & 3);
 }
 
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Element offset of (row, col) in a swizzled [64][DP] bf16 tile (col % 4 == 0).
+template <int DP>
+__device__ __forceinline__ int toff(int row, int col) {
+  constexpr int CH = DP / 8;
+  return row * DP + ((((col >> 3) ^ swz(row)) & (CH - 1)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
+
+// Each lane copies 16 bytes from g to (wave-uniform) dst + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 16, 0, 0);
+}
+// Each lane copies 4 bytes from g to (wave-uniform) dst + 4 * lane.
+__device__ __forceinline__ void dma4(const void* g, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copies 64 head-major rows [row0 + rowmap(r)] of a [*][DP] bf16 array into a
+// swizzled LDS tile. Each wave issues DP/32 16-byte-per-lane instructions;
+// every lane's offset inside the 64-row block is fixed, so it is computed once.
+template <int DP, bool PERM>
+struct TileDma {
+  static constexpr int CH = DP / 8;  // 16-byte chunks per row
+  static constexpr int NI = CH / 4;  // instructions per wave
+  int off[NI];
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int p = (w + 4 * j) * 64 + lane;
+      const int r = p / CH;
+      const int c = ((p % CH) ^ swz(r)) & (CH - 1);
+      off[j] = (PERM ? perm_row(r) : r) * DP + 8 * c;
+    }
+  }
+  // rows: the global address of row row0 of the source; w: wave index (uniform)
+  __device__ __forceinline__ void issue(const bf16* rows, bf16* tile, int w) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) dma16(rows + off[j], tile + (w + 4 * j) * 512);
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds128(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
 // ------------------------------------------------------------------------
-// Prep: RoPE on q and k into the padded head-major workspace, and the cos /
-// sin table. Angles are formed and reduced in float64, then evaluated in
-// float32 on [-pi, pi].
+// Prep: RoPE on q and k, the padded bf16 copy of v, the padded subtree ends
+// and the cos / sin table. Angles are formed and reduced in float64, then
+// evaluated in float32 on [-pi, pi].
 template <typename Tin>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
-                                                        const int* __restrict__ pos, int T, int Tp, int Hq,
-                                                        int Hkv, int D, int DP, float theta,
-                                                        bf16* __restrict__ qr, bf16* __restrict__ kr,
-                                                        float2* __restrict__ cs) {
+                                                        const Tin* __restrict__ v, const int* __restrict__ pos,
+                                                        const int* __restrict__ se, int T, int Tp, int Hq,
+                                                        int Hkv, int D, int DP, float theta, bf16* __restrict__ qr,
+                                                        bf16* __restrict__ kr, bf16* __restrict__ vr,
+                                                        int* __restrict__ sep, float2* __restrict__ cs) {
   __shared__ float2 tab[64];
   const int t = blockIdx.x;
   const int half = D / 2;
@@ -78,20 +142,26 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
     tab[threadIdx.x] = make_float2(c, s);
     cs[(size_t)t * half + threadIdx.x] = make_float2(c, s);
   }
+  if (threadIdx.x == 0) sep[t] = t < T ? se[t] : 0;
   __syncthreads();
-  const int H = Hq + Hkv;
-  const int per_head = DP / 2;  // pairs (kk, kk + half) for kk < half; zero fill beyond D
+  const int H = Hq + 2 * Hkv;
+  const int per_head = DP / 2;  // element pairs (kk, kk + half) for kk < half; zero fill past D
   for (int idx = threadIdx.x; idx < H * per_head; idx += blockDim.x) {
     const int h = idx / per_head;
     const int kk = idx % per_head;
     const Tin* src;
     bf16* dst;
+    bool rotate = true;
     if (h < Hq) {
       src = q + ((size_t)t * Hq + h) * D;
       dst = qr + ((size_t)h * Tp + t) * DP;
-    } else {
+    } else if (h < Hq + Hkv) {
       src = k + ((size_t)t * Hkv + (h - Hq)) * D;
       dst = kr + ((size_t)(h - Hq) * Tp + t) * DP;
+    } else {
+      src = v + ((size_t)t * Hkv + (h - Hq - Hkv)) * D;
+      dst = vr + ((size_t)(h - Hq - Hkv) * Tp + t) * DP;
+      rotate = false;
     }
     if (kk < half) {
       float x1 = 0.0f, x2 = 0.0f;
@@ -99,9 +169,14 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
         x1 = to_f32(src[kk]);
         x2 = to_f32(src[kk + half]);
       }
-      const float2 c = tab[kk];
-      dst[kk] = (bf16)(x1 * c.x - x2 * c.y);
-      dst[kk + half] = (bf16)(x2 * c.x + x1 * c.y);
+      if (rotate) {
+        const float2 c = tab[kk];
+        dst[kk] = (bf16)(x1 * c.x - x2 * c.y);
+        dst[kk + half] = (bf16)(x2 * c.x + x1 * c.y);
+      } else {
+        dst[kk] = (bf16)x1;
+        dst[kk + half] = (bf16)x2;
+      }
     } else {
       // DP > D only for D = 16: columns D..DP-1 are zero padding
       dst[D + 2 * (kk - half)] = (bf16)0.0f;
@@ -154,6 +229,34 @@ __global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm
   if (lane == 0) counts[qt] = n;
 }
 
+// Work of a dK/dV key tile: the number of 64-row query blocks it can see.
+__global__ __launch_bounds__(256) void k_work_kernel(const int2* __restrict__ kmm, int nk, int* __restrict__ work) {
+  const int kt = blockIdx.x * blockDim.x + threadIdx.x;
+  if (kt >= nk) return;
+  work[kt] = (kmm[kt].y + kBwdBQ - 1) / kBwdBQ - (kt * kBwdBK) / kBwdBQ;
+}
+
+// Tile indices sorted by work, heaviest first (counting sort on the work
+// clipped to 1023). The order within one work value is arbitrary; it only
+// affects scheduling, never results.
+__global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ work, int n, int* __restrict__ order) {
+  __shared__ int hist[1024];
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[min(work[i], 1023)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int b = 1023; b >= 0; --b) {
+      const int c = hist[b];
+      hist[b] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) order[atomicAdd(&hist[min(work[i], 1023)], 1)] = i;
+}
+
 // Loads 8 elements [c, c+8) of a caller row; zero past the row end or for
 // rows past T.
 template <typename Tio>
@@ -164,31 +267,123 @@ __device__ __forceinline__ bf16x8 load_row8(const Tio* rowp, bool row_ok, int c,
 // ------------------------------------------------------------------------
 // Forward. One workgroup = 128 query rows of one head (4 waves x 32 rows),
 // looping over the query tile's non-empty 64-key tiles.
+struct FwdState {
+  float mref, lsum;
+};
+
+template <int DP>
+__device__ __forceinline__ void fwd_issue(const TileDma<DP, true>& kd, const TileDma<DP, false>& vd,
+                                          const bf16* kg, const bf16* vg, const int* sep, int j0, bf16* kb,
+                                          bf16* vb, int* sb, int w, int lane) {
+  kd.issue(kg + (size_t)j0 * DP, kb, w);
+  vd.issue(vg + (size_t)j0 * DP, vb, w);
+  if (w == 0) dma4(sep + j0 + lane, sb);
+}
+
+// One key tile: S^T = K' Q'^T, mask, lazy-rescaled online softmax, O^T += V^T P^T.
+template <int DP>
+__device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const int* sb, bool full, int j0, int qrow,
+                                         int lane, int lg, int lc, float sl2, const bf16x8* qop, f32x16* acc,
+                                         FwdState& st) {
+  constexpr int KS = DP / 16;
+  constexpr int NDB = DP / 32;
+  f32x16 s[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      s[mb] = mfma32x32x16(lds128(kb + toff<DP>(32 * mb + lc, 16 * k + 8 * lg)), qop[k], s[mb]);
+  }
+  if (!full) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int kk0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
+        const int4 s4 = *reinterpret_cast<const int4*>(sb + kk0);
+        const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bool vis = (j0 + kk0 + b <= qrow) & (qrow < sv[b]);
+          s[mb][4 * q4 + b] = vis ? s[mb][4 * q4 + b] : kNegInf;
+        }
+      }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mt2 = mx * sl2;
+  if (__any(mt2 > st.mref + kRescaleLog2)) {
+    const float mnew = fmaxf(st.mref, mt2);
+    const float alpha = (st.mref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(st.mref - mnew);
+    st.mref = mnew;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+  }
+  const float nmu = (st.mref == kNegInf) ? 0.0f : -st.mref;
+  float ps = 0.0f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, nmu));
+      ps += p;
+      pb[2 * mb + (i >> 3)][i & 7] = (bf16)p;
+    }
+  st.lsum += ps;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = 16 * t + 8 * lg + ((lane & 15) >> 2);
+      const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const bf16x8 a = cat(lds_read_tr(vb + toff<DP>(row, col)), lds_read_tr(vb + toff<DP>(row + 4, col)));
+      acc[b] = mfma32x32x16(a, pb[t], acc[b]);
+    }
+}
+
 template <int DP, typename Tio>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
-    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const Tio* __restrict__ v,
-    const int* __restrict__ se, const int* __restrict__ counts, const int* __restrict__ lists, int T, int Tp,
-    int Hq, int Hkv, int nq, int nk, float sl2, Tio* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
+    const int* __restrict__ sep, const int* __restrict__ counts, const int* __restrict__ lists,
+    const int* __restrict__ order, int T, int Tp, int Hq, int Hkv, int nq, int nk, float sl2,
+    Tio* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = DP == 32 ? 16 : DP;  // head dim (16 is padded to 32 for the MFMA shapes)
-  constexpr int BK = kFwdBK;
-  constexpr int KS = DP / 16;   // k steps of S^T = K' Q'^T
-  constexpr int NDB = DP / 32;  // 32-wide d blocks of O^T
-  constexpr int SK = DP + 8;    // LDS row strides (elements)
-  constexpr int SV = DP + 16;
-  __shared__ __attribute__((aligned(16))) bf16 ks_[BK * SK];
-  __shared__ __attribute__((aligned(16))) bf16 vs_[BK * SV];
-  __shared__ int ses[BK];
+  constexpr int KS = DP / 16;            // k steps of S^T = K' Q'^T
+  constexpr int NDB = DP / 32;           // 32-wide d blocks of O^T
+  constexpr int TILE = 64 * DP;
+  // two buffers per operand as separate objects, so the compiler can tell
+  // the tile being computed from the one being loaded
+  __shared__ __attribute__((aligned(1024))) bf16 kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vb1[TILE];
+  __shared__ __attribute__((aligned(256))) int sb0[64];
+  __shared__ __attribute__((aligned(256))) int sb1[64];
 
   const int G = Hq / Hkv;
   const int lid = xcd_remap(blockIdx.x, nq * Hq);
   const int gq = lid % G;
   const int hk = (lid / G) % Hkv;
-  const int qt = lid / (G * Hkv);
+  const int qt = order[lid / Hq];
   const int h = hk * G + gq;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int qrow = qt * kFwdBQ + 32 * w + lc;
+  TileDma<DP, true> kd;
+  TileDma<DP, false> vd;
+  kd.init(w, lane);
+  vd.init(w, lane);
 
   bf16x8 qop[KS];
   {
@@ -199,85 +394,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   f32x16 acc[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
-  float m2 = kNegInf, lsum = 0.0f;
+  FwdState st{kNegInf, 0.0f};
 
   const int cnt = counts[qt];
   const int* lst = lists + (size_t)qt * nk;
-  const bf16* kbase = kr + (size_t)hk * Tp * DP;
+  const bf16* kg = kr + (size_t)hk * Tp * DP;
+  const bf16* vg = vr + (size_t)hk * Tp * DP;
 
-  for (int it = 0; it < cnt; ++it) {
-    const int e = lst[it];
-    const int kt = e >> 1;
-    const bool full = e & 1;
-    const int j0 = kt * BK;
-    __syncthreads();
-    for (int vi = tid; vi < BK * DP / 8; vi += 256) {
-      const int r = vi / (DP / 8), c = 8 * (vi % (DP / 8));
-      *reinterpret_cast<bf16x8*>(ks_ + perm_row(r) * SK + c) = load8(kbase + (size_t)(j0 + r) * DP + c);
-      const int j = j0 + r;
-      *reinterpret_cast<bf16x8*>(vs_ + r * SV + c) =
-          load_row8(v + ((size_t)j * Hkv + hk) * D, j < T, c, D);
+  if (cnt > 0) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[0] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
+  for (int it = 0; it < cnt; it += 2) {
+    {
+      const int e = lst[it];
+      wait_dma();
+      __syncthreads();
+      if (it + 1 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1, w, lane);
+      fwd_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, qop, acc, st);
     }
-    if (tid < BK) ses[tid] = (j0 + tid < T) ? se[j0 + tid] : 0;
-    __syncthreads();
-
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks_ + (32 * mb + lc) * SK + 16 * st + 8 * lg);
-        s[mb] = mfma32x32x16(a, qop[st], s[mb]);
-      }
+    if (it + 1 < cnt) {
+      const int e = lst[it + 1];
+      wait_dma();
+      __syncthreads();
+      if (it + 2 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
+      fwd_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, qop, acc, st);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[mb][i] * sl2;
-        if (!full) {
-          const int kk = c_row(mb, i, lg);
-          const bool vis = (j0 + kk <= qrow) && (qrow < ses[kk]);
-          x = vis ? x : kNegInf;
-        }
-        s[mb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m2, mx);
-    const float muse = (mnew == kNegInf) ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - muse);
-    m2 = mnew;
-    float ps = 0.0f;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[mb][i] - muse);
-        ps += p;
-        pb[2 * mb + (i >> 3)][i & 7] = (bf16)p;
-      }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
-
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16* pa = vs_ + (16 * t + 8 * lg + ((lane & 15) >> 2)) * SV + 32 * b + 16 * ((lane >> 4) & 1) +
-                         4 * (lane & 3);
-        const bf16x8 a = cat(lds_read_tr(pa), lds_read_tr(pa + 4 * SV));
-        acc[b] = mfma32x32x16(a, pb[t], acc[b]);
-      }
   }
 
-  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float lt = st.lsum + __shfl_xor(st.lsum, 32);
   if (qrow < T) {
     const float inv = 1.0f / lt;
     Tio* orow = o + ((size_t)qrow * Hq + h) * D;
@@ -288,64 +430,128 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         const int d = 32 * b + 8 * (i >> 2) + 4 * lg + (i & 3);
         if (d < D) orow[d] = from_f32<Tio>(acc[b][i] * inv);
       }
-    if (lg == 0) lse[(size_t)h * T + qrow] = (m2 + log2f(lt)) * kLn2;
+    const float mu = (st.mref == kNegInf) ? 0.0f : st.mref;
+    if (lg == 0) lse[(size_t)h * T + qrow] = (mu + log2f(lt)) * kLn2;
   }
 }
 
 // ------------------------------------------------------------------------
 // Backward dQ. Same shape as the forward: a workgroup owns 128 query rows of
-// one head and loops over their non-empty key tiles. It first forms
-// D_i = dO_i . O_i from the dO operand registers it holds anyway and stores
-// it for the dK/dV kernel.
+// one head and loops over their non-empty key tiles.
 //   S^T = K' Q'^T,  P^T = exp2(S^T * scale*log2e - lse*log2e)
 //   dP^T = V dO^T,  dS^T = P^T (dP^T - D)
 //   dQ'^T += K'^T dS^T  (A operand read transposed from the K' tile)
-// then dQ = R(pos)^T * scale * dQ'.
-template <int DP, typename Tio>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
-    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const Tio* __restrict__ v,
-    const Tio* __restrict__ o, const Tio* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ dd, const int* __restrict__ se, const int* __restrict__ counts,
-    const int* __restrict__ lists, const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nq,
-    int nk, float sl2, float scale, Tio* __restrict__ dq) {
-  constexpr int D = DP == 32 ? 16 : DP;
-  constexpr int BK = kFwdBK;
+// then dQ = R(pos)^T * scale * dQ'. Before the loop it forms
+// D_i = dO_i . O_i from the dO registers it holds anyway, and stores D,
+// lse * log2(e) and a bf16 head-major copy of dO for the dK/dV kernel.
+template <int DP>
+__device__ __forceinline__ void dq_tile(const bf16* kb, const bf16* vb, const int* sb, bool full, int j0, int qrow,
+                                        int lane, int lg, int lc, float sl2, float lse2, float dval,
+                                        const bf16x8* qop, const bf16x8* dop, f32x16* acc) {
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
-  constexpr int SK = DP + 8;
-  __shared__ __attribute__((aligned(16))) bf16 ks_[BK * SK];
-  __shared__ __attribute__((aligned(16))) bf16 vs_[BK * SK];
-  __shared__ int ses[BK];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int off = toff<DP>(32 * mb + lc, 16 * k + 8 * lg);
+      s = mfma32x32x16(lds128(kb + off), qop[k], s);
+      dp = mfma32x32x16(lds128(vb + off), dop[k], dp);
+    }
+    bf16x8 db8[2];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
+        db8[i >> 3][i & 7] = (bf16)(p * (dp[i] - dval));
+      }
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int kk0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
+        const int4 s4 = *reinterpret_cast<const int4*>(sb + kk0);
+        const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * q4 + b;
+          const bool vis = (j0 + kk0 + b <= qrow) & (qrow < sv[b]);
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2)) : 0.0f;
+          db8[i >> 3][i & 7] = (bf16)(p * (dp[i] - dval));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        // K'^T operand: rows d = 32b + lane%32, k slots = keys 16t + 8lg + s
+        const int kb0 = 32 * mb + 16 * t2 + 8 * lg;
+        const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int r0 = perm_row(kb0) + ((lane & 15) >> 2);
+        const int r1 = perm_row(kb0 + 4) + ((lane & 15) >> 2);
+        const bf16x8 a = cat(lds_read_tr(kb + toff<DP>(r0, col)), lds_read_tr(kb + toff<DP>(r1, col)));
+        acc[b] = mfma32x32x16(a, db8[t2], acc[b]);
+      }
+  }
+}
+
+template <int DP, typename Tio>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
+    const Tio* __restrict__ o, const Tio* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ dd, float* __restrict__ l2, bf16* __restrict__ dor, const int* __restrict__ sep,
+    const int* __restrict__ counts, const int* __restrict__ lists, const int* __restrict__ order,
+    const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nq, int nk, float sl2, float scale,
+    Tio* __restrict__ dq) {
+  constexpr int D = DP == 32 ? 16 : DP;
+  constexpr int KS = DP / 16;
+  constexpr int NDB = DP / 32;
+  constexpr int TILE = 64 * DP;
+  __shared__ __attribute__((aligned(1024))) bf16 kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vb1[TILE];
+  __shared__ __attribute__((aligned(256))) int sb0[64];
+  __shared__ __attribute__((aligned(256))) int sb1[64];
 
   const int G = Hq / Hkv;
   const int lid = xcd_remap(blockIdx.x, nq * Hq);
   const int gq = lid % G;
   const int hk = (lid / G) % Hkv;
-  const int qt = lid / (G * Hkv);
+  const int qt = order[lid / Hq];
   const int h = hk * G + gq;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int qrow = qt * kFwdBQ + 32 * w + lc;
   const bool qok = qrow < T;
+  TileDma<DP, true> td;
+  td.init(w, lane);
 
   bf16x8 qop[KS], dop[KS];
   float dval = 0.0f;
   {
     const bf16* qb = qr + ((size_t)h * Tp + qrow) * DP + 8 * lg;
+    bf16* dob = dor + ((size_t)h * Tp + qrow) * DP + 8 * lg;
     const size_t roff = ((size_t)(qok ? qrow : 0) * Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qop[s] = load8(qb + 16 * s);
       dop[s] = load_row8(dout + roff, qok, 16 * s + 8 * lg, D);
+      *reinterpret_cast<bf16x8*>(dob + 16 * s) = dop[s];
       const bf16x8 ov = load_row8(o + roff, qok, 16 * s + 8 * lg, D);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dval += (float)dop[s][e] * (float)ov[e];
     }
   }
   dval += __shfl_xor(dval, 32);
-  if (lg == 0) dd[(size_t)h * Tp + qrow] = dval;
   const float lse2 = qok ? lse[(size_t)h * T + qrow] * kLog2e : 0.0f;
+  if (lg == 0) {
+    dd[(size_t)h * Tp + qrow] = dval;
+    l2[(size_t)h * Tp + qrow] = lse2;
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -353,62 +559,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 
   const int cnt = counts[qt];
   const int* lst = lists + (size_t)qt * nk;
-  const bf16* kbase = kr + (size_t)hk * Tp * DP;
+  const bf16* kg = kr + (size_t)hk * Tp * DP;
+  const bf16* vg = vr + (size_t)hk * Tp * DP;
+  auto issue = [&](int j, bf16* kb, bf16* vb, int* sb) {
+    td.issue(kg + (size_t)j * DP, kb, w);
+    td.issue(vg + (size_t)j * DP, vb, w);
+    if (w == 0) dma4(sep + j + lane, sb);
+  };
 
-  for (int it = 0; it < cnt; ++it) {
-    const int e = lst[it];
-    const int kt = e >> 1;
-    const bool full = e & 1;
-    const int j0 = kt * BK;
-    __syncthreads();
-    for (int vi = tid; vi < BK * DP / 8; vi += 256) {
-      const int r = vi / (DP / 8), c = 8 * (vi % (DP / 8));
-      const int pr = perm_row(r);
-      *reinterpret_cast<bf16x8*>(ks_ + pr * SK + c) = load8(kbase + (size_t)(j0 + r) * DP + c);
-      const int j = j0 + r;
-      *reinterpret_cast<bf16x8*>(vs_ + pr * SK + c) = load_row8(v + ((size_t)j * Hkv + hk) * D, j < T, c, D);
+  if (cnt > 0) issue((lst[0] >> 1) * kFwdBK, kb0, vb0, sb0);
+  for (int it = 0; it < cnt; it += 2) {
+    {
+      const int e = lst[it];
+      wait_dma();
+      __syncthreads();
+      if (it + 1 < cnt) issue((lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1);
+      dq_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, lse2, dval, qop, dop, acc);
     }
-    if (tid < BK) ses[tid] = (j0 + tid < T) ? se[j0 + tid] : 0;
-    __syncthreads();
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-      dp[mb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int off = (32 * mb + lc) * SK + 16 * st + 8 * lg;
-        s[mb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ks_ + off), qop[st], s[mb]);
-        dp[mb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vs_ + off), dop[st], dp[mb]);
-      }
+    if (it + 1 < cnt) {
+      const int e = lst[it + 1];
+      wait_dma();
+      __syncthreads();
+      if (it + 2 < cnt) issue((lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0);
+      dq_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, lse2, dval, qop, dop, acc);
     }
-    bf16x8 db8[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(s[mb][i] * sl2 - lse2);
-        if (!full) {
-          const int kk = c_row(mb, i, lg);
-          const bool vis = (j0 + kk <= qrow) && (qrow < ses[kk]);
-          p = vis ? p : 0.0f;
-        }
-        db8[2 * mb + (i >> 3)][i & 7] = (bf16)(p * (dp[mb][i] - dval));
-      }
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // K'^T operand: rows d = 32b + lane%32, k slots = keys 16t + 8lg + s
-        const int kb = 16 * t + 8 * lg;
-        const bf16* pa = ks_ + (perm_row(kb) + ((lane & 15) >> 2)) * SK + 32 * b + 16 * ((lane >> 4) & 1) +
-                         4 * (lane & 3);
-        const bf16* pb = ks_ + (perm_row(kb + 4) + ((lane & 15) >> 2)) * SK + 32 * b + 16 * ((lane >> 4) & 1) +
-                         4 * (lane & 3);
-        const bf16x8 a = cat(lds_read_tr(pa), lds_read_tr(pb));
-        acc[b] = mfma32x32x16(a, db8[t], acc[b]);
-      }
   }
 
   if (qok) {
@@ -417,22 +591,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     constexpr int half = D / 2;
     const float2* csr = cs + (size_t)qrow * half;
     Tio* out = dq + ((size_t)qrow * Hq + h) * D;
-    float g[NDB * 16];
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) g[16 * b + i] = acc[b][i] * scale;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int d = 32 * b + 8 * (i >> 2) + 4 * lg + (i & 3);
         if (d < half) {
-          // partner register: d + half = 32 b' + 8 a' + 4 lg + (i & 3)
           const int dp2 = d + half;
           const int b2 = dp2 >> 5, a2 = (dp2 & 31) >> 3;
-          const float g1 = g[16 * b + i];
-          const float g2 = g[16 * b2 + 4 * a2 + (i & 3)];
+          const float g1 = acc[b][i] * scale;
+          const float g2 = acc[b2][4 * a2 + (i & 3)] * scale;
           const float2 c = csr[d];
           out[d] = from_f32<Tio>(g1 * c.x + g2 * c.y);
           out[dp2] = from_f32<Tio>(g2 * c.x - g1 * c.y);
@@ -450,47 +618,103 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 //   dS = P (dP - D);  dV += P^T dO;  dK' += dS^T Q'
 // The accumulators never leave registers until the epilogue, which rotates
 // dK back (R(pos)^T) through an LDS transpose and writes both once.
+template <int DP>
+__device__ __forceinline__ void dkdv_tile(const bf16* qs_, const bf16* ds_, const float* ls, const float* dl,
+                                          bool full, int i0, int key, int myse, int lane, int lg, int lc, float sl2,
+                                          const bf16x8* kop, const bf16x8* vop, f32x16* acck, f32x16* accv) {
+  constexpr int KS = DP / 16;
+  constexpr int NDB = DP / 32;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int off = toff<DP>(32 * mb + lc, 16 * k + 8 * lg);
+      s = mfma32x32x16(lds128(qs_ + off), kop[k], s);
+      dp = mfma32x32x16(lds128(ds_ + off), vop[k], dp);
+    }
+    // C register i <-> query row c_row(mb, i, lg) of this block; lane <-> key
+    bf16x8 pa[2], sa[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + qi0);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl + qi0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * q4 + b;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lv[b]));
+        if (!full) {
+          const int iq = i0 + qi0 + b;
+          p = ((key <= iq) & (iq < myse)) ? p : 0.0f;
+        }
+        pa[i >> 3][i & 7] = (bf16)p;
+        sa[i >> 3][i & 7] = (bf16)(p * (dp[i] - dv4[b]));
+      }
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int qb0 = 32 * mb + 16 * t2 + 8 * lg;  // natural query row of slot 0
+      const int r0 = perm_row(qb0) + ((lane & 15) >> 2);
+      const int r1 = perm_row(qb0 + 4) + ((lane & 15) >> 2);
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const bf16x8 bdo = cat(lds_read_tr(ds_ + toff<DP>(r0, col)), lds_read_tr(ds_ + toff<DP>(r1, col)));
+        accv[b] = mfma32x32x16(pa[t2], bdo, accv[b]);
+        const bf16x8 bq = cat(lds_read_tr(qs_ + toff<DP>(r0, col)), lds_read_tr(qs_ + toff<DP>(r1, col)));
+        acck[b] = mfma32x32x16(sa[t2], bq, acck[b]);
+      }
+    }
+  }
+}
+
 template <int DP, typename Tio>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
-    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const Tio* __restrict__ v,
-    const Tio* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dd,
-    const int* __restrict__ se, const int2* __restrict__ kmm, const float2* __restrict__ cs, int T, int Tp,
-    int Hq, int Hkv, int nkb, float sl2, float scale, Tio* __restrict__ dk, Tio* __restrict__ dv) {
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
+    const bf16* __restrict__ dor, const float* __restrict__ l2, const float* __restrict__ dd,
+    const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ korder,
+    const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nkb, float sl2, float scale,
+    Tio* __restrict__ dk, Tio* __restrict__ dv) {
   constexpr int D = DP == 32 ? 16 : DP;
   constexpr int BQ = kBwdBQ;
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
-  constexpr int SQ = DP + 8;
-  constexpr int SE = DP + 4;  // epilogue f32 row stride
-  constexpr int kTileBytes = 2 * BQ * SQ * 2;
-  constexpr int kEpiBytes = 4 * 32 * SE * 4;
-  constexpr int kSmem = kTileBytes > kEpiBytes ? kTileBytes : kEpiBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
-  __shared__ __attribute__((aligned(16))) float lse_s[BQ];
-  __shared__ __attribute__((aligned(16))) float dd_s[BQ];
-  bf16* qs_ = reinterpret_cast<bf16*>(smem);
-  bf16* ds_ = qs_ + BQ * SQ;
+  constexpr int TILE = 64 * DP;
+  constexpr int SE = DP;  // epilogue f32 row stride: 32 rows x DP floats = one tile buffer
+  __shared__ __attribute__((aligned(1024))) bf16 qb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 qb1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ob0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 ob1[TILE];
+  __shared__ __attribute__((aligned(256))) float lb0[BQ];
+  __shared__ __attribute__((aligned(256))) float lb1[BQ];
+  __shared__ __attribute__((aligned(256))) float db0[BQ];
+  __shared__ __attribute__((aligned(256))) float db1[BQ];
 
   const int G = Hq / Hkv;
   const int lid = xcd_remap(blockIdx.x, nkb * Hkv);
-  const int kt = lid % nkb;
+  const int kt = korder[lid % nkb];
   const int hk = lid / nkb;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int j0 = kt * kBwdBK;
   const int key = j0 + 32 * w + lc;
-  const bool kok = key < T;
-  const int myse = kok ? se[key] : 0;
+  const int myse = sep[key];
+  TileDma<DP, true> td;
+  td.init(w, lane);
 
   bf16x8 kop[KS], vop[KS];
   {
     const bf16* kb = kr + ((size_t)hk * Tp + key) * DP + 8 * lg;
-    const Tio* vb = v + ((size_t)(kok ? key : 0) * Hkv + hk) * D;
+    const bf16* vb = vr + ((size_t)hk * Tp + key) * DP + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       kop[s] = load8(kb + 16 * s);
-      vop[s] = load_row8(vb, kok, 16 * s + 8 * lg, D);
+      vop[s] = load8(vb + 16 * s);
     }
   }
   f32x16 acck[NDB], accv[NDB];
@@ -502,74 +726,44 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   const int2 mm = kmm[kt];
   const int qb_lo = j0 / BQ;
-  const int qb_hi = (mm.y + BQ - 1) / BQ;
+  const int nqb = (mm.y + BQ - 1) / BQ - qb_lo;
+  const int n_it = G * nqb;
 
-  for (int gq = 0; gq < G; ++gq) {
-    const int h = hk * G + gq;
-    const bf16* qbase = qr + (size_t)h * Tp * DP;
-    for (int qb = qb_lo; qb < qb_hi; ++qb) {
-      const int i0 = qb * BQ;
-      const int i1 = min(i0 + BQ, T);
-      const bool full = (j0 + kBwdBK - 1 <= i0) && (mm.x >= i1);
+  auto issue = [&](int it, bf16* qs_, bf16* ds_, float* ls, float* dl) {
+    const int h = hk * G + it / nqb;
+    const int i0 = (qb_lo + it % nqb) * BQ;
+    td.issue(qr + ((size_t)h * Tp + i0) * DP, qs_, w);
+    td.issue(dor + ((size_t)h * Tp + i0) * DP, ds_, w);
+    if (w == 0) dma4(l2 + (size_t)h * Tp + i0 + lane, ls);
+    if (w == 1) dma4(dd + (size_t)h * Tp + i0 + lane, dl);
+  };
+  auto tile_full = [&](int it) {
+    const int i0 = (qb_lo + it % nqb) * BQ;
+    return (j0 + kBwdBK - 1 <= i0) && (mm.x >= min(i0 + BQ, T));
+  };
+  if (n_it > 0) issue(0, qb0, ob0, lb0, db0);
+  for (int it = 0; it < n_it; it += 2) {
+    {
+      wait_dma();
       __syncthreads();
-      for (int vi = tid; vi < BQ * DP / 8; vi += 256) {
-        const int r = vi / (DP / 8), c = 8 * (vi % (DP / 8));
-        const int pr = perm_row(r);
-        const int i = i0 + r;
-        *reinterpret_cast<bf16x8*>(qs_ + pr * SQ + c) = load8(qbase + (size_t)i * DP + c);
-        *reinterpret_cast<bf16x8*>(ds_ + pr * SQ + c) =
-            load_row8(dout + ((size_t)(i < T ? i : 0) * Hq + h) * D, i < T, c, D);
-      }
-      if (tid < BQ) {
-        const int i = i0 + tid;
-        lse_s[tid] = i < T ? lse[(size_t)h * T + i] * kLog2e : 0.0f;
-        dd_s[tid] = dd[(size_t)h * Tp + i];
-      }
+      if (it + 1 < n_it) issue(it + 1, qb1, ob1, lb1, db1);
+      dkdv_tile<DP>(qb0, ob0, lb0, db0, tile_full(it), (qb_lo + it % nqb) * BQ, key, myse, lane, lg, lc, sl2, kop,
+                    vop, acck, accv);
+    }
+    if (it + 1 < n_it) {
+      wait_dma();
       __syncthreads();
-
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const int off = (32 * mb + lc) * SQ + 16 * st + 8 * lg;
-          s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(qs_ + off), kop[st], s);
-          dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ds_ + off), vop[st], dp);
-        }
-        // C register i <-> query row c_row(mb, i, lg) of this block; lane <-> key
-        bf16x8 pa[2], sa[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = c_row(mb, i, lg);
-          float p = __builtin_amdgcn_exp2f(s[i] * sl2 - lse_s[qi]);
-          if (!full) {
-            const int iq = i0 + qi;
-            p = (key <= iq && iq < myse) ? p : 0.0f;
-          }
-          pa[i >> 3][i & 7] = (bf16)p;
-          sa[i >> 3][i & 7] = (bf16)(p * (dp[i] - dd_s[qi]));
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int qb0 = 32 * mb + 16 * t2 + 8 * lg;  // natural query row of slot 0
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) {
-            const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const int r0 = perm_row(qb0) + ((lane & 15) >> 2);
-            const int r1 = perm_row(qb0 + 4) + ((lane & 15) >> 2);
-            const bf16x8 bdo = cat(lds_read_tr(ds_ + r0 * SQ + col), lds_read_tr(ds_ + r1 * SQ + col));
-            accv[b] = mfma32x32x16(pa[t2], bdo, accv[b]);
-            const bf16x8 bq = cat(lds_read_tr(qs_ + r0 * SQ + col), lds_read_tr(qs_ + r1 * SQ + col));
-            acck[b] = mfma32x32x16(sa[t2], bq, acck[b]);
-          }
-        }
-      }
+      if (it + 2 < n_it) issue(it + 2, qb0, ob0, lb0, db0);
+      dkdv_tile<DP>(qb1, ob1, lb1, db1, tile_full(it + 1), (qb_lo + (it + 1) % nqb) * BQ, key, myse, lane, lg, lc,
+                    sl2, kop, vop, acck, accv);
     }
   }
 
-  // Epilogue: stage each wave's 32 x DP block in LDS as [key][d] f32.
+  // Epilogue: stage each wave's 32 x DP block in LDS as [key][d] f32 (the
+  // tile buffers are free now; 4 waves x 32 x SE floats fit in them).
+  static_assert(32 * SE * 4 <= TILE * 2, "a wave's epilogue block must fit in one tile buffer");
   __syncthreads();
-  float* ep = reinterpret_cast<float*>(smem) + w * 32 * SE;
+  float* ep = reinterpret_cast<float*>(w < 2 ? (w == 0 ? qb0 : qb1) : (w == 2 ? ob0 : ob1));
   constexpr int half = D / 2;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -607,7 +801,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 // Host side
 struct AttnLayout {
   int T, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
-  size_t off_qr, off_kr, off_cs, off_kmm64, off_kmm128, off_qcount, off_qlist, off_dd, total;
+  size_t off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qorder, off_qlist;
+  size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -624,22 +819,28 @@ AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   L.nk64 = (T + kFwdBK - 1) / kFwdBK;
   L.nk128 = (T + kBwdBK - 1) / kBwdBK;
   size_t o = 0;
-  L.off_qr = o;
-  o = align256(o + (size_t)Hq * L.Tp * L.DP * 2);
-  L.off_kr = o;
-  o = align256(o + (size_t)Hkv * L.Tp * L.DP * 2);
-  L.off_cs = o;
-  o = align256(o + (size_t)L.Tp * (D / 2) * 8);
-  L.off_kmm64 = o;
-  o = align256(o + (size_t)L.nk64 * 8);
-  L.off_kmm128 = o;
-  o = align256(o + (size_t)L.nk128 * 8);
-  L.off_qcount = o;
-  o = align256(o + (size_t)L.nq * 4);
-  L.off_qlist = o;
-  o = align256(o + (size_t)L.nq * L.nk64 * 4);
-  L.off_dd = o;
-  if (with_bwd) o = align256(o + (size_t)Hq * L.Tp * 4);
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.off_qr = take((size_t)Hq * L.Tp * L.DP * 2);
+  L.off_kr = take((size_t)Hkv * L.Tp * L.DP * 2);
+  L.off_vr = take((size_t)Hkv * L.Tp * L.DP * 2);
+  L.off_sep = take((size_t)L.Tp * 4);
+  L.off_cs = take((size_t)L.Tp * (D / 2) * 8);
+  L.off_kmm64 = take((size_t)L.nk64 * 8);
+  L.off_kmm128 = take((size_t)L.nk128 * 8);
+  L.off_qcount = take((size_t)L.nq * 4);
+  L.off_qorder = take((size_t)L.nq * 4);
+  L.off_qlist = take((size_t)L.nq * L.nk64 * 4);
+  L.off_kwork = take((size_t)L.nk128 * 4);
+  L.off_korder = take((size_t)L.nk128 * 4);
+  if (with_bwd) {
+    L.off_dd = take((size_t)Hq * L.Tp * 4);
+    L.off_l2 = take((size_t)Hq * L.Tp * 4);
+    L.off_dor = take((size_t)Hq * L.Tp * L.DP * 2);
+  }
   L.total = o;
   return L;
 }
@@ -658,60 +859,68 @@ int check_launch(const char* fn) {
   return TA_OK;
 }
 
+template <typename T>
+T* at(char* ws, size_t off) {
+  return reinterpret_cast<T*>(ws + off);
+}
+
 template <typename Tio>
-int run_prep(const AttnLayout& L, const void* q, const void* k, const int* pos, const int* se, float theta,
-             char* ws, hipStream_t st) {
+int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, const int* pos, const int* se,
+             float theta, char* ws, hipStream_t st) {
   {
-  ProfScope ps("rope_prep", st);
-  hipLaunchKernelGGL(rope_prep_kernel<Tio>, dim3(L.Tp), dim3(256), 0, st, static_cast<const Tio*>(q),
-                     static_cast<const Tio*>(k), pos, L.T, L.Tp, L.Hq, L.Hkv, L.D, L.DP, theta,
-                     reinterpret_cast<bf16*>(ws + L.off_qr), reinterpret_cast<bf16*>(ws + L.off_kr),
-                     reinterpret_cast<float2*>(ws + L.off_cs));
+    ProfScope ps("rope_prep", st);
+    hipLaunchKernelGGL(rope_prep_kernel<Tio>, dim3(L.Tp), dim3(256), 0, st, static_cast<const Tio*>(q),
+                       static_cast<const Tio*>(k), static_cast<const Tio*>(v), pos, se, L.T, L.Tp, L.Hq, L.Hkv,
+                       L.D, L.DP, theta, at<bf16>(ws, L.off_qr), at<bf16>(ws, L.off_kr), at<bf16>(ws, L.off_vr),
+                       at<int>(ws, L.off_sep), at<float2>(ws, L.off_cs));
   }
   ProfScope ps("tile_plan", st);
   hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, se, L.T, kFwdBK, L.nk64,
-                     reinterpret_cast<int2*>(ws + L.off_kmm64));
+                     at<int2>(ws, L.off_kmm64));
   hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk128 + 255) / 256), dim3(256), 0, st, se, L.T, kBwdBK,
-                     L.nk128, reinterpret_cast<int2*>(ws + L.off_kmm128));
-  hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, reinterpret_cast<const int2*>(ws + L.off_kmm64),
-                     L.T, kFwdBQ, kFwdBK, L.nk64, reinterpret_cast<int*>(ws + L.off_qcount),
-                     reinterpret_cast<int*>(ws + L.off_qlist));
+                     L.nk128, at<int2>(ws, L.off_kmm128));
+  hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.T, kFwdBQ,
+                     kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
+                     at<int>(ws, L.off_qorder));
+  hipLaunchKernelGGL(k_work_kernel, dim3((L.nk128 + 255) / 256), dim3(256), 0, st,
+                     at<const int2>(ws, L.off_kmm128), L.nk128, at<int>(ws, L.off_kwork));
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_kwork), L.nk128,
+                     at<int>(ws, L.off_korder));
   return check_launch("prep");
 }
 
 template <int DP, typename Tio>
-int run_fwd(const AttnLayout& L, const void* v, const int* se, float sl2, void* o, float* lse, char* ws,
-            hipStream_t st) {
+int run_fwd(const AttnLayout& L, float sl2, void* o, float* lse, char* ws, hipStream_t st) {
   ProfScope ps("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st,
-                     reinterpret_cast<const bf16*>(ws + L.off_qr), reinterpret_cast<const bf16*>(ws + L.off_kr),
-                     static_cast<const Tio*>(v), se, reinterpret_cast<const int*>(ws + L.off_qcount),
-                     reinterpret_cast<const int*>(ws + L.off_qlist), L.T, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64,
-                     sl2, static_cast<Tio*>(o), lse);
+  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st, at<const bf16>(ws, L.off_qr),
+                     at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr), at<const int>(ws, L.off_sep),
+                     at<const int>(ws, L.off_qcount), at<const int>(ws, L.off_qlist),
+                     at<const int>(ws, L.off_qorder), L.T, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64, sl2,
+                     static_cast<Tio*>(o), lse);
   return check_launch("tree_attn_fwd");
 }
 
 template <int DP, typename Tio>
-int run_bwd(const AttnLayout& L, const void* v, const void* o, const float* lse, const void* dout, const int* se,
-            float sl2, float scale, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
+int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* dout, float sl2, float scale,
+            void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
   {
-  ProfScope ps("attn_bwd_dq", st);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st,
-                     reinterpret_cast<const bf16*>(ws + L.off_qr), reinterpret_cast<const bf16*>(ws + L.off_kr),
-                     static_cast<const Tio*>(v), static_cast<const Tio*>(o), static_cast<const Tio*>(dout), lse,
-                     reinterpret_cast<float*>(ws + L.off_dd), se,
-                     reinterpret_cast<const int*>(ws + L.off_qcount), reinterpret_cast<const int*>(ws + L.off_qlist),
-                     reinterpret_cast<const float2*>(ws + L.off_cs), L.T, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64,
-                     sl2, scale, static_cast<Tio*>(dq));
+    ProfScope ps("attn_bwd_dq", st);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st,
+                       at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
+                       static_cast<const Tio*>(o), static_cast<const Tio*>(dout), lse, at<float>(ws, L.off_dd),
+                       at<float>(ws, L.off_l2), at<bf16>(ws, L.off_dor), at<const int>(ws, L.off_sep),
+                       at<const int>(ws, L.off_qcount), at<const int>(ws, L.off_qlist),
+                       at<const int>(ws, L.off_qorder), at<const float2>(ws, L.off_cs), L.T, L.Tp, L.Hq, L.Hkv,
+                       L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
   }
   ProfScope ps("attn_bwd_dkdv", st);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.nk128 * L.Hkv), dim3(256), 0, st,
-                     reinterpret_cast<const bf16*>(ws + L.off_qr), reinterpret_cast<const bf16*>(ws + L.off_kr),
-                     static_cast<const Tio*>(v), static_cast<const Tio*>(dout), lse,
-                     reinterpret_cast<const float*>(ws + L.off_dd), se,
-                     reinterpret_cast<const int2*>(ws + L.off_kmm128), reinterpret_cast<const float2*>(ws + L.off_cs),
-                     L.T, L.Tp, L.Hq, L.Hkv, L.nk128, sl2, scale, static_cast<Tio*>(dk),
-                     static_cast<Tio*>(dv));
+                     at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
+                     at<const bf16>(ws, L.off_dor), at<const float>(ws, L.off_l2), at<const float>(ws, L.off_dd),
+                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm128), at<const int>(ws, L.off_korder),
+                     at<const float2>(ws, L.off_cs), L.T, L.Tp, L.Hq, L.Hkv, L.nk128, sl2, scale,
+                     static_cast<Tio*>(dk), static_cast<Tio*>(dv));
   return check_launch("tree_attn_bwd");
 }
 
@@ -744,17 +953,17 @@ extern "C" int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dty
   const float sl2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, pos, subtree_end, rope_theta, ws, st)
-                         : run_prep<float>(L, q, k, pos, subtree_end, rope_theta, ws, st);
+  int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, subtree_end, rope_theta, ws, st)
+                         : run_prep<float>(L, q, k, v, pos, subtree_end, rope_theta, ws, st);
   if (rc) return rc;
   if (dt == TA_BF16) {
-    if (L.DP == 32) return run_fwd<32, bf16>(L, v, subtree_end, sl2, o, lse, ws, st);
-    if (L.DP == 64) return run_fwd<64, bf16>(L, v, subtree_end, sl2, o, lse, ws, st);
-    return run_fwd<128, bf16>(L, v, subtree_end, sl2, o, lse, ws, st);
+    if (L.DP == 32) return run_fwd<32, bf16>(L, sl2, o, lse, ws, st);
+    if (L.DP == 64) return run_fwd<64, bf16>(L, sl2, o, lse, ws, st);
+    return run_fwd<128, bf16>(L, sl2, o, lse, ws, st);
   }
-  if (L.DP == 32) return run_fwd<32, float>(L, v, subtree_end, sl2, o, lse, ws, st);
-  if (L.DP == 64) return run_fwd<64, float>(L, v, subtree_end, sl2, o, lse, ws, st);
-  return run_fwd<128, float>(L, v, subtree_end, sl2, o, lse, ws, st);
+  if (L.DP == 32) return run_fwd<32, float>(L, sl2, o, lse, ws, st);
+  if (L.DP == 64) return run_fwd<64, float>(L, sl2, o, lse, ws, st);
+  return run_fwd<128, float>(L, sl2, o, lse, ws, st);
 }
 
 extern "C" int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -779,16 +988,16 @@ extern "C" int tree_attn_bwd(const void* q, const void* k, const void* v, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (!(flags & TA_REUSE_PREP)) {
-    int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, pos, subtree_end, rope_theta, ws, st)
-                           : run_prep<float>(L, q, k, pos, subtree_end, rope_theta, ws, st);
+    int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, subtree_end, rope_theta, ws, st)
+                           : run_prep<float>(L, q, k, v, pos, subtree_end, rope_theta, ws, st);
     if (rc) return rc;
   }
   if (dt == TA_BF16) {
-    if (L.DP == 32) return run_bwd<32, bf16>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
-    if (L.DP == 64) return run_bwd<64, bf16>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
-    return run_bwd<128, bf16>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
+    if (L.DP == 32) return run_bwd<32, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
+    if (L.DP == 64) return run_bwd<64, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
+    return run_bwd<128, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
   }
-  if (L.DP == 32) return run_bwd<32, float>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
-  if (L.DP == 64) return run_bwd<64, float>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
-  return run_bwd<128, float>(L, v, o, lse, dout, subtree_end, sl2, scale, dq, dk, dv, ws, st);
+  if (L.DP == 32) return run_bwd<32, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
+  if (L.DP == 64) return run_bwd<64, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
+  return run_bwd<128, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
 }
