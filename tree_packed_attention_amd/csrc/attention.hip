@@ -47,8 +47,28 @@
 #include "ta_error.h"
 #include "tree_attn.h"
 
+// Build-time scheduling knobs (defaults are the measured best).
+#ifndef TA_IGLP
+#define TA_IGLP -1  // >= 0: __builtin_amdgcn_iglp_opt(TA_IGLP) in the tile bodies
+#endif
+#ifndef TA_DKDV_WAVES_PER_EU
+#define TA_DKDV_WAVES_PER_EU 1
+#endif
+#ifndef TA_DKDV_SFIRST
+#define TA_DKDV_SFIRST 0  // 1: dK/dV computes both halves' S and dP before their softmax work
+#endif
+#ifndef TA_FWD_WAVES
+#define TA_FWD_WAVES 4  // forward workgroup: TA_FWD_WAVES waves x 32 query rows
+#endif
+
 namespace ta {
 namespace {
+
+__device__ __forceinline__ void sched_hint() {
+#if TA_IGLP >= 0
+  __builtin_amdgcn_iglp_opt(TA_IGLP);
+#endif
+}
 
 constexpr int kFwdBQ = 128;  // query rows per forward / dQ workgroup (4 waves x 32)
 constexpr int kFwdBK = 64;   // keys per forward / dQ iteration
@@ -93,16 +113,16 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // Copies 64 head-major rows [row0 + rowmap(r)] of a [*][DP] bf16 array into a
 // swizzled LDS tile. Each wave issues DP/32 16-byte-per-lane instructions;
 // every lane's offset inside the 64-row block is fixed, so it is computed once.
-template <int DP, bool PERM>
+template <int DP, bool PERM, int NW = 4>
 struct TileDma {
-  static constexpr int CH = DP / 8;  // 16-byte chunks per row
-  static constexpr int NI = CH / 4;  // instructions per wave
+  static constexpr int CH = DP / 8;                // 16-byte chunks per row (= instructions per tile)
+  static constexpr int NI = (CH + NW - 1) / NW;    // instructions per wave (the last may be idle)
   int off[NI];
   __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int p = (w + 4 * j) * 64 + lane;
-      const int r = p / CH;
+      const int p = (w + NW * j) * 64 + lane;
+      const int r = min(p / CH, 63);
       const int c = ((p % CH) ^ swz(r)) & (CH - 1);
       off[j] = (PERM ? perm_row(r) : r) * DP + 8 * c;
     }
@@ -110,11 +130,32 @@ struct TileDma {
   // rows: the global address of row row0 of the source; w: wave index (uniform)
   __device__ __forceinline__ void issue(const bf16* rows, bf16* tile, int w) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) dma16(rows + off[j], tile + (w + 4 * j) * 512);
+    for (int j = 0; j < NI; ++j)
+      if (w + NW * j < CH) dma16(rows + off[j], tile + (w + NW * j) * 512);
   }
 };
 
 __device__ __forceinline__ bf16x8 lds128(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Per-lane element offsets into a swizzled [64][DP] tile, computed once:
+//   op[k]: 16-byte operand read of LDS row lc (+32 mb), columns 16k + 8lg
+//   tr[b]: transposed read of rows 4lg + (lane%16)/4 (+16 t, +8, +32 mb),
+//          columns 32b + 16((lane/16)%2) + 4(lane%4)
+// The swizzle of a row depends only on its low 3 bits, which the row
+// offsets added at the call sites (multiples of 8) leave unchanged.
+template <int DP>
+struct SwzAddr {
+  int op[DP / 16];
+  int tr[DP / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int lg = lane >> 5, lc = lane & 31;
+#pragma unroll
+    for (int k = 0; k < DP / 16; ++k) op[k] = toff<DP>(lc, 16 * k + 8 * lg);
+#pragma unroll
+    for (int b = 0; b < DP / 32; ++b)
+      tr[b] = toff<DP>(4 * lg + ((lane & 15) >> 2), 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  }
+};
 
 // ------------------------------------------------------------------------
 // Prep: RoPE on q and k, the padded bf16 copy of v, the padded subtree ends
@@ -265,35 +306,84 @@ __device__ __forceinline__ bf16x8 load_row8(const Tio* rowp, bool row_ok, int c,
 }
 
 // ------------------------------------------------------------------------
-// Forward. One workgroup = 128 query rows of one head (4 waves x 32 rows),
-// looping over the query tile's non-empty 64-key tiles.
+// Forward. One workgroup = 128 query rows of one head (kFwdWaves waves x
+// kNB 32-row column blocks), looping over the query tile's non-empty 64-key
+// tiles. With kNB = 2 every K' / V operand read from LDS would feed two MFMAs,
+// but one wave per SIMD then hides too little latency; 4 waves x 32 rows at
+// two waves per SIMD is faster on gfx950.
+//
+// LDS: the K' tile (read only as 16-byte operands) uses rows padded to DP + 8
+// elements, which is conflict-free and keeps every read address an immediate
+// offset from one per-lane base; the V tile (read only transposed) uses the
+// XOR swizzle, whose 8 distinct per-lane bases are computed once.
+constexpr int kFwdWaves = TA_FWD_WAVES;
+constexpr int kNB = 1;  // 32-query column blocks per wave
+constexpr int kFwdRows = 32 * kNB * kFwdWaves;  // query rows per forward workgroup
+
 struct FwdState {
   float mref, lsum;
 };
 
+// DMA of one padded 64-row tile (row stride DP + 8): a flat copy of
+// 64 * (DP/8 + 1) 16-byte positions; a padding position copies any valid chunk.
+template <int DP, bool PERM, int NW>
+struct PadTileDma {
+  static constexpr int RC = DP / 8 + 1;                // 16-byte positions per padded row
+  static constexpr int NINS = RC;                      // 64 * RC positions / 64 lanes
+  static constexpr int NI = (NINS + NW - 1) / NW;      // instructions per wave (last may be partial)
+  int off[NI];
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int p = (w + NW * j) * 64 + lane;
+      const int r = min(p / RC, 63);
+      const int c = p % RC;
+      off[j] = (PERM ? perm_row(r) : r) * DP + (c < DP / 8 ? 8 * c : 0);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16* rows, bf16* tile, int w) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      if (w + NW * j < NINS) dma16(rows + off[j], tile + (w + NW * j) * 512);
+  }
+};
+
 template <int DP>
-__device__ __forceinline__ void fwd_issue(const TileDma<DP, true>& kd, const TileDma<DP, false>& vd,
-                                          const bf16* kg, const bf16* vg, const int* sep, int j0, bf16* kb,
-                                          bf16* vb, int* sb, int w, int lane) {
+struct FwdAddr {
+  int k;          // element offset of this lane's first K' operand in a padded tile
+  int v[2][DP / 32];  // element offsets of the transposed V reads, per (half, d block), t = 0
+};
+
+template <int DP>
+__device__ __forceinline__ void fwd_issue(const PadTileDma<DP, true, kFwdWaves>& kd,
+                                          const TileDma<DP, false, kFwdWaves>& vd, const bf16* kg, const bf16* vg,
+                                          const int* sep, int j0, bf16* kb, bf16* vb, int* sb, int w, int lane) {
   kd.issue(kg + (size_t)j0 * DP, kb, w);
   vd.issue(vg + (size_t)j0 * DP, vb, w);
   if (w == 0) dma4(sep + j0 + lane, sb);
 }
 
-// One key tile: S^T = K' Q'^T, mask, lazy-rescaled online softmax, O^T += V^T P^T.
+// One key tile for both column blocks: S^T = K' Q'^T, mask, lazy-rescaled
+// online softmax, O^T += V^T P^T.
 template <int DP>
-__device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const int* sb, bool full, int j0, int qrow,
-                                         int lane, int lg, int lc, float sl2, const bf16x8* qop, f32x16* acc,
-                                         FwdState& st) {
+__device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const int* sb, bool full, int j0,
+                                         const int* qrow, int lg, const FwdAddr<DP>& ad, float sl2,
+                                         const bf16x8 (*qop)[DP / 16], f32x16 (*acc)[DP / 32], FwdState* st) {
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
-  f32x16 s[2];
+  constexpr int SKP = DP + 8;
+  sched_hint();
+  f32x16 s[2][kNB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    s[mb] = f32x16{};
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
-      s[mb] = mfma32x32x16(lds128(kb + toff<DP>(32 * mb + lc, 16 * k + 8 * lg)), qop[k], s[mb]);
+    for (int nb = 0; nb < kNB; ++nb) s[mb][nb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const bf16x8 a = lds128(kb + ad.k + 32 * mb * SKP + 16 * k);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) s[mb][nb] = mfma32x32x16(a, qop[nb][k], s[mb][nb]);
+    }
   }
   if (!full) {
 #pragma unroll
@@ -304,66 +394,72 @@ __device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const i
         const int4 s4 = *reinterpret_cast<const int4*>(sb + kk0);
         const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bool vis = (j0 + kk0 + b <= qrow) & (qrow < sv[b]);
-          s[mb][4 * q4 + b] = vis ? s[mb][4 * q4 + b] : kNegInf;
-        }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            const bool vis = (j0 + kk0 + b <= qrow[nb]) & (qrow[nb] < sv[b]);
+            s[mb][nb][4 * q4 + b] = vis ? s[mb][nb][4 * q4 + b] : kNegInf;
+          }
       }
   }
-  float mx = kNegInf;
+  bf16x8 pb[kNB][4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int nb = 0; nb < kNB; ++nb) {
+    float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mt2 = mx * sl2;
-  if (__any(mt2 > st.mref + kRescaleLog2)) {
-    const float mnew = fmaxf(st.mref, mt2);
-    const float alpha = (st.mref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(st.mref - mnew);
-    st.mref = mnew;
-    st.lsum *= alpha;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][nb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt2 = mx * sl2;
+    if (__any(mt2 > st[nb].mref + kRescaleLog2)) {
+      const float mnew = fmaxf(st[nb].mref, mt2);
+      const float alpha = (st[nb].mref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(st[nb].mref - mnew);
+      st[nb].mref = mnew;
+      st[nb].lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
-  }
-  const float nmu = (st.mref == kNegInf) ? 0.0f : -st.mref;
-  float ps = 0.0f;
-  bf16x8 pb[4];
+      for (int b = 0; b < NDB; ++b)
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, nmu));
-      ps += p;
-      pb[2 * mb + (i >> 3)][i & 7] = (bf16)p;
+        for (int i = 0; i < 16; ++i) acc[nb][b][i] *= alpha;
     }
-  st.lsum += ps;
+    const float nmu = (st[nb].mref == kNegInf) ? 0.0f : -st[nb].mref;
+    float ps = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], sl2, nmu));
+        ps += p;
+        pb[nb][2 * mb + (i >> 3)][i & 7] = (bf16)p;
+      }
+    st[nb].lsum += ps;
+  }
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = 16 * t + 8 * lg + ((lane & 15) >> 2);
-      const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      const bf16x8 a = cat(lds_read_tr(vb + toff<DP>(row, col)), lds_read_tr(vb + toff<DP>(row + 4, col)));
-      acc[b] = mfma32x32x16(a, pb[t], acc[b]);
+      // rows 16t + 8lg + (lane%16)/4 (+4): the 16t part only moves whole rows
+      const bf16x8 a = cat(lds_read_tr(vb + ad.v[0][b] + 16 * t * DP), lds_read_tr(vb + ad.v[1][b] + 16 * t * DP));
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[nb][b] = mfma32x32x16(a, pb[nb][t], acc[nb][b]);
     }
 }
 
 template <int DP, typename Tio>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
-    const int* __restrict__ sep, const int* __restrict__ counts, const int* __restrict__ lists,
-    const int* __restrict__ order, int T, int Tp, int Hq, int Hkv, int nq, int nk, float sl2,
-    Tio* __restrict__ o, float* __restrict__ lse) {
+    const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ counts,
+    const int* __restrict__ lists, const int* __restrict__ order, int T, int Tp, int Hq, int Hkv, int nq, int nk,
+    float sl2, Tio* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = DP == 32 ? 16 : DP;  // head dim (16 is padded to 32 for the MFMA shapes)
   constexpr int KS = DP / 16;            // k steps of S^T = K' Q'^T
   constexpr int NDB = DP / 32;           // 32-wide d blocks of O^T
   constexpr int TILE = 64 * DP;
+  constexpr int KTILE = 64 * (DP + 8);
   // two buffers per operand as separate objects, so the compiler can tell
   // the tile being computed from the one being loaded
-  __shared__ __attribute__((aligned(1024))) bf16 kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kb0[KTILE];
+  __shared__ __attribute__((aligned(1024))) bf16 kb1[KTILE];
   __shared__ __attribute__((aligned(1024))) bf16 vb0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vb1[TILE];
   __shared__ __attribute__((aligned(256))) int sb0[64];
@@ -379,22 +475,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
-  const int qrow = qt * kFwdBQ + 32 * w + lc;
-  TileDma<DP, true> kd;
-  TileDma<DP, false> vd;
+  int qrow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) qrow[nb] = qt * kFwdRows + 32 * kNB * w + 32 * nb + lc;
+  PadTileDma<DP, true, kFwdWaves> kd;
+  TileDma<DP, false, kFwdWaves> vd;
   kd.init(w, lane);
   vd.init(w, lane);
+  FwdAddr<DP> ad;
+  ad.k = lc * (DP + 8) + 8 * lg;
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+      ad.v[hi][b] = toff<DP>(8 * lg + ((lane & 15) >> 2) + 4 * hi, 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-  bf16x8 qop[KS];
-  {
-    const bf16* qb = qr + ((size_t)h * Tp + qrow) * DP + 8 * lg;
+  bf16x8 qop[kNB][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = load8(qb + 16 * s);
+  for (int nb = 0; nb < kNB; ++nb) {
+    const bf16* qb = qr + ((size_t)h * Tp + qrow[nb]) * DP + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qop[nb][s] = load8(qb + 16 * s);
   }
-  f32x16 acc[NDB];
+  f32x16 acc[kNB][NDB];
+  FwdState st[kNB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
-  FwdState st{kNegInf, 0.0f};
+  for (int nb = 0; nb < kNB; ++nb) {
+    st[nb] = FwdState{kNegInf, 0.0f};
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) acc[nb][b] = f32x16{};
+  }
 
   const int cnt = counts[qt];
   const int* lst = lists + (size_t)qt * nk;
@@ -402,36 +512,51 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const bf16* vg = vr + (size_t)hk * Tp * DP;
 
   if (cnt > 0) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[0] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
+  // this wave's own rows [r0, r1): a key tile can be empty or full for them
+  // even when it is partial for the whole query tile
+  const int r0 = qt * kFwdRows + 32 * kNB * w;
+  const int r1 = min(r0 + 32 * kNB, T);
+  auto wave_tile = [&](int e, const bf16* kb, const bf16* vb, const int* sb) {
+    const int kt = e >> 1;
+    const int j0 = kt * kFwdBK;
+    const int2 m = kmm[kt];
+    if (r0 >= r1 || j0 > r1 - 1 || m.y <= r0) return;  // nothing visible to this wave
+    const bool full = (e & 1) || ((j0 + kFwdBK - 1 <= r0) && (m.x >= r1));
+    fwd_tile<DP>(kb, vb, sb, full, j0, qrow, lg, ad, sl2, qop, acc, st);
+  };
   for (int it = 0; it < cnt; it += 2) {
     {
       const int e = lst[it];
       wait_dma();
       __syncthreads();
       if (it + 1 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1, w, lane);
-      fwd_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, qop, acc, st);
+      wave_tile(e, kb0, vb0, sb0);
     }
     if (it + 1 < cnt) {
       const int e = lst[it + 1];
       wait_dma();
       __syncthreads();
       if (it + 2 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
-      fwd_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, qop, acc, st);
+      wave_tile(e, kb1, vb1, sb1);
     }
   }
 
-  const float lt = st.lsum + __shfl_xor(st.lsum, 32);
-  if (qrow < T) {
-    const float inv = 1.0f / lt;
-    Tio* orow = o + ((size_t)qrow * Hq + h) * D;
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float lt = st[nb].lsum + __shfl_xor(st[nb].lsum, 32);
+    if (qrow[nb] < T) {
+      const float inv = 1.0f / lt;
+      Tio* orow = o + ((size_t)qrow[nb] * Hq + h) * D;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * b + 8 * (i >> 2) + 4 * lg + (i & 3);
-        if (d < D) orow[d] = from_f32<Tio>(acc[b][i] * inv);
-      }
-    const float mu = (st.mref == kNegInf) ? 0.0f : st.mref;
-    if (lg == 0) lse[(size_t)h * T + qrow] = (mu + log2f(lt)) * kLn2;
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = 32 * b + 8 * (i >> 2) + 4 * lg + (i & 3);
+          if (d < D) orow[d] = from_f32<Tio>(acc[nb][b][i] * inv);
+        }
+      const float mu = (st[nb].mref == kNegInf) ? 0.0f : st[nb].mref;
+      if (lg == 0) lse[(size_t)h * T + qrow[nb]] = (mu + log2f(lt)) * kLn2;
+    }
   }
 }
 
@@ -446,16 +571,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 // lse * log2(e) and a bf16 head-major copy of dO for the dK/dV kernel.
 template <int DP>
 __device__ __forceinline__ void dq_tile(const bf16* kb, const bf16* vb, const int* sb, bool full, int j0, int qrow,
-                                        int lane, int lg, int lc, float sl2, float lse2, float dval,
+                                        int lg, const SwzAddr<DP>& ad, float sl2, float lse2, float dval,
                                         const bf16x8* qop, const bf16x8* dop, f32x16* acc) {
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
+  sched_hint();
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      const int off = toff<DP>(32 * mb + lc, 16 * k + 8 * lg);
+      const int off = ad.op[k] + 32 * mb * DP;
       s = mfma32x32x16(lds128(kb + off), qop[k], s);
       dp = mfma32x32x16(lds128(vb + off), dop[k], dp);
     }
@@ -485,12 +611,9 @@ __device__ __forceinline__ void dq_tile(const bf16* kb, const bf16* vb, const in
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        // K'^T operand: rows d = 32b + lane%32, k slots = keys 16t + 8lg + s
-        const int kb0 = 32 * mb + 16 * t2 + 8 * lg;
-        const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const int r0 = perm_row(kb0) + ((lane & 15) >> 2);
-        const int r1 = perm_row(kb0 + 4) + ((lane & 15) >> 2);
-        const bf16x8 a = cat(lds_read_tr(kb + toff<DP>(r0, col)), lds_read_tr(kb + toff<DP>(r1, col)));
+        // K'^T operand: rows d = 32b + lane%32, k slots = keys 32mb + 16t2 + 8lg + s
+        const int r0 = (32 * mb + 16 * t2) * DP;
+        const bf16x8 a = cat(lds_read_tr(kb + ad.tr[b] + r0), lds_read_tr(kb + ad.tr[b] + r0 + 8 * DP));
         acc[b] = mfma32x32x16(a, db8[t2], acc[b]);
       }
   }
@@ -529,6 +652,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const bool qok = qrow < T;
   TileDma<DP, true> td;
   td.init(w, lane);
+  SwzAddr<DP> ad;
+  ad.init(lane);
 
   bf16x8 qop[KS], dop[KS];
   float dval = 0.0f;
@@ -574,14 +699,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       wait_dma();
       __syncthreads();
       if (it + 1 < cnt) issue((lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1);
-      dq_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, lse2, dval, qop, dop, acc);
+      dq_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
     }
     if (it + 1 < cnt) {
       const int e = lst[it + 1];
       wait_dma();
       __syncthreads();
       if (it + 2 < cnt) issue((lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0);
-      dq_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lane, lg, lc, sl2, lse2, dval, qop, dop, acc);
+      dq_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
     }
   }
 
@@ -620,19 +745,35 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // dK back (R(pos)^T) through an LDS transpose and writes both once.
 template <int DP>
 __device__ __forceinline__ void dkdv_tile(const bf16* qs_, const bf16* ds_, const float* ls, const float* dl,
-                                          bool full, int i0, int key, int myse, int lane, int lg, int lc, float sl2,
-                                          const bf16x8* kop, const bf16x8* vop, f32x16* acck, f32x16* accv) {
+                                          bool full, int i0, int key, int myse, int lg, const SwzAddr<DP>& ad,
+                                          float sl2, const bf16x8* kop, const bf16x8* vop, f32x16* acck,
+                                          f32x16* accv) {
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    f32x16 s = f32x16{}, dp = f32x16{};
+  sched_hint();
+  // S and dP of one 32-row half, then its softmax work and dV / dK products
+  // (computing both halves' S and dP first measured slower: more live
+  // registers for no extra overlap).
+  f32x16 s[2], dp[2];
+  auto products = [&](int mb) {
+    s[mb] = f32x16{};
+    dp[mb] = f32x16{};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      const int off = toff<DP>(32 * mb + lc, 16 * k + 8 * lg);
-      s = mfma32x32x16(lds128(qs_ + off), kop[k], s);
-      dp = mfma32x32x16(lds128(ds_ + off), vop[k], dp);
+      const int off = ad.op[k] + 32 * mb * DP;
+      s[mb] = mfma32x32x16(lds128(qs_ + off), kop[k], s[mb]);
+      dp[mb] = mfma32x32x16(lds128(ds_ + off), vop[k], dp[mb]);
     }
+  };
+#if TA_DKDV_SFIRST
+  products(0);
+  products(1);
+#endif
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#if !TA_DKDV_SFIRST
+    products(mb);
+#endif
     // C register i <-> query row c_row(mb, i, lg) of this block; lane <-> key
     bf16x8 pa[2], sa[2];
 #pragma unroll
@@ -645,26 +786,26 @@ __device__ __forceinline__ void dkdv_tile(const bf16* qs_, const bf16* ds_, cons
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int i = 4 * q4 + b;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lv[b]));
+        float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, -lv[b]));
         if (!full) {
           const int iq = i0 + qi0 + b;
           p = ((key <= iq) & (iq < myse)) ? p : 0.0f;
         }
         pa[i >> 3][i & 7] = (bf16)p;
-        sa[i >> 3][i & 7] = (bf16)(p * (dp[i] - dv4[b]));
+        sa[i >> 3][i & 7] = (bf16)(p * (dp[mb][i] - dv4[b]));
       }
     }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      const int qb0 = 32 * mb + 16 * t2 + 8 * lg;  // natural query row of slot 0
-      const int r0 = perm_row(qb0) + ((lane & 15) >> 2);
-      const int r1 = perm_row(qb0 + 4) + ((lane & 15) >> 2);
+      // natural query rows 32mb + 16t2 + 8lg + s sit in LDS rows
+      // 32mb + 16t2 + 4lg + (s / 4) * 8 + s % 4 (perm_row order)
+      const int r0 = (32 * mb + 16 * t2) * DP;
+      const int r1 = r0 + 8 * DP;
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
-        const int col = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const bf16x8 bdo = cat(lds_read_tr(ds_ + toff<DP>(r0, col)), lds_read_tr(ds_ + toff<DP>(r1, col)));
+        const bf16x8 bdo = cat(lds_read_tr(ds_ + ad.tr[b] + r0), lds_read_tr(ds_ + ad.tr[b] + r1));
         accv[b] = mfma32x32x16(pa[t2], bdo, accv[b]);
-        const bf16x8 bq = cat(lds_read_tr(qs_ + toff<DP>(r0, col)), lds_read_tr(qs_ + toff<DP>(r1, col)));
+        const bf16x8 bq = cat(lds_read_tr(qs_ + ad.tr[b] + r0), lds_read_tr(qs_ + ad.tr[b] + r1));
         acck[b] = mfma32x32x16(sa[t2], bq, acck[b]);
       }
     }
@@ -672,7 +813,7 @@ __device__ __forceinline__ void dkdv_tile(const bf16* qs_, const bf16* ds_, cons
 }
 
 template <int DP, typename Tio>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, TA_DKDV_WAVES_PER_EU) void attn_bwd_dkdv_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const bf16* __restrict__ dor, const float* __restrict__ l2, const float* __restrict__ dd,
     const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ korder,
@@ -706,6 +847,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int myse = sep[key];
   TileDma<DP, true> td;
   td.init(w, lane);
+  SwzAddr<DP> ad;
+  ad.init(lane);
 
   bf16x8 kop[KS], vop[KS];
   {
@@ -741,26 +884,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const int i0 = (qb_lo + it % nqb) * BQ;
     return (j0 + kBwdBK - 1 <= i0) && (mm.x >= min(i0 + BQ, T));
   };
+  // Two query blocks in LDS (the one computed, the one loaded), as separate
+  // arrays and an unrolled pair of iterations so the compiler can tell them
+  // apart. Deeper pipelines measured slower on gfx950: LDS bandwidth, not
+  // load latency, bounds this loop.
   if (n_it > 0) issue(0, qb0, ob0, lb0, db0);
   for (int it = 0; it < n_it; it += 2) {
     {
       wait_dma();
       __syncthreads();
       if (it + 1 < n_it) issue(it + 1, qb1, ob1, lb1, db1);
-      dkdv_tile<DP>(qb0, ob0, lb0, db0, tile_full(it), (qb_lo + it % nqb) * BQ, key, myse, lane, lg, lc, sl2, kop,
-                    vop, acck, accv);
+      dkdv_tile<DP>(qb0, ob0, lb0, db0, tile_full(it), (qb_lo + it % nqb) * BQ, key, myse, lg, ad, sl2, kop, vop,
+                    acck, accv);
     }
     if (it + 1 < n_it) {
       wait_dma();
       __syncthreads();
       if (it + 2 < n_it) issue(it + 2, qb0, ob0, lb0, db0);
-      dkdv_tile<DP>(qb1, ob1, lb1, db1, tile_full(it + 1), (qb_lo + (it + 1) % nqb) * BQ, key, myse, lane, lg, lc,
-                    sl2, kop, vop, acck, accv);
+      dkdv_tile<DP>(qb1, ob1, lb1, db1, tile_full(it + 1), (qb_lo + (it + 1) % nqb) * BQ, key, myse, lg, ad, sl2,
+                    kop, vop, acck, accv);
     }
   }
 
   // Epilogue: stage each wave's 32 x DP block in LDS as [key][d] f32 (the
-  // tile buffers are free now; 4 waves x 32 x SE floats fit in them).
+  // tile buffers are free now; one wave's block fills one tile buffer).
   static_assert(32 * SE * 4 <= TILE * 2, "a wave's epilogue block must fit in one tile buffer");
   __syncthreads();
   float* ep = reinterpret_cast<float*>(w < 2 ? (w == 0 ? qb0 : qb1) : (w == 2 ? ob0 : ob1));
@@ -801,7 +948,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 // Host side
 struct AttnLayout {
   int T, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
+  int nqf;  // forward query tiles (kFwdRows rows)
   size_t off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qorder, off_qlist;
+  size_t off_fcount, off_forder, off_flist;
   size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
 
@@ -810,12 +959,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   AttnLayout L{};
   L.T = T;
-  L.Tp = (T + kFwdBQ - 1) / kFwdBQ * kFwdBQ;
+  L.Tp = (T + 255) / 256 * 256;  // a multiple of every query tile size
   L.Hq = Hq;
   L.Hkv = Hkv;
   L.D = D;
   L.DP = D < 32 ? 32 : D;
   L.nq = L.Tp / kFwdBQ;
+  L.nqf = L.Tp / kFwdRows;
   L.nk64 = (T + kFwdBK - 1) / kFwdBK;
   L.nk128 = (T + kBwdBK - 1) / kBwdBK;
   size_t o = 0;
@@ -834,6 +984,15 @@ AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   L.off_qcount = take((size_t)L.nq * 4);
   L.off_qorder = take((size_t)L.nq * 4);
   L.off_qlist = take((size_t)L.nq * L.nk64 * 4);
+  if (kFwdRows == kFwdBQ) {  // the forward shares the dQ pass's plan
+    L.off_fcount = L.off_qcount;
+    L.off_forder = L.off_qorder;
+    L.off_flist = L.off_qlist;
+  } else {
+    L.off_fcount = take((size_t)L.nqf * 4);
+    L.off_forder = take((size_t)L.nqf * 4);
+    L.off_flist = take((size_t)L.nqf * L.nk64 * 4);
+  }
   L.off_kwork = take((size_t)L.nk128 * 4);
   L.off_korder = take((size_t)L.nk128 * 4);
   if (with_bwd) {
@@ -883,6 +1042,12 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
                      kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
   hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
                      at<int>(ws, L.off_qorder));
+  if (kFwdRows != kFwdBQ) {
+    hipLaunchKernelGGL(q_plan_kernel, dim3(L.nqf), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.T, kFwdRows,
+                       kFwdBK, L.nk64, at<int>(ws, L.off_fcount), at<int>(ws, L.off_flist));
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_fcount), L.nqf,
+                       at<int>(ws, L.off_forder));
+  }
   hipLaunchKernelGGL(k_work_kernel, dim3((L.nk128 + 255) / 256), dim3(256), 0, st,
                      at<const int2>(ws, L.off_kmm128), L.nk128, at<int>(ws, L.off_kwork));
   hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_kwork), L.nk128,
@@ -893,10 +1058,11 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
 template <int DP, typename Tio>
 int run_fwd(const AttnLayout& L, float sl2, void* o, float* lse, char* ws, hipStream_t st) {
   ProfScope ps("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st, at<const bf16>(ws, L.off_qr),
-                     at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr), at<const int>(ws, L.off_sep),
-                     at<const int>(ws, L.off_qcount), at<const int>(ws, L.off_qlist),
-                     at<const int>(ws, L.off_qorder), L.T, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64, sl2,
+  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nqf * L.Hq), dim3(64 * kFwdWaves), 0, st,
+                     at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
+                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_fcount),
+                     at<const int>(ws, L.off_flist), at<const int>(ws, L.off_forder), L.T, L.Tp, L.Hq, L.Hkv, L.nqf,
+                     L.nk64, sl2,
                      static_cast<Tio*>(o), lse);
   return check_launch("tree_attn_fwd");
 }
