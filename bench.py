@@ -41,10 +41,9 @@ DESCR = {
 KERNEL_FLOPS = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 
 
-def cpu_baseline(seqs, groups, cfg):
-    """The float64 oracle (per-branch fwd + bwd) on tree 0 and kv group 0."""
-    import numpy as np
-
+def cpu_baseline(seqs, groups, cfg, n_trees=2, n_groups=2):
+    """The float64 oracle (per-branch fwd + bwd) on the first n_trees trees x
+    the first n_groups kv groups of the workload (a bounded sample)."""
     import workloads
     from oracle import attention as OA
     from oracle import pack as OP
@@ -56,21 +55,49 @@ def cpu_baseline(seqs, groups, cfg):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     po = OP.pack(seqs, groups)
-    ts, te = int(po["tree_start"][0]), int(po["tree_start"][1])
-    par = po["par"][ts:te].copy()
-    par[par >= 0] -= ts
+    n_trees = min(n_trees, len(po["tree_start"]) - 1)
     G = cfg["Hq"] // cfg["Hkv"]
-    q, k, v, do = workloads.dense_inputs(te - ts, G, 1, cfg["d"], "bf16", 77)
     f = lambda t: t.float().numpy()
-    t0 = time.perf_counter()
-    OA.forward_branches(f(q), f(k), f(v), par, po["pos"][ts:te], check_agree=False)
-    OA.backward_branches(f(q), f(k), f(v), f(do), par, po["pos"][ts:te])
-    dt = time.perf_counter() - t0
-    P = int((po["pos"][ts:te] + 1).sum())
-    flops = 14.0 * cfg["d"] * P * G
+    dt, flops, toks = 0.0, 0.0, 0
+    for tr in range(n_trees):
+        ts, te = int(po["tree_start"][tr]), int(po["tree_start"][tr + 1])
+        par = po["par"][ts:te].copy()
+        par[par >= 0] -= ts
+        P = int((po["pos"][ts:te] + 1).sum())
+        toks += te - ts
+        for g in range(n_groups):
+            q, k, v, do = workloads.dense_inputs(te - ts, G, 1, cfg["d"], "bf16", 77 + 100 * tr + g)
+            t0 = time.perf_counter()
+            OA.forward_branches(f(q), f(k), f(v), par, po["pos"][ts:te], check_agree=False)
+            OA.backward_branches(f(q), f(k), f(v), f(do), par, po["pos"][ts:te])
+            dt += time.perf_counter() - t0
+            flops += 14.0 * cfg["d"] * P * G
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"tree 0 ({te - ts} tokens) x kv group 0 ({G} q heads), fwd+bwd, float64 NumPy, "
-                      f"{dt:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP"}
+            "sample": f"trees 0..{n_trees - 1} ({toks} tokens) x kv groups 0..{n_groups - 1} ({G} q heads each), "
+                      f"fwd+bwd, float64 NumPy, {dt:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP"}
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per dispatch of `kernel` from the committed
+    rocprofv3 counter summaries, if they were taken on the current library
+    sources (else None)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for fn in sorted(glob.glob(os.path.join(ROOT, "tree_packed_attention_amd", "csrc", "*"))):
+        if fn.endswith((".hip", ".cpp", ".h")):
+            with open(fn, "rb") as fh:
+                h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(fn) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("source_sha") == sha and kernel in rec.get("bytes_per_dispatch", {}):
+                        return int(rec["bytes_per_dispatch"][kernel])
+    return None
 
 
 def main():
@@ -144,7 +171,8 @@ def main():
     dom = max((n for n in kernel_ms if n in KERNEL_FLOPS), key=lambda n: kernel_ms[n])
     achieved = KERNEL_FLOPS[dom] * d * P * Hq / (kernel_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom + "_kernel"), "traffic_unit": "bytes per launch (HBM, calibrated)",
                 "flops_per_launch": KERNEL_FLOPS[dom] * d * P * Hq}
 
     lp = None
