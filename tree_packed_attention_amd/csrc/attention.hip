@@ -51,12 +51,6 @@
 #ifndef TA_IGLP
 #define TA_IGLP -1  // >= 0: __builtin_amdgcn_iglp_opt(TA_IGLP) in the tile bodies
 #endif
-#ifndef TA_DKDV_WAVES_PER_EU
-#define TA_DKDV_WAVES_PER_EU 1
-#endif
-#ifndef TA_DKDV_SFIRST
-#define TA_DKDV_SFIRST 0  // 1: dK/dV computes both halves' S and dP before their softmax work
-#endif
 #ifndef TA_FWD_WAVES
 #define TA_FWD_WAVES 4  // forward workgroup: TA_FWD_WAVES waves x 32 query rows
 #endif
@@ -735,85 +729,99 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------------
-// Backward dK / dV. One workgroup owns 128 keys of one kv head (4 waves x 32
-// keys, K' and V rows held in registers) and loops over the query blocks its
-// keys can see, for every query head of the group. The visible queries of a
-// key tile form the contiguous range [j0, max se), so no list is needed.
+// Backward dK / dV. One workgroup owns 128 keys of one kv head and loops over
+// the 64-row query blocks those keys can see, for every query head of the
+// group. The visible queries of a key tile form the contiguous range
+// [j0, max se), so no list is needed.
 //   S = Q' K'^T, P = exp2(S*scale*log2e - lse*log2e), dP = dO V^T
 //   dS = P (dP - D);  dV += P^T dO;  dK' += dS^T Q'
-// The accumulators never leave registers until the epilogue, which rotates
-// dK back (R(pos)^T) through an LDS transpose and writes both once.
+// Eight waves: key slice ks = w % 4 (32 keys) x role m = w / 4; both waves of
+// a slice sit on the same SIMD. The m = 0 wave holds the slice's K' rows,
+// computes S and P for all 64 rows and accumulates dV; the m = 1 wave holds
+// the V rows, computes dP, takes P (bf16, as the dV product uses it) from
+// its partner through LDS, forms dS and accumulates dK. Both run the same
+// MFMA sequence on different operands: 32 MFMAs per block, one 32 x DP
+// accumulator and one operand set per wave, all in VGPRs. The epilogue
+// rotates dK back (R(pos)^T) through an LDS transpose and writes both once;
+// no atomics, so results are reproducible.
+constexpr int kDkdvWaves = 8;
+
 template <int DP>
-__device__ __forceinline__ void dkdv_tile(const bf16* qs_, const bf16* ds_, const float* ls, const float* dl,
-                                          bool full, int i0, int key, int myse, int lg, const SwzAddr<DP>& ad,
-                                          float sl2, const bf16x8* kop, const bf16x8* vop, f32x16* acck,
-                                          f32x16* accv) {
+__device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const float* rowv, bool full, int m,
+                                          int rel_lo, int rel_hi, int lg, const SwzAddr<DP>& ad, float sl2,
+                                          const bf16x8* op, bf16x8* xch, f32x16* acc) {
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
   sched_hint();
-  // S and dP of one 32-row half, then its softmax work and dV / dK products
-  // (computing both halves' S and dP first measured slower: more live
-  // registers for no extra overlap).
-  f32x16 s[2], dp[2];
-  auto products = [&](int mb) {
-    s[mb] = f32x16{};
-    dp[mb] = f32x16{};
+  // role 0: S = Q' K'^T (xs = Q' tile); role 1: dP = dO V^T (xs = dO tile)
+  f32x16 x[2];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int off = ad.op[k] + 32 * mb * DP;
-      s[mb] = mfma32x32x16(lds128(qs_ + off), kop[k], s[mb]);
-      dp[mb] = mfma32x32x16(lds128(ds_ + off), vop[k], dp[mb]);
-    }
-  };
-#if TA_DKDV_SFIRST
-  products(0);
-  products(1);
-#endif
+  for (int mb = 0; mb < 2; ++mb) x[mb] = f32x16{};
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#if !TA_DKDV_SFIRST
-    products(mb);
-#endif
-    // C register i <-> query row c_row(mb, i, lg) of this block; lane <-> key
-    bf16x8 pa[2], sa[2];
+  for (int k = 0; k < KS; ++k)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
-      const float4 l4 = *reinterpret_cast<const float4*>(ls + qi0);
-      const float4 d4 = *reinterpret_cast<const float4*>(dl + qi0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int mb = 0; mb < 2; ++mb) x[mb] = mfma32x32x16(lds128(xs + ad.op[k] + 32 * mb * DP), op[k], x[mb]);
+  // C register i of block mb <-> query row c_row(mb, i, lg); lane <-> key.
+  // a[2 mb + t2] is the A operand (keys x 16 query rows) of the second product.
+  bf16x8 a[4];
+  if (m == 0) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int i = 4 * q4 + b;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], sl2, -lv[b]));
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
+        const float4 l4 = *reinterpret_cast<const float4*>(rowv + qi0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float p[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(fmaf(x[mb][4 * q4 + b], sl2, -lv[b]));
         if (!full) {
-          const int iq = i0 + qi0 + b;
-          p = ((key <= iq) & (iq < myse)) ? p : 0.0f;
+          // this lane's key sees block rows [rel_lo, rel_hi)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) p[b] = ((qi0 + b >= rel_lo) & (qi0 + b < rel_hi)) ? p[b] : 0.0f;
         }
-        pa[i >> 3][i & 7] = (bf16)p;
-        sa[i >> 3][i & 7] = (bf16)(p * (dp[mb][i] - dv4[b]));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a[2 * mb + (q4 >> 1)][4 * (q4 & 1) + b] = (bf16)p[b];
       }
-    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xch[64 * j] = a[j];
+  }
+  __syncthreads();
+  if (m == 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = xch[64 * j];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
+        const float4 d4 = *reinterpret_cast<const float4*>(rowv + qi0);
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int j = 2 * mb + (q4 >> 1), e = 4 * (q4 & 1) + b;
+          a[j][e] = (bf16)((float)a[j][e] * (x[mb][4 * q4 + b] - dv4[b]));
+        }
+      }
+  }
+  // role 0: dV += P^T dO (ys = dO tile); role 1: dK' += dS^T Q' (ys = Q' tile)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       // natural query rows 32mb + 16t2 + 8lg + s sit in LDS rows
       // 32mb + 16t2 + 4lg + (s / 4) * 8 + s % 4 (perm_row order)
       const int r0 = (32 * mb + 16 * t2) * DP;
-      const int r1 = r0 + 8 * DP;
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
-        const bf16x8 bdo = cat(lds_read_tr(ds_ + ad.tr[b] + r0), lds_read_tr(ds_ + ad.tr[b] + r1));
-        accv[b] = mfma32x32x16(pa[t2], bdo, accv[b]);
-        const bf16x8 bq = cat(lds_read_tr(qs_ + ad.tr[b] + r0), lds_read_tr(qs_ + ad.tr[b] + r1));
-        acck[b] = mfma32x32x16(sa[t2], bq, acck[b]);
+        const bf16x8 bt = cat(lds_read_tr(ys + ad.tr[b] + r0), lds_read_tr(ys + ad.tr[b] + r0 + 8 * DP));
+        acc[b] = mfma32x32x16(a[2 * mb + t2], bt, acc[b]);
       }
     }
-  }
 }
 
 template <int DP, typename Tio>
-__global__ __launch_bounds__(256, TA_DKDV_WAVES_PER_EU) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const bf16* __restrict__ dor, const float* __restrict__ l2, const float* __restrict__ dd,
     const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ korder,
@@ -833,6 +841,8 @@ __global__ __launch_bounds__(256, TA_DKDV_WAVES_PER_EU) void attn_bwd_dkdv_kerne
   __shared__ __attribute__((aligned(256))) float lb1[BQ];
   __shared__ __attribute__((aligned(256))) float db0[BQ];
   __shared__ __attribute__((aligned(256))) float db1[BQ];
+  // P exchange: [key slice][4 operands][lane] 16 bytes
+  __shared__ __attribute__((aligned(1024))) bf16x8 xb[4 * 4 * 64];
 
   const int G = Hq / Hkv;
   const int lid = xcd_remap(blockIdx.x, nkb * Hkv);
@@ -841,91 +851,102 @@ __global__ __launch_bounds__(256, TA_DKDV_WAVES_PER_EU) void attn_bwd_dkdv_kerne
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = w & 3, m = w >> 2;
   const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int j0 = kt * kBwdBK;
-  const int key = j0 + 32 * w + lc;
+  const int key = j0 + 32 * ks + lc;
   const int myse = sep[key];
-  TileDma<DP, true> td;
+  TileDma<DP, true, kDkdvWaves> td;
   td.init(w, lane);
   SwzAddr<DP> ad;
   ad.init(lane);
+  bf16x8* xch = xb + ks * 256 + lane;
 
-  bf16x8 kop[KS], vop[KS];
+  // role 0 holds K' rows, role 1 V rows, as MFMA B operands
+  bf16x8 op[KS];
   {
-    const bf16* kb = kr + ((size_t)hk * Tp + key) * DP + 8 * lg;
-    const bf16* vb = vr + ((size_t)hk * Tp + key) * DP + 8 * lg;
+    const bf16* ob = (m == 0 ? kr : vr) + ((size_t)hk * Tp + key) * DP + 8 * lg;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kop[s] = load8(kb + 16 * s);
-      vop[s] = load8(vb + 16 * s);
-    }
+    for (int s = 0; s < KS; ++s) op[s] = load8(ob + 16 * s);
   }
-  f32x16 acck[NDB], accv[NDB];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) {
-    acck[b] = f32x16{};
-    accv[b] = f32x16{};
-  }
+  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
 
   const int2 mm = kmm[kt];
   const int qb_lo = j0 / BQ;
   const int nqb = (mm.y + BQ - 1) / BQ - qb_lo;
   const int n_it = G * nqb;
 
-  auto issue = [&](int it, bf16* qs_, bf16* ds_, float* ls, float* dl) {
-    const int h = hk * G + it / nqb;
-    const int i0 = (qb_lo + it % nqb) * BQ;
+  // iteration it covers query head hk * G + it / nqb, block qb_lo + it % nqb;
+  // (hh, qq) track that pair for the block being loaded next
+  int hh = 0, qq = 0;
+  auto issue = [&](bf16* qs_, bf16* ds_, float* lsb, float* dlb) {
+    const int h = hk * G + hh;
+    const int i0 = (qb_lo + qq) * BQ;
     td.issue(qr + ((size_t)h * Tp + i0) * DP, qs_, w);
     td.issue(dor + ((size_t)h * Tp + i0) * DP, ds_, w);
-    if (w == 0) dma4(l2 + (size_t)h * Tp + i0 + lane, ls);
-    if (w == 1) dma4(dd + (size_t)h * Tp + i0 + lane, dl);
+    if (w == 0) dma4(l2 + (size_t)h * Tp + i0 + lane, lsb);
+    if (w == 1) dma4(dd + (size_t)h * Tp + i0 + lane, dlb);
+    if (++qq == nqb) {
+      qq = 0;
+      ++hh;
+    }
   };
-  auto tile_full = [&](int it) {
-    const int i0 = (qb_lo + it % nqb) * BQ;
-    return (j0 + kBwdBK - 1 <= i0) && (mm.x >= min(i0 + BQ, T));
+  auto tile = [&](int cq, const bf16* qs_, const bf16* ds_, const float* lsb, const float* dlb) {
+    const int i0 = (qb_lo + cq) * BQ;
+    const bool full = (j0 + kBwdBK - 1 <= i0) && (mm.x >= min(i0 + BQ, T));
+    dkdv_tile<DP>(m == 0 ? qs_ : ds_, m == 0 ? ds_ : qs_, m == 0 ? lsb : dlb, full, m, key - i0, myse - i0, lg, ad,
+                  sl2, op, xch, acc);
   };
   // Two query blocks in LDS (the one computed, the one loaded), as separate
   // arrays and an unrolled pair of iterations so the compiler can tell them
-  // apart. Deeper pipelines measured slower on gfx950: LDS bandwidth, not
-  // load latency, bounds this loop.
-  if (n_it > 0) issue(0, qb0, ob0, lb0, db0);
+  // apart.
+  if (n_it > 0) issue(qb0, ob0, lb0, db0);
+  int cq = 0;  // block index (within the head) of the block being computed
   for (int it = 0; it < n_it; it += 2) {
     {
       wait_dma();
       __syncthreads();
-      if (it + 1 < n_it) issue(it + 1, qb1, ob1, lb1, db1);
-      dkdv_tile<DP>(qb0, ob0, lb0, db0, tile_full(it), (qb_lo + it % nqb) * BQ, key, myse, lg, ad, sl2, kop, vop,
-                    acck, accv);
+      if (it + 1 < n_it) issue(qb1, ob1, lb1, db1);
+      tile(cq, qb0, ob0, lb0, db0);
+      if (++cq == nqb) cq = 0;
     }
     if (it + 1 < n_it) {
       wait_dma();
       __syncthreads();
-      if (it + 2 < n_it) issue(it + 2, qb0, ob0, lb0, db0);
-      dkdv_tile<DP>(qb1, ob1, lb1, db1, tile_full(it + 1), (qb_lo + (it + 1) % nqb) * BQ, key, myse, lg, ad, sl2,
-                    kop, vop, acck, accv);
+      if (it + 2 < n_it) issue(qb0, ob0, lb0, db0);
+      tile(cq, qb1, ob1, lb1, db1);
+      if (++cq == nqb) cq = 0;
     }
   }
 
-  // Epilogue: stage each wave's 32 x DP block in LDS as [key][d] f32 (the
-  // tile buffers are free now; one wave's block fills one tile buffer).
-  static_assert(32 * SE * 4 <= TILE * 2, "a wave's epilogue block must fit in one tile buffer");
+  // Epilogue, dK (pass 0) then dV (pass 1): the waves holding that gradient
+  // stage their 32 x DP block in LDS as [key][d] f32 (one tile buffer per key
+  // slice; the tile buffers are free now), then all waves write 16 keys each.
+  static_assert(32 * SE * 4 <= TILE * 2, "a key slice's epilogue block must fit in one tile buffer");
   __syncthreads();
-  float* ep = reinterpret_cast<float*>(w < 2 ? (w == 0 ? qb0 : qb1) : (w == 2 ? ob0 : ob1));
   constexpr int half = D / 2;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
+    if (m == 1 - pass) {
+      float* ep = reinterpret_cast<float*>(ks < 2 ? (ks == 0 ? qb0 : qb1) : (ks == 2 ? ob0 : ob1));
+      const float mul = pass == 0 ? scale : 1.0f;
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
+      for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * lg + (i & 3);
-        ep[r * SE + 32 * b + lc] = pass == 0 ? acck[b][i] * scale : accv[b][i];
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * lg + (i & 3);
+          ep[r * SE + 32 * b + lc] = acc[b][i] * mul;
+        }
+    }
     __syncthreads();
-    for (int r = 0; r < 32; ++r) {
-      const int j = j0 + 32 * w + r;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = 16 * w + rr;  // key row within the workgroup's 128
+      const int j = j0 + r;
       if (j >= T) break;
-      const float* er = ep + r * SE;
+      const bf16* eb = (r >> 5) < 2 ? ((r >> 5) == 0 ? qb0 : qb1) : ((r >> 5) == 2 ? ob0 : ob1);
+      const float* er = reinterpret_cast<const float*>(eb) + (r & 31) * SE;
       if (pass == 0) {
         Tio* out = dk + ((size_t)j * Hkv + hk) * D;
         const float2* csr = cs + (size_t)j * half;
@@ -1081,7 +1102,7 @@ int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* do
                        L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
   }
   ProfScope ps("attn_bwd_dkdv", st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.nk128 * L.Hkv), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.nk128 * L.Hkv), dim3(64 * kDkdvWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
                      at<const bf16>(ws, L.off_dor), at<const float>(ws, L.off_l2), at<const float>(ws, L.off_dd),
                      at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm128), at<const int>(ws, L.off_korder),
