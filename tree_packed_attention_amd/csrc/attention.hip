@@ -20,7 +20,7 @@
 //                                        query tile (2 * tile + full flag);
 //                                        qorder = query tiles, heaviest first
 //   kwork, korder [nk128]                dK/dV work per 128-key tile, order
-//   dd, l2 [Hq][Tp] f32                  rowsum(dO * O) and lse * log2(e)
+//   dd, l2 [Hq][Tp] f32                  -rowsum(dO * O) and -lse / scale
 //   dor [Hq][Tp][DP] bf16                dO, head-major (written by dQ pass)
 //
 // Products use v_mfma_f32_32x32x16_bf16 with float32 accumulation. The
@@ -460,10 +460,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
   __shared__ __attribute__((aligned(256))) int sb1[64];
 
   const int G = Hq / Hkv;
+  // kv-head-major: consecutive workgroups (one XCD's share) work on one kv
+  // head, the G query heads of a query tile side by side, so K' / V tiles
+  // are reused from that XCD's L2; query tiles in heaviest-first order
   const int lid = xcd_remap(blockIdx.x, nq * Hq);
   const int gq = lid % G;
-  const int hk = (lid / G) % Hkv;
-  const int qt = order[lid / Hq];
+  const int hk = lid / (G * nq);
+  const int qt = order[(lid / G) % nq];
   const int h = hk * G + gq;
 
   const int tid = threadIdx.x;
@@ -633,10 +636,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(256))) int sb1[64];
 
   const int G = Hq / Hkv;
+  // kv-head-major: consecutive workgroups (one XCD's share) work on one kv
+  // head, the G query heads of a query tile side by side, so K' / V tiles
+  // are reused from that XCD's L2; query tiles in heaviest-first order
   const int lid = xcd_remap(blockIdx.x, nq * Hq);
   const int gq = lid % G;
-  const int hk = (lid / G) % Hkv;
-  const int qt = order[lid / Hq];
+  const int hk = lid / (G * nq);
+  const int qt = order[(lid / G) % nq];
   const int h = hk * G + gq;
 
   const int tid = threadIdx.x;
@@ -668,8 +674,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   dval += __shfl_xor(dval, 32);
   const float lse2 = qok ? lse[(size_t)h * T + qrow] * kLog2e : 0.0f;
   if (lg == 0) {
-    dd[(size_t)h * Tp + qrow] = dval;
-    l2[(size_t)h * Tp + qrow] = lse2;
+    dd[(size_t)h * Tp + qrow] = -dval;
+    l2[(size_t)h * Tp + qrow] = qok ? -lse[(size_t)h * T + qrow] / scale : 0.0f;
   }
 
   f32x16 acc[NDB];
@@ -753,32 +759,43 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
   sched_hint();
-  // role 0: S = Q' K'^T (xs = Q' tile); role 1: dP = dO V^T (xs = dO tile)
+  // role 0: x = S - lse/scale = Q' K'^T + rowv (rowv holds -lse/scale);
+  // role 1: x = dP - D = dO V^T + rowv (rowv holds -D). The accumulators
+  // start at the per-row value, read from LDS straight into them.
+  // C register i of block mb <-> query row c_row(mb, i, lg); lane <-> key.
   f32x16 x[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) x[mb] = f32x16{};
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v = *reinterpret_cast<const float4*>(rowv + 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1));
+      x[mb][4 * q4 + 0] = v.x;
+      x[mb][4 * q4 + 1] = v.y;
+      x[mb][4 * q4 + 2] = v.z;
+      x[mb][4 * q4 + 3] = v.w;
+    }
 #pragma unroll
   for (int k = 0; k < KS; ++k)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) x[mb] = mfma32x32x16(lds128(xs + ad.op[k] + 32 * mb * DP), op[k], x[mb]);
-  // C register i of block mb <-> query row c_row(mb, i, lg); lane <-> key.
   // a[2 mb + t2] is the A operand (keys x 16 query rows) of the second product.
   bf16x8 a[4];
   if (m == 0) {
+    // P = exp2(x * scale * log2(e)); this lane's key sees block rows
+    // [rel_lo, rel_hi): row 8lg + c, c a compile-time constant, is compared
+    // with the bounds shifted by 8lg
+    const int lo8 = rel_lo - 8 * lg, hi8 = rel_hi - 8 * lg;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
-        const float4 l4 = *reinterpret_cast<const float4*>(rowv + qi0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const int c0 = 32 * mb + 16 * (q4 >> 1) + 4 * (q4 & 1);
         float p[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(fmaf(x[mb][4 * q4 + b], sl2, -lv[b]));
+        for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(x[mb][4 * q4 + b] * sl2);
         if (!full) {
-          // this lane's key sees block rows [rel_lo, rel_hi)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) p[b] = ((qi0 + b >= rel_lo) & (qi0 + b < rel_hi)) ? p[b] : 0.0f;
+          for (int b = 0; b < 4; ++b) p[b] = ((c0 + b >= lo8) & (c0 + b < hi8)) ? p[b] : 0.0f;
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) a[2 * mb + (q4 >> 1)][4 * (q4 & 1) + b] = (bf16)p[b];
@@ -788,20 +805,15 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
   }
   __syncthreads();
   if (m == 1) {
+    // dS = P (dP - D), P from the partner
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = xch[64 * j];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int qi0 = 32 * mb + 16 * (q4 >> 1) + 8 * lg + 4 * (q4 & 1);
-        const float4 d4 = *reinterpret_cast<const float4*>(rowv + qi0);
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int j = 2 * mb + (q4 >> 1), e = 4 * (q4 & 1) + b;
-          a[j][e] = (bf16)((float)a[j][e] * (x[mb][4 * q4 + b] - dv4[b]));
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int j = 2 * mb + (i >> 3), e = i & 7;
+        a[j][e] = (bf16)((float)a[j][e] * x[mb][i]);
       }
   }
   // role 0: dV += P^T dO (ys = dO tile); role 1: dK' += dS^T Q' (ys = Q' tile)
