@@ -41,7 +41,7 @@ DESCR = {
 KERNEL_FLOPS = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 
 
-def cpu_baseline(seqs, groups, cfg, n_trees=2, n_groups=2):
+def cpu_baseline(seqs, groups, cfg, n_trees=3, n_groups=2):
     """The float64 oracle (per-branch fwd + bwd) on the first n_trees trees x
     the first n_groups kv groups of the workload (a bounded sample)."""
     import workloads
