@@ -774,10 +774,13 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
       x[mb][4 * q4 + 2] = v.z;
       x[mb][4 * q4 + 3] = v.w;
     }
+  // role 0's products go first on the SIMD's shared MFMA pipe
+  if (m == 0) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int k = 0; k < KS; ++k)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) x[mb] = mfma32x32x16(lds128(xs + ad.op[k] + 32 * mb * DP), op[k], x[mb]);
+  if (m == 0) __builtin_amdgcn_s_setprio(0);
   // a[2 mb + t2] is the A operand (keys x 16 query rows) of the second product.
   bf16x8 a[4];
   if (m == 0) {
@@ -868,8 +871,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   const int j0 = kt * kBwdBK;
   const int key = j0 + 32 * ks + lc;
   const int myse = sep[key];
-  TileDma<DP, true, kDkdvWaves> td;
-  td.init(w, lane);
+  // Only the role-1 waves load query blocks: role 0 is the critical path
+  // (its P feeds role 1's dS), so it starts its products right after the
+  // barrier instead of waiting behind its share of the load issue.
+  TileDma<DP, true, 4> td;
+  td.init(w & 3, lane);
   SwzAddr<DP> ad;
   ad.init(lane);
   bf16x8* xch = xb + ks * 256 + lane;
@@ -896,10 +902,12 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   auto issue = [&](bf16* qs_, bf16* ds_, float* lsb, float* dlb) {
     const int h = hk * G + hh;
     const int i0 = (qb_lo + qq) * BQ;
-    td.issue(qr + ((size_t)h * Tp + i0) * DP, qs_, w);
-    td.issue(dor + ((size_t)h * Tp + i0) * DP, ds_, w);
-    if (w == 0) dma4(l2 + (size_t)h * Tp + i0 + lane, lsb);
-    if (w == 1) dma4(dd + (size_t)h * Tp + i0 + lane, dlb);
+    if (m == 1) {
+      td.issue(qr + ((size_t)h * Tp + i0) * DP, qs_, w & 3);
+      td.issue(dor + ((size_t)h * Tp + i0) * DP, ds_, w & 3);
+      if (w == 4) dma4(l2 + (size_t)h * Tp + i0 + lane, lsb);
+      if (w == 5) dma4(dd + (size_t)h * Tp + i0 + lane, dlb);
+    }
     if (++qq == nqb) {
       qq = 0;
       ++hh;
