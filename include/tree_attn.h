@@ -127,6 +127,8 @@ int tree_pack(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
  *
  * dt: TA_BF16 or TA_F32 for q, k, v, o, dout, dq, dk, dv (TA_F32 inputs are
  * rounded to bf16 for the matrix products; accumulation stays float32).
+ * q, k, v, o, dout must be 16-byte aligned (they are read with 16-byte
+ * vector loads; else TA_EINVAL).
  * d must be 16, 64 or 128 (else TA_EUNSUPPORTED). 1 <= T <= 2^22,
  * Hq % Hkv == 0, Hq <= 256.
  * pos, subtree_end: device int32 [T] as produced by tree_pack (a forest of

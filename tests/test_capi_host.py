@@ -124,6 +124,9 @@ def test_device_entry_points_validate_before_hip():
     a = list(args())
     a[8] = None  # pos
     assert lib.tree_attn_fwd(*a) == ta.TA_EINVAL
+    a = list(args())
+    a[1] = ctypes.c_void_p(0x1008)  # k not 16-byte aligned
+    assert lib.tree_attn_fwd(*a) == ta.TA_EINVAL and "16-byte aligned" in ta.last_error()
     bw = lib.tree_attn_workspace_bytes(100, 4, 2, 64, 1)
     bargs = [bogus] * 6 + [ta.TA_BF16, 100, 4, 2, 64, bogus, bogus, 0.0, 1e4, 0, bogus, bogus, bogus, bogus, bw, None]
     bad_flags = list(bargs)
@@ -132,6 +135,9 @@ def test_device_entry_points_validate_before_hip():
     small = list(bargs)
     small[20] = ws_need  # forward-sized workspace is too small for the backward
     assert lib.tree_attn_bwd(*small) == ta.TA_EINVAL
+    mis = list(bargs)
+    mis[5] = ctypes.c_void_p(0x1004)  # dout not 16-byte aligned
+    assert lib.tree_attn_bwd(*mis) == ta.TA_EINVAL and "16-byte aligned" in ta.last_error()
     lw = lib.tree_logprob_workspace_bytes(16, 48)
     assert lw > 0
     largs = lambda R=16, V=100, M=48, ws=lw: (bogus, ta.TA_BF16, R, V, bogus, bogus, bogus, M, bogus, None, None,

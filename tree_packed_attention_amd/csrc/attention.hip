@@ -154,7 +154,24 @@ struct SwzAddr {
 // ------------------------------------------------------------------------
 // Prep: RoPE on q and k, the padded bf16 copy of v, the padded subtree ends
 // and the cos / sin table. Angles are formed and reduced in float64, then
-// evaluated in float32 on [-pi, pi].
+// evaluated in float32 on [-pi, pi]. One workgroup per token; each thread
+// rotates 8-element chunks (kk .. kk+7 with their partners kk+half ..) with
+// 16-byte loads and stores.
+__device__ __forceinline__ void load8f(const bf16* p, float* x) {
+  const bf16x8 v = load8(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8f(const float* p, float* x) {  // rotated in float, rounded once
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                         const Tin* __restrict__ v, const int* __restrict__ pos,
@@ -180,10 +197,10 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
   if (threadIdx.x == 0) sep[t] = t < T ? se[t] : 0;
   __syncthreads();
   const int H = Hq + 2 * Hkv;
-  const int per_head = DP / 2;  // element pairs (kk, kk + half) for kk < half; zero fill past D
-  for (int idx = threadIdx.x; idx < H * per_head; idx += blockDim.x) {
-    const int h = idx / per_head;
-    const int kk = idx % per_head;
+  const int nc = half / 8;  // 8-element chunks per half row
+  for (int idx = threadIdx.x; idx < H * nc; idx += blockDim.x) {
+    const int h = idx / nc;
+    const int kk = 8 * (idx % nc);
     const Tin* src;
     bf16* dst;
     bool rotate = true;
@@ -198,24 +215,32 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
       dst = vr + ((size_t)(h - Hq - Hkv) * Tp + t) * DP;
       rotate = false;
     }
-    if (kk < half) {
-      float x1 = 0.0f, x2 = 0.0f;
-      if (t < T) {
-        x1 = to_f32(src[kk]);
-        x2 = to_f32(src[kk + half]);
-      }
-      if (rotate) {
-        const float2 c = tab[kk];
-        dst[kk] = (bf16)(x1 * c.x - x2 * c.y);
-        dst[kk + half] = (bf16)(x2 * c.x + x1 * c.y);
-      } else {
-        dst[kk] = (bf16)x1;
-        dst[kk + half] = (bf16)x2;
-      }
+    float x1[8], x2[8];
+    if (t < T) {
+      load8f(src + kk, x1);
+      load8f(src + kk + half, x2);
     } else {
-      // DP > D only for D = 16: columns D..DP-1 are zero padding
-      dst[D + 2 * (kk - half)] = (bf16)0.0f;
-      dst[D + 2 * (kk - half) + 1] = (bf16)0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x1[e] = x2[e] = 0.0f;
+    }
+    bf16x8 y1, y2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (rotate) {
+        const float2 c = tab[kk + e];
+        y1[e] = (bf16)(x1[e] * c.x - x2[e] * c.y);
+        y2[e] = (bf16)(x2[e] * c.x + x1[e] * c.y);
+      } else {
+        y1[e] = (bf16)x1[e];
+        y2[e] = (bf16)x2[e];
+      }
+    }
+    *reinterpret_cast<bf16x8*>(dst + kk) = y1;
+    *reinterpret_cast<bf16x8*>(dst + kk + half) = y2;
+    // DP > D only for D = 16: columns D..DP-1 are zero padding
+    if (DP > D && kk == 0) {
+      *reinterpret_cast<bf16x8*>(dst + D) = zero8();
+      *reinterpret_cast<bf16x8*>(dst + D + 8) = zero8();
     }
   }
 }
@@ -996,6 +1021,7 @@ struct AttnLayout {
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   AttnLayout L{};
@@ -1150,6 +1176,8 @@ extern "C" int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dty
   if (!q || !k || !v || !pos || !subtree_end || !o || !lse || !workspace)
     return fail(TA_EINVAL, "tree_attn_fwd: NULL pointer argument");
   if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_attn_fwd: bad dtype %d", (int)dt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(TA_EINVAL, "tree_attn_fwd: q, k, v must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TA_EINVAL, "tree_attn_fwd: workspace must be 256-byte aligned");
   if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "tree_attn_fwd: rope_theta must be >= 0");
@@ -1183,6 +1211,8 @@ extern "C" int tree_attn_bwd(const void* q, const void* k, const void* v, const 
   if (!q || !k || !v || !o || !lse || !dout || !pos || !subtree_end || !dq || !dk || !dv || !workspace)
     return fail(TA_EINVAL, "tree_attn_bwd: NULL pointer argument");
   if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_attn_bwd: bad dtype %d", (int)dt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout))
+    return fail(TA_EINVAL, "tree_attn_bwd: q, k, v, o, dout must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TA_EINVAL, "tree_attn_bwd: workspace must be 256-byte aligned");
   if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "tree_attn_bwd: rope_theta must be >= 0");
