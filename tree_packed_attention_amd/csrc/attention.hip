@@ -245,18 +245,29 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
   }
 }
 
-// Per key tile: min and max subtree end (keys past T count as 0).
-__global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict__ se, int T, int BK, int nk,
-                                                          int2* __restrict__ out) {
-  const int kt = blockIdx.x * blockDim.x + threadIdx.x;
-  if (kt >= nk) return;
+// Per key tile: min and max subtree end (keys past T count as 0), for the
+// 64-key tiles of the forward / dQ pass and the 128-key tiles of the dK/dV
+// pass, whose work (the number of 64-row query blocks it can see) is also
+// recorded.
+__device__ __forceinline__ int2 key_range_minmax(const int* __restrict__ se, int T, int j0, int n) {
   int mn = INT_MAX, mx = 0;
-  for (int j = kt * BK; j < kt * BK + BK; ++j) {
+  for (int j = j0; j < j0 + n; ++j) {
     const int s = j < T ? se[j] : 0;
     mn = min(mn, s);
     mx = max(mx, s);
   }
-  out[kt] = make_int2(mn, mx);
+  return make_int2(mn, mx);
+}
+__global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict__ se, int T, int nk64, int nk128,
+                                                          int2* __restrict__ kmm64, int2* __restrict__ kmm128,
+                                                          int* __restrict__ work) {
+  const int kt = blockIdx.x * blockDim.x + threadIdx.x;
+  if (kt < nk64) kmm64[kt] = key_range_minmax(se, T, kt * kFwdBK, kFwdBK);
+  if (kt < nk128) {
+    const int2 m = key_range_minmax(se, T, kt * kBwdBK, kBwdBK);
+    kmm128[kt] = m;
+    work[kt] = (m.y + kBwdBQ - 1) / kBwdBQ - (kt * kBwdBK) / kBwdBQ;
+  }
 }
 
 // One wave per query tile: the compacted, ascending list of key tiles that
@@ -289,17 +300,15 @@ __global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm
   if (lane == 0) counts[qt] = n;
 }
 
-// Work of a dK/dV key tile: the number of 64-row query blocks it can see.
-__global__ __launch_bounds__(256) void k_work_kernel(const int2* __restrict__ kmm, int nk, int* __restrict__ work) {
-  const int kt = blockIdx.x * blockDim.x + threadIdx.x;
-  if (kt >= nk) return;
-  work[kt] = (kmm[kt].y + kBwdBQ - 1) / kBwdBQ - (kt * kBwdBK) / kBwdBQ;
-}
-
 // Tile indices sorted by work, heaviest first (counting sort on the work
 // clipped to 1023). The order within one work value is arbitrary; it only
 // affects scheduling, never results.
-__global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ work, int n, int* __restrict__ order) {
+// Workgroup 0 sorts list (work0, n0), workgroup 1 list (work1, n1).
+__global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ work0, int n0, int* __restrict__ order0,
+                                                     const int* __restrict__ work1, int n1, int* __restrict__ order1) {
+  const int* __restrict__ work = blockIdx.x == 0 ? work0 : work1;
+  const int n = blockIdx.x == 0 ? n0 : n1;
+  int* __restrict__ order = blockIdx.x == 0 ? order0 : order1;
   __shared__ int hist[1024];
   hist[threadIdx.x] = 0;
   __syncthreads();
@@ -1014,9 +1023,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
 // Host side
 struct AttnLayout {
   int T, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
-  int nqf;  // forward query tiles (kFwdRows rows)
   size_t off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qorder, off_qlist;
-  size_t off_fcount, off_forder, off_flist;
   size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
 
@@ -1032,7 +1039,6 @@ AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   L.D = D;
   L.DP = D < 32 ? 32 : D;
   L.nq = L.Tp / kFwdBQ;
-  L.nqf = L.Tp / kFwdRows;
   L.nk64 = (T + kFwdBK - 1) / kFwdBK;
   L.nk128 = (T + kBwdBK - 1) / kBwdBK;
   size_t o = 0;
@@ -1051,15 +1057,6 @@ AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   L.off_qcount = take((size_t)L.nq * 4);
   L.off_qorder = take((size_t)L.nq * 4);
   L.off_qlist = take((size_t)L.nq * L.nk64 * 4);
-  if (kFwdRows == kFwdBQ) {  // the forward shares the dQ pass's plan
-    L.off_fcount = L.off_qcount;
-    L.off_forder = L.off_qorder;
-    L.off_flist = L.off_qlist;
-  } else {
-    L.off_fcount = take((size_t)L.nqf * 4);
-    L.off_forder = take((size_t)L.nqf * 4);
-    L.off_flist = take((size_t)L.nqf * L.nk64 * 4);
-  }
   L.off_kwork = take((size_t)L.nk128 * 4);
   L.off_korder = take((size_t)L.nk128 * 4);
   if (with_bwd) {
@@ -1101,36 +1098,24 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
                        at<int>(ws, L.off_sep), at<float2>(ws, L.off_cs));
   }
   ProfScope ps("tile_plan", st);
-  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, se, L.T, kFwdBK, L.nk64,
-                     at<int2>(ws, L.off_kmm64));
-  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk128 + 255) / 256), dim3(256), 0, st, se, L.T, kBwdBK,
-                     L.nk128, at<int2>(ws, L.off_kmm128));
+  static_assert(kFwdRows == kFwdBQ, "the forward shares the dQ pass's query-tile plan");
+  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, se, L.T, L.nk64, L.nk128,
+                     at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128), at<int>(ws, L.off_kwork));
   hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.T, kFwdBQ,
                      kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
-                     at<int>(ws, L.off_qorder));
-  if (kFwdRows != kFwdBQ) {
-    hipLaunchKernelGGL(q_plan_kernel, dim3(L.nqf), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.T, kFwdRows,
-                       kFwdBK, L.nk64, at<int>(ws, L.off_fcount), at<int>(ws, L.off_flist));
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_fcount), L.nqf,
-                       at<int>(ws, L.off_forder));
-  }
-  hipLaunchKernelGGL(k_work_kernel, dim3((L.nk128 + 255) / 256), dim3(256), 0, st,
-                     at<const int2>(ws, L.off_kmm128), L.nk128, at<int>(ws, L.off_kwork));
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, at<const int>(ws, L.off_kwork), L.nk128,
-                     at<int>(ws, L.off_korder));
+  hipLaunchKernelGGL(order_kernel, dim3(2), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
+                     at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, at<int>(ws, L.off_korder));
   return check_launch("prep");
 }
 
 template <int DP, typename Tio>
 int run_fwd(const AttnLayout& L, float sl2, void* o, float* lse, char* ws, hipStream_t st) {
   ProfScope ps("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nqf * L.Hq), dim3(64 * kFwdWaves), 0, st,
+  hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(64 * kFwdWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
-                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_fcount),
-                     at<const int>(ws, L.off_flist), at<const int>(ws, L.off_forder), L.T, L.Tp, L.Hq, L.Hkv, L.nqf,
-                     L.nk64, sl2,
-                     static_cast<Tio*>(o), lse);
+                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_qcount),
+                     at<const int>(ws, L.off_qlist), at<const int>(ws, L.off_qorder), L.T, L.Tp, L.Hq, L.Hkv, L.nq,
+                     L.nk64, sl2, static_cast<Tio*>(o), lse);
   return check_launch("tree_attn_fwd");
 }
 
