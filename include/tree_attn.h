@@ -47,10 +47,13 @@ enum {
 
 typedef enum { TA_BF16 = 0, TA_F32 = 1 } ta_dtype;
 
-/* tree_attn_bwd flag: the workspace still holds what tree_attn_fwd put there
- * for the same q, k, pos, subtree_end, T, heads, d and rope_theta, so the
- * RoPE and tile-plan pass is skipped. */
-enum { TA_REUSE_PREP = 1 };
+/* Backward flags.
+ * TA_REUSE_PREP: the workspace still holds what the matching forward put
+ *   there for the same q, k, pos, subtree_end, T, heads, d and rope_theta
+ *   (and cached rows), so the RoPE and tile-plan pass is skipped.
+ * TA_ACCUMULATE_PAST (tree_attn_gw_bwd only): add the cached rows' gradients
+ *   to dk_past / dv_past instead of overwriting them. */
+enum { TA_REUSE_PREP = 1, TA_ACCUMULATE_PAST = 2 };
 
 /* Thread-local text of the last error ("" if none). Never NULL. */
 const char* tree_attn_last_error(void);
@@ -151,6 +154,54 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const int32_t* pos, const int32_t* subtree_end,
                   float softmax_scale, float rope_theta, int32_t flags,
                   void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tree-masked attention across a partition boundary (DEVICE)
+ *
+ * "Tree Training" §3.3 and App. B.2-B.5: a tree too large for one pass is
+ * split at node boundaries; a child partition does not re-run its
+ * ancestors but attends to the parent partition's cached, already rotated
+ * keys and values (the "gateway", App. B.2). Its attention mask (Eq. 14) is
+ *   cached row j:  0 if past_visible[j] else -inf  (the ancestor bias of
+ *                  Eq. 15-16, the same for every query of the partition)
+ *   own row j:     the ordinary tree mask of the partition's packed subtree
+ * Own tokens take RoPE at pos_offset + pos[i] (Eq. 17: the depth of the
+ * cut node's last token + 1). The gradients of the cached rows come out in
+ * float32 (Eq. 18) and, with TA_ACCUMULATE_PAST, are added to what the
+ * previous child partitions of the same cut node left there.
+ *
+ * Arguments as for tree_attn_fwd / tree_attn_bwd (q, k, v, o, dout, dq, dk,
+ * dv, lse hold the T own tokens; pos and subtree_end are the partition's own
+ * packing), plus:
+ * k_past, v_past: device [past_len][Hkv][d] in dtype dt; k_past already
+ *   rotated (RoPE at the parent's positions), v_past as is; 16-byte aligned.
+ * past_visible: device uint8 [past_len], 1 = bias 0, 0 = bias -inf.
+ * past_len: >= 0 (0 gives plain tree attention); T + past_len <= 2^22 - 128.
+ * pos_offset: >= 0.
+ * dk_past, dv_past: device float32 [past_len][Hkv][d]; dk_past is the
+ *   gradient with respect to the rotated k_past (the caller relays it
+ *   through the parent's RoPE); rows the bias masks get 0.
+ * workspace: >= tree_attn_gw_workspace_bytes(T, past_len, ...) bytes.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_EHIP. No allocation; asynchronous
+ * on `stream`; bitwise reproducible for a fixed TA_ACCUMULATE_PAST order.
+ * ---------------------------------------------------------------------- */
+size_t tree_attn_gw_workspace_bytes(int32_t T, int32_t past_len, int32_t Hq, int32_t Hkv, int32_t d,
+                                    int32_t with_bwd);
+
+int tree_attn_gw_fwd(const void* q, const void* k, const void* v, ta_dtype dt,
+                     int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                     const int32_t* pos, const int32_t* subtree_end, int32_t pos_offset,
+                     const void* k_past, const void* v_past, const uint8_t* past_visible, int32_t past_len,
+                     float softmax_scale, float rope_theta,
+                     void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+int tree_attn_gw_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, ta_dtype dt, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                     const int32_t* pos, const int32_t* subtree_end, int32_t pos_offset,
+                     const void* k_past, const void* v_past, const uint8_t* past_visible, int32_t past_len,
+                     float softmax_scale, float rope_theta, int32_t flags,
+                     void* dq, void* dk, void* dv, float* dk_past, float* dv_past,
+                     void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * tree_logprob  (DEVICE)

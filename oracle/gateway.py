@@ -13,10 +13,10 @@ The gradients of the cached rows leave in float32 and are summed over all
 child partitions of the cut node before they are relayed into the parent
 partition's backward (Eq. 18).
 
-The oracle below is that definition written out one query row at a time, in
-float64: row i of the child sees the visible cached rows (given post-RoPE)
-plus its own ancestors-or-self, with q and the own keys rotated at
-pos_offset + depth.
+The oracle below is that definition written out one query row at a time
+(the heads of one kv group as one batched product), in float64: row i of the child sees the
+visible cached rows (given post-RoPE) plus its own ancestors-or-self, with q
+and the own keys rotated at pos_offset + depth.
 
 Conventions as in oracle.attention: q [T, Hq, d], k and v [T, Hkv, d];
 k_past and v_past [past_len, Hkv, d] (k_past post-RoPE); visible [past_len]
@@ -56,14 +56,13 @@ def forward(q, k, v, par, k_past, v_past, visible, pos_offset, scale=None, theta
     LSE = np.zeros((Hq, T))
     for i in range(T):
         chain = ancestors_or_self(par, i)
-        kc, vc = _row_keys(k, v, kp, vp, chain, depth[chain], pos_offset, theta)
-        qi = rope(_f64(q[i:i + 1]), [pos_offset + depth[i]], theta)[0]
-        for h in range(Hq):
-            s = (kc[:, h // G] @ qi[h]) * scale
-            m = s.max()
-            e = np.exp(s - m)
-            O[i, h] = (e / e.sum()) @ vc[:, h // G]
-            LSE[h, i] = m + np.log(e.sum())
+        kc, vc = _row_keys(k, v, kp, vp, chain, depth[chain], pos_offset, theta)  # [L, Hkv, d]
+        qi = rope(_f64(q[i:i + 1]), [pos_offset + depth[i]], theta)[0]            # [Hq, d]
+        s = (qi.reshape(Hkv, G, d) @ kc.transpose(1, 2, 0)) * scale              # [Hkv, G, L]
+        m = s.max(axis=2, keepdims=True)
+        e = np.exp(s - m)
+        O[i] = ((e / e.sum(axis=2, keepdims=True)) @ vc.transpose(1, 0, 2)).reshape(Hq, d)
+        LSE[:, i] = (m + np.log(e.sum(axis=2, keepdims=True))).reshape(Hq)
     return O, LSE
 
 
@@ -88,24 +87,25 @@ def backward(q, k, v, do, par, k_past, v_past, visible, pos_offset, scale=None, 
     dv_past = np.zeros((Lp, Hkv, d))
     for i in range(T):
         chain = ancestors_or_self(par, i)
-        kc, vc = _row_keys(k, v, kp, vp, chain, depth[chain], pos_offset, theta)
+        kc, vc = _row_keys(k, v, kp, vp, chain, depth[chain], pos_offset, theta)  # [L, Hkv, d]
+        kh, vh = kc.transpose(1, 0, 2), vc.transpose(1, 0, 2)                    # [Hkv, L, d]
         qi = rope(_f64(q[i:i + 1]), [pos_offset + depth[i]], theta)[0]
-        for h in range(Hq):
-            hk = h // G
-            s = (kc[:, hk] @ qi[h]) * scale
-            e = np.exp(s - s.max())
-            p = e / e.sum()
-            o = p @ vc[:, hk]
-            doi = _f64(do[i, h])
-            ds = p * (vc[:, hk] @ doi - doi @ o)
-            gq = (ds @ kc[:, hk]) * scale
-            dq[i, h] = rope_transpose(gq[None, None, :], [pos_offset + depth[i]], theta)[0, 0]
-            gk = ds[:, None] * qi[h][None, :] * scale
-            gv = p[:, None] * doi[None, :]
-            dk_past[vidx, hk] += gk[:nv]
-            dv_past[vidx, hk] += gv[:nv]
-            dkr[chain, hk] += gk[nv:]
-            dv[chain, hk] += gv[nv:]
+        qg = qi.reshape(Hkv, G, d)
+        s = (qg @ kh.transpose(0, 2, 1)) * scale                                  # [Hkv, G, L]
+        e = np.exp(s - s.max(axis=2, keepdims=True))
+        p = e / e.sum(axis=2, keepdims=True)
+        o = p @ vh                                                                # [Hkv, G, d]
+        dg = _f64(do[i]).reshape(Hkv, G, d)
+        ds = p * ((dg @ vh.transpose(0, 2, 1)) - np.sum(dg * o, axis=2, keepdims=True))
+        gq = (ds @ kh).reshape(Hq, d) * scale
+        dq[i] = rope_transpose(gq[None], [pos_offset + depth[i]], theta)[0]
+        # per key and kv head, summed over the G query heads of the group
+        gk = ((ds.transpose(0, 2, 1) @ qg) * scale).transpose(1, 0, 2)           # [L, Hkv, d]
+        gv = (p.transpose(0, 2, 1) @ dg).transpose(1, 0, 2)
+        dk_past[vidx] += gk[:nv]
+        dv_past[vidx] += gv[:nv]
+        dkr[chain] += gk[nv:]
+        dv[chain] += gv[nv:]
     dk = rope_transpose(dkr, pos_offset + depth, theta)
     return dq, dk, dv, dk_past, dv_past
 

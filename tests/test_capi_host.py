@@ -138,6 +138,31 @@ def test_device_entry_points_validate_before_hip():
     mis = list(bargs)
     mis[5] = ctypes.c_void_p(0x1004)  # dout not 16-byte aligned
     assert lib.tree_attn_bwd(*mis) == ta.TA_EINVAL and "16-byte aligned" in ta.last_error()
+    acc_plain = list(bargs)
+    acc_plain[15] = ta.TA_ACCUMULATE_PAST  # only meaningful with cached rows
+    assert lib.tree_attn_bwd(*acc_plain) == ta.TA_EINVAL
+    # partition-boundary entry points
+    gw_need = lib.tree_attn_gw_workspace_bytes(100, 300, 4, 2, 64, 0)
+    assert gw_need > ws_need
+    assert lib.tree_attn_gw_workspace_bytes(100, -1, 4, 2, 64, 0) == 0
+    gargs = lambda Lp=300, off=5, kp=bogus, vis=bogus, ws=gw_need: (
+        bogus, bogus, bogus, ta.TA_BF16, 100, 4, 2, 64, bogus, bogus, off, kp, bogus, vis, Lp, 0.0, 1e4, bogus,
+        bogus, bogus, ws, None)
+    assert lib.tree_attn_gw_fwd(*gargs(Lp=-3)) == ta.TA_EINVAL
+    assert lib.tree_attn_gw_fwd(*gargs(off=-1)) == ta.TA_EINVAL
+    assert lib.tree_attn_gw_fwd(*gargs(kp=None)) == ta.TA_EINVAL and "past" in ta.last_error()
+    assert lib.tree_attn_gw_fwd(*gargs(vis=None)) == ta.TA_EINVAL
+    assert lib.tree_attn_gw_fwd(*gargs(kp=ctypes.c_void_p(0x1008))) == ta.TA_EINVAL
+    assert lib.tree_attn_gw_fwd(*gargs(ws=gw_need - 1)) == ta.TA_EINVAL
+    gbw = lib.tree_attn_gw_workspace_bytes(100, 300, 4, 2, 64, 1)
+    gb = [bogus] * 6 + [ta.TA_BF16, 100, 4, 2, 64, bogus, bogus, 5, bogus, bogus, bogus, 300, 0.0, 1e4, 0,
+                        bogus, bogus, bogus, bogus, bogus, bogus, gbw, None]
+    nodk = list(gb)
+    nodk[24] = None  # dk_past
+    assert lib.tree_attn_gw_bwd(*nodk) == ta.TA_EINVAL
+    badf = list(gb)
+    badf[20] = 4
+    assert lib.tree_attn_gw_bwd(*badf) == ta.TA_EINVAL
     lw = lib.tree_logprob_workspace_bytes(16, 48)
     assert lw > 0
     largs = lambda R=16, V=100, M=48, ws=lw: (bogus, ta.TA_BF16, R, V, bogus, bogus, bogus, M, bogus, None, None,

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
 
 TA_OK, TA_EINVAL, TA_ECAPACITY, TA_EUNSUPPORTED, TA_EHIP = 0, -1, -2, -3, -4
 TA_BF16, TA_F32 = 0, 1
-TA_REUSE_PREP = 1
+TA_REUSE_PREP, TA_ACCUMULATE_PAST = 1, 2
 
 EXPORTS = (
     "tree_attn_last_error",
@@ -34,6 +34,9 @@ EXPORTS = (
     "tree_attn_workspace_bytes",
     "tree_attn_fwd",
     "tree_attn_bwd",
+    "tree_attn_gw_workspace_bytes",
+    "tree_attn_gw_fwd",
+    "tree_attn_gw_bwd",
     "tree_logprob_workspace_bytes",
     "tree_logprob",
     "tree_tile_stats",
@@ -78,6 +81,14 @@ _lib.tree_attn_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32,
 _lib.tree_attn_bwd.restype = ctypes.c_int
 _lib.tree_attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _f32, _f32,
                                _i32, _p, _p, _p, _p, _sz, _p]
+_lib.tree_attn_gw_workspace_bytes.restype = _sz
+_lib.tree_attn_gw_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.tree_attn_gw_fwd.restype = ctypes.c_int
+_lib.tree_attn_gw_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32,
+                                  _f32, _f32, _p, _p, _p, _sz, _p]
+_lib.tree_attn_gw_bwd.restype = ctypes.c_int
+_lib.tree_attn_gw_bwd.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p,
+                                  _p, _i32, _f32, _f32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.tree_logprob_workspace_bytes.restype = _sz
 _lib.tree_logprob_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tree_logprob.restype = ctypes.c_int
@@ -267,6 +278,88 @@ def tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, softmax_scale=0.0, ro
                             workspace.numel(), _stream(dev))
     _check(rc)
     return dq, dk, dv
+
+
+def gw_workspace(T, past_len, Hq, Hkv, d, with_bwd, device):
+    nbytes = _lib.tree_attn_gw_workspace_bytes(T, past_len, Hq, Hkv, d, 1 if with_bwd else 0)
+    if nbytes == 0:
+        raise TreeAttnError(TA_EINVAL, f"bad gateway shape T={T} past_len={past_len} Hq={Hq} Hkv={Hkv} d={d}")
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+def _past_args(q, k_past, v_past, past_visible):
+    torch = _torch()
+    dev = q.device
+    Lp = k_past.shape[0]
+    if Lp == 0:
+        return (None, None, None, 0)
+    return (_dev_ptr(k_past, "k_past", q.dtype, dev), _dev_ptr(v_past, "v_past", q.dtype, dev),
+            _dev_ptr(past_visible, "past_visible", torch.uint8, dev), Lp)
+
+
+def tree_attn_gw_fwd(q, k, v, pos, subtree_end, pos_offset, k_past, v_past, past_visible, softmax_scale=0.0,
+                     rope_theta=10000.0, workspace=None, with_bwd_workspace=False):
+    """Tree attention of a child partition over cached ancestor rows.
+
+    q [T,Hq,d], k/v [T,Hkv,d]: the partition's own tokens (pos, subtree_end
+    from its packing); k_past (rotated), v_past [past_len,Hkv,d] in q's dtype;
+    past_visible uint8 [past_len] (1 = bias 0, 0 = -inf); own positions are
+    pos_offset + pos. Returns (o, lse, workspace).
+    """
+    torch = _torch()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    kp, vp, vis, Lp = _past_args(q, k_past, v_past, past_visible)
+    if workspace is None:
+        workspace = gw_workspace(T, Lp, Hq, Hkv, d, with_bwd_workspace, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(Hq, T, dtype=torch.float32, device=dev)
+    rc = _lib.tree_attn_gw_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev),
+                               _dt(q), T, Hq, Hkv, d, _dev_ptr(pos, "pos", torch.int32, dev),
+                               _dev_ptr(subtree_end, "subtree_end", torch.int32, dev), int(pos_offset), kp, vp, vis,
+                               Lp, float(softmax_scale), float(rope_theta), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"),
+                               _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return o, lse, workspace
+
+
+def tree_attn_gw_bwd(q, k, v, o, lse, dout, pos, subtree_end, pos_offset, k_past, v_past, past_visible,
+                     softmax_scale=0.0, rope_theta=10000.0, workspace=None, reuse_prep=False, dk_past=None,
+                     dv_past=None, accumulate=False):
+    """Gradients (dq, dk, dv, dk_past, dv_past); dk_past / dv_past float32,
+    with respect to the rotated k_past and v_past. With accumulate=True the
+    cached rows' gradients are added to the given dk_past / dv_past."""
+    torch = _torch()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    kp, vp, vis, Lp = _past_args(q, k_past, v_past, past_visible)
+    if workspace is None:
+        if reuse_prep:
+            raise ValueError("reuse_prep needs the forward's workspace")
+        workspace = gw_workspace(T, Lp, Hq, Hkv, d, True, dev)
+    if dk_past is None or dv_past is None:
+        if accumulate:
+            raise ValueError("accumulate needs dk_past and dv_past")
+        dk_past = torch.empty(Lp, Hkv, d, dtype=torch.float32, device=dev)
+        dv_past = torch.empty(Lp, Hkv, d, dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    flags = (TA_REUSE_PREP if reuse_prep else 0) | (TA_ACCUMULATE_PAST if accumulate else 0)
+    rc = _lib.tree_attn_gw_bwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev),
+                               _dev_ptr(o, "o", q.dtype, dev), _dev_ptr(lse, "lse", torch.float32, dev),
+                               _dev_ptr(dout, "dout", q.dtype, dev), _dt(q), T, Hq, Hkv, d,
+                               _dev_ptr(pos, "pos", torch.int32, dev),
+                               _dev_ptr(subtree_end, "subtree_end", torch.int32, dev), int(pos_offset), kp, vp, vis,
+                               Lp, float(softmax_scale), float(rope_theta), flags, _dev_ptr(dq, "dq"),
+                               _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
+                               _dev_ptr(dk_past, "dk_past", torch.float32, dev) if Lp else None,
+                               _dev_ptr(dv_past, "dv_past", torch.float32, dev) if Lp else None,
+                               _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return dq, dk, dv, dk_past, dv_past
 
 
 def tree_logprob(logits, src_row, target, weight, grad_scale=1.0, with_grad=True, with_row_lse=True,

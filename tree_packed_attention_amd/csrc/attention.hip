@@ -175,18 +175,30 @@ __device__ __forceinline__ void load8f(const float* p, float* x) {  // rotated i
 template <typename Tin>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                         const Tin* __restrict__ v, const int* __restrict__ pos,
-                                                        const int* __restrict__ se, int T, int Tp, int Hq,
-                                                        int Hkv, int D, int DP, float theta, bf16* __restrict__ qr,
+                                                        const int* __restrict__ se, const Tin* __restrict__ k_past,
+                                                        const Tin* __restrict__ v_past,
+                                                        const unsigned char* __restrict__ past_vis, int Lp, int Lq,
+                                                        int pos_offset, int T, int Tp, int Hq, int Hkv, int D,
+                                                        int DP, float theta, bf16* __restrict__ qr,
                                                         bf16* __restrict__ kr, bf16* __restrict__ vr,
                                                         int* __restrict__ sep, float2* __restrict__ cs) {
+  // Row t of the combined sequence (T = Lq + own tokens, padded to Tp):
+  //   t <  Lp        a cached row: key and value copied as given (the key is
+  //                  already rotated), no query; visible to every own query
+  //                  (subtree end T) when past_vis[t], else to none (t)
+  //   Lp <= t < Lq   padding: zeros, visible to none
+  //   Lq <= t < T    own token i = t - Lq at position pos_offset + pos[i]
+  //   t >= T         padding
   __shared__ float2 tab[64];
   const int t = blockIdx.x;
   const int half = D / 2;
+  const bool own = t >= Lq && t < T;
+  const int i = t - Lq;
   if ((int)threadIdx.x < half) {
     float c = 1.0f, s = 0.0f;
-    if (t < T && theta > 0.0f) {
+    if (own && theta > 0.0f) {
       const double inv = exp2(-2.0 * (double)threadIdx.x / (double)D * log2((double)theta));
-      const double ang = (double)pos[t] * inv;
+      const double ang = (double)(pos_offset + pos[i]) * inv;
       const double twopi = 6.283185307179586476925286766559;
       const double r = ang - rint(ang / twopi) * twopi;
       sincosf((float)r, &s, &c);
@@ -194,29 +206,46 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
     tab[threadIdx.x] = make_float2(c, s);
     cs[(size_t)t * half + threadIdx.x] = make_float2(c, s);
   }
-  if (threadIdx.x == 0) sep[t] = t < T ? se[t] : 0;
+  if (threadIdx.x == 0) {
+    int e = 0;
+    if (own)
+      e = se[i] + Lq;
+    else if (t < Lp)
+      e = past_vis[t] ? T : t;
+    else if (t < Lq)
+      e = t;
+    sep[t] = e;
+  }
   __syncthreads();
   const int H = Hq + 2 * Hkv;
   const int nc = half / 8;  // 8-element chunks per half row
   for (int idx = threadIdx.x; idx < H * nc; idx += blockDim.x) {
     const int h = idx / nc;
     const int kk = 8 * (idx % nc);
-    const Tin* src;
+    const Tin* src = nullptr;
     bf16* dst;
-    bool rotate = true;
+    bool rotate = own;
     if (h < Hq) {
-      src = q + ((size_t)t * Hq + h) * D;
+      if (own) src = q + ((size_t)i * Hq + h) * D;
       dst = qr + ((size_t)h * Tp + t) * DP;
     } else if (h < Hq + Hkv) {
-      src = k + ((size_t)t * Hkv + (h - Hq)) * D;
-      dst = kr + ((size_t)(h - Hq) * Tp + t) * DP;
+      const int hk = h - Hq;
+      if (own)
+        src = k + ((size_t)i * Hkv + hk) * D;
+      else if (t < Lp)
+        src = k_past + ((size_t)t * Hkv + hk) * D;
+      dst = kr + ((size_t)hk * Tp + t) * DP;
     } else {
-      src = v + ((size_t)t * Hkv + (h - Hq - Hkv)) * D;
-      dst = vr + ((size_t)(h - Hq - Hkv) * Tp + t) * DP;
+      const int hk = h - Hq - Hkv;
+      if (own)
+        src = v + ((size_t)i * Hkv + hk) * D;
+      else if (t < Lp)
+        src = v_past + ((size_t)t * Hkv + hk) * D;
+      dst = vr + ((size_t)hk * Tp + t) * DP;
       rotate = false;
     }
     float x1[8], x2[8];
-    if (t < T) {
+    if (src) {
       load8f(src + kk, x1);
       load8f(src + kk + half, x2);
     } else {
@@ -247,8 +276,8 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
 
 // Per key tile: min and max subtree end (keys past T count as 0), for the
 // 64-key tiles of the forward / dQ pass and the 128-key tiles of the dK/dV
-// pass, whose work (the number of 64-row query blocks it can see) is also
-// recorded.
+// pass, whose work (the number of 64-row query blocks from row Lq on it can
+// see) is also recorded.
 __device__ __forceinline__ int2 key_range_minmax(const int* __restrict__ se, int T, int j0, int n) {
   int mn = INT_MAX, mx = 0;
   for (int j = j0; j < j0 + n; ++j) {
@@ -258,27 +287,33 @@ __device__ __forceinline__ int2 key_range_minmax(const int* __restrict__ se, int
   }
   return make_int2(mn, mx);
 }
-__global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict__ se, int T, int nk64, int nk128,
-                                                          int2* __restrict__ kmm64, int2* __restrict__ kmm128,
-                                                          int* __restrict__ work) {
+__global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict__ se, int T, int Lq, int nk64,
+                                                          int nk128, int2* __restrict__ kmm64,
+                                                          int2* __restrict__ kmm128, int* __restrict__ work) {
   const int kt = blockIdx.x * blockDim.x + threadIdx.x;
   if (kt < nk64) kmm64[kt] = key_range_minmax(se, T, kt * kFwdBK, kFwdBK);
   if (kt < nk128) {
     const int2 m = key_range_minmax(se, T, kt * kBwdBK, kBwdBK);
     kmm128[kt] = m;
-    work[kt] = (m.y + kBwdBQ - 1) / kBwdBQ - (kt * kBwdBK) / kBwdBQ;
+    work[kt] = max((m.y + kBwdBQ - 1) / kBwdBQ - max(kt * kBwdBK, Lq) / kBwdBQ, 0);  // queries start at Lq
   }
 }
 
 // One wave per query tile: the compacted, ascending list of key tiles that
 // hold at least one visible pair. Keys of tile kt cover [j0, max se) without
 // gaps (every key's interval starts inside the tile), so the tile meets query
-// rows [i0, i1) iff j0 <= i1 - 1 and max se > i0.
-__global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm, int T, int BQ, int BK, int nk,
-                                                    int* __restrict__ counts, int* __restrict__ lists) {
+// rows [i0, i1) iff j0 <= i1 - 1 and max se > i0. (Cached rows visible to all
+// queries span [j, T) and masked ones nothing, so for the query rows, which
+// start at Lq after all cached rows, the same test holds.)
+__global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm, int T, int Lq, int BQ, int BK,
+                                                    int nk, int* __restrict__ counts, int* __restrict__ lists) {
   const int qt = blockIdx.x;
   const int lane = threadIdx.x;
   const int i0 = qt * BQ;
+  if (i0 < Lq) {  // rows before Lq (cached keys) have no queries
+    if (lane == 0) counts[qt] = 0;
+    return;
+  }
   const int i1 = min(i0 + BQ, T);
   const int nkc = min(nk, (i1 - 1) / BK + 1);
   int* out = lists + (size_t)qt * nk;
@@ -477,8 +512,10 @@ template <int DP, typename Tio>
 __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ counts,
-    const int* __restrict__ lists, const int* __restrict__ order, int T, int Tp, int Hq, int Hkv, int nq, int nk,
-    float sl2, Tio* __restrict__ o, float* __restrict__ lse) {
+    const int* __restrict__ lists, const int* __restrict__ order, int T, int Lq, int Tp, int Hq, int Hkv, int nq,
+    int nk, float sl2, Tio* __restrict__ o, float* __restrict__ lse) {
+  // Row indices are those of the combined sequence: Lq cached / padding rows
+  // (keys only, no queries) and then the packed tokens; T = Lq + own tokens.
   constexpr int D = DP == 32 ? 16 : DP;  // head dim (16 is padded to 32 for the MFMA shapes)
   constexpr int KS = DP / 16;            // k steps of S^T = K' Q'^T
   constexpr int NDB = DP / 32;           // 32-wide d blocks of O^T
@@ -502,6 +539,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
   const int hk = lid / (G * nq);
   const int qt = order[(lid / G) % nq];
   const int h = hk * G + gq;
+  if (qt * kFwdRows < Lq) return;  // a tile of cached rows: no queries (Lq is a multiple of the tile)
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -577,7 +615,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
     const float lt = st[nb].lsum + __shfl_xor(st[nb].lsum, 32);
     if (qrow[nb] < T) {
       const float inv = 1.0f / lt;
-      Tio* orow = o + ((size_t)qrow[nb] * Hq + h) * D;
+      Tio* orow = o + ((size_t)(qrow[nb] - Lq) * Hq + h) * D;
 #pragma unroll
       for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -586,7 +624,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
           if (d < D) orow[d] = from_f32<Tio>(acc[nb][b][i] * inv);
         }
       const float mu = (st[nb].mref == kNegInf) ? 0.0f : st[nb].mref;
-      if (lg == 0) lse[(size_t)h * T + qrow[nb]] = (mu + log2f(lt)) * kLn2;
+      if (lg == 0) lse[(size_t)h * (T - Lq) + (qrow[nb] - Lq)] = (mu + log2f(lt)) * kLn2;
     }
   }
 }
@@ -656,8 +694,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const Tio* __restrict__ o, const Tio* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dd, float* __restrict__ l2, bf16* __restrict__ dor, const int* __restrict__ sep,
     const int* __restrict__ counts, const int* __restrict__ lists, const int* __restrict__ order,
-    const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nq, int nk, float sl2, float scale,
+    const float2* __restrict__ cs, int T, int Lq, int Tp, int Hq, int Hkv, int nq, int nk, float sl2, float scale,
     Tio* __restrict__ dq) {
+  // Row indices are those of the combined sequence (Lq cached / padding
+  // rows, then the packed tokens; T = Lq + own tokens). o, dout, lse and dq
+  // hold the own rows only.
   constexpr int D = DP == 32 ? 16 : DP;
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
@@ -678,12 +719,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const int hk = lid / (G * nq);
   const int qt = order[(lid / G) % nq];
   const int h = hk * G + gq;
+  if (qt * kFwdBQ < Lq) return;  // a tile of cached rows: no queries (Lq is a multiple of the tile)
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int qrow = qt * kFwdBQ + 32 * w + lc;
   const bool qok = qrow < T;
+  const int own = qrow - Lq;  // row in o, dout, lse and dq
   TileDma<DP, true> td;
   td.init(w, lane);
   SwzAddr<DP> ad;
@@ -694,7 +737,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   {
     const bf16* qb = qr + ((size_t)h * Tp + qrow) * DP + 8 * lg;
     bf16* dob = dor + ((size_t)h * Tp + qrow) * DP + 8 * lg;
-    const size_t roff = ((size_t)(qok ? qrow : 0) * Hq + h) * D;
+    const size_t roff = ((size_t)(qok ? own : 0) * Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qop[s] = load8(qb + 16 * s);
@@ -706,10 +749,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     }
   }
   dval += __shfl_xor(dval, 32);
-  const float lse2 = qok ? lse[(size_t)h * T + qrow] * kLog2e : 0.0f;
+  const float lse_row = qok ? lse[(size_t)h * (T - Lq) + own] : 0.0f;
+  const float lse2 = lse_row * kLog2e;
   if (lg == 0) {
     dd[(size_t)h * Tp + qrow] = -dval;
-    l2[(size_t)h * Tp + qrow] = qok ? -lse[(size_t)h * T + qrow] / scale : 0.0f;
+    l2[(size_t)h * Tp + qrow] = qok ? -lse_row / scale : 0.0f;
   }
 
   f32x16 acc[NDB];
@@ -749,7 +793,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     // RoPE partner d + D/2 sits in the same lane (D/2 is a multiple of 8).
     constexpr int half = D / 2;
     const float2* csr = cs + (size_t)qrow * half;
-    Tio* out = dq + ((size_t)qrow * Hq + h) * D;
+    Tio* out = dq + ((size_t)own * Hq + h) * D;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -874,8 +918,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const bf16* __restrict__ dor, const float* __restrict__ l2, const float* __restrict__ dd,
     const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ korder,
-    const float2* __restrict__ cs, int T, int Tp, int Hq, int Hkv, int nkb, float sl2, float scale,
-    Tio* __restrict__ dk, Tio* __restrict__ dv) {
+    const float2* __restrict__ cs, int T, int Lq, int Lp, int Tp, int Hq, int Hkv, int nkb, float sl2, float scale,
+    Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dk_past, float* __restrict__ dv_past,
+    int acc_past) {
+  // Key rows are those of the combined sequence: Lp cached rows (gradients to
+  // dk_past / dv_past in float32, added to their contents when acc_past),
+  // padding up to Lq, then the packed tokens (dk, dv); T = Lq + own tokens.
+  // Queries exist from row Lq on.
   constexpr int D = DP == 32 ? 16 : DP;
   constexpr int BQ = kBwdBQ;
   constexpr int KS = DP / 16;
@@ -926,8 +975,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
 
   const int2 mm = kmm[kt];
-  const int qb_lo = j0 / BQ;
-  const int nqb = (mm.y + BQ - 1) / BQ - qb_lo;
+  const int qb_lo = max(j0, Lq) / BQ;
+  const int nqb = max((mm.y + BQ - 1) / BQ - qb_lo, 0);
   const int n_it = G * nqb;
 
   // iteration it covers query head hk * G + it / nqb, block qb_lo + it % nqb;
@@ -999,10 +1048,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
       const int r = 16 * w + rr;  // key row within the workgroup's 128
       const int j = j0 + r;
       if (j >= T) break;
+      if (j >= Lp && j < Lq) continue;  // padding after the cached rows
       const bf16* eb = (r >> 5) < 2 ? ((r >> 5) == 0 ? qb0 : qb1) : ((r >> 5) == 2 ? ob0 : ob1);
       const float* er = reinterpret_cast<const float*>(eb) + (r & 31) * SE;
-      if (pass == 0) {
-        Tio* out = dk + ((size_t)j * Hkv + hk) * D;
+      if (j < Lp) {
+        // cached rows: their keys came in rotated, so dK is left unrotated
+        float* out = (pass == 0 ? dk_past : dv_past) + ((size_t)j * Hkv + hk) * D;
+        for (int c = lane; c < D; c += 64) out[c] = acc_past ? out[c] + er[c] : er[c];
+      } else if (pass == 0) {
+        Tio* out = dk + ((size_t)(j - Lq) * Hkv + hk) * D;
         const float2* csr = cs + (size_t)j * half;
         for (int kk = lane; kk < half; kk += 64) {
           const float g1 = er[kk], g2 = er[kk + half];
@@ -1011,7 +1065,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
           out[kk + half] = from_f32<Tio>(g2 * c.x - g1 * c.y);
         }
       } else {
-        Tio* out = dv + ((size_t)j * Hkv + hk) * D;
+        Tio* out = dv + ((size_t)(j - Lq) * Hkv + hk) * D;
         for (int c = lane; c < D; c += 64) out[c] = from_f32<Tio>(er[c]);
       }
     }
@@ -1021,8 +1075,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------------
 // Host side
+// Workspace layout. Rows are those of the combined sequence: Lp cached rows
+// padded to Lq (a multiple of the 128-row query tile), then the T packed
+// tokens; Tc = Lq + T rows in all, padded to Tp.
 struct AttnLayout {
-  int T, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
+  int T, Lp, Lq, Tc, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
   size_t off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qorder, off_qlist;
   size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
@@ -1030,17 +1087,20 @@ struct AttnLayout {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
+AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   AttnLayout L{};
   L.T = T;
-  L.Tp = (T + 255) / 256 * 256;  // a multiple of every query tile size
+  L.Lp = Lp;
+  L.Lq = (Lp + kFwdBQ - 1) / kFwdBQ * kFwdBQ;
+  L.Tc = L.Lq + T;
+  L.Tp = (L.Tc + 255) / 256 * 256;  // a multiple of every query tile size
   L.Hq = Hq;
   L.Hkv = Hkv;
   L.D = D;
   L.DP = D < 32 ? 32 : D;
   L.nq = L.Tp / kFwdBQ;
-  L.nk64 = (T + kFwdBK - 1) / kFwdBK;
-  L.nk128 = (T + kBwdBK - 1) / kBwdBK;
+  L.nk64 = (L.Tc + kFwdBK - 1) / kFwdBK;
+  L.nk128 = (L.Tc + kBwdBK - 1) / kBwdBK;
   size_t o = 0;
   auto take = [&o](size_t bytes) {
     const size_t at = o;
@@ -1068,8 +1128,12 @@ AttnLayout make_layout(int T, int Hq, int Hkv, int D, bool with_bwd) {
   return L;
 }
 
-int validate_shape(const char* fn, int T, int Hq, int Hkv, int d) {
-  if (T < 1 || T > (1 << 22)) return fail(TA_EINVAL, "%s: T must be in [1, 2^22] (got %d)", fn, T);
+constexpr int kMaxRows = 1 << 22;
+
+int validate_shape(const char* fn, int T, int Lp, int Hq, int Hkv, int d) {
+  if (T < 1 || T > kMaxRows) return fail(TA_EINVAL, "%s: T must be in [1, 2^22] (got %d)", fn, T);
+  if (Lp < 0 || Lp > kMaxRows - T - kFwdBQ)
+    return fail(TA_EINVAL, "%s: past_len must be in [0, 2^22 - T - 128] (got %d)", fn, Lp);
   if (Hq < 1 || Hkv < 1 || Hq > 256 || Hq % Hkv != 0)
     return fail(TA_EINVAL, "%s: need 1 <= Hkv, Hq <= 256 and Hq %% Hkv == 0 (got Hq=%d Hkv=%d)", fn, Hq, Hkv);
   if (d != 16 && d != 64 && d != 128) return fail(TA_EUNSUPPORTED, "%s: head dim %d not in {16, 64, 128}", fn, d);
@@ -1087,22 +1151,36 @@ T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);
 }
 
+// The cached rows of a child partition (none: Lp = 0).
+struct Past {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const unsigned char* vis = nullptr;
+  int pos_offset = 0;
+  float* dk = nullptr;
+  float* dv = nullptr;
+  int accumulate = 0;
+};
+
 template <typename Tio>
 int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, const int* pos, const int* se,
-             float theta, char* ws, hipStream_t st) {
+             const Past& past, float theta, char* ws, hipStream_t st) {
   {
     ProfScope ps("rope_prep", st);
     hipLaunchKernelGGL(rope_prep_kernel<Tio>, dim3(L.Tp), dim3(256), 0, st, static_cast<const Tio*>(q),
-                       static_cast<const Tio*>(k), static_cast<const Tio*>(v), pos, se, L.T, L.Tp, L.Hq, L.Hkv,
-                       L.D, L.DP, theta, at<bf16>(ws, L.off_qr), at<bf16>(ws, L.off_kr), at<bf16>(ws, L.off_vr),
-                       at<int>(ws, L.off_sep), at<float2>(ws, L.off_cs));
+                       static_cast<const Tio*>(k), static_cast<const Tio*>(v), pos, se,
+                       static_cast<const Tio*>(past.k), static_cast<const Tio*>(past.v), past.vis, L.Lp, L.Lq,
+                       past.pos_offset, L.Tc, L.Tp, L.Hq, L.Hkv, L.D, L.DP, theta, at<bf16>(ws, L.off_qr),
+                       at<bf16>(ws, L.off_kr), at<bf16>(ws, L.off_vr), at<int>(ws, L.off_sep),
+                       at<float2>(ws, L.off_cs));
   }
   ProfScope ps("tile_plan", st);
   static_assert(kFwdRows == kFwdBQ, "the forward shares the dQ pass's query-tile plan");
-  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, se, L.T, L.nk64, L.nk128,
-                     at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128), at<int>(ws, L.off_kwork));
-  hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.T, kFwdBQ,
-                     kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
+  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, at<const int>(ws, L.off_sep),
+                     L.Tc, L.Lq, L.nk64, L.nk128, at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128),
+                     at<int>(ws, L.off_kwork));
+  hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.Tc, L.Lq,
+                     kFwdBQ, kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
   hipLaunchKernelGGL(order_kernel, dim3(2), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
                      at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, at<int>(ws, L.off_korder));
   return check_launch("prep");
@@ -1114,14 +1192,14 @@ int run_fwd(const AttnLayout& L, float sl2, void* o, float* lse, char* ws, hipSt
   hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(64 * kFwdWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
                      at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_qcount),
-                     at<const int>(ws, L.off_qlist), at<const int>(ws, L.off_qorder), L.T, L.Tp, L.Hq, L.Hkv, L.nq,
-                     L.nk64, sl2, static_cast<Tio*>(o), lse);
+                     at<const int>(ws, L.off_qlist), at<const int>(ws, L.off_qorder), L.Tc, L.Lq, L.Tp, L.Hq, L.Hkv,
+                     L.nq, L.nk64, sl2, static_cast<Tio*>(o), lse);
   return check_launch("tree_attn_fwd");
 }
 
 template <int DP, typename Tio>
 int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* dout, float sl2, float scale,
-            void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
+            void* dq, void* dk, void* dv, const Past& past, char* ws, hipStream_t st) {
   {
     ProfScope ps("attn_bwd_dq", st);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(256), 0, st,
@@ -1129,52 +1207,41 @@ int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* do
                        static_cast<const Tio*>(o), static_cast<const Tio*>(dout), lse, at<float>(ws, L.off_dd),
                        at<float>(ws, L.off_l2), at<bf16>(ws, L.off_dor), at<const int>(ws, L.off_sep),
                        at<const int>(ws, L.off_qcount), at<const int>(ws, L.off_qlist),
-                       at<const int>(ws, L.off_qorder), at<const float2>(ws, L.off_cs), L.T, L.Tp, L.Hq, L.Hkv,
-                       L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
+                       at<const int>(ws, L.off_qorder), at<const float2>(ws, L.off_cs), L.Tc, L.Lq, L.Tp, L.Hq,
+                       L.Hkv, L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
   }
   ProfScope ps("attn_bwd_dkdv", st);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.nk128 * L.Hkv), dim3(64 * kDkdvWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
                      at<const bf16>(ws, L.off_dor), at<const float>(ws, L.off_l2), at<const float>(ws, L.off_dd),
                      at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm128), at<const int>(ws, L.off_korder),
-                     at<const float2>(ws, L.off_cs), L.T, L.Tp, L.Hq, L.Hkv, L.nk128, sl2, scale,
-                     static_cast<Tio*>(dk), static_cast<Tio*>(dv));
+                     at<const float2>(ws, L.off_cs), L.Tc, L.Lq, L.Lp, L.Tp, L.Hq, L.Hkv, L.nk128, sl2, scale,
+                     static_cast<Tio*>(dk), static_cast<Tio*>(dv), past.dk, past.dv, past.accumulate);
   return check_launch("tree_attn_bwd");
 }
 
-}  // namespace
-}  // namespace ta
-
-using namespace ta;
-
-extern "C" size_t tree_attn_workspace_bytes(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t with_bwd) {
-  if (T < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
-  return make_layout(T, Hq, Hkv, d, with_bwd != 0).total;
-}
-
-extern "C" int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dtype dt, int32_t T, int32_t Hq,
-                             int32_t Hkv, int32_t d, const int32_t* pos, const int32_t* subtree_end,
-                             float softmax_scale, float rope_theta, void* o, float* lse, void* workspace,
-                             size_t ws_bytes, void* stream) {
-  clear_error();
-  if (int rc = validate_shape("tree_attn_fwd", T, Hq, Hkv, d)) return rc;
-  if (!q || !k || !v || !pos || !subtree_end || !o || !lse || !workspace)
-    return fail(TA_EINVAL, "tree_attn_fwd: NULL pointer argument");
-  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_attn_fwd: bad dtype %d", (int)dt);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-    return fail(TA_EINVAL, "tree_attn_fwd: q, k, v must be 16-byte aligned");
+// Shared by the plain and the partition-boundary entry points.
+int attn_fwd(const char* fn, const void* q, const void* k, const void* v, ta_dtype dt, int T, int Hq, int Hkv, int d,
+             const int* pos, const int* se, const Past& past, int Lp, float softmax_scale, float rope_theta, void* o,
+             float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (int rc = validate_shape(fn, T, Lp, Hq, Hkv, d)) return rc;
+  if (!q || !k || !v || !pos || !se || !o || !lse || !workspace) return fail(TA_EINVAL, "%s: NULL pointer argument", fn);
+  if (Lp > 0 && (!past.k || !past.v || !past.vis)) return fail(TA_EINVAL, "%s: NULL past pointer argument", fn);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "%s: bad dtype %d", fn, (int)dt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (Lp > 0 && (!aligned16(past.k) || !aligned16(past.v))))
+    return fail(TA_EINVAL, "%s: q, k, v (and k_past, v_past) must be 16-byte aligned", fn);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(TA_EINVAL, "tree_attn_fwd: workspace must be 256-byte aligned");
-  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "tree_attn_fwd: rope_theta must be >= 0");
-  const AttnLayout L = make_layout(T, Hq, Hkv, d, false);
-  if (ws_bytes < L.total)
-    return fail(TA_EINVAL, "tree_attn_fwd: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+    return fail(TA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "%s: rope_theta must be >= 0", fn);
+  if (past.pos_offset < 0) return fail(TA_EINVAL, "%s: pos_offset must be >= 0", fn);
+  const AttnLayout L = make_layout(T, Lp, Hq, Hkv, d, false);
+  if (ws_bytes < L.total) return fail(TA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, ws_bytes, L.total);
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
   const float sl2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, subtree_end, rope_theta, ws, st)
-                         : run_prep<float>(L, q, k, v, pos, subtree_end, rope_theta, ws, st);
+  int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, se, past, rope_theta, ws, st)
+                         : run_prep<float>(L, q, k, v, pos, se, past, rope_theta, ws, st);
   if (rc) return rc;
   if (dt == TA_BF16) {
     if (L.DP == 32) return run_fwd<32, bf16>(L, sl2, o, lse, ws, st);
@@ -1186,40 +1253,113 @@ extern "C" int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dty
   return run_fwd<128, float>(L, sl2, o, lse, ws, st);
 }
 
+int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, ta_dtype dt, int T, int Hq, int Hkv, int d, const int* pos, const int* se,
+             const Past& past, int Lp, float softmax_scale, float rope_theta, int flags, void* dq, void* dk, void* dv,
+             void* workspace, size_t ws_bytes, void* stream) {
+  if (int rc = validate_shape(fn, T, Lp, Hq, Hkv, d)) return rc;
+  if (!q || !k || !v || !o || !lse || !dout || !pos || !se || !dq || !dk || !dv || !workspace)
+    return fail(TA_EINVAL, "%s: NULL pointer argument", fn);
+  if (Lp > 0 && (!past.k || !past.v || !past.vis || !past.dk || !past.dv))
+    return fail(TA_EINVAL, "%s: NULL past pointer argument", fn);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "%s: bad dtype %d", fn, (int)dt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      (Lp > 0 && (!aligned16(past.k) || !aligned16(past.v))))
+    return fail(TA_EINVAL, "%s: q, k, v, o, dout (and k_past, v_past) must be 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "%s: rope_theta must be >= 0", fn);
+  if (past.pos_offset < 0) return fail(TA_EINVAL, "%s: pos_offset must be >= 0", fn);
+  if (flags & ~(TA_REUSE_PREP | TA_ACCUMULATE_PAST)) return fail(TA_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const AttnLayout L = make_layout(T, Lp, Hq, Hkv, d, true);
+  if (ws_bytes < L.total) return fail(TA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, ws_bytes, L.total);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
+  const float sl2 = scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (!(flags & TA_REUSE_PREP)) {
+    int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, se, past, rope_theta, ws, st)
+                           : run_prep<float>(L, q, k, v, pos, se, past, rope_theta, ws, st);
+    if (rc) return rc;
+  }
+  if (dt == TA_BF16) {
+    if (L.DP == 32) return run_bwd<32, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+    if (L.DP == 64) return run_bwd<64, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+    return run_bwd<128, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+  }
+  if (L.DP == 32) return run_bwd<32, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+  if (L.DP == 64) return run_bwd<64, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+  return run_bwd<128, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, past, ws, st);
+}
+
+}  // namespace
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" size_t tree_attn_workspace_bytes(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t with_bwd) {
+  if (T < 1 || T > kMaxRows || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  return make_layout(T, 0, Hq, Hkv, d, with_bwd != 0).total;
+}
+
+extern "C" int tree_attn_fwd(const void* q, const void* k, const void* v, ta_dtype dt, int32_t T, int32_t Hq,
+                             int32_t Hkv, int32_t d, const int32_t* pos, const int32_t* subtree_end,
+                             float softmax_scale, float rope_theta, void* o, float* lse, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  clear_error();
+  return attn_fwd("tree_attn_fwd", q, k, v, dt, T, Hq, Hkv, d, pos, subtree_end, Past{}, 0, softmax_scale,
+                  rope_theta, o, lse, workspace, ws_bytes, stream);
+}
+
 extern "C" int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, ta_dtype dt, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
                              const int32_t* pos, const int32_t* subtree_end, float softmax_scale, float rope_theta,
                              int32_t flags, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                              void* stream) {
   clear_error();
-  if (int rc = validate_shape("tree_attn_bwd", T, Hq, Hkv, d)) return rc;
-  if (!q || !k || !v || !o || !lse || !dout || !pos || !subtree_end || !dq || !dk || !dv || !workspace)
-    return fail(TA_EINVAL, "tree_attn_bwd: NULL pointer argument");
-  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_attn_bwd: bad dtype %d", (int)dt);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout))
-    return fail(TA_EINVAL, "tree_attn_bwd: q, k, v, o, dout must be 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(TA_EINVAL, "tree_attn_bwd: workspace must be 256-byte aligned");
-  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "tree_attn_bwd: rope_theta must be >= 0");
-  if (flags & ~TA_REUSE_PREP) return fail(TA_EINVAL, "tree_attn_bwd: unknown flags 0x%x", flags);
-  const AttnLayout L = make_layout(T, Hq, Hkv, d, true);
-  if (ws_bytes < L.total)
-    return fail(TA_EINVAL, "tree_attn_bwd: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
-  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
-  const float sl2 = scale * kLog2e;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (!(flags & TA_REUSE_PREP)) {
-    int rc = dt == TA_BF16 ? run_prep<bf16>(L, q, k, v, pos, subtree_end, rope_theta, ws, st)
-                           : run_prep<float>(L, q, k, v, pos, subtree_end, rope_theta, ws, st);
-    if (rc) return rc;
-  }
-  if (dt == TA_BF16) {
-    if (L.DP == 32) return run_bwd<32, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
-    if (L.DP == 64) return run_bwd<64, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
-    return run_bwd<128, bf16>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
-  }
-  if (L.DP == 32) return run_bwd<32, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
-  if (L.DP == 64) return run_bwd<64, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
-  return run_bwd<128, float>(L, o, lse, dout, sl2, scale, dq, dk, dv, ws, st);
+  if (flags & TA_ACCUMULATE_PAST) return fail(TA_EINVAL, "tree_attn_bwd: TA_ACCUMULATE_PAST needs cached rows");
+  return attn_bwd("tree_attn_bwd", q, k, v, o, lse, dout, dt, T, Hq, Hkv, d, pos, subtree_end, Past{}, 0,
+                  softmax_scale, rope_theta, flags, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+extern "C" size_t tree_attn_gw_workspace_bytes(int32_t T, int32_t past_len, int32_t Hq, int32_t Hkv, int32_t d,
+                                               int32_t with_bwd) {
+  if (T < 1 || T > kMaxRows || past_len < 0 || past_len > kMaxRows - T - kFwdBQ || Hq < 1 || Hkv < 1 || d < 1)
+    return 0;
+  return make_layout(T, past_len, Hq, Hkv, d, with_bwd != 0).total;
+}
+
+extern "C" int tree_attn_gw_fwd(const void* q, const void* k, const void* v, ta_dtype dt, int32_t T, int32_t Hq,
+                                int32_t Hkv, int32_t d, const int32_t* pos, const int32_t* subtree_end,
+                                int32_t pos_offset, const void* k_past, const void* v_past,
+                                const uint8_t* past_visible, int32_t past_len, float softmax_scale, float rope_theta,
+                                void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  Past past;
+  past.k = k_past;
+  past.v = v_past;
+  past.vis = past_visible;
+  past.pos_offset = pos_offset;
+  return attn_fwd("tree_attn_gw_fwd", q, k, v, dt, T, Hq, Hkv, d, pos, subtree_end, past, past_len, softmax_scale,
+                  rope_theta, o, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int tree_attn_gw_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, ta_dtype dt, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                                const int32_t* pos, const int32_t* subtree_end, int32_t pos_offset,
+                                const void* k_past, const void* v_past, const uint8_t* past_visible,
+                                int32_t past_len, float softmax_scale, float rope_theta, int32_t flags, void* dq,
+                                void* dk, void* dv, float* dk_past, float* dv_past, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  clear_error();
+  Past past;
+  past.k = k_past;
+  past.v = v_past;
+  past.vis = past_visible;
+  past.pos_offset = pos_offset;
+  past.dk = dk_past;
+  past.dv = dv_past;
+  past.accumulate = (flags & TA_ACCUMULATE_PAST) ? 1 : 0;
+  return attn_bwd("tree_attn_gw_bwd", q, k, v, o, lse, dout, dt, T, Hq, Hkv, d, pos, subtree_end, past, past_len,
+                  softmax_scale, rope_theta, flags, dq, dk, dv, workspace, ws_bytes, stream);
 }
