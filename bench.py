@@ -6,7 +6,9 @@ through the C ABI. Inputs (q, k, v, dO and the packer's pos / subtree_end)
 are resident in HBM before the timed region. Reported value: visible-pair
 TFLOP/s, 14 * d * P * Hq per step (forward 4, backward 10), P = sum(pos + 1).
 
-Also reported on the same line: the host packer's time (not in the step),
+Also reported on the same line: the host packer's time (not in the step), a
+partition-boundary leg (tree 0 unsplit vs split after its prompt, the child
+partitions through the gateway entry points),
 the tile classification, tree_logprob on 16384 bf16 rows x 151936 vocab with
 every row referenced 3 times (its own timed leg, HBM GB/s), per-kernel HIP
 event timings, the roofline of the dominant kernel and the CPU oracle timed
@@ -77,6 +79,79 @@ def cpu_baseline(seqs, groups, cfg, n_trees=3, n_groups=2):
                       f"fwd+bwd, float64 NumPy, {dt:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP"}
 
 
+def gateway_leg(seqs, groups, cfg, dev, steps):
+    """Partition boundary ("Tree Training" §3.3, App. B): tree 0 of the batch
+    unsplit vs split after its shared prefix (parent partition = the prefix
+    chain; the subtrees under it = child partitions of that cut, in one
+    gateway call over the cached, rotated prefix K/V). Both are timed
+    fwd+bwd."""
+    import torch
+
+    import tree_packed_attention_amd as ta
+    import workloads
+
+    g0 = [s_ for s_, g in zip(seqs, groups) if g == groups[0]]
+    L = 0
+    while all(len(s_) > L and s_[L] == g0[0][L] for s_ in g0):
+        L += 1
+    full = ta.tree_pack(g0, None)
+    T, Hq, Hkv, d = full["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    q, k, v, do = workloads.dense_inputs(T, Hq, Hkv, d, "bf16", cfg["seed"] + 7, device=dev)
+    pos = torch.from_numpy(full["pos"]).to(dev)
+    se = torch.from_numpy(full["subtree_end"]).to(dev)
+    assert int(full["pos"][L - 1]) == L - 1 and int(full["subtree_end"][L - 1]) == T  # the prompt is a chain
+
+    # cached prompt K rotated at its positions (what the parent's forward hands over)
+    half = d // 2
+    inv = 10000.0 ** (-torch.arange(half, dtype=torch.float64, device=dev) * 2.0 / d)
+    ang = torch.arange(L, dtype=torch.float64, device=dev)[:, None] * inv[None, :]
+    c, s_ = torch.cos(ang)[:, None, :].float(), torch.sin(ang)[:, None, :].float()
+    kf = k[:L].float()
+    k_past = torch.cat([kf[..., :half] * c - kf[..., half:] * s_, kf[..., half:] * c + kf[..., :half] * s_],
+                       -1).to(torch.bfloat16).contiguous()
+    v_past = v[:L].contiguous()
+    vis = torch.ones(L, dtype=torch.uint8, device=dev)
+    ppos, pse = pos[:L].contiguous(), torch.full((L,), L, dtype=torch.int32, device=dev)
+    cq, ck, cv, cdo = (t[L:].contiguous() for t in (q, k, v, do))
+    cpos, cse = (pos[L:] - L).contiguous(), (se[L:] - L).contiguous()
+    ws_full = ta.attn_workspace(T, Hq, Hkv, d, True, dev)
+    ws_par = ta.attn_workspace(L, Hq, Hkv, d, True, dev)
+    ws_ch = ta.gw_workspace(T - L, L, Hq, Hkv, d, True, dev)
+
+    def unsplit():
+        o, lse, _ = ta.tree_attn_fwd(q, k, v, pos, se, workspace=ws_full)
+        return o, ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws_full, reuse_prep=True)
+
+    def split():
+        o1, l1, _ = ta.tree_attn_fwd(q[:L].contiguous(), k[:L].contiguous(), v_past, ppos, pse, workspace=ws_par)
+        ta.tree_attn_bwd(q[:L].contiguous(), k[:L].contiguous(), v_past, o1, l1, do[:L].contiguous(), ppos, pse,
+                         workspace=ws_par, reuse_prep=True)
+        o2, l2, _ = ta.tree_attn_gw_fwd(cq, ck, cv, cpos, cse, L, k_past, v_past, vis, workspace=ws_ch)
+        g = ta.tree_attn_gw_bwd(cq, ck, cv, o2, l2, cdo, cpos, cse, L, k_past, v_past, vis, workspace=ws_ch,
+                                reuse_prep=True)
+        return o2, g
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            out = fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3, out
+
+    ms_full, (o_full, _) = timed(unsplit)
+    ms_split, (o_child, _) = timed(split)
+    P_child = int((cpos.long() + 1).sum().item()) + L * (T - L)
+    return {"workload": f"tree 0 (T={T}) split after its {L}-token shared prefix: parent partition = the prefix, "
+                        f"child partitions = the subtrees under it ({T - L} tokens) in one gateway call",
+            "unsplit_ms": round(ms_full, 4), "split_ms": round(ms_split, 4),
+            "split_overhead": round(ms_split / ms_full - 1.0, 4),
+            "child_visible_pairs": P_child,
+            "max_abs_child_o_vs_unsplit": round(float((o_child.float() - o_full[L:].float()).abs().max()), 5)}
+
+
 def measured_traffic(kernel):
     """Calibrated HBM bytes per dispatch of `kernel` from the committed
     rocprofv3 counter summaries, if they were taken on the current library
@@ -108,6 +183,7 @@ def main():
     ap.add_argument("--workload", default="multistep", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--no-gateway", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run a plain device copy of this many bytes (calibrates HBM counters)")
     args = ap.parse_args()
@@ -209,6 +285,12 @@ def main():
         print(f"[bench] tree_logprob {lp['ms']:.3f} ms, {lp['gbps']:.0f} GB/s", flush=True)
         del z
 
+    gw = None
+    if not args.no_gateway:
+        print("[bench] gateway leg ...", flush=True)
+        gw = gateway_leg(seqs, groups, cfg, dev, max(3, args.steps // 2))
+        print(f"[bench] gateway: unsplit {gw['unsplit_ms']:.3f} ms, split {gw['split_ms']:.3f} ms", flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline ...", flush=True)
@@ -226,7 +308,7 @@ def main():
                          "skip": round(empty / causal, 4)},
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "pack_ms_host": round(pack_ms, 2),
-        "roofline": roofline, "tree_logprob": lp, "cpu_baseline": cpu,
+        "roofline": roofline, "tree_logprob": lp, "gateway": gw, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
