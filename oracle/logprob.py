@@ -98,3 +98,44 @@ def sep_avg_loss(z, packed, seqs, groups=None):
             seq_sum += -(z[r, int(s[a + 1])] - lse[r])
         total += seq_sum / K
     return total
+
+
+def clipped_policy_loss(z, src, tgt, w, adv, old_logp, mask=None, eps_low=0.2, eps_high=0.2, grad_scale=1.0,
+                        with_grad=True):
+    """Per-occurrence clipped policy loss on shared logit rows.
+
+    Follows the "Trie packing" page (the PPO/GRPO paragraph after "Why
+    indexing matters": every occurrence keeps its own advantage, old
+    log-probability, clipping, mask and weight; advantages are not averaged
+    before the nonlinear loss) and "Tree Training" §3.1 (an RL per-token
+    objective -A_t log p, weighted like any per-token loss). The clipping
+    rule is not spelled out on the pages; it is read as the PPO clipped
+    surrogate (Schulman et al., 2017, the clipped objective):
+
+      r_m    = exp(logp_m - old_logp_m)
+      l_m    = -min(r_m A_m, clip(r_m, 1 - eps_low, 1 + eps_high) A_m)
+      loss   = sum_m w_m mask_m l_m
+      dloss/dlogp_m = -w_m mask_m A_m r_m   if r_m A_m <= clip(r_m) A_m
+                      0                     otherwise (the clipped branch is
+                                            the minimum, a constant in logp)
+      dlogits_r = grad_scale * sum_{m: src_m = r} dloss/dlogp_m (e_{tgt_m} - softmax(z_r))
+
+    At a tie inside the clip range both branches have the same derivative, so
+    ties count as unclipped. Returns (logp [M], lse [R], loss, dlogits [R, V]
+    or None, coef [M] = -dloss/dlogp)."""
+    logp, lse, _, _ = logprob(z, src, tgt, np.zeros(len(np.asarray(src))), with_grad=False)
+    w = np.asarray(w, dtype=np.float64)
+    adv = np.asarray(adv, dtype=np.float64)
+    old = np.asarray(old_logp, dtype=np.float64)
+    mk = np.ones_like(w) if mask is None else np.asarray(mask, dtype=np.float64)
+    r = np.exp(logp - old)
+    a = r * adv
+    b = np.clip(r, 1.0 - eps_low, 1.0 + eps_high) * adv
+    loss = float(np.sum(w * mk * -np.minimum(a, b)))
+    coef = np.where(a <= b, w * mk * adv * r, 0.0)
+    if not with_grad:
+        return logp, lse, loss, None, coef
+    # the gradient through logp is the weighted log-prob gradient with the
+    # per-entry coefficients in place of the weights
+    _, _, _, dz = logprob(z, src, tgt, coef, grad_scale=grad_scale)
+    return logp, lse, loss, dz, coef
