@@ -282,7 +282,30 @@ def main():
               "row_kernel_ms": round(rows_ms, 4), "row_kernel_gbps": round(2.0 * R * V * 2 / (rows_ms * 1e-3) / 1e9, 1),
               "hbm_peak_gbps": PEAK_HBM_GBPS,
               "kernel_ms": {n: round(tot / max(c, 1), 4) for n, (tot, c) in lk.items()}}
-        print(f"[bench] tree_logprob {lp['ms']:.3f} ms, {lp['gbps']:.0f} GB/s", flush=True)
+        # the clipped policy loss on the same rows: per-entry advantage, old
+        # log-probability (ratios in every clip region) and mask
+        adv, ratio, mask = workloads.policy_inputs(M, 5)
+        a_t = torch.as_tensor(adv, device=dev)
+        o_t = ta.tree_logprob(z, s_t, t_t, w_t, with_grad=False, workspace=lws)[0] - torch.as_tensor(
+            np.log(ratio).astype(np.float32), device=dev)
+        m_t = torch.as_tensor(mask, device=dev)
+        for _ in range(2):
+            ta.tree_logprob_ppo(z, s_t, t_t, w_t, a_t, o_t, m_t, workspace=lws)
+        torch.cuda.synchronize()
+        ta.tree_attn_profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(n_lp):
+            ta.tree_logprob_ppo(z, s_t, t_t, w_t, a_t, o_t, m_t, workspace=lws)
+        torch.cuda.synchronize()
+        pp_dt = (time.perf_counter() - t0) / n_lp
+        pk = ta.tree_attn_profile_read()
+        ta.tree_attn_profile_enable(False)
+        alg_pp = 2.0 * R * V * 2 + 25.0 * M + 4.0 * R
+        lp["policy_loss"] = {"ms": round(pp_dt * 1e3, 4), "gbps": round(alg_pp / pp_dt / 1e9, 1),
+                             "eps": [0.2, 0.2], "masked_frac": round(1.0 - float(mask.mean()), 4),
+                             "kernel_ms": {n: round(tot / max(c, 1), 4) for n, (tot, c) in pk.items()}}
+        print(f"[bench] tree_logprob {lp['ms']:.3f} ms, {lp['gbps']:.0f} GB/s; clipped policy loss "
+              f"{lp['policy_loss']['ms']:.3f} ms", flush=True)
         del z
 
     gw = None

@@ -237,6 +237,38 @@ int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * tree_logprob_ppo  (DEVICE)
+ *
+ * Per-occurrence clipped policy loss on shared logit rows. The "Trie
+ * packing" page (its PPO/GRPO paragraph) keeps, for every prediction
+ * occurrence, its own advantage, old log-probability, clipping, mask and
+ * weight, and warns against averaging advantages before the nonlinear loss;
+ * "Tree Training" §3.1 gives the RL per-token objective -A_t log p. The
+ * clipping rule, which the pages do not spell out, is the PPO clipped
+ * surrogate:
+ *   logp_m  as tree_logprob
+ *   r_m     = exp(logp_m - old_logp_m)
+ *   l_m     = -min(r_m A_m, clip(r_m, 1 - eps_low, 1 + eps_high) A_m)
+ *   loss    = sum_m w_m mask_m l_m
+ *   c_m     = -dloss/dlogp_m = w_m mask_m A_m r_m if r_m A_m <= clip(r_m) A_m, else 0
+ *   dlogits[r, :] = grad_scale * sum_{m: src_m = r} c_m (softmax(z_r) - e_{tgt_m})
+ * advantage, old_logp: device float32 [M]; mask: device uint8 [M] or NULL
+ * (all on); a masked entry still gets logp but adds nothing to loss or
+ * dlogits. eps_low, eps_high >= 0 (INFINITY: no clipping on that side).
+ * Other arguments, layouts, limits and the workspace are those of
+ * tree_logprob (same tree_logprob_workspace_bytes); an invalid entry gets
+ * logp = NaN and, unless masked, makes the loss NaN. Bitwise reproducible.
+ * Errors: TA_EINVAL (also for a negative or NaN eps), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+int tree_logprob_ppo(const void* logits, ta_dtype dt, int64_t R, int64_t V,
+                     const int32_t* src_row, const int32_t* target, const float* weight,
+                     const float* advantage, const float* old_logp, const uint8_t* mask, int64_t M,
+                     float eps_low, float eps_high,
+                     float* logp, float* row_lse, float* loss,
+                     void* dlogits, float grad_scale,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * tree_tile_stats  (HOST)
  *
  * Counts of (query-tile, key-tile) pairs under the tile classification the

@@ -171,3 +171,11 @@ def test_device_entry_points_validate_before_hip():
     assert lib.tree_logprob(*largs(V=0)) == ta.TA_EINVAL
     assert lib.tree_logprob(*largs(M=-1)) == ta.TA_EINVAL
     assert lib.tree_logprob(*largs(ws=lw - 1)) == ta.TA_EINVAL
+    pargs = lambda eps_low=0.2, eps_high=0.2, adv=bogus, old=bogus, ws=lw: (
+        bogus, ta.TA_BF16, 16, 100, bogus, bogus, bogus, adv, old, None, 48, eps_low, eps_high, bogus, None, None,
+        None, 1.0, bogus, ws, None)
+    assert lib.tree_logprob_ppo(*pargs(eps_low=-0.1)) == ta.TA_EINVAL and "eps" in ta.last_error()
+    assert lib.tree_logprob_ppo(*pargs(eps_high=float("nan"))) == ta.TA_EINVAL
+    assert lib.tree_logprob_ppo(*pargs(adv=None)) == ta.TA_EINVAL and "advantage" in ta.last_error()
+    assert lib.tree_logprob_ppo(*pargs(old=None)) == ta.TA_EINVAL
+    assert lib.tree_logprob_ppo(*pargs(ws=lw - 1)) == ta.TA_EINVAL

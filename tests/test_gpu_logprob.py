@@ -150,3 +150,147 @@ def test_bitwise_deterministic():
     b = _run(z, src, tgt, w)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- clipped policy loss
+
+EPS = 0.2
+
+
+def _run_ppo(z, src, tgt, w, adv, old, mask, gs=1.0, with_grad=True, eps=(EPS, EPS)):
+    cu = lambda a, dt: torch.as_tensor(np.asarray(a), dtype=dt).cuda()
+    out = ta.tree_logprob_ppo(z.cuda(), cu(src, torch.int32), cu(tgt, torch.int32), cu(w, torch.float32),
+                              cu(adv, torch.float32), cu(old, torch.float32),
+                              None if mask is None else cu(mask, torch.uint8), eps_low=eps[0], eps_high=eps[1],
+                              grad_scale=gs, with_grad=with_grad)
+    torch.cuda.synchronize()
+    return out
+
+
+def _old_logp(zd, src, tgt, ratio):
+    """old_logp from the oracle's logp and the drawn ratios (rounded to fp32,
+    as the kernel reads it)."""
+    lp = zd[src, tgt] - OL.row_lse(zd)[src]
+    return (lp - np.log(ratio)).astype(np.float32)
+
+
+@pytest.mark.parametrize("V,dtype", [(1000, "bf16"), (1003, "bf16"), (32000, "bf16"), (5000, "f32"), (7, "f32")])
+def test_policy_loss_random_rows(V, dtype):
+    R, M = 50, 400
+    rng = np.random.default_rng(V + 7)
+    src = rng.integers(0, R - 3, M)      # the last 3 rows are never referenced
+    tgt = rng.integers(0, V, M)
+    tgt[:40] = tgt[40:80]                # repeated predictions, each with its own advantage
+    src[:40] = src[40:80]
+    w = (rng.random(M) + 0.1).astype(np.float32)
+    adv, ratio, mask = workloads.policy_inputs(M, V)
+    z = workloads.logits_input(R, V, dtype, V) * 3
+    zd = z.double().numpy()
+    old = _old_logp(zd, src, tgt, ratio)
+    logp, lse, loss, dz = _run_ppo(z, src, tgt, w, adv, old, mask, gs=1.5)
+    r_logp, r_lse, r_loss, r_dz, coef = OL.clipped_policy_loss(zd, src, tgt, w, adv, old, mask, EPS, EPS, 1.5)
+    assert np.any(coef == 0) and np.any(coef != 0)
+    assert np.max(np.abs(host(logp) - r_logp)) <= (1e-3 if dtype == "f32" else 2e-2)
+    assert np.max(np.abs(host(lse) - r_lse)) <= 2e-2
+    assert abs(float(loss) - r_loss) <= 1e-3 * max(1.0, abs(r_loss))
+    d = host(dz)
+    assert np.linalg.norm(d - r_dz) / np.linalg.norm(r_dz) <= 5e-2
+    assert np.all(d[R - 3:] == 0)
+
+
+def test_policy_loss_small_exact_f32():
+    """The worked example's occurrence entries (fp32 logits, vocab 32) with
+    per-occurrence advantages: tight agreement."""
+    seqs, groups = workloads.sequences("ex_a")
+    po = OP.pack(seqs, groups)
+    src, tgt, w = OL.occurrence_entries(po, seqs)
+    M = len(src)
+    adv, ratio, mask = workloads.policy_inputs(M, 1, mask_frac=0.2)
+    z = workloads.logits_input(po["T"], 32, "f32", 1)
+    zd = z.double().numpy()
+    old = _old_logp(zd, src, tgt, ratio)
+    logp, lse, loss, dz = _run_ppo(z, src, tgt, w.astype(np.float32), adv, old, mask, gs=0.5)
+    r_logp, _, r_loss, r_dz, _ = OL.clipped_policy_loss(zd, src, tgt, w.astype(np.float32), adv, old, mask, EPS, EPS,
+                                                        0.5)
+    assert np.max(np.abs(host(logp) - r_logp)) <= 1e-5
+    assert abs(float(loss) - r_loss) <= 1e-5
+    assert np.max(np.abs(host(dz) - r_dz)) <= 1e-6
+
+
+def test_policy_loss_unclipped_on_policy_equals_weighted_logprob():
+    """No clipping (eps = inf): the gradient coefficient is w A r, so with
+    ratio ~1 the result matches tree_logprob with weights w A (up to r - 1,
+    i.e. fp32 rounding of old_logp)."""
+    R, V, M = 40, 2000, 300
+    rng = np.random.default_rng(3)
+    src = rng.integers(0, R, M)
+    tgt = rng.integers(0, V, M)
+    w = (rng.random(M) + 0.1).astype(np.float32)
+    adv, _, _ = workloads.policy_inputs(M, 3)
+    z = workloads.logits_input(R, V, "f32", 9)
+    zd = z.double().numpy()
+    old = _old_logp(zd, src, tgt, np.ones(M))
+    _, _, loss, dz = _run_ppo(z, src, tgt, w, adv, old, None, eps=(float("inf"), float("inf")))
+    _, _, _, dz2 = _run(z, src, tgt, (w * adv).astype(np.float32))
+    assert abs(float(loss) + float(np.sum(w.astype(np.float64) * adv))) <= 1e-4 * np.sum(np.abs(w * adv))
+    assert np.max(np.abs(host(dz) - host(dz2))) <= 1e-5
+
+
+def test_policy_loss_large_vocab_full_size():
+    """16384 bf16 rows x 151936 vocab, every row referenced 3 times (M =
+    49152), per-entry advantages, ratios in every clip region, 10 % masked.
+    Loss and logp over all entries (row lse from the oracle, in chunks);
+    dlogits on sampled rows."""
+    R, V = 16384, 151936
+    src, tgt, w = workloads.repeated_rows_entries(R, V, 3, 5)
+    M = len(src)
+    adv, ratio, mask = workloads.policy_inputs(M, 5)
+    z = workloads.logits_input(R, V, "bf16", 5, device="cuda")
+    r_lse = np.empty(R)
+    for a in range(0, R, 512):
+        r_lse[a:a + 512] = OL.row_lse(host(z[a:a + 512]))
+    zt = host(z[torch.as_tensor(src.astype(np.int64), device="cuda"), torch.as_tensor(tgt.astype(np.int64), device="cuda")])
+    r_logp = zt - r_lse[src]
+    old = (r_logp - np.log(ratio)).astype(np.float32)
+    logp, lse, loss, dz = _run_ppo(z, src, tgt, w, adv, old, mask)
+    r = np.exp(r_logp - old.astype(np.float64))
+    a_, b_ = r * adv, np.clip(r, 1 - EPS, 1 + EPS) * adv
+    r_loss = float(np.sum(w * mask * -np.minimum(a_, b_)))
+    assert np.max(np.abs(host(lse) - r_lse)) <= 2e-2
+    assert np.max(np.abs(host(logp) - r_logp)) <= 2e-2
+    assert abs(float(loss) - r_loss) <= 1e-3 * np.sum(np.abs(w * adv)) + 2e-2
+    rows = np.array([0, 1, 777, 8191, 16383])
+    sel = np.isin(src, rows)
+    remap = {int(x): n for n, x in enumerate(rows)}
+    _, _, _, r_dz, _ = OL.clipped_policy_loss(host(z[torch.as_tensor(rows, device="cuda")]),
+                                              np.array([remap[int(x)] for x in src[sel]]), tgt[sel], w[sel], adv[sel],
+                                              old[sel], mask[sel], EPS, EPS)
+    d = host(dz[torch.as_tensor(rows, device="cuda")])
+    assert np.linalg.norm(d - r_dz) / np.linalg.norm(r_dz) <= 5e-2
+
+
+def test_policy_loss_invalid_and_masked_entries_and_determinism():
+    R, V = 8, 64
+    z = workloads.logits_input(R, V, "f32", 2)
+    src = np.array([0, 9, 3, 2, 2, 5])
+    tgt = np.array([1, 1, 3, 3, 3, 70])
+    w = np.ones(6, np.float32)
+    adv = np.array([1, 1, -1, 2, -2, 1], np.float32)
+    old = np.full(6, -3.0, np.float32)
+    mask = np.array([1, 1, 1, 1, 1, 0], np.uint8)   # the second invalid entry is masked
+    logp, _, loss, dz = _run_ppo(z, src, tgt, w, adv, old, mask)
+    lp = host(logp)
+    assert np.isnan(lp[[1, 5]]).all() and np.isfinite(lp[[0, 2, 3, 4]]).all()
+    assert np.isnan(float(loss))                    # entry 1 is invalid and on
+    valid = [0, 2, 3, 4]
+    _, _, _, r_dz, _ = OL.clipped_policy_loss(z.double().numpy(), src[valid], tgt[valid], w[valid], adv[valid],
+                                              old[valid], mask[valid], EPS, EPS)
+    assert np.max(np.abs(host(dz) - r_dz)) <= 1e-5
+    mask[1] = 0
+    _, _, loss2, _ = _run_ppo(z, src, tgt, w, adv, old, mask)
+    assert np.isfinite(float(loss2))
+    a = _run_ppo(z, src, tgt, w, adv, old, mask)
+    b = _run_ppo(z, src, tgt, w, adv, old, mask)
+    bits = lambda t: t.reshape(-1).view(torch.uint8)  # NaN logp of invalid entries compared bitwise
+    for x, y in zip(a, b):
+        assert torch.equal(bits(x), bits(y))

@@ -9,6 +9,7 @@ The names follow the C ABI in include/tree_attn.h:
   tree_attn_fwd(q, k, v, pos, subtree_end, ...)    -> (o, lse)
   tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, ...) -> (dq, dk, dv)
   tree_logprob(logits, src_row, target, weight, ...) -> (logp, row_lse, loss, dlogits)
+  tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, ...) -> (logp, row_lse, loss, dlogits)
   TreeAttention                                    torch.autograd.Function over fwd/bwd
 
 The library must be built first (python tree_packed_attention_amd/build.py);
@@ -39,6 +40,7 @@ EXPORTS = (
     "tree_attn_gw_bwd",
     "tree_logprob_workspace_bytes",
     "tree_logprob",
+    "tree_logprob_ppo",
     "tree_tile_stats",
     "tree_attn_profile_enable",
     "tree_attn_profile_read",
@@ -93,6 +95,9 @@ _lib.tree_logprob_workspace_bytes.restype = _sz
 _lib.tree_logprob_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tree_logprob.restype = ctypes.c_int
 _lib.tree_logprob.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _f32, _p, _sz, _p]
+_lib.tree_logprob_ppo.restype = ctypes.c_int
+_lib.tree_logprob_ppo.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _f32, _p, _p, _p,
+                                  _p, _f32, _p, _sz, _p]
 _lib.tree_tile_stats.restype = ctypes.c_int
 _lib.tree_tile_stats.argtypes = [_p, _i32, _i32, _i32] + [ctypes.POINTER(ctypes.c_int64)] * 4
 _lib.tree_attn_profile_enable.restype = ctypes.c_int
@@ -384,6 +389,37 @@ def tree_logprob(logits, src_row, target, weight, grad_scale=1.0, with_grad=True
                            _dev_ptr(logp, "logp"), _dev_ptr(row_lse, "row_lse") if with_row_lse else null,
                            _dev_ptr(loss, "loss"), _dev_ptr(dlogits, "dlogits") if with_grad else null,
                            float(grad_scale), _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return logp[:M], row_lse, loss, dlogits
+
+
+def tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, mask=None, eps_low=0.2, eps_high=0.2,
+                     grad_scale=1.0, with_grad=True, with_row_lse=True, workspace=None):
+    """Clipped policy loss per occurrence. Returns (logp [M] f32, row_lse [R] f32 or None, loss [] f32,
+    dlogits [R,V] or None)."""
+    torch = _torch()
+    R, V = logits.shape
+    M = src_row.numel()
+    dev = logits.device
+    if workspace is None:
+        nbytes = _lib.tree_logprob_workspace_bytes(R, M)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    logp = torch.empty(max(M, 1), dtype=torch.float32, device=dev)
+    row_lse = torch.empty(R, dtype=torch.float32, device=dev) if with_row_lse else None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dlogits = torch.empty_like(logits) if with_grad else None
+    null = ctypes.c_void_p(None)
+    rc = _lib.tree_logprob_ppo(_dev_ptr(logits, "logits"), _dt(logits), R, V,
+                               _dev_ptr(src_row, "src_row", torch.int32, dev) if M else null,
+                               _dev_ptr(target, "target", torch.int32, dev) if M else null,
+                               _dev_ptr(weight, "weight", torch.float32, dev) if M else null,
+                               _dev_ptr(advantage, "advantage", torch.float32, dev) if M else null,
+                               _dev_ptr(old_logp, "old_logp", torch.float32, dev) if M else null,
+                               _dev_ptr(mask, "mask", torch.uint8, dev) if (M and mask is not None) else null, M,
+                               float(eps_low), float(eps_high),
+                               _dev_ptr(logp, "logp"), _dev_ptr(row_lse, "row_lse") if with_row_lse else null,
+                               _dev_ptr(loss, "loss"), _dev_ptr(dlogits, "dlogits") if with_grad else null,
+                               float(grad_scale), _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
     _check(rc)
     return logp[:M], row_lse, loss, dlogits
 

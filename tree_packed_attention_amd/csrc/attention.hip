@@ -76,11 +76,6 @@ constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ int perm_row(int r) { return (r & ~31) | swap23(r & 31); }
 
-// Key (or query) index inside a 64-row tile of C register i of M-block mb
-// for lane group lg, when the A operand rows were fed in perm_row order.
-__device__ __forceinline__ int c_row(int mb, int i, int lg) {
-  return 32 * mb + 16 * (i >> 3) + 8 * lg + 4 * ((i >> 2) & 1) + (i & 3);
-}
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
@@ -840,7 +835,7 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
   // role 0: x = S - lse/scale = Q' K'^T + rowv (rowv holds -lse/scale);
   // role 1: x = dP - D = dO V^T + rowv (rowv holds -D). The accumulators
   // start at the per-row value, read from LDS straight into them.
-  // C register i of block mb <-> query row c_row(mb, i, lg); lane <-> key.
+  // C register i of block mb <-> query row 32mb + 16(i/8) + 8lg + 4((i/4)%2) + i%4; lane <-> key.
   f32x16 x[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)

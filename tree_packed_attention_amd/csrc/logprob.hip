@@ -19,6 +19,15 @@
 //   5. loss = -sum_m w_m logp_m in entry order (one workgroup)
 // The row is read from HBM once and dlogits written once. Sums run in a
 // fixed order, so results are bitwise reproducible.
+//
+// The clipped policy loss (tree_logprob_ppo) runs the same pipeline. Each
+// entry keeps its own advantage, old log-probability, mask and weight (the
+// "Trie packing" page, its PPO/GRPO paragraph); the row kernel, which holds
+// the row and has just formed logp, turns every entry into its coefficient
+// c_m = -dloss/dlogp_m (PPO clipped surrogate: w mask A r while the
+// unclipped branch is the minimum, else 0) and writes
+// dlogits = s * (sum c) * softmax - s * (sum of c aiming at each target),
+// so the loss needs no second pass over the logits.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -134,11 +143,41 @@ struct Vec16<float> {
   typedef f32x4 type;
 };
 
+// How an entry's log-probability becomes its gradient coefficient
+// c_m = -dloss/dlogp_m. Weighted log-likelihood (adv == nullptr): c = w.
+// Clipped policy loss: r = exp(logp - old), c = w mask A r when r A <=
+// clip(r, lo, hi) A (the unclipped branch is the minimum; ties inside the
+// range have equal derivatives), else 0; written to coef[m].
+struct EntryRule {
+  const float* w;
+  const float* adv;           // nullptr: weighted log-likelihood
+  const float* old;
+  const unsigned char* mask;  // nullptr: every entry on
+  float lo, hi;               // clip range [1 - eps_low, 1 + eps_high]
+  float* coef;                // per-entry coefficients (policy loss only)
+  __device__ __forceinline__ const float* coefs() const { return adv ? coef : w; }
+};
+
+__device__ __forceinline__ float policy_ratio(float logp, float old) { return expf(logp - old); }
+
+// -min(r A, clip(r) A) and whether the unclipped branch is the minimum. A NaN
+// ratio (the logp of an invalid entry) stays NaN: fminf / fmaxf would drop it.
+__device__ __forceinline__ float policy_term(float r, float A, float lo, float hi, bool* unclipped) {
+  if (__builtin_isnan(r)) {
+    *unclipped = false;
+    return r;
+  }
+  const float a = r * A;
+  const float b = fminf(fmaxf(r, lo), hi) * A;
+  *unclipped = a <= b;
+  return -fminf(a, b);
+}
+
 // Rows of the CSR range [beg, beg + n): rank-sort the ids (all distinct) into
 // `sorted`, then logp, W_r and the per-target corrections in entry order.
 template <typename T>
 __device__ void row_entries(const T* __restrict__ row, int beg, int n, const int* __restrict__ ids,
-                            int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w,
+                            int* __restrict__ sorted, const int* __restrict__ tgt, const EntryRule& er,
                             float lse, float* __restrict__ logp, float* red, float* W_out) {
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int id = ids[beg + e];
@@ -150,8 +189,18 @@ __device__ void row_entries(const T* __restrict__ row, int beg, int n, const int
   float ws = 0.0f;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int m = sorted[beg + e];
-    logp[m] = to_f32(row[tgt[m]]) - lse;
-    ws += w[m];
+    const float lp = to_f32(row[tgt[m]]) - lse;
+    logp[m] = lp;
+    float c = er.w[m];
+    if (er.adv) {
+      bool unclipped;
+      const float r = policy_ratio(lp, er.old[m]);
+      policy_term(r, er.adv[m], er.lo, er.hi, &unclipped);
+      const bool on = er.mask == nullptr || er.mask[m] != 0;
+      c = (unclipped && on) ? c * er.adv[m] * r : 0.0f;
+      er.coef[m] = c;
+    }
+    ws += c;
   }
   *W_out = block_reduce(ws, SumOp(), red);
 }
@@ -160,6 +209,7 @@ template <typename T>
 __device__ void row_corrections(const T* __restrict__ row, int beg, int n, const int* __restrict__ sorted,
                                 const int* __restrict__ tgt, const float* __restrict__ w, float lse, float W,
                                 float gs, T* __restrict__ drow) {
+  // w: the per-entry coefficients (weights, or the policy-loss coefficients)
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int t = tgt[sorted[beg + e]];
     bool first = true;
@@ -179,7 +229,7 @@ __device__ void row_corrections(const T* __restrict__ row, int beg, int n, const
 template <typename T, int NV>
 __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
-    int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w, float* __restrict__ logp,
+    int* __restrict__ sorted, const int* __restrict__ tgt, EntryRule er, float* __restrict__ logp,
     float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
   typedef typename Vec16<T>::type vec;
   constexpr int EPV = Vec16<T>::N;
@@ -214,7 +264,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
   const float lse = mx + logf(se);
   if (row_lse != nullptr && threadIdx.x == 0) row_lse[r] = lse;
   float W = 0.0f;
-  row_entries(row, beg, n, ids, sorted, tgt, w, lse, logp, red, &W);
+  row_entries(row, beg, n, ids, sorted, tgt, er, lse, logp, red, &W);
   if (dlogits == nullptr) return;
   T* drow = dlogits + r * V;
   const float sw = gs * W;
@@ -230,7 +280,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     }
   }
   __syncthreads();
-  row_corrections(row, beg, n, sorted, tgt, w, lse, W, gs, drow);
+  row_corrections(row, beg, n, sorted, tgt, er.coefs(), lse, W, gs, drow);
 }
 
 // Row kernel for any V and alignment: streams the row twice (the second
@@ -238,7 +288,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void lp_row_stream_kernel(
     const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
-    int* __restrict__ sorted, const int* __restrict__ tgt, const float* __restrict__ w, float* __restrict__ logp,
+    int* __restrict__ sorted, const int* __restrict__ tgt, EntryRule er, float* __restrict__ logp,
     float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
   __shared__ float red[16];
   const int64_t r = blockIdx.x;
@@ -261,14 +311,14 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_stream_kernel(
   const float lse = gm + logf(sc);
   if (row_lse != nullptr && threadIdx.x == 0) row_lse[r] = lse;
   float W = 0.0f;
-  row_entries(row, beg, n, ids, sorted, tgt, w, lse, logp, red, &W);
+  row_entries(row, beg, n, ids, sorted, tgt, er, lse, logp, red, &W);
   if (dlogits == nullptr) return;
   T* drow = dlogits + r * V;
   const float sw = gs * W;
   for (int64_t c = threadIdx.x; c < V; c += blockDim.x)
     drow[c] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(row[c]) - lse) * kLog2e));
   __syncthreads();
-  row_corrections(row, beg, n, sorted, tgt, w, lse, W, gs, drow);
+  row_corrections(row, beg, n, sorted, tgt, er.coefs(), lse, W, gs, drow);
 }
 
 __global__ __launch_bounds__(1024) void lp_loss_kernel(const float* __restrict__ logp, const float* __restrict__ w,
@@ -280,8 +330,25 @@ __global__ __launch_bounds__(1024) void lp_loss_kernel(const float* __restrict__
   if (threadIdx.x == 0) *loss = -acc;
 }
 
+// Clipped policy loss: sum_m w_m mask_m (-min(r A, clip(r) A)) in entry order,
+// from the logp the row kernel wrote (NaN for an invalid entry, which then
+// makes the loss NaN unless the entry is masked).
+__global__ __launch_bounds__(1024) void lp_policy_loss_kernel(const float* __restrict__ logp, EntryRule er,
+                                                              int64_t M, float* __restrict__ loss) {
+  __shared__ float red[16];
+  float acc = 0.0f;
+  for (int64_t m = threadIdx.x; m < M; m += blockDim.x) {
+    if (er.mask != nullptr && er.mask[m] == 0) continue;
+    bool unclipped;
+    const float l = policy_term(policy_ratio(logp[m], er.old[m]), er.adv[m], er.lo, er.hi, &unclipped);
+    acc += er.w[m] * l;
+  }
+  acc = block_reduce(acc, SumOp(), red);
+  if (threadIdx.x == 0) *loss = acc;
+}
+
 struct LpLayout {
-  size_t off_cnt, off_ptr, off_fill, off_ids, off_sorted, total;
+  size_t off_cnt, off_ptr, off_fill, off_ids, off_sorted, off_coef, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -299,12 +366,14 @@ LpLayout lp_layout(int64_t R, int64_t M) {
   o = al256(o + (size_t)(M > 0 ? M : 1) * 4);
   L.off_sorted = o;
   o = al256(o + (size_t)(M > 0 ? M : 1) * 4);
+  L.off_coef = o;
+  o = al256(o + (size_t)(M > 0 ? M : 1) * 4);
   L.total = o;
   return L;
 }
 
 template <typename T, int NV>
-void launch_reg(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const float* w,
+void launch_reg(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const EntryRule& w,
                 float* logp, float* row_lse, void* dlogits, float gs, int need_all, hipStream_t st) {
   hipLaunchKernelGGL((lp_row_reg_kernel<T, NV>), dim3((unsigned)R), dim3(kRowThreads), 0, st,
                      static_cast<const T*>(logits), V, reinterpret_cast<const int*>(ws + L.off_ptr),
@@ -313,7 +382,7 @@ void launch_reg(int64_t R, const void* logits, int64_t V, char* ws, const LpLayo
 }
 
 template <typename T>
-void launch_rows(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const float* w,
+void launch_rows(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const EntryRule& w,
                  float* logp, float* row_lse, void* dlogits, float gs, hipStream_t st) {
   constexpr int EPV = 16 / sizeof(T);
   const int need_all = (row_lse != nullptr || dlogits != nullptr) ? 1 : 0;
@@ -345,26 +414,26 @@ extern "C" size_t tree_logprob_workspace_bytes(int64_t R, int64_t M) {
   return lp_layout(R, M).total;
 }
 
-extern "C" int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
-                            const int32_t* target, const float* weight, int64_t M, float* logp, float* row_lse,
-                            float* loss, void* dlogits, float grad_scale, void* workspace, size_t ws_bytes,
-                            void* stream) {
-  clear_error();
+namespace {
+
+int logprob_impl(const char* fn, const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
+                 const int32_t* target, EntryRule er, int64_t M, float* logp, float* row_lse, float* loss,
+                 void* dlogits, float grad_scale, void* workspace, size_t ws_bytes, void* stream) {
   if (R < 1 || R >= INT32_MAX || V < 1 || V >= INT32_MAX || M < 0 || M >= INT32_MAX - 1)
-    return fail(TA_EINVAL, "tree_logprob: need 1 <= R, V < 2^31 and 0 <= M < 2^31-1 (R=%lld V=%lld M=%lld)",
-                (long long)R, (long long)V, (long long)M);
-  if (!logits || !workspace || (M > 0 && (!src_row || !target || !weight || !logp)))
-    return fail(TA_EINVAL, "tree_logprob: NULL pointer argument");
-  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_logprob: bad dtype %d", (int)dt);
+    return fail(TA_EINVAL, "%s: need 1 <= R, V < 2^31 and 0 <= M < 2^31-1 (R=%lld V=%lld M=%lld)", fn, (long long)R,
+                (long long)V, (long long)M);
+  if (!logits || !workspace || (M > 0 && (!src_row || !target || !er.w || !logp)))
+    return fail(TA_EINVAL, "%s: NULL pointer argument", fn);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "%s: bad dtype %d", fn, (int)dt);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(TA_EINVAL, "tree_logprob: workspace must be 256-byte aligned");
+    return fail(TA_EINVAL, "%s: workspace must be 256-byte aligned", fn);
   const LpLayout L = lp_layout(R, M);
-  if (ws_bytes < L.total)
-    return fail(TA_EINVAL, "tree_logprob: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  if (ws_bytes < L.total) return fail(TA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, ws_bytes, L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int* cnt = reinterpret_cast<int*>(ws + L.off_cnt);
   int* fill = reinterpret_cast<int*>(ws + L.off_fill);
+  er.coef = reinterpret_cast<float*>(ws + L.off_coef);
   {
   ProfScope ps("lp_csr", st);
   hipLaunchKernelGGL(lp_zero_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, cnt, R);
@@ -380,15 +449,45 @@ extern "C" int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t 
   {
   ProfScope ps("lp_rows", st);
   if (dt == TA_BF16)
-    launch_rows<bf16>(R, logits, V, ws, L, target, weight, logp, row_lse, dlogits, grad_scale, st);
+    launch_rows<bf16>(R, logits, V, ws, L, target, er, logp, row_lse, dlogits, grad_scale, st);
   else
-    launch_rows<float>(R, logits, V, ws, L, target, weight, logp, row_lse, dlogits, grad_scale, st);
+    launch_rows<float>(R, logits, V, ws, L, target, er, logp, row_lse, dlogits, grad_scale, st);
   }
   if (loss != nullptr) {
     ProfScope ps("lp_loss", st);
-    hipLaunchKernelGGL(lp_loss_kernel, dim3(1), dim3(1024), 0, st, logp, weight, M, loss);
+    if (er.adv)
+      hipLaunchKernelGGL(lp_policy_loss_kernel, dim3(1), dim3(1024), 0, st, logp, er, M, loss);
+    else
+      hipLaunchKernelGGL(lp_loss_kernel, dim3(1), dim3(1024), 0, st, logp, er.w, M, loss);
   }
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TA_EHIP, "tree_logprob: kernel launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(TA_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return TA_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
+                            const int32_t* target, const float* weight, int64_t M, float* logp, float* row_lse,
+                            float* loss, void* dlogits, float grad_scale, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  clear_error();
+  EntryRule er{weight, nullptr, nullptr, nullptr, 0.0f, 0.0f, nullptr};
+  return logprob_impl("tree_logprob", logits, dt, R, V, src_row, target, er, M, logp, row_lse, loss, dlogits,
+                      grad_scale, workspace, ws_bytes, stream);
+}
+
+extern "C" int tree_logprob_ppo(const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
+                                const int32_t* target, const float* weight, const float* advantage,
+                                const float* old_logp, const uint8_t* mask, int64_t M, float eps_low, float eps_high,
+                                float* logp, float* row_lse, float* loss, void* dlogits, float grad_scale,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!(eps_low >= 0.0f) || !(eps_high >= 0.0f))
+    return fail(TA_EINVAL, "tree_logprob_ppo: eps_low and eps_high must be >= 0 (got %g, %g)", (double)eps_low,
+                (double)eps_high);
+  if (M > 0 && (!advantage || !old_logp)) return fail(TA_EINVAL, "tree_logprob_ppo: NULL advantage or old_logp");
+  EntryRule er{weight, advantage, old_logp, mask, 1.0f - eps_low, 1.0f + eps_high, nullptr};
+  return logprob_impl("tree_logprob_ppo", logits, dt, R, V, src_row, target, er, M, logp, row_lse, loss, dlogits,
+                      grad_scale, workspace, ws_bytes, stream);
 }

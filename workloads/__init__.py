@@ -241,3 +241,19 @@ def repeated_rows_entries(R, V, repeats, seed):
     tgt = rng.integers(0, V, size=R * repeats)
     w = np.full(R * repeats, 1.0 / repeats, dtype=np.float32)
     return src.astype(np.int32), tgt.astype(np.int32), w
+
+
+# ratios r = exp(logp - old_logp) for policy-loss inputs: below, inside and
+# above the default clip range [0.8, 1.2], each at least 0.05 from its edges
+POLICY_RATIOS = np.array([0.5, 0.7, 0.9, 1.0, 1.1, 1.3, 1.6])
+
+
+def policy_inputs(M, seed, mask_frac=0.1):
+    """Per-entry advantages N(0, 1), a ratio drawn from POLICY_RATIOS (the
+    caller sets old_logp = logp - ln r from its own logp) and a mask with
+    about mask_frac of the entries off."""
+    rng = np.random.default_rng(seed + 4000)
+    adv = rng.standard_normal(M).astype(np.float32)
+    ratio = POLICY_RATIOS[rng.integers(0, len(POLICY_RATIOS), M)]
+    mask = (rng.random(M) >= mask_frac).astype(np.uint8)
+    return adv, ratio, mask
