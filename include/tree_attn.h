@@ -286,6 +286,93 @@ int tree_tile_stats(const int32_t* subtree_end, int32_t T, int32_t BQ, int32_t B
                     int64_t* full, int64_t* partial, int64_t* empty, int64_t* causal);
 
 /* ------------------------------------------------------------------------
+ * tree_conv_fwd / tree_conv_bwd  (DEVICE)
+ *
+ * Tree-correct depthwise causal conv1d ("Tree Training" §3.2, SSM Layers,
+ * Eq. 11; App. A.3). In the DFS layout the tokens just before a child chunk
+ * belong to a sibling branch, so every token's window is taken along its own
+ * ancestor chain, as an independent per-branch pass would see it:
+ *   a_t = bias + sum_{n=0}^{K-1} weight[:, K-1-n] * x_{anc_n(t)}
+ *   y_t = SiLU(a_t) (activation = 1) or a_t (activation = 0)
+ * anc_0(t) = t, anc_{n+1}(t) = parent[anc_n(t)]; terms past a root are zero.
+ * x, y, dy, dx: device [T][C] in dt (TA_BF16 or TA_F32), 16-byte aligned;
+ * weight: device float32 [C][K]; bias: device float32 [C] or NULL.
+ * parent, pos, subtree_end: device int32 [T] from tree_pack.
+ * Backward: dx in dt; dweight float32 [C][K]; dbias float32 [C] or NULL.
+ * Gradients are summed in a fixed order (bitwise reproducible). The backward
+ * gathers each token's descendants at most K-1 levels down from the
+ * preorder range (t, subtree_end[t]) and pos.
+ * Limits: T >= 1, C a positive multiple of 8, 1 <= K <= 8.
+ * workspace (backward): >= tree_conv_workspace_bytes(T, C, K) bytes, 256-byte
+ * aligned. Errors: TA_EINVAL, TA_EHIP.
+ * ---------------------------------------------------------------------- */
+int tree_conv_fwd(const void* x, ta_dtype dt, int32_t T, int32_t C, int32_t K,
+                  const float* weight, const float* bias, const int32_t* parent, int32_t activation,
+                  void* y, void* stream);
+
+size_t tree_conv_workspace_bytes(int32_t T, int32_t C, int32_t K);
+
+int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t T, int32_t C, int32_t K,
+                  const float* weight, const float* bias, const int32_t* parent, const int32_t* pos,
+                  const int32_t* subtree_end, int32_t activation,
+                  void* dx, float* dweight, float* dbias,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_gdn_plan  (HOST)
+ *
+ * Chunk schedule for tree_gdn_fwd ("Tree Training" §3.2, SSM Layers, Eq. 10:
+ * each tree node's segment starts from its parent node's end state; App.
+ * A.2). Every node of the tree_pack chunk table (node_start, node_end
+ * exclusive, node_parent; nodes in preorder, contiguous from 0) is cut into
+ * chunks of at most `chunk` tokens (1..64). A chunk's parent is the previous
+ * chunk of its node or the last chunk of the parent node (-1 at a root). A
+ * chain is a maximal run of chunks each of whose parent is the chunk before
+ * it; a chain's level is 0 at a root, else one more than the level of the
+ * chain holding its parent chunk.
+ * plan: host int32, `cap` entries; NULL or too small -> TA_ECAPACITY with
+ * sizes filled in. Layout: header [n_chunks, n_chains, n_levels, chunk, T,
+ * 0, 0, 0], chunk_start[n_chunks], chunk_len[n_chunks],
+ * chunk_parent[n_chunks], chain_begin[n_chains + 1], chains by level
+ * [n_chains], level_off[n_levels + 1].
+ * Errors: TA_EINVAL (non-contiguous nodes, bad parent, chunk out of range),
+ * TA_ECAPACITY.
+ * ---------------------------------------------------------------------- */
+typedef struct { int32_t n_chunks, n_chains, n_levels, plan_ints; } ta_gdn_plan_sizes;
+
+int tree_gdn_plan(const int32_t* node_start, const int32_t* node_end, const int32_t* node_parent,
+                  int32_t n_nodes, int32_t chunk, int32_t* plan, int32_t cap, ta_gdn_plan_sizes* sizes);
+
+/* ------------------------------------------------------------------------
+ * tree_gdn_fwd  (DEVICE)
+ *
+ * Gated delta rule with the recurrent state routed along the tree ("Tree
+ * Training" §3.2, Eq. 10; App. A.2): per v-head, with alpha_t = exp(g_t),
+ *   h_t = alpha_t (I - beta_t k_t k_t^T) h_{parent(t)} + beta_t k_t v_t^T,
+ *   h = 0 before a root,  o_t = h_t^T q_t,
+ * which equals running every root-to-leaf branch on its own. q/k head of
+ * v-head j is j / (Hv / H); q and k are used as given (normalisation and
+ * scaling are the caller's). Computed in chunks of the plan: WY form inside
+ * a chunk, bf16 matrix products with float32 accumulation, the state carried
+ * in float32 from chunk to chunk.
+ * q, k: device [T][H][dk]; v, o: device [T][Hv][dv], dt TA_BF16 or TA_F32
+ * (float inputs are rounded to bf16 for the products), 16-byte aligned.
+ * g (log decay, <= 0 expected), beta: device float32 [T][Hv].
+ * plan: device copy of the tree_gdn_plan blob; plan_host: the same blob in
+ * host memory (its header and level table drive the launches).
+ * dk, dv in {64, 128}; Hv a multiple of H.
+ * workspace: >= tree_gdn_workspace_bytes(H, Hv, dk, dv, n_chunks) bytes,
+ * 256-byte aligned. Asynchronous on `stream`; one launch per chain level.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED (dk, dv), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t tree_gdn_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, int32_t n_chunks);
+
+int tree_gdn_fwd(const void* q, const void* k, const void* v, ta_dtype dt,
+                 const float* g, const float* beta, int32_t T, int32_t H, int32_t Hv, int32_t dk, int32_t dv,
+                 const int32_t* plan, const int32_t* plan_host, void* o,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (HOST control; for benchmarks and tracing)
  *
  * tree_attn_profile_enable(1) clears the table and starts bracketing every

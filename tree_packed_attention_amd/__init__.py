@@ -10,6 +10,9 @@ The names follow the C ABI in include/tree_attn.h:
   tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, ...) -> (dq, dk, dv)
   tree_logprob(logits, src_row, target, weight, ...) -> (logp, row_lse, loss, dlogits)
   tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, ...) -> (logp, row_lse, loss, dlogits)
+  tree_conv_fwd / tree_conv_bwd(x, ..., parent, ...)  tree-correct causal conv1d and its gradients
+  tree_gdn_plan(node_start, node_end, node_parent)  host chunk schedule -> int32 numpy plan
+  tree_gdn_fwd(q, k, v, g, beta, plan, ...)        tree-routed gated delta rule -> o
   TreeAttention                                    torch.autograd.Function over fwd/bwd
 
 The library must be built first (python tree_packed_attention_amd/build.py);
@@ -42,6 +45,12 @@ EXPORTS = (
     "tree_logprob",
     "tree_logprob_ppo",
     "tree_tile_stats",
+    "tree_conv_fwd",
+    "tree_conv_workspace_bytes",
+    "tree_conv_bwd",
+    "tree_gdn_plan",
+    "tree_gdn_workspace_bytes",
+    "tree_gdn_fwd",
     "tree_attn_profile_enable",
     "tree_attn_profile_read",
 )
@@ -71,6 +80,11 @@ class PackSizes(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("n_nodes", ctypes.c_int32), ("n_trees", ctypes.c_int32)]
 
 
+class GdnPlanSizes(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int32), ("n_chains", ctypes.c_int32), ("n_levels", ctypes.c_int32),
+                ("plan_ints", ctypes.c_int32)]
+
+
 _lib.tree_attn_last_error.restype = ctypes.c_char_p
 _lib.tree_attn_last_error.argtypes = []
 _lib.tree_pack.restype = ctypes.c_int
@@ -98,6 +112,19 @@ _lib.tree_logprob.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p
 _lib.tree_logprob_ppo.restype = ctypes.c_int
 _lib.tree_logprob_ppo.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _f32, _p, _p, _p,
                                   _p, _f32, _p, _sz, _p]
+_lib.tree_conv_fwd.restype = ctypes.c_int
+_lib.tree_conv_fwd.argtypes = [_p, ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p]
+_lib.tree_conv_workspace_bytes.restype = _sz
+_lib.tree_conv_workspace_bytes.argtypes = [_i32, _i32, _i32]
+_lib.tree_conv_bwd.restype = ctypes.c_int
+_lib.tree_conv_bwd.argtypes = [_p, _p, ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz,
+                               _p]
+_lib.tree_gdn_plan.restype = ctypes.c_int
+_lib.tree_gdn_plan.argtypes = [_p, _p, _p, _i32, _i32, _p, _i32, ctypes.POINTER(GdnPlanSizes)]
+_lib.tree_gdn_workspace_bytes.restype = _sz
+_lib.tree_gdn_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.tree_gdn_fwd.restype = ctypes.c_int
+_lib.tree_gdn_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]
 _lib.tree_tile_stats.restype = ctypes.c_int
 _lib.tree_tile_stats.argtypes = [_p, _i32, _i32, _i32] + [ctypes.POINTER(ctypes.c_int64)] * 4
 _lib.tree_attn_profile_enable.restype = ctypes.c_int
@@ -422,6 +449,79 @@ def tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, mask=
                                float(grad_scale), _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
     _check(rc)
     return logp[:M], row_lse, loss, dlogits
+
+
+def tree_conv_fwd(x, weight, bias, parent, activation=1):
+    """x [T, C] (bf16 / f32), weight [C, K] f32, bias [C] f32 or None, parent [T] int32 -> y [T, C]."""
+    torch = _torch()
+    T, C = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    y = torch.empty_like(x)
+    rc = _lib.tree_conv_fwd(_dev_ptr(x, "x"), _dt(x), T, C, K, _dev_ptr(weight, "weight", torch.float32, dev),
+                            _dev_ptr(bias, "bias", torch.float32, dev) if bias is not None else None,
+                            _dev_ptr(parent, "parent", torch.int32, dev), int(activation), _dev_ptr(y, "y"),
+                            _stream(dev))
+    _check(rc)
+    return y
+
+
+def tree_conv_bwd(x, dy, weight, bias, parent, pos, subtree_end, activation=1, workspace=None):
+    """Returns (dx [T, C] like x, dweight [C, K] f32, dbias [C] f32 or None)."""
+    torch = _torch()
+    T, C = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    if workspace is None:
+        workspace = torch.empty(max(_lib.tree_conv_workspace_bytes(T, C, K), 256), dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(weight)
+    db = torch.empty(C, dtype=torch.float32, device=dev) if bias is not None else None
+    rc = _lib.tree_conv_bwd(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype, dev), _dt(x), T, C, K,
+                            _dev_ptr(weight, "weight", torch.float32, dev),
+                            _dev_ptr(bias, "bias", torch.float32, dev) if bias is not None else None,
+                            _dev_ptr(parent, "parent", torch.int32, dev), _dev_ptr(pos, "pos", torch.int32, dev),
+                            _dev_ptr(subtree_end, "subtree_end", torch.int32, dev), int(activation),
+                            _dev_ptr(dx, "dx"), _dev_ptr(dw, "dweight"), _dev_ptr(db, "dbias") if db is not None else None,
+                            _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return dx, dw, db
+
+
+def tree_gdn_plan(node_start, node_end, node_parent, chunk=64):
+    """Host chunk schedule (int32 numpy array) for tree_gdn_fwd."""
+    ns = np.ascontiguousarray(node_start, dtype=np.int32)
+    ne = np.ascontiguousarray(node_end, dtype=np.int32)
+    npar = np.ascontiguousarray(node_parent, dtype=np.int32)
+    sz = GdnPlanSizes()
+    rc = _lib.tree_gdn_plan(_np_ptr(ns), _np_ptr(ne), _np_ptr(npar), len(ns), int(chunk), None, 0, ctypes.byref(sz))
+    if rc != TA_ECAPACITY:
+        _check(rc)
+    plan = np.zeros(sz.plan_ints, dtype=np.int32)
+    _check(_lib.tree_gdn_plan(_np_ptr(ns), _np_ptr(ne), _np_ptr(npar), len(ns), int(chunk), _np_ptr(plan), len(plan),
+                              ctypes.byref(sz)))
+    return plan
+
+
+def tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=None, workspace=None):
+    """q, k [T, H, dk]; v [T, Hv, dv] (bf16 / f32); g, beta [T, Hv] f32; plan from tree_gdn_plan -> o [T, Hv, dv]."""
+    torch = _torch()
+    T, H, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev = q.device
+    plan = np.ascontiguousarray(plan, dtype=np.int32)
+    if plan_dev is None:
+        plan_dev = torch.from_numpy(plan).to(dev)
+    if workspace is None:
+        nbytes = _lib.tree_gdn_workspace_bytes(H, Hv, dk, dv, int(plan[0]))
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(v)
+    rc = _lib.tree_gdn_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev), _dt(q),
+                           _dev_ptr(g, "g", torch.float32, dev), _dev_ptr(beta, "beta", torch.float32, dev), T, H, Hv,
+                           dk, dv, _dev_ptr(plan_dev, "plan", torch.int32, dev), _np_ptr(plan), _dev_ptr(o, "o"),
+                           _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return o
 
 
 def _make_autograd():

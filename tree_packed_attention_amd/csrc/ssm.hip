@@ -1,0 +1,756 @@
+// Tree-correct SSM pieces for gfx950: the depthwise causal conv1d over each
+// token's ancestor chain, and the gated delta rule with the state routed
+// along the tree.
+//
+// "Tree Training" §3.2 (SSM Layers, Eq. 10 and 11) and App. A.2-A.3: in the
+// DFS layout the tokens just before a child chunk belong to a sibling branch,
+// so a chunk must take its conv context and its initial recurrent state from
+// its parent. Both reduce to following par[t]:
+//   conv   a_t = b + sum_{n<K} w[:, K-1-n] x_{anc_n(t)},  y_t = act(a_t)
+//   delta  h_t = alpha_t (I - beta_t k_t k_t^T) h_{par(t)} + beta_t k_t v_t^T,
+//          o_t = h_t^T q_t,  alpha_t = exp(g_t)
+//
+// Conv: one thread per (token, 8 channels) walks the K-1 parents; the
+// backward forms g = dy * act'(a) once, gathers dx_j over the descendants of
+// j that lie at most K-1 levels below it (a walk of the preorder range
+// (j, se[j]) that jumps over every deeper subtree), and reduces dw / db over
+// token blocks in a fixed order.
+//
+// Gated delta rule, per v-head, in chunks of <= 64 tokens inside tree nodes
+// (the host plan, tree_gdn_plan, gives chunk ranges, chunk parents and the
+// chain / level schedule):
+//   1. prep (all chunks at once): gc = in-chunk cumulative log decay,
+//      M = strictly-lower (beta k) k^T * exp(gc_i - gc_j) (bf16 MFMA),
+//      [u | w] = (I + M)^-1 [beta v | beta k exp(gc)] by forward substitution
+//      (one thread per right-hand-side column, the column in registers)
+//   2. state (one launch per level; a workgroup walks one chain): starting
+//      from the parent's end state, per chunk h0 is stored, vn = u - w h0
+//      and h = exp(gc_last) h0 + k^T (exp(gc_last - gc) * vn), both bf16 MFMA
+//      with float32 accumulators that carry h from chunk to chunk
+//   3. output (all chunks at once): o = (q exp(gc)) h0 + (q k^T * exp(gc_i -
+//      gc_j), j <= i) vn
+// The start state of a chunk's first child chunk is the chunk's end state, so
+// a chain that starts under chunk p loads the stored start state of p + 1.
+//
+// Workspace (chunk-local, rows past a chunk's length are zero):
+//   gc  [Hv][nc][64] f32        u  [Hv][nc][64][dv] f32
+//   w   [Hv][nc][64][dk] bf16   (columns in swap23 order within each 16)
+//   kt  [H][nc][dk][64] bf16    vnt [Hv][nc][dv][64] bf16
+//   h0  [nc][Hv][dv][dk] f32    (start state of each chunk, transposed)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "profile.h"
+#include "ta_device.h"
+#include "ta_error.h"
+#include "tree_attn.h"
+
+namespace ta {
+namespace {
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ void ld8f(const bf16* p, float* f) {
+  const bf16x8 v = load8(p);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f[s] = (float)v[s];
+}
+__device__ __forceinline__ void ld8f(const float* p, float* f) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f[s] = a[s];
+    f[4 + s] = b[s];
+  }
+}
+__device__ __forceinline__ void st8f(bf16* p, const float* f) {
+  bf16x8 v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = (bf16)f[s];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void st8f(float* p, const float* f) {
+  f32x4 a, b;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    a[s] = f[s];
+    b[s] = f[4 + s];
+  }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+// one element, rounded to bf16 as the matrix products see it
+__device__ __forceinline__ float rd_bf(const bf16* p) { return (float)*p; }
+__device__ __forceinline__ float rd_bf(const float* p) { return (float)(bf16)*p; }
+
+__device__ __forceinline__ float sigmoidf(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+// ---------------------------------------------------------------- tree conv
+
+constexpr int kConvThreads = 256;
+constexpr int kConvMaxK = 8;
+constexpr int kConvTokBlock = 128;  // tokens per dw / db partial
+
+// pre-activation of token t for channels c0..c0+7
+template <typename Tio>
+__device__ __forceinline__ void conv_pre(const Tio* __restrict__ x, const float* __restrict__ w,
+                                         const float* __restrict__ bias, const int* __restrict__ par, int t, int C,
+                                         int K, int c0, float* a) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = bias ? bias[c0 + e] : 0.0f;
+  int s = t;
+  for (int n = 0; n < K && s >= 0; ++n) {
+    float xv[8];
+    ld8f(x + (size_t)s * C + c0, xv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = fmaf(w[(size_t)(c0 + e) * K + (K - 1 - n)], xv[e], a[e]);
+    s = par[s];
+  }
+}
+
+template <typename Tio>
+__global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __restrict__ x, const float* __restrict__ w,
+                                                                const float* __restrict__ bias,
+                                                                const int* __restrict__ par, int T, int C, int K,
+                                                                int act, Tio* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  float a[8];
+  conv_pre(x, w, bias, par, t, C, K, c0, a);
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+  }
+  st8f(y + (size_t)t * C + c0, a);
+}
+
+// g = dy * act'(a) for a block of kConvTokBlock tokens, plus that block's
+// partial sums of dw[c][K-1-n] = sum g_t x_{anc_n(t)} and db = sum g_t.
+template <typename Tio>
+__global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
+    const Tio* __restrict__ x, const Tio* __restrict__ dy, const float* __restrict__ w,
+    const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, float* __restrict__ gbuf,
+    float* __restrict__ part) {
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  float dw[kConvMaxK][8], db[8];
+#pragma unroll
+  for (int n = 0; n < kConvMaxK; ++n)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dw[n][e] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) db[e] = 0.0f;
+  const int tb = blockIdx.x * kConvTokBlock;
+  const int te = min(tb + kConvTokBlock, T);
+  for (int t = tb; t < te; ++t) {
+    float a[8], g[8];
+    conv_pre(x, w, bias, par, t, C, K, c0, a);
+    ld8f(dy + (size_t)t * C + c0, g);
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = sigmoidf(a[e]);
+        g[e] *= s * (1.0f + a[e] * (1.0f - s));
+      }
+    }
+    st8f(gbuf + (size_t)t * C + c0, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) db[e] += g[e];
+    int s = t;
+#pragma unroll
+    for (int n = 0; n < kConvMaxK; ++n) {
+      if (n < K && s >= 0) {
+        float xv[8];
+        ld8f(x + (size_t)s * C + c0, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dw[n][e] = fmaf(g[e], xv[e], dw[n][e]);
+        s = par[s];
+      }
+    }
+  }
+  // partials [block][c][K + 1]: taps in weight order (index K-1-n), then db
+  float* pp = part + ((size_t)blockIdx.x * C + c0) * (K + 1);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int n = 0; n < kConvMaxK; ++n)
+      if (n < K) pp[(size_t)e * (K + 1) + (K - 1 - n)] = dw[n][e];
+    pp[(size_t)e * (K + 1) + K] = db[e];
+  }
+}
+
+// dx_j = sum_{t: anc_n(t) = j, n < K} w[:, K-1-n] g_t. The descendants of j
+// are the preorder range (j, se[j]); depth below j is pos[t] - pos[j]; a
+// token K or more levels down is skipped together with its subtree.
+template <typename Tio>
+__global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* __restrict__ gbuf,
+                                                                   const float* __restrict__ w,
+                                                                   const int* __restrict__ pos,
+                                                                   const int* __restrict__ se, int T, int C, int K,
+                                                                   Tio* __restrict__ dx) {
+  const int j = blockIdx.x;
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  float acc[8], g[8];
+  ld8f(gbuf + (size_t)j * C + c0, g);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = w[(size_t)(c0 + e) * K + (K - 1)] * g[e];
+  const int pj = pos[j], end = se[j];
+  int t = j + 1;
+  while (t < end) {
+    const int dd = pos[t] - pj;
+    if (dd < K) {
+      ld8f(gbuf + (size_t)t * C + c0, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[(size_t)(c0 + e) * K + (K - 1 - dd)], g[e], acc[e]);
+      ++t;
+    } else {
+      t = se[t];
+    }
+  }
+  st8f(dx + (size_t)j * C + c0, acc);
+}
+
+// Fixed-order sum of the per-block partials.
+__global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* __restrict__ part, int nblk, int C, int K,
+                                                              float* __restrict__ dw, float* __restrict__ db) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float acc[kConvMaxK + 1];
+#pragma unroll
+  for (int n = 0; n <= kConvMaxK; ++n) acc[n] = 0.0f;
+  for (int b = 0; b < nblk; ++b) {
+    const float* pp = part + ((size_t)b * C + c) * (K + 1);
+#pragma unroll
+    for (int n = 0; n <= kConvMaxK; ++n)
+      if (n <= K) acc[n] += pp[n];
+  }
+#pragma unroll
+  for (int n = 0; n < kConvMaxK; ++n)
+    if (n < K) dw[(size_t)c * K + n] = acc[n];
+  if (db) db[c] = acc[K];
+}
+
+// ---------------------------------------------------------------- gated delta rule
+
+constexpr int kCh = 64;  // chunk rows (the plan's chunk size is at most this)
+
+struct GdnLayout {
+  size_t gc, u, w, kt, vnt, h0, total;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
+  GdnLayout L{};
+  size_t o = 0;
+  L.gc = o;
+  o = al256(o + (size_t)Hv * nc * kCh * 4);
+  L.u = o;
+  o = al256(o + (size_t)Hv * nc * kCh * dv * 4);
+  L.w = o;
+  o = al256(o + (size_t)Hv * nc * kCh * dk * 2);
+  L.kt = o;
+  o = al256(o + (size_t)H * nc * dk * kCh * 2);
+  L.vnt = o;
+  o = al256(o + (size_t)Hv * nc * dv * kCh * 2);
+  L.h0 = o;
+  o = al256(o + (size_t)nc * Hv * dv * dk * 4);
+  L.total = o;
+  return L;
+}
+
+// Stage 1: per (chunk, v-head). 256 threads.
+template <int DK, int DV, typename Tin>
+__global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v,
+                                                       const float* __restrict__ g, const float* __restrict__ beta,
+                                                       const int* __restrict__ cstart, const int* __restrict__ clen,
+                                                       int nc, int H, int Hv, float* __restrict__ gcw,
+                                                       float* __restrict__ u, bf16* __restrict__ wp,
+                                                       bf16* __restrict__ kt) {
+  __shared__ float gcs[kCh];
+  __shared__ float bs[kCh];
+  __shared__ __attribute__((aligned(16))) float Ms[kCh][kCh + 4];
+  __shared__ __attribute__((aligned(16))) bf16 ks[kCh][DK + 8];
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int hk = hv / (Hv / H);
+  const int t0 = cstart[c], L = clen[c];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  if (wv == 0) {
+    float gv = lane < L ? g[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(gv, o);
+      if (lane >= o) gv += y;
+    }
+    gcs[lane] = gv;
+    bs[lane] = lane < L ? beta[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
+    gcw[((size_t)hv * nc + c) * kCh + lane] = gv;
+  }
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&ks[r][cc]) = r < L ? load8(k + ((size_t)(t0 + r) * H + hk) * DK + cc) : zero8();
+  }
+  __syncthreads();
+  // M (rows m > n only are read): waves 0-2 form the lower 32x32 blocks of k k^T
+  if (wv < 3) {
+    const int mb = wv == 0 ? 0 : 1, nb = wv == 2 ? 1 : 0;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+      acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(&ks[32 * mb + lc][16 * a + 8 * lg]),
+                         *reinterpret_cast<const bf16x8*>(&ks[32 * nb + lc][16 * a + 8 * lg]), acc);
+    const int n = 32 * nb + lc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3);
+      Ms[m][n] = n < m ? bs[m] * acc[i] * expf(gcs[m] - gcs[n]) : 0.0f;
+    }
+  }
+  // k^T, chunk-local, for the state pass (once per k-head)
+  if (hv % (Hv / H) == 0) {
+    bf16* kto = kt + ((size_t)hk * nc + c) * DK * kCh;
+    for (int idx = tid; idx < DK * kCh; idx += 256) {
+      const int kk = idx / kCh, r = idx % kCh;
+      kto[idx] = ks[r][kk];
+    }
+  }
+  __syncthreads();
+  // forward substitution, one right-hand-side column per thread: x starts as
+  // the right-hand side and row r becomes x_r = rhs_r - sum_{j<r} M[r][j] x_j.
+  // The compiler barrier per row keeps only that row's LDS reads in flight
+  // (hoisting all of them would need ~2000 registers).
+  const int col = tid;
+  if (col < DV + DK) {
+    float x[kCh];
+    if (col < DV) {
+#pragma unroll
+      for (int r = 0; r < kCh; ++r) x[r] = r < L ? bs[r] * rd_bf(v + ((size_t)(t0 + r) * Hv + hv) * DV + col) : 0.0f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < kCh; ++r) x[r] = bs[r] * (float)ks[r][col - DV] * expf(gcs[r]);
+    }
+#pragma unroll
+    for (int r = 1; r < kCh; ++r) {
+      asm volatile("" ::: "memory");
+      float acc = x[r];
+#pragma unroll
+      for (int j = 0; j < r; j += 4) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(&Ms[r][j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < r) acc = fmaf(-m4[e], x[j + e], acc);
+      }
+      x[r] = acc;
+    }
+    if (col < DV) {
+      float* uo = u + ((size_t)hv * nc + c) * kCh * DV + col;
+#pragma unroll
+      for (int r = 0; r < kCh; ++r) uo[(size_t)r * DV] = x[r];
+    } else {
+      bf16* wo = wp + ((size_t)hv * nc + c) * kCh * DK + swap23(col - DV);
+#pragma unroll
+      for (int r = 0; r < kCh; ++r) wo[(size_t)r * DK] = (bf16)x[r];
+    }
+  }
+}
+
+// Stage 2: one workgroup per (chain of this level, v-head); wave s owns state
+// columns [32 s, 32 s + 32) of dv. The state h (dk x 32 per wave) lives in
+// MFMA C registers: block b, register i <-> row 32b + 8(i/4) + 4(lane/32) + i%4.
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DV / 32)) void gdn_state_kernel(
+    const int* __restrict__ level_chains, int lvl0, const int* __restrict__ chain_begin,
+    const int* __restrict__ cpar, const int* __restrict__ clen, int nc, int H, int Hv, const float* __restrict__ gcw,
+    const float* __restrict__ u, const bf16* __restrict__ wp, const bf16* __restrict__ kt, bf16* __restrict__ vnt,
+    float* __restrict__ h0w) {
+  constexpr int NB = DK / 32;
+  const int ch = level_chains[lvl0 + blockIdx.x];
+  const int hv = blockIdx.y;
+  const int hk = hv / (Hv / H);
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 5, lc = lane & 31;
+  const int n = 32 * wv + lc;  // state column (dv index) of this lane
+  const int cb = chain_begin[ch], ce = chain_begin[ch + 1];
+  const int p = cpar[cb];
+  f32x16 h[NB];
+  if (p < 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) h[b] = f32x16{};
+  } else {
+    // the start state of p's first child chunk p + 1 is p's end state
+    const float* hp = h0w + (((size_t)(p + 1) * Hv + hv) * DV + n) * DK;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(hp + 32 * b + 8 * j + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[b][4 * j + e] = x[e];
+      }
+  }
+  for (int c = cb; c < ce; ++c) {
+    const int L = clen[c];
+    const size_t hc = (size_t)hv * nc + c;
+    // store the start state (transposed: [dv][dk])
+    float* ho = h0w + (((size_t)c * Hv + hv) * DV + n) * DK;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = h[b][4 * j + e];
+        *reinterpret_cast<f32x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
+      }
+    // vn = u - w h0: B operand of k-step a = -h0 registers 8(a%2)..+7 of block a/2
+    // (w's columns are stored in the matching swap23 order)
+    bf16x8 hb[DK / 16];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) hb[a][s] = (bf16)(-h[a >> 1][8 * (a & 1) + s]);
+    f32x16 vn[2];
+    const float* uc = u + hc * kCh * DV;
+    const bf16* wc = wp + hc * kCh * DK;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vn[mb][i] = uc[(size_t)(32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3)) * DV + n];
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a)
+        vn[mb] = mfma32x32x16(load8(wc + (size_t)(32 * mb + lc) * DK + 16 * a + 8 * lg), hb[a], vn[mb]);
+    }
+    // vn, transposed [dv][64], for the output stage
+    bf16* vo = vnt + (hc * DV + n) * kCh;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
+        *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+      }
+    // h = exp(gc_last) h0 + k^T (exp(gc_last - gc) vn). Contraction over the
+    // chunk rows in the order whose k-step a, slot s is row
+    // 16a + 8(s/4) + 4(lane/32) + s%4 = vn register 8(a%2)+s of block a/2.
+    const float* gcc = gcw + hc * kCh;
+    const float gl = gcc[L - 1];
+    const float al = expf(gl);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) h[b] *= al;
+    bf16x8 vb[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int r = 16 * a + 8 * (s >> 2) + 4 * lg + (s & 3);
+        vb[a][s] = (bf16)(r < L ? vn[a >> 1][8 * (a & 1) + s] * expf(gl - gcc[r]) : 0.0f);
+      }
+    const bf16* kc = kt + ((size_t)hk * nc + c) * DK * kCh;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const bf16* kp = kc + (size_t)(32 * b + lc) * kCh + 16 * a + 4 * lg;
+        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(kp), *reinterpret_cast<const bf16x4*>(kp + 8));
+        h[b] = mfma32x32x16(A, vb[a], h[b]);
+      }
+  }
+}
+
+// Stage 3: per (chunk, v-head), 256 threads. Wave w: query rows 32(w%2) ..
+// +31 (one per lane), dv blocks of 32 assigned by w/2. Works on O^T so that
+// each lane owns one query: S^T = K Q^T, then O^T += vn^T P^T (P^T from the
+// C registers; vn read in the matching row order) and O^T += h0^T (q e^gc)^T.
+template <int DK, int DV, typename Tio>
+__global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
+                                                      const int* __restrict__ cstart, const int* __restrict__ clen,
+                                                      int nc, int H, int Hv, const float* __restrict__ gcw,
+                                                      const bf16* __restrict__ vnt, const float* __restrict__ h0w,
+                                                      Tio* __restrict__ o) {
+  constexpr int NDW = DV / 64;  // 32-wide dv blocks per wave
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int hk = hv / (Hv / H);
+  const int t0 = cstart[c], L = clen[c];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 5, lc = lane & 31;
+  const int qb = wv & 1;
+  const int i = 32 * qb + lc;
+  const bool qok = i < L;
+  const size_t hc = (size_t)hv * nc + c;
+  const float* gcc = gcw + hc * kCh;
+  const float gi = gcc[i];
+  bf16x8 qop[DK / 16];
+  const Tio* qrow = q + ((size_t)(t0 + (qok ? i : 0)) * H + hk) * DK;
+#pragma unroll
+  for (int a = 0; a < DK / 16; ++a) qop[a] = qok ? load8(qrow + 16 * a + 8 * lg) : zero8();
+  f32x16 acc[NDW];
+#pragma unroll
+  for (int bb = 0; bb < NDW; ++bb) acc[bb] = f32x16{};
+  // inter-chunk term with the chunk's start state
+  {
+    const float eg = expf(gi);
+    bf16x8 qs[DK / 16];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qs[a][s] = (bf16)((float)qop[a][s] * eg);
+#pragma unroll
+    for (int bb = 0; bb < NDW; ++bb) {
+      const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
+      const float* hp = h0w + (((size_t)c * Hv + hv) * DV + d) * DK;
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(hp + 16 * a + 8 * lg);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(hp + 16 * a + 8 * lg + 4);
+        bf16x8 A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          A[e] = (bf16)x0[e];
+          A[4 + e] = (bf16)x1[e];
+        }
+        acc[bb] = mfma32x32x16(A, qs[a], acc[bb]);
+      }
+    }
+  }
+  // intra-chunk term; key blocks above the query block are fully masked
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int j = 32 * kb + lc;
+    const bool kok = j < L;
+    const Tio* krow = k + ((size_t)(t0 + (kok ? j : 0)) * H + hk) * DK;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a) s = mfma32x32x16(kok ? load8(krow + 16 * a + 8 * lg) : zero8(), qop[a], s);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jj = 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3);
+      pb[r >> 3][r & 7] = (bf16)((jj <= i && qok) ? s[r] * expf(gi - gcc[jj]) : 0.0f);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int a2 = 2 * kb + h2;
+#pragma unroll
+      for (int bb = 0; bb < NDW; ++bb) {
+        const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
+        const bf16* vp = vnt + (hc * DV + d) * kCh + 16 * a2 + 4 * lg;
+        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 8));
+        acc[bb] = mfma32x32x16(A, pb[h2], acc[bb]);
+      }
+    }
+  }
+  if (qok) {
+    Tio* orow = o + ((size_t)(t0 + i) * Hv + hv) * DV;
+#pragma unroll
+    for (int bb = 0; bb < NDW; ++bb)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d = 32 * (NDW * (wv >> 1) + bb) + 8 * j4 + 4 * lg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) orow[d + e] = from_f32<Tio>(acc[bb][4 * j4 + e]);
+      }
+  }
+}
+
+struct PlanView {
+  int nc, nch, nl, chunk, T;
+  int off_cstart, off_clen, off_cpar, off_chain, off_lchains, off_loff;
+};
+
+bool plan_view(const int32_t* ph, PlanView* v) {
+  v->nc = ph[0];
+  v->nch = ph[1];
+  v->nl = ph[2];
+  v->chunk = ph[3];
+  v->T = ph[4];
+  if (v->nc < 1 || v->nch < 1 || v->nch > v->nc || v->nl < 1 || v->nl > v->nch || v->chunk < 1 || v->chunk > kCh)
+    return false;
+  v->off_cstart = 8;
+  v->off_clen = v->off_cstart + v->nc;
+  v->off_cpar = v->off_clen + v->nc;
+  v->off_chain = v->off_cpar + v->nc;
+  v->off_lchains = v->off_chain + v->nch + 1;
+  v->off_loff = v->off_lchains + v->nch;
+  return true;
+}
+
+template <int DK, int DV, typename Tio>
+void gdn_launch(const void* q, const void* k, const void* v, const float* g, const float* beta, int H, int Hv,
+                const int32_t* plan, const int32_t* ph, const PlanView& pv, void* o, char* ws, const GdnLayout& L,
+                hipStream_t st) {
+  float* gcw = reinterpret_cast<float*>(ws + L.gc);
+  float* u = reinterpret_cast<float*>(ws + L.u);
+  bf16* wp = reinterpret_cast<bf16*>(ws + L.w);
+  bf16* kt = reinterpret_cast<bf16*>(ws + L.kt);
+  bf16* vnt = reinterpret_cast<bf16*>(ws + L.vnt);
+  float* h0w = reinterpret_cast<float*>(ws + L.h0);
+  const int* cstart = plan + pv.off_cstart;
+  const int* clen = plan + pv.off_clen;
+  {
+    ProfScope ps("gdn_prep", st);
+    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, Tio>), dim3(pv.nc, Hv), dim3(256), 0, st, static_cast<const Tio*>(k),
+                       static_cast<const Tio*>(v), g, beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, kt);
+  }
+  {
+    ProfScope ps("gdn_state", st);
+    const int32_t* loff = ph + pv.off_loff;
+    for (int l = 0; l < pv.nl; ++l) {
+      const int n = loff[l + 1] - loff[l];
+      hipLaunchKernelGGL((gdn_state_kernel<DK, DV>), dim3(n, Hv), dim3(64 * (DV / 32)), 0, st,
+                         plan + pv.off_lchains, loff[l], plan + pv.off_chain, plan + pv.off_cpar, clen, pv.nc, H, Hv,
+                         gcw, u, wp, kt, vnt, h0w);
+    }
+  }
+  {
+    ProfScope ps("gdn_out", st);
+    hipLaunchKernelGGL((gdn_out_kernel<DK, DV, Tio>), dim3(pv.nc, Hv), dim3(256), 0, st, static_cast<const Tio*>(q),
+                       static_cast<const Tio*>(k), cstart, clen, pv.nc, H, Hv, gcw, vnt, h0w, static_cast<Tio*>(o));
+  }
+}
+
+template <typename Tio>
+int gdn_dispatch(int dk, int dv, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                 int H, int Hv, const int32_t* plan, const int32_t* ph, const PlanView& pv, void* o, char* ws,
+                 const GdnLayout& L, hipStream_t st) {
+  if (dk == 128 && dv == 128)
+    gdn_launch<128, 128, Tio>(q, k, v, g, beta, H, Hv, plan, ph, pv, o, ws, L, st);
+  else if (dk == 128 && dv == 64)
+    gdn_launch<128, 64, Tio>(q, k, v, g, beta, H, Hv, plan, ph, pv, o, ws, L, st);
+  else if (dk == 64 && dv == 128)
+    gdn_launch<64, 128, Tio>(q, k, v, g, beta, H, Hv, plan, ph, pv, o, ws, L, st);
+  else
+    gdn_launch<64, 64, Tio>(q, k, v, g, beta, H, Hv, plan, ph, pv, o, ws, L, st);
+  return TA_OK;
+}
+
+bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+}  // namespace ta
+
+using namespace ta;
+
+// ---------------------------------------------------------------- C ABI: conv
+
+extern "C" int tree_conv_fwd(const void* x, ta_dtype dt, int32_t T, int32_t C, int32_t K, const float* weight,
+                             const float* bias, const int32_t* parent, int32_t activation, void* y, void* stream) {
+  clear_error();
+  if (!x || !weight || !parent || !y) return fail(TA_EINVAL, "tree_conv_fwd: NULL pointer argument");
+  if (T < 1 || C < 8 || C % 8 != 0 || K < 1 || K > kConvMaxK)
+    return fail(TA_EINVAL, "tree_conv_fwd: need T >= 1, C a positive multiple of 8, 1 <= K <= %d (T=%d C=%d K=%d)",
+                kConvMaxK, T, C, K);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_conv_fwd: bad dtype %d", (int)dt);
+  if (activation != 0 && activation != 1) return fail(TA_EINVAL, "tree_conv_fwd: activation must be 0 or 1");
+  if (!al16(x) || !al16(y)) return fail(TA_EINVAL, "tree_conv_fwd: x and y must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(T, (C / 8 + kConvThreads - 1) / kConvThreads);
+  {
+    ProfScope ps("conv_fwd", st);
+    if (dt == TA_BF16)
+      hipLaunchKernelGGL(conv_fwd_kernel<bf16>, grid, dim3(kConvThreads), 0, st, static_cast<const bf16*>(x), weight,
+                         bias, parent, T, C, K, activation, static_cast<bf16*>(y));
+    else
+      hipLaunchKernelGGL(conv_fwd_kernel<float>, grid, dim3(kConvThreads), 0, st, static_cast<const float*>(x),
+                         weight, bias, parent, T, C, K, activation, static_cast<float*>(y));
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TA_EHIP, "tree_conv_fwd: kernel launch failed: %s", hipGetErrorString(e));
+  return TA_OK;
+}
+
+namespace {
+size_t conv_ws_part_off(int32_t T, int32_t C) { return al256((size_t)T * C * 4); }
+}  // namespace
+
+extern "C" size_t tree_conv_workspace_bytes(int32_t T, int32_t C, int32_t K) {
+  if (T < 1 || C < 1 || K < 1 || K > kConvMaxK) return 0;
+  const size_t nblk = (T + kConvTokBlock - 1) / kConvTokBlock;
+  return conv_ws_part_off(T, C) + al256(nblk * C * (K + 1) * 4);
+}
+
+extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t T, int32_t C, int32_t K,
+                             const float* weight, const float* bias, const int32_t* parent, const int32_t* pos,
+                             const int32_t* subtree_end, int32_t activation, void* dx, float* dweight, float* dbias,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!x || !dy || !weight || !parent || !pos || !subtree_end || !dx || !dweight || !workspace)
+    return fail(TA_EINVAL, "tree_conv_bwd: NULL pointer argument");
+  if (T < 1 || C < 8 || C % 8 != 0 || K < 1 || K > kConvMaxK)
+    return fail(TA_EINVAL, "tree_conv_bwd: need T >= 1, C a positive multiple of 8, 1 <= K <= %d (T=%d C=%d K=%d)",
+                kConvMaxK, T, C, K);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_conv_bwd: bad dtype %d", (int)dt);
+  if (activation != 0 && activation != 1) return fail(TA_EINVAL, "tree_conv_bwd: activation must be 0 or 1");
+  if (!al16(x) || !al16(dy) || !al16(dx)) return fail(TA_EINVAL, "tree_conv_bwd: x, dy, dx must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TA_EINVAL, "tree_conv_bwd: workspace must be 256-byte aligned");
+  const size_t need = tree_conv_workspace_bytes(T, C, K);
+  if (ws_bytes < need) return fail(TA_EINVAL, "tree_conv_bwd: workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* gbuf = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + conv_ws_part_off(T, C));
+  const int nblk = (T + kConvTokBlock - 1) / kConvTokBlock;
+  const int cy = (C / 8 + kConvThreads - 1) / kConvThreads;
+  {
+    ProfScope ps("conv_bwd", st);
+    if (dt == TA_BF16) {
+      hipLaunchKernelGGL(conv_bwd_g_kernel<bf16>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
+                         static_cast<const bf16*>(x), static_cast<const bf16*>(dy), weight, bias, parent, T, C, K,
+                         activation, gbuf, part);
+      hipLaunchKernelGGL(conv_bwd_dx_kernel<bf16>, dim3(T, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
+                         subtree_end, T, C, K, static_cast<bf16*>(dx));
+    } else {
+      hipLaunchKernelGGL(conv_bwd_g_kernel<float>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
+                         static_cast<const float*>(x), static_cast<const float*>(dy), weight, bias, parent, T, C, K,
+                         activation, gbuf, part);
+      hipLaunchKernelGGL(conv_bwd_dx_kernel<float>, dim3(T, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
+                         subtree_end, T, C, K, static_cast<float*>(dx));
+    }
+    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, st, part, nblk, C, K, dweight,
+                       dbias);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TA_EHIP, "tree_conv_bwd: kernel launch failed: %s", hipGetErrorString(e));
+  return TA_OK;
+}
+
+// ---------------------------------------------------------------- C ABI: gated delta rule
+
+extern "C" size_t tree_gdn_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, int32_t n_chunks) {
+  if (H < 1 || Hv < 1 || dk < 1 || dv < 1 || n_chunks < 1) return 0;
+  return gdn_layout(H, Hv, dk, dv, n_chunks).total;
+}
+
+extern "C" int tree_gdn_fwd(const void* q, const void* k, const void* v, ta_dtype dt, const float* g,
+                            const float* beta, int32_t T, int32_t H, int32_t Hv, int32_t dk, int32_t dv,
+                            const int32_t* plan, const int32_t* plan_host, void* o, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  clear_error();
+  if (!q || !k || !v || !g || !beta || !plan || !plan_host || !o || !workspace)
+    return fail(TA_EINVAL, "tree_gdn_fwd: NULL pointer argument");
+  if (T < 1 || H < 1 || Hv < H || Hv % H != 0)
+    return fail(TA_EINVAL, "tree_gdn_fwd: need T >= 1, H >= 1 and Hv a multiple of H (T=%d H=%d Hv=%d)", T, H, Hv);
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(TA_EUNSUPPORTED, "tree_gdn_fwd: dk and dv must be 64 or 128 (dk=%d dv=%d)", dk, dv);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_gdn_fwd: bad dtype %d", (int)dt);
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(o))
+    return fail(TA_EINVAL, "tree_gdn_fwd: q, k, v and o must be 16-byte aligned");
+  PlanView pv;
+  if (!plan_view(plan_host, &pv)) return fail(TA_EINVAL, "tree_gdn_fwd: plan header is not a tree_gdn_plan output");
+  if (pv.T != T) return fail(TA_EINVAL, "tree_gdn_fwd: the plan covers %d tokens, T = %d", pv.T, T);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TA_EINVAL, "tree_gdn_fwd: workspace must be 256-byte aligned");
+  const GdnLayout L = gdn_layout(H, Hv, dk, dv, pv.nc);
+  if (ws_bytes < L.total) return fail(TA_EINVAL, "tree_gdn_fwd: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (dt == TA_BF16)
+    gdn_dispatch<bf16>(dk, dv, q, k, v, g, beta, H, Hv, plan, plan_host, pv, o, ws, L, st);
+  else
+    gdn_dispatch<float>(dk, dv, q, k, v, g, beta, H, Hv, plan, plan_host, pv, o, ws, L, st);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TA_EHIP, "tree_gdn_fwd: kernel launch failed: %s", hipGetErrorString(e));
+  return TA_OK;
+}

@@ -257,3 +257,35 @@ def policy_inputs(M, seed, mask_frac=0.1):
     ratio = POLICY_RATIOS[rng.integers(0, len(POLICY_RATIOS), M)]
     mask = (rng.random(M) >= mask_frac).astype(np.uint8)
     return adv, ratio, mask
+
+
+def gdn_inputs(T, H, Hv, dk, dv, dtype, seed, device="cpu"):
+    """Gated-delta-rule inputs: q, k rows of unit length (the caller-side
+    normalisation GDN layers apply), v N(0, 1), log decays g = -softplus(x)
+    with x ~ N(-2, 1) (decay factors mostly 0.8-0.95), beta = sigmoid(N(0, 1))."""
+    import torch
+
+    gen = torch.Generator().manual_seed(seed + 5000)
+    q = torch.randn(T, H, dk, generator=gen)
+    k = torch.randn(T, H, dk, generator=gen)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn(T, Hv, dv, generator=gen)
+    g = -torch.nn.functional.softplus(torch.randn(T, Hv, generator=gen) - 2.0)
+    beta = torch.sigmoid(torch.randn(T, Hv, generator=gen))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return (q.to(dt).to(device), k.to(dt).to(device), v.to(dt).to(device), g.to(device), beta.to(device))
+
+
+def conv_inputs(T, C, K, dtype, seed, device="cpu"):
+    """Tree conv inputs: x and dy N(0, 1) [T, C], weight N(0, 0.25) [C, K],
+    bias N(0, 0.01) [C]."""
+    import torch
+
+    gen = torch.Generator().manual_seed(seed + 6000)
+    x = torch.randn(T, C, generator=gen)
+    dy = torch.randn(T, C, generator=gen)
+    w = torch.randn(C, K, generator=gen) * 0.5
+    b = torch.randn(C, generator=gen) * 0.1
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return x.to(dt).to(device), dy.to(dt).to(device), w.to(device), b.to(device)
