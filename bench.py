@@ -152,6 +152,63 @@ def gateway_leg(seqs, groups, cfg, dev, steps):
             "max_abs_child_o_vs_unsplit": round(float((o_child.float() - o_full[L:].float()).abs().max()), 5)}
 
 
+def ssm_leg(seqs, groups, dev, steps):
+    """Tree SSM kernels on the same packed batch, at the shape of a hybrid
+    model's linear-attention layer: 16 q/k heads and 32 v heads of 128, conv
+    width 2*16*128 + 32*128 = 8192 channels, K = 4, bf16. Times the tree conv
+    forward and backward and the tree-routed gated delta rule forward, each
+    against its algorithmic HBM bytes (inputs read once, outputs written once)."""
+    import numpy as np
+    import torch
+
+    import tree_packed_attention_amd as ta
+    import workloads
+
+    p = ta.tree_pack(seqs, groups)
+    T = p["T"]
+    H, Hv, d, C, K = 16, 32, 128, 8192, 4
+    t0 = time.perf_counter()
+    plan = ta.tree_gdn_plan(p["node_start"], p["node_end"], p["node_parent"], 64)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan_dev = torch.from_numpy(plan).to(dev)
+    q, k, v, g, beta = workloads.gdn_inputs(T, H, Hv, d, d, "bf16", 3, device=dev)
+    gws = torch.empty(ta.library().tree_gdn_workspace_bytes(H, Hv, d, d, int(plan[0])), dtype=torch.uint8, device=dev)
+    x, dy, w, b = workloads.conv_inputs(T, C, K, "bf16", 3, device=dev)
+    par = torch.from_numpy(p["parent"]).to(dev)
+    pos = torch.from_numpy(p["pos"]).to(dev)
+    se = torch.from_numpy(p["subtree_end"]).to(dev)
+    cws = torch.empty(ta.library().tree_conv_workspace_bytes(T, C, K), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ta.tree_attn_profile_enable(True)
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t1) / steps
+        ks = ta.tree_attn_profile_read()
+        ta.tree_attn_profile_enable(False)
+        return dt, {n: round(tot / max(c, 1), 4) for n, (tot, c) in ks.items()}
+
+    gdn_s, gdn_k = timed(lambda: ta.tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=plan_dev, workspace=gws))
+    cf_s, _ = timed(lambda: ta.tree_conv_fwd(x, w, b, par, 1))
+    cb_s, _ = timed(lambda: ta.tree_conv_bwd(x, dy, w, b, par, pos, se, 1, workspace=cws))
+    gdn_bytes = T * (2 * H * d * 2 + 2 * Hv * d * 2 + 8 * Hv)
+    cf_bytes, cb_bytes = 2.0 * T * C * 2, 3.0 * T * C * 2
+    nc = int(plan[0])
+    gdn_flop = nc * Hv * (6.0 * 64 * d * d + 64 * 64 * 4.0 * d)
+    return {"workload": f"multistep batch T={T}, gated delta rule 16 q/k x 32 v heads, dk=dv=128; conv C=8192 K=4; bf16",
+            "chunks": nc, "chains": int(plan[1]), "levels": int(plan[2]), "plan_ms_host": round(plan_ms, 3),
+            "gdn_fwd_ms": round(gdn_s * 1e3, 4), "gdn_fwd_gbps": round(gdn_bytes / gdn_s / 1e9, 1),
+            "gdn_fwd_tflops_chunked": round(gdn_flop / gdn_s / 1e12, 2), "gdn_kernel_ms": gdn_k,
+            "conv_fwd_ms": round(cf_s * 1e3, 4), "conv_fwd_gbps": round(cf_bytes / cf_s / 1e9, 1),
+            "conv_bwd_ms": round(cb_s * 1e3, 4), "conv_bwd_gbps": round(cb_bytes / cb_s / 1e9, 1),
+            "hbm_peak_gbps": PEAK_HBM_GBPS}
+
+
 def measured_traffic(kernel):
     """Calibrated HBM bytes per dispatch of `kernel` from the committed
     rocprofv3 counter summaries, if they were taken on the current library
@@ -184,6 +241,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--no-gateway", action="store_true")
+    ap.add_argument("--no-ssm", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run a plain device copy of this many bytes (calibrates HBM counters)")
     args = ap.parse_args()
@@ -314,6 +372,13 @@ def main():
         gw = gateway_leg(seqs, groups, cfg, dev, max(3, args.steps // 2))
         print(f"[bench] gateway: unsplit {gw['unsplit_ms']:.3f} ms, split {gw['split_ms']:.3f} ms", flush=True)
 
+    ssm = None
+    if not args.no_ssm:
+        print("[bench] tree SSM leg ...", flush=True)
+        ssm = ssm_leg(seqs, groups, dev, max(3, args.steps // 2))
+        print(f"[bench] gdn fwd {ssm['gdn_fwd_ms']:.3f} ms, conv fwd {ssm['conv_fwd_ms']:.3f} ms "
+              f"({ssm['conv_fwd_gbps']:.0f} GB/s), conv bwd {ssm['conv_bwd_ms']:.3f} ms", flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline ...", flush=True)
@@ -331,7 +396,7 @@ def main():
                          "skip": round(empty / causal, 4)},
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "pack_ms_host": round(pack_ms, 2),
-        "roofline": roofline, "tree_logprob": lp, "gateway": gw, "cpu_baseline": cpu,
+        "roofline": roofline, "tree_logprob": lp, "gateway": gw, "tree_ssm": ssm, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
