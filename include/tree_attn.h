@@ -286,6 +286,39 @@ int tree_tile_stats(const int32_t* subtree_end, int32_t T, int32_t BQ, int32_t B
                     int64_t* full, int64_t* partial, int64_t* empty, int64_t* causal);
 
 /* ------------------------------------------------------------------------
+ * tree_partition  (HOST)
+ *
+ * Partition plan for a tree that does not fit one pass ("Tree Training"
+ * §3.3, Partitioning): cuts only at node boundaries; every partition has
+ * exactly one parent partition (or none), so a backward pass keeps one
+ * root-to-leaf chain of partition graphs alive; each partition holds at most
+ * `capacity` tokens; the number of partitions is kept small. The pages leave
+ * the algorithm to a general solver; this planner:
+ *   1. cuts the tree into the fewest connected pieces of <= capacity tokens
+ *      (bottom-up; while a node's residual, its length plus its attached
+ *      children's residuals, exceeds capacity, the child with the largest
+ *      residual -- ties: the earlier child -- is cut off);
+ *   2. packs pieces cut from the same node (or tree roots), which share every
+ *      ancestor, into shared partitions, first-fit decreasing by tokens
+ *      (ties: preorder); tree roots first, then, for the partitions in
+ *      creation order, the groups hanging from their nodes in preorder.
+ * Inputs: the tree_pack chunk table (node_start, node_end exclusive,
+ * node_parent; preorder). Outputs (host, caller-owned, n_nodes entries each
+ * suffice): node_part[n] = partition of node n; part_tokens[p];
+ * part_parent[p] (-1 for a partition of tree roots); part_cut[p] = the node
+ * its pieces hang from (-1 for tree roots); *n_parts.
+ * A child partition runs through tree_attn_gw_* with one gateway: the cached
+ * rows of the cut node's last token and its ancestors (all visible), at
+ * pos_offset = that token's depth + 1.
+ * Errors: TA_EINVAL (a node longer than capacity, a parent not before its
+ * node, an empty node, NULL arguments).
+ * ---------------------------------------------------------------------- */
+int tree_partition(const int32_t* node_start, const int32_t* node_end, const int32_t* node_parent,
+                   int32_t n_nodes, int64_t capacity,
+                   int32_t* node_part, int32_t* part_tokens, int32_t* part_parent, int32_t* part_cut,
+                   int32_t* n_parts);
+
+/* ------------------------------------------------------------------------
  * tree_conv_fwd / tree_conv_bwd  (DEVICE)
  *
  * Tree-correct depthwise causal conv1d ("Tree Training" §3.2, SSM Layers,

@@ -15,10 +15,12 @@ Reading taken (the pages leave the algorithm open):
    largest residual is cut off (ties: the earlier child). This greedy is
    optimal for connected pieces (Kundu and Misra, "A linear tree partitioning
    algorithm", SIAM J. Comput. 1977); pinned here by brute force.
-2. Pack. Pieces whose parent nodes lie in the same partition (or that are
-   tree roots) may share a partition without giving it a second parent.
-   Groups are taken in order (tree roots first, then by partition in creation
-   order); inside a group, first-fit decreasing by tokens (ties: preorder).
+2. Pack. Pieces cut from the same node (or tree roots) share every ancestor,
+   so they may share a partition with one parent partition and one gateway
+   of cached ancestor rows (App. B.2 keeps one gateway per cut node). Groups
+   are taken in order: tree roots first, then, partition by partition in
+   creation order, the nodes of that partition in preorder; inside a group,
+   first-fit decreasing by tokens (ties: preorder).
 A node longer than C cannot be placed (a cut inside a node is not a node
 boundary): the planner rejects it.
 """
@@ -60,40 +62,41 @@ def cut(node_len, node_parent, C):
 
 def plan(node_len, node_parent, C):
     """Both stages. Returns dict: node_part [n], part_tokens [P], part_parent
-    [P] (-1: no parent partition), piece_root_of_node [n]."""
+    [P] (-1: no parent partition), part_cut [P] (the node the partition's
+    pieces hang from, -1 for tree roots), piece [n] (piece root of each node)."""
     piece, tokens = cut(node_len, node_parent, C)
     roots = sorted(tokens)                            # piece roots in preorder
     part_of_piece = {}
-    part_tokens, part_parent = [], []
-    # groups: pieces whose parent node lies in one partition (-1: tree roots)
-    queue = [-1]
-    done = set()
+    part_tokens, part_parent, part_cut = [], [], []
+    queue = [-1]                                      # -1: the tree roots, then partitions in creation order
     while queue:
         gp = queue.pop(0)
-        if gp in done:
-            continue
-        done.add(gp)
-        members = [r for r in roots if r not in part_of_piece and
-                   ((node_parent[r] < 0) if gp == -1 else
-                    (node_parent[r] >= 0 and part_of_piece.get(piece[node_parent[r]]) == gp))]
-        members.sort(key=lambda r: (-tokens[r], r))
-        mine = []
-        for r in members:
-            for b in mine:
-                if part_tokens[b] + tokens[r] <= C:
+        if gp == -1:
+            cut_nodes = [-1]
+        else:                                         # nodes of partition gp with pieces hanging from them
+            cut_nodes = sorted({node_parent[r] for r in roots
+                                if node_parent[r] >= 0 and part_of_piece.get(piece[node_parent[r]]) == gp})
+        for u in cut_nodes:
+            members = [r for r in roots if node_parent[r] == u]
+            members.sort(key=lambda r: (-tokens[r], r))
+            mine = []
+            for r in members:
+                for b in mine:
+                    if part_tokens[b] + tokens[r] <= C:
+                        part_of_piece[r] = b
+                        part_tokens[b] += tokens[r]
+                        break
+                else:
+                    b = len(part_tokens)
+                    part_tokens.append(tokens[r])
+                    part_parent.append(gp)
+                    part_cut.append(u)
                     part_of_piece[r] = b
-                    part_tokens[b] += tokens[r]
-                    break
-            else:
-                b = len(part_tokens)
-                part_tokens.append(tokens[r])
-                part_parent.append(gp)
-                part_of_piece[r] = b
-                mine.append(b)
-                queue.append(b)
+                    mine.append(b)
+                    queue.append(b)
     node_part = [part_of_piece[piece[v]] for v in range(len(node_len))]
     return {"node_part": np.array(node_part), "part_tokens": np.array(part_tokens),
-            "part_parent": np.array(part_parent), "piece": np.array(piece)}
+            "part_parent": np.array(part_parent), "part_cut": np.array(part_cut), "piece": np.array(piece)}
 
 
 def min_connected_pieces_brute(node_len, node_parent, C):

@@ -50,6 +50,7 @@ def _check_plan(lens, par, C, r):
             assert r["part_parent"][part[v]] == -1
         elif part[p] != part[v]:
             assert r["part_parent"][part[v]] == part[p]      # exactly one parent partition
+            assert r["part_cut"][part[v]] == p               # and one cut node (one gateway)
         piece = r["piece"][v]
         assert piece == v or r["piece"][p] == piece            # pieces are connected
     assert P >= -(-sum(lens) // C)
@@ -76,10 +77,18 @@ def test_special_cases():
     assert r["part_tokens"].tolist() == [4, 4, 4] and r["part_parent"].tolist() == [-1, 0, 1]
     # root 10 with children 6, 5, 4 at C = 16: cut the heaviest child (6); the
     # remaining root piece is 19 > 16, so 5 goes too; root piece 14; the two cut
-    # pieces (6, 5) share the parent partition and pack together (11)
+    # pieces (6, 5) hang from the same node and pack together (11)
     r = OPT.plan([10, 6, 5, 4], [-1, 0, 0, 0], 16)
     assert r["part_tokens"].tolist() == [14, 11] and r["part_parent"].tolist() == [-1, 0]
-    assert r["node_part"].tolist() == [0, 1, 1, 0]
+    assert r["node_part"].tolist() == [0, 1, 1, 0] and r["part_cut"].tolist() == [-1, 0]
+    # r(1) with children a(3) -> a1(2) and b(3) -> b1(2), C = 4. Cut: a
+    # (3 + 2 > 4) drops a1, b drops b1, r (1 + 3 + 3 > 4) drops a (tie: the
+    # earlier child): pieces {r, b} 4, {a} 3, {a1} 2, {b1} 2. Pack: {r, b};
+    # then the pieces hanging from its nodes in preorder: from r: {a}; from
+    # b: {b1}; then from a (in the second partition): {a1}.
+    r = OPT.plan([1, 3, 2, 3, 2], [-1, 0, 1, 0, 3], 4)
+    assert r["part_tokens"].tolist() == [4, 3, 2, 2] and r["part_cut"].tolist() == [-1, 0, 3, 1]
+    assert r["part_parent"].tolist() == [-1, 0, 0, 1] and r["node_part"].tolist() == [0, 1, 3, 0, 2]
 
 
 def test_token_counts_worked_case():

@@ -98,3 +98,41 @@ def test_ssm_argument_validation():
     bad = plan.copy()
     bad[3] = 99
     assert lib.tree_gdn_fwd(*gargs(ph=bad.ctypes.data_as(ctypes.c_void_p))) == ta.TA_EINVAL
+
+
+# ----------------------------------------------------------------- partition planner
+
+from oracle import partition as OPT  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_partition_bit_exact_against_oracle(seed):
+    seqs, groups = workloads.random_forest(seed, [400, 150, 33], max_depth=6, seg_lo=1, seg_hi=70)
+    po = OP.pack(seqs, groups)
+    lens = (po["node_end"] - po["node_start"]).tolist()
+    for C in sorted(c for c in {max(lens), max(lens) + 7, 120, 300, 10 ** 7} if c >= max(lens)):
+        got = ta.tree_partition(po["node_start"], po["node_end"], po["node_parent"], C)
+        want = OPT.plan(lens, po["node_parent"].tolist(), C)
+        for key in ("node_part", "part_tokens", "part_parent", "part_cut"):
+            assert np.array_equal(got[key], want[key]), (C, key)
+
+
+def test_partition_random_agentic_tree():
+    """The 131072-token depth-10 tree at a 32768-token capacity: invariants
+    and agreement with the oracle."""
+    seqs, groups = workloads.sequences("agentic_l")
+    p = ta.tree_pack(seqs, groups)
+    got = ta.tree_partition(p["node_start"], p["node_end"], p["node_parent"], 32768)
+    lens = (p["node_end"] - p["node_start"]).tolist()
+    want = OPT.plan(lens, p["node_parent"].tolist(), 32768)
+    assert np.array_equal(got["node_part"], want["node_part"])
+    assert got["part_tokens"].max() <= 32768 and got["part_tokens"].sum() == p["T"]
+    assert len(got["part_tokens"]) >= -(-p["T"] // 32768)
+
+
+def test_partition_errors():
+    ns, ne, npar = np.array([0, 5], np.int32), np.array([5, 9], np.int32), np.array([-1, 0], np.int32)
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_partition(ns, ne, npar, 4)                            # node 0 is longer than the capacity
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_partition(ns, ne, np.array([-1, 1], np.int32), 10)    # parent not before its node

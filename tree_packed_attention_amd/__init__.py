@@ -11,6 +11,7 @@ The names follow the C ABI in include/tree_attn.h:
   tree_logprob(logits, src_row, target, weight, ...) -> (logp, row_lse, loss, dlogits)
   tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, ...) -> (logp, row_lse, loss, dlogits)
   tree_conv_fwd / tree_conv_bwd(x, ..., parent, ...)  tree-correct causal conv1d and its gradients
+  tree_partition(node_start, node_end, node_parent, capacity)  host partition plan -> dict
   tree_gdn_plan(node_start, node_end, node_parent)  host chunk schedule -> int32 numpy plan
   tree_gdn_fwd(q, k, v, g, beta, plan, ...)        tree-routed gated delta rule -> o
   TreeAttention                                    torch.autograd.Function over fwd/bwd
@@ -45,6 +46,7 @@ EXPORTS = (
     "tree_logprob",
     "tree_logprob_ppo",
     "tree_tile_stats",
+    "tree_partition",
     "tree_conv_fwd",
     "tree_conv_workspace_bytes",
     "tree_conv_bwd",
@@ -112,6 +114,8 @@ _lib.tree_logprob.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p
 _lib.tree_logprob_ppo.restype = ctypes.c_int
 _lib.tree_logprob_ppo.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _f32, _p, _p, _p,
                                   _p, _f32, _p, _sz, _p]
+_lib.tree_partition.restype = ctypes.c_int
+_lib.tree_partition.argtypes = [_p, _p, _p, _i32, _i64, _p, _p, _p, _p, ctypes.POINTER(ctypes.c_int32)]
 _lib.tree_conv_fwd.restype = ctypes.c_int
 _lib.tree_conv_fwd.argtypes = [_p, ctypes.c_int, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p]
 _lib.tree_conv_workspace_bytes.restype = _sz
@@ -449,6 +453,24 @@ def tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, mask=
                                float(grad_scale), _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
     _check(rc)
     return logp[:M], row_lse, loss, dlogits
+
+
+def tree_partition(node_start, node_end, node_parent, capacity):
+    """Host partition plan: dict(node_part [n], part_tokens [P], part_parent [P], part_cut [P]) as int32 arrays."""
+    ns = np.ascontiguousarray(node_start, dtype=np.int32)
+    ne = np.ascontiguousarray(node_end, dtype=np.int32)
+    npar = np.ascontiguousarray(node_parent, dtype=np.int32)
+    n = len(ns)
+    node_part = np.zeros(n, np.int32)
+    part_tokens = np.zeros(n, np.int32)
+    part_parent = np.zeros(n, np.int32)
+    part_cut = np.zeros(n, np.int32)
+    n_parts = ctypes.c_int32(0)
+    _check(_lib.tree_partition(_np_ptr(ns), _np_ptr(ne), _np_ptr(npar), n, int(capacity), _np_ptr(node_part),
+                               _np_ptr(part_tokens), _np_ptr(part_parent), _np_ptr(part_cut), ctypes.byref(n_parts)))
+    P = n_parts.value
+    return {"node_part": node_part, "part_tokens": part_tokens[:P].copy(), "part_parent": part_parent[:P].copy(),
+            "part_cut": part_cut[:P].copy()}
 
 
 def tree_conv_fwd(x, weight, bias, parent, activation=1):
