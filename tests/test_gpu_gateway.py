@@ -196,3 +196,92 @@ def test_masked_gateway_rows_get_no_gradient_and_no_weight():
     for a, b in ((dq, rq), (dk, rk), (dv, rv)):
         assert rel_l2(host(a), b) <= GRAD_TOL
     assert not dkp.any() and not dvp.any()
+
+
+# ----------------------------------------------------------------- planned partitions end to end
+
+
+def _run_partitioned(seqs, groups, Hq, Hkv, d, dtype, seed, capacity):
+    """Plans the packed tree with tree_partition and runs every partition on
+    the GPU: tree-root partitions through the plain entry points, the others
+    through the gateway of their cut token's ancestors (the cut token
+    included, all visible) at pos_offset = its depth + 1. Gradients of the
+    cached rows are relayed back (un-rotated for dK, Tree Training App. B.5)
+    and summed. Returns the assembled outputs and the plan."""
+    p = ta.tree_pack(seqs, groups)
+    T = p["T"]
+    par, pos = p["parent"], p["pos"]
+    q, k, v, do = workloads.dense_inputs(T, Hq, Hkv, d, dtype, seed)
+    plan = ta.tree_partition(p["node_start"], p["node_end"], p["node_parent"], capacity)
+    node_of = np.repeat(np.arange(p["n_nodes"]), p["node_end"] - p["node_start"])
+    tok_part = plan["node_part"][node_of]
+    O = np.zeros((T, Hq, d))
+    LSE = np.zeros((Hq, T))
+    dq = np.zeros((T, Hq, d))
+    dk = np.zeros((T, Hkv, d))
+    dv = np.zeros((T, Hkv, d))
+    for b in range(len(plan["part_tokens"])):
+        R = np.nonzero(tok_part == b)[0]
+        loc = -np.ones(T, np.int64)
+        loc[R] = np.arange(len(R))
+        lpar = np.where(par[R] >= 0, loc[np.maximum(par[R], 0)], -1)
+        lpar[par[R] < 0] = -1
+        cutn = int(plan["part_cut"][b])
+        off = 0 if cutn < 0 else int(pos[p["node_end"][cutn] - 1]) + 1
+        lpos = (pos[R] - off).astype(np.int32)
+        assert np.all(lpos[lpar < 0] == 0)
+        lse_ = _subtree_ends(lpar).astype(np.int32)
+        c = lambda t: t[torch.as_tensor(R)].contiguous().cuda()
+        qb, kb, vb, dob = c(q), c(k), c(v), c(do)
+        pt, st = torch.from_numpy(lpos).cuda(), torch.from_numpy(lse_).cuda()
+        if cutn < 0:
+            o, lse, ws = ta.tree_attn_fwd(qb, kb, vb, pt, st, rope_theta=THETA, with_bwd_workspace=True)
+            g = ta.tree_attn_bwd(qb, kb, vb, o, lse, dob, pt, st, rope_theta=THETA, workspace=ws, reuse_prep=True)
+        else:
+            A = [int(p["node_end"][cutn] - 1)]
+            while par[A[-1]] >= 0:
+                A.append(int(par[A[-1]]))
+            A = np.array(A[::-1])
+            assert len(A) == off
+            kp = torch.from_numpy(OA.rope(k[torch.as_tensor(A)].double().numpy(), pos[A], THETA)).to(q.dtype).cuda()
+            vp = v[torch.as_tensor(A)].contiguous().cuda()
+            vis = torch.ones(len(A), dtype=torch.uint8).cuda()
+            o, lse, ws = ta.tree_attn_gw_fwd(qb, kb, vb, pt, st, off, kp, vp, vis, rope_theta=THETA,
+                                             with_bwd_workspace=True)
+            g = ta.tree_attn_gw_bwd(qb, kb, vb, o, lse, dob, pt, st, off, kp, vp, vis, rope_theta=THETA,
+                                    workspace=ws, reuse_prep=True)
+            dk[A] += OA.rope_transpose(host(g[3]), pos[A], THETA)
+            dv[A] += host(g[4])
+        torch.cuda.synchronize()
+        O[R], LSE[:, R], dq[R] = host(o), host(lse), host(g[0])
+        dk[R] += host(g[1])
+        dv[R] += host(g[2])
+    return dict(p=p, plan=plan, q=q, k=k, v=v, do=do, O=O, LSE=LSE, dq=dq, dk=dk, dv=dv)
+
+
+@pytest.mark.parametrize("capacity", [600, 1500])
+def test_planned_partitions_reproduce_the_unsplit_tree(capacity):
+    """A 3000-token tree (depth <= 6) cut by tree_partition into partitions of
+    at most `capacity` tokens, several levels deep; the assembled result
+    equals the oracle on the unsplit tree."""
+    seqs, groups = workloads.random_tree(41, 6, 3000, 16, 300)
+    print(f"\n[case] planned partitions, capacity {capacity}", flush=True)
+    r = _run_partitioned(seqs, groups, 8, 2, 128, "bf16", 41, capacity)
+    plan = r["plan"]
+    depth = 0
+    for b in range(len(plan["part_parent"])):
+        lvl, x = 0, b
+        while plan["part_parent"][x] >= 0:
+            x, lvl = plan["part_parent"][x], lvl + 1
+        depth = max(depth, lvl)
+    print(f"partitions {len(plan['part_tokens'])}, levels {depth + 1}", flush=True)
+    assert len(plan["part_tokens"]) >= 3 and depth >= 1
+    po = OP.pack(seqs, groups)
+    qn, kn, vn, don = host(r["q"]), host(r["k"]), host(r["v"]), host(r["do"])
+    O, LSE = OA.forward_branches(qn, kn, vn, po["par"], po["pos"])
+    rdq, rdk, rdv = OA.backward_branches(qn, kn, vn, don, po["par"], po["pos"])
+    errs = dict(o=max_abs(r["O"], O), lse=max_abs(r["LSE"], LSE), dq=rel_l2(r["dq"], rdq), dk=rel_l2(r["dk"], rdk),
+                dv=rel_l2(r["dv"], rdv))
+    print({k: f"{x:.2e}" for k, x in errs.items()}, flush=True)
+    assert errs["o"] <= O_TOL and errs["lse"] <= LSE_TOL
+    assert errs["dq"] <= GRAD_TOL and errs["dk"] <= GRAD_TOL and errs["dv"] <= GRAD_TOL
