@@ -209,6 +209,49 @@ def ssm_leg(seqs, groups, dev, steps):
             "hbm_peak_gbps": PEAK_HBM_GBPS}
 
 
+def partition_leg():
+    """The host partition planner on the large random agentic tree (131072
+    tokens, depth <= 10) at a 32768-token capacity: partitions, levels, host
+    time, and the tokens one pass processes when every sequence is
+    flattened, when partitions re-read their ancestors (no differentiable
+    boundaries), and with boundaries (every token once; "Tree Training"
+    Fig. 5 compares the same three)."""
+    import numpy as np
+
+    import tree_packed_attention_amd as ta
+    import workloads
+
+    seqs, groups = workloads.sequences("agentic_l")
+    p = ta.tree_pack(seqs, groups)
+    cap = 32768
+    t0 = time.perf_counter()
+    plan = ta.tree_partition(p["node_start"], p["node_end"], p["node_parent"], cap)
+    ms = (time.perf_counter() - t0) * 1e3
+    lens = (p["node_end"] - p["node_start"]).astype(np.int64)
+    npar = p["node_parent"]
+    part = plan["node_part"]
+    recompute = int(lens.sum())
+    for b in range(len(plan["part_tokens"])):
+        anc = set()
+        for v in np.nonzero((part == b) & ((npar < 0) | (part[np.maximum(npar, 0)] != b)))[0]:
+            u = npar[v]
+            while u >= 0:
+                anc.add(int(u))
+                u = npar[u]
+        recompute += int(sum(lens[u] for u in anc))
+    levels = []
+    for b in range(len(plan["part_parent"])):
+        lv, x = 0, b
+        while plan["part_parent"][x] >= 0:
+            x, lv = plan["part_parent"][x], lv + 1
+        levels.append(lv)
+    return {"workload": "random agentic tree, depth<=10, T=131072", "capacity": cap,
+            "partitions": int(len(plan["part_tokens"])), "levels": int(max(levels) + 1),
+            "max_partition_tokens": int(plan["part_tokens"].max()), "plan_ms_host": round(ms, 3),
+            "tokens_flattened": int(sum(len(s_) for s_ in seqs)), "tokens_standard_partitioning": recompute,
+            "tokens_with_boundaries": int(p["T"])}
+
+
 def measured_traffic(kernel):
     """Calibrated HBM bytes per dispatch of `kernel` from the committed
     rocprofv3 counter summaries, if they were taken on the current library
@@ -379,6 +422,10 @@ def main():
         print(f"[bench] gdn fwd {ssm['gdn_fwd_ms']:.3f} ms, conv fwd {ssm['conv_fwd_ms']:.3f} ms "
               f"({ssm['conv_fwd_gbps']:.0f} GB/s), conv bwd {ssm['conv_bwd_ms']:.3f} ms", flush=True)
 
+    part = partition_leg()
+    print(f"[bench] partition plan: {part['partitions']} partitions, {part['levels']} levels, "
+          f"{part['plan_ms_host']:.2f} ms host", flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline ...", flush=True)
@@ -396,7 +443,8 @@ def main():
                          "skip": round(empty / causal, 4)},
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
         "pack_ms_host": round(pack_ms, 2),
-        "roofline": roofline, "tree_logprob": lp, "gateway": gw, "tree_ssm": ssm, "cpu_baseline": cpu,
+        "roofline": roofline, "tree_logprob": lp, "gateway": gw, "tree_ssm": ssm, "partition": part,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
