@@ -44,6 +44,7 @@
 
 #include "profile.h"
 #include "ta_device.h"
+#include "ta_lds.h"
 #include "ta_error.h"
 #include "tree_attn.h"
 
@@ -74,57 +75,6 @@ constexpr float kNegInf = -__builtin_inff();
 // probabilities stay <= 256 and the O accumulator is rarely touched.
 constexpr float kRescaleLog2 = 8.0f;
 
-__device__ __forceinline__ int perm_row(int r) { return (r & ~31) | swap23(r & 31); }
-
-
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-// Element offset of (row, col) in a swizzled [64][DP] bf16 tile (col % 4 == 0).
-template <int DP>
-__device__ __forceinline__ int toff(int row, int col) {
-  constexpr int CH = DP / 8;
-  return row * DP + ((((col >> 3) ^ swz(row)) & (CH - 1)) << 3) + (col & 7);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_void;
-
-// Each lane copies 16 bytes from g to (wave-uniform) dst + 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, void* dst) {
-  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 16, 0, 0);
-}
-// Each lane copies 4 bytes from g to (wave-uniform) dst + 4 * lane.
-__device__ __forceinline__ void dma4(const void* g, void* dst) {
-  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 4, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Copies 64 head-major rows [row0 + rowmap(r)] of a [*][DP] bf16 array into a
-// swizzled LDS tile. Each wave issues DP/32 16-byte-per-lane instructions;
-// every lane's offset inside the 64-row block is fixed, so it is computed once.
-template <int DP, bool PERM, int NW = 4>
-struct TileDma {
-  static constexpr int CH = DP / 8;                // 16-byte chunks per row (= instructions per tile)
-  static constexpr int NI = (CH + NW - 1) / NW;    // instructions per wave (the last may be idle)
-  int off[NI];
-  __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int p = (w + NW * j) * 64 + lane;
-      const int r = min(p / CH, 63);
-      const int c = ((p % CH) ^ swz(r)) & (CH - 1);
-      off[j] = (PERM ? perm_row(r) : r) * DP + 8 * c;
-    }
-  }
-  // rows: the global address of row row0 of the source; w: wave index (uniform)
-  __device__ __forceinline__ void issue(const bf16* rows, bf16* tile, int w) const {
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if (w + NW * j < CH) dma16(rows + off[j], tile + (w + NW * j) * 512);
-  }
-};
-
-__device__ __forceinline__ bf16x8 lds128(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Per-lane element offsets into a swizzled [64][DP] tile, computed once:
 //   op[k]: 16-byte operand read of LDS row lc (+32 mb), columns 16k + 8lg

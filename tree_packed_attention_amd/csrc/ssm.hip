@@ -10,11 +10,13 @@
 //   delta  h_t = alpha_t (I - beta_t k_t k_t^T) h_{par(t)} + beta_t k_t v_t^T,
 //          o_t = h_t^T q_t,  alpha_t = exp(g_t)
 //
-// Conv: one thread per (token, 8 channels) walks the K-1 parents; the
-// backward forms g = dy * act'(a) once, gathers dx_j over the descendants of
-// j that lie at most K-1 levels below it (a walk of the preorder range
-// (j, se[j]) that jumps over every deeper subtree), and reduces dw / db over
-// token blocks in a fixed order.
+// Conv: a workgroup takes a tile of tokens; one thread per token first
+// lists its K-1 ancestors in LDS, then every thread (8 channels) loads the
+// ancestor rows independently. The backward forms g = dy * act'(a) once,
+// gathers dx_j over the descendants of j at most K-1 levels below it (listed
+// per token in LDS by a walk of the preorder range (j, se[j]) that jumps over
+// every deeper subtree), and reduces dw / db over token blocks in a fixed
+// order.
 //
 // Gated delta rule, per v-head, in chunks of <= 64 tokens inside tree nodes
 // (the host plan, tree_gdn_plan, gives chunk ranges, chunk parents and the
@@ -25,18 +27,22 @@
 //      (one thread per right-hand-side column, the column in registers)
 //   2. state (one launch per level; a workgroup walks one chain): starting
 //      from the parent's end state, per chunk h0 is stored, vn = u - w h0
-//      and h = exp(gc_last) h0 + k^T (exp(gc_last - gc) * vn), both bf16 MFMA
-//      with float32 accumulators that carry h from chunk to chunk
+//      and h = exp(gc_last) h0 + kd^T vn with kd = k exp(gc_last - gc), both
+//      bf16 MFMA with float32 accumulators that carry h from chunk to chunk;
+//      the next chunk's w, kd^T and u stream into LDS (direct HBM -> LDS
+//      copies, double buffered) while the current one is computed
 //   3. output (all chunks at once): o = (q exp(gc)) h0 + (q k^T * exp(gc_i -
 //      gc_j), j <= i) vn
 // The start state of a chunk's first child chunk is the chunk's end state, so
 // a chain that starts under chunk p loads the stored start state of p + 1.
 //
 // Workspace (chunk-local, rows past a chunk's length are zero):
-//   gc  [Hv][nc][64] f32        u  [Hv][nc][64][dv] f32
+//   gc  [Hv][nc][64] f32        (past the chunk length: the last value)
+//   u   [Hv][nc][64][dv] f32
 //   w   [Hv][nc][64][dk] bf16   (columns in swap23 order within each 16)
-//   kt  [H][nc][dk][64] bf16    vnt [Hv][nc][dv][64] bf16
-//   h0  [nc][Hv][dv][dk] f32    (start state of each chunk, transposed)
+//   kd  [Hv][nc][dk][64] bf16   (k^T exp(gc_last - gc), zero past the length)
+//   vnt [Hv][nc][dv][64] bf16
+//   h0  [nc][Hv][dv][dk] bf16   (start state of each chunk, transposed)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,6 +50,7 @@
 #include "profile.h"
 #include "ta_device.h"
 #include "ta_error.h"
+#include "ta_lds.h"
 #include "tree_attn.h"
 
 namespace ta {
@@ -91,22 +98,49 @@ __device__ __forceinline__ float sigmoidf(float a) { return 1.0f / (1.0f + expf(
 
 constexpr int kConvThreads = 256;
 constexpr int kConvMaxK = 8;
-constexpr int kConvTokBlock = 128;  // tokens per dw / db partial
+constexpr int kConvTB = 16;          // tokens per forward / dx workgroup
+constexpr int kConvTokBlock = 128;   // tokens per dw / db partial (g pass)
+constexpr int kConvMaxDesc = 48;     // listed descendants per token in the dx pass
 
-// pre-activation of token t for channels c0..c0+7
+// Ancestor table of tokens [t0, t0 + n): anc[i][m] = m-th ancestor of
+// t0 + i (m < K), -1 past a root or for tokens past T. One thread per token
+// walks its parents, so the row loads that follow are independent.
+__device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int t0, int n, int T, int K,
+                                               int (*anc)[kConvMaxK]) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    int s = t0 + i < T ? t0 + i : -1;
+#pragma unroll
+    for (int m = 0; m < kConvMaxK; ++m) {
+      if (m < K) {
+        anc[i][m] = s;
+        if (s >= 0) s = par[s];
+      }
+    }
+  }
+}
+
+// weights of channels c0..c0+7 in tap order m (tap m multiplies the m-th ancestor)
+__device__ __forceinline__ void conv_weights(const float* __restrict__ w, int c0, int K, float (*wr)[8]) {
+#pragma unroll
+  for (int m = 0; m < kConvMaxK; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wr[m][e] = m < K ? w[(size_t)(c0 + e) * K + (K - 1 - m)] : 0.0f;
+}
+
 template <typename Tio>
-__device__ __forceinline__ void conv_pre(const Tio* __restrict__ x, const float* __restrict__ w,
-                                         const float* __restrict__ bias, const int* __restrict__ par, int t, int C,
-                                         int K, int c0, float* a) {
+__device__ __forceinline__ void conv_pre(const Tio* __restrict__ x, const float (*wr)[8], const float* br,
+                                         const int* anc, int K, int C, int c0, float* a) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = bias ? bias[c0 + e] : 0.0f;
-  int s = t;
-  for (int n = 0; n < K && s >= 0; ++n) {
-    float xv[8];
-    ld8f(x + (size_t)s * C + c0, xv);
+  for (int e = 0; e < 8; ++e) a[e] = br[e];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = fmaf(w[(size_t)(c0 + e) * K + (K - 1 - n)], xv[e], a[e]);
-    s = par[s];
+  for (int m = 0; m < kConvMaxK; ++m) {
+    const int s = m < K ? anc[m] : -1;
+    if (s >= 0) {
+      float xv[8];
+      ld8f(x + (size_t)s * C + c0, xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xv[e], a[e]);
+    }
   }
 }
 
@@ -115,39 +149,57 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __res
                                                                 const float* __restrict__ bias,
                                                                 const int* __restrict__ par, int T, int C, int K,
                                                                 int act, Tio* __restrict__ y) {
-  const int t = blockIdx.x;
+  __shared__ int anc[kConvTB][kConvMaxK];
+  const int t0 = blockIdx.x * kConvTB;
+  conv_ancestors(par, t0, kConvTB, T, K, anc);
+  __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
-  float a[8];
-  conv_pre(x, w, bias, par, t, C, K, c0, a);
-  if (act) {
+  float wr[kConvMaxK][8], br[8];
+  conv_weights(w, c0, K, wr);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+  for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+  const int n = min(kConvTB, T - t0);
+  for (int i = 0; i < n; ++i) {
+    float a[8];
+    conv_pre(x, wr, br, anc[i], K, C, c0, a);
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+    }
+    st8f(y + (size_t)(t0 + i) * C + c0, a);
   }
-  st8f(y + (size_t)t * C + c0, a);
 }
 
 // g = dy * act'(a) for a block of kConvTokBlock tokens, plus that block's
-// partial sums of dw[c][K-1-n] = sum g_t x_{anc_n(t)} and db = sum g_t.
+// partial sums of dw (per tap) and db.
 template <typename Tio>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     const Tio* __restrict__ x, const Tio* __restrict__ dy, const float* __restrict__ w,
     const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, float* __restrict__ gbuf,
     float* __restrict__ part) {
+  __shared__ int anc[kConvTokBlock][kConvMaxK];
+  const int tb = blockIdx.x * kConvTokBlock;
+  conv_ancestors(par, tb, kConvTokBlock, T, K, anc);
+  __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
+  float wr[kConvMaxK][8], br[8];
+  conv_weights(w, c0, K, wr);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
   float dw[kConvMaxK][8], db[8];
 #pragma unroll
-  for (int n = 0; n < kConvMaxK; ++n)
+  for (int m = 0; m < kConvMaxK; ++m)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dw[n][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) dw[m][e] = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) db[e] = 0.0f;
-  const int tb = blockIdx.x * kConvTokBlock;
-  const int te = min(tb + kConvTokBlock, T);
-  for (int t = tb; t < te; ++t) {
+  const int n = min(kConvTokBlock, T - tb);
+  for (int i = 0; i < n; ++i) {
+    const int t = tb + i;
     float a[8], g[8];
-    conv_pre(x, w, bias, par, t, C, K, c0, a);
+    conv_pre(x, wr, br, anc[i], K, C, c0, a);
     ld8f(dy + (size_t)t * C + c0, g);
     if (act) {
 #pragma unroll
@@ -159,59 +211,107 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     st8f(gbuf + (size_t)t * C + c0, g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) db[e] += g[e];
-    int s = t;
 #pragma unroll
-    for (int n = 0; n < kConvMaxK; ++n) {
-      if (n < K && s >= 0) {
+    for (int m = 0; m < kConvMaxK; ++m) {
+      const int s = m < K ? anc[i][m] : -1;
+      if (s >= 0) {
         float xv[8];
         ld8f(x + (size_t)s * C + c0, xv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dw[n][e] = fmaf(g[e], xv[e], dw[n][e]);
-        s = par[s];
+        for (int e = 0; e < 8; ++e) dw[m][e] = fmaf(g[e], xv[e], dw[m][e]);
       }
     }
   }
-  // partials [block][c][K + 1]: taps in weight order (index K-1-n), then db
+  // partials [block][c][K + 1]: taps in weight order (index K-1-m), then db
   float* pp = part + ((size_t)blockIdx.x * C + c0) * (K + 1);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
 #pragma unroll
-    for (int n = 0; n < kConvMaxK; ++n)
-      if (n < K) pp[(size_t)e * (K + 1) + (K - 1 - n)] = dw[n][e];
+    for (int m = 0; m < kConvMaxK; ++m)
+      if (m < K) pp[(size_t)e * (K + 1) + (K - 1 - m)] = dw[m][e];
     pp[(size_t)e * (K + 1) + K] = db[e];
   }
 }
 
-// dx_j = sum_{t: anc_n(t) = j, n < K} w[:, K-1-n] g_t. The descendants of j
+// dx_j = sum_{t: anc_m(t) = j, m < K} w[:, K-1-m] g_t. The descendants of j
 // are the preorder range (j, se[j]); depth below j is pos[t] - pos[j]; a
-// token K or more levels down is skipped together with its subtree.
+// token K or more levels down is skipped together with its subtree. One
+// thread per token lists (token, depth) pairs in LDS; a token with more than
+// kConvMaxDesc of them is walked again by the channel threads.
 template <typename Tio>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* __restrict__ gbuf,
                                                                    const float* __restrict__ w,
                                                                    const int* __restrict__ pos,
                                                                    const int* __restrict__ se, int T, int C, int K,
                                                                    Tio* __restrict__ dx) {
-  const int j = blockIdx.x;
+  __shared__ int dlist[kConvTB][kConvMaxDesc];
+  __shared__ int dcount[kConvTB];
+  const int t0 = blockIdx.x * kConvTB;
+  for (int i = threadIdx.x; i < kConvTB; i += blockDim.x) {
+    const int j = t0 + i;
+    int cnt = 0;
+    if (j < T) {
+      const int pj = pos[j], end = se[j];
+      int t = j + 1;
+      while (t < end) {
+        const int dd = pos[t] - pj;
+        if (dd < K) {
+          if (cnt < kConvMaxDesc) dlist[i][cnt] = (t << 3) | dd;
+          ++cnt;
+          ++t;
+        } else {
+          t = se[t];
+        }
+      }
+    }
+    dcount[i] = cnt;
+  }
+  __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
-  float acc[8], g[8];
-  ld8f(gbuf + (size_t)j * C + c0, g);
+  float wr[kConvMaxK][8];
+  conv_weights(w, c0, K, wr);
+  const int n = min(kConvTB, T - t0);
+  for (int i = 0; i < n; ++i) {
+    const int j = t0 + i;
+    float acc[8], g[8];
+    ld8f(gbuf + (size_t)j * C + c0, g);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = w[(size_t)(c0 + e) * K + (K - 1)] * g[e];
-  const int pj = pos[j], end = se[j];
-  int t = j + 1;
-  while (t < end) {
-    const int dd = pos[t] - pj;
-    if (dd < K) {
-      ld8f(gbuf + (size_t)t * C + c0, g);
+    for (int e = 0; e < 8; ++e) acc[e] = wr[0][e] * g[e];
+    const int cnt = dcount[i];
+    if (cnt <= kConvMaxDesc) {
+      for (int q = 0; q < cnt; ++q) {
+        const int code = dlist[i][q];
+        const int t = code >> 3, dd = code & 7;
+        ld8f(gbuf + (size_t)t * C + c0, g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[(size_t)(c0 + e) * K + (K - 1 - dd)], g[e], acc[e]);
-      ++t;
+        for (int m = 1; m < kConvMaxK; ++m)
+          if (m == dd) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
+          }
+      }
     } else {
-      t = se[t];
+      const int pj = pos[j], end = se[j];
+      int t = j + 1;
+      while (t < end) {
+        const int dd = pos[t] - pj;
+        if (dd < K) {
+          ld8f(gbuf + (size_t)t * C + c0, g);
+#pragma unroll
+          for (int m = 1; m < kConvMaxK; ++m)
+            if (m == dd) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
+            }
+          ++t;
+        } else {
+          t = se[t];
+        }
+      }
     }
+    st8f(dx + (size_t)j * C + c0, acc);
   }
-  st8f(dx + (size_t)j * C + c0, acc);
 }
 
 // Fixed-order sum of the per-block partials.
@@ -254,11 +354,11 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
   L.w = o;
   o = al256(o + (size_t)Hv * nc * kCh * dk * 2);
   L.kt = o;
-  o = al256(o + (size_t)H * nc * dk * kCh * 2);
+  o = al256(o + (size_t)Hv * nc * dk * kCh * 2);
   L.vnt = o;
   o = al256(o + (size_t)Hv * nc * dv * kCh * 2);
   L.h0 = o;
-  o = al256(o + (size_t)nc * Hv * dv * dk * 4);
+  o = al256(o + (size_t)nc * Hv * dv * dk * 2);
   L.total = o;
   return L;
 }
@@ -273,6 +373,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
                                                        bf16* __restrict__ kt) {
   __shared__ float gcs[kCh];
   __shared__ float bs[kCh];
+  __shared__ float dec[kCh];
   __shared__ __attribute__((aligned(16))) float Ms[kCh][kCh + 4];
   __shared__ __attribute__((aligned(16))) bf16 ks[kCh][DK + 8];
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -289,6 +390,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
     gcs[lane] = gv;
     bs[lane] = lane < L ? beta[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
     gcw[((size_t)hv * nc + c) * kCh + lane] = gv;
+    const float glast = __shfl(gv, 63);  // g is zero past L, so lane 63 holds gc of the last row
+    dec[lane] = lane < L ? expf(glast - gv) : 0.0f;
   }
   for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
     const int r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
@@ -310,12 +413,12 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
       Ms[m][n] = n < m ? bs[m] * acc[i] * expf(gcs[m] - gcs[n]) : 0.0f;
     }
   }
-  // k^T, chunk-local, for the state pass (once per k-head)
-  if (hv % (Hv / H) == 0) {
-    bf16* kto = kt + ((size_t)hk * nc + c) * DK * kCh;
+  // kd^T = (k exp(gc_last - gc))^T, chunk-local, for the state pass
+  {
+    bf16* kto = kt + ((size_t)hv * nc + c) * DK * kCh;
     for (int idx = tid; idx < DK * kCh; idx += 256) {
       const int kk = idx / kCh, r = idx % kCh;
-      kto[idx] = ks[r][kk];
+      kto[idx] = (bf16)((float)ks[r][kk] * dec[r]);
     }
   }
   __syncthreads();
@@ -361,104 +464,157 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
 // Stage 2: one workgroup per (chain of this level, v-head); wave s owns state
 // columns [32 s, 32 s + 32) of dv. The state h (dk x 32 per wave) lives in
 // MFMA C registers: block b, register i <-> row 32b + 8(i/4) + 4(lane/32) + i%4.
+// Per chunk the workgroup reads w (swizzled [64][dk]), kd^T (dk/64 swizzled
+// [64][64] tiles) and u ([64][dv]) from LDS; the next chunk's copies are in
+// flight meanwhile.
+template <int DK, int DV>
+struct StateBuf {
+  bf16* w;
+  bf16* k;
+  float* u;
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void gdn_state_chunk(const StateBuf<DK, DV>& sb, float gl, int lg, int lc, int n,
+                                                f32x16 (&h)[DK / 32], bf16* __restrict__ vo, bf16* __restrict__ ho) {
+  constexpr int NB = DK / 32;
+  // store the start state (bf16, transposed: [dv][dk])
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (bf16)h[b][4 * j + e];
+      *reinterpret_cast<bf16x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
+    }
+  // vn = u - w h0: B operand of k-step a = -h0 registers 8(a%2)..+7 of block a/2
+  // (w's columns are stored in the matching swap23 order)
+  bf16x8 hb[DK / 16];
+#pragma unroll
+  for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) hb[a][s] = (bf16)(-h[a >> 1][8 * (a & 1) + s]);
+  f32x16 vn[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vn[mb][i] = sb.u[(32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3)) * DV + n];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+      vn[mb] = mfma32x32x16(lds128(sb.w + toff<DK>(32 * mb + lc, 16 * a + 8 * lg)), hb[a], vn[mb]);
+  }
+  // vn, transposed [dv][64], for the output stage
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
+      *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+    }
+  // h = exp(gc_last) h0 + kd^T vn. Contraction over the chunk rows in the
+  // order whose k-step a, slot s is row 16a + 8(s/4) + 4(lane/32) + s%4 =
+  // vn register 8(a%2)+s of block a/2; kd^T is read in the same row order.
+  const float al = expf(gl);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) h[b] *= al;
+  bf16x8 vb[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) vb[a][s] = (bf16)vn[a >> 1][8 * (a & 1) + s];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bf16* kt = sb.k + (b >> 1) * 64 * kCh;
+    const int rr = 32 * (b & 1) + lc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(kt + toff<kCh>(rr, 16 * a + 4 * lg)),
+                           *reinterpret_cast<const bf16x4*>(kt + toff<kCh>(rr, 16 * a + 8 + 4 * lg)));
+      h[b] = mfma32x32x16(A, vb[a], h[b]);
+    }
+  }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 32)) void gdn_state_kernel(
     const int* __restrict__ level_chains, int lvl0, const int* __restrict__ chain_begin,
-    const int* __restrict__ cpar, const int* __restrict__ clen, int nc, int H, int Hv, const float* __restrict__ gcw,
-    const float* __restrict__ u, const bf16* __restrict__ wp, const bf16* __restrict__ kt, bf16* __restrict__ vnt,
-    float* __restrict__ h0w) {
+    const int* __restrict__ cpar, int nc, int Hv, const float* __restrict__ gcw, const float* __restrict__ u,
+    const bf16* __restrict__ wp, const bf16* __restrict__ kd, bf16* __restrict__ vnt, bf16* __restrict__ h0w) {
+  constexpr int NW = DV / 32;
   constexpr int NB = DK / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 w0[kCh * DK];
+  __shared__ __attribute__((aligned(1024))) bf16 w1[kCh * DK];
+  __shared__ __attribute__((aligned(1024))) bf16 k0[DK * kCh];
+  __shared__ __attribute__((aligned(1024))) bf16 k1[DK * kCh];
+  __shared__ __attribute__((aligned(1024))) float u0[kCh * DV];
+  __shared__ __attribute__((aligned(1024))) float u1[kCh * DV];
   const int ch = level_chains[lvl0 + blockIdx.x];
   const int hv = blockIdx.y;
-  const int hk = hv / (Hv / H);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 5, lc = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lg = lane >> 5, lc = lane & 31;
   const int n = 32 * wv + lc;  // state column (dv index) of this lane
   const int cb = chain_begin[ch], ce = chain_begin[ch + 1];
   const int p = cpar[cb];
+  TileDma<DK, false, NW> wdma;
+  TileDma<kCh, false, NW> kdma;
+  wdma.init(wv, lane);
+  kdma.init(wv, lane);
+  auto issue = [&](int c, bf16* wb, bf16* kb, float* ub) {
+    const size_t hc = (size_t)hv * nc + c;
+    wdma.issue(wp + hc * kCh * DK, wb, wv);
+#pragma unroll
+    for (int t = 0; t < DK / 64; ++t) kdma.issue(kd + (hc * DK + 64 * t) * kCh, kb + t * 64 * kCh, wv);
+    const float* us = u + hc * kCh * DV;
+#pragma unroll
+    for (int j = wv; j < kCh * DV / 256; j += NW) dma16(us + 256 * j + 4 * lane, ub + 256 * j);
+  };
   f32x16 h[NB];
   if (p < 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) h[b] = f32x16{};
   } else {
     // the start state of p's first child chunk p + 1 is p's end state
-    const float* hp = h0w + (((size_t)(p + 1) * Hv + hv) * DV + n) * DK;
+    const bf16* hp = h0w + (((size_t)(p + 1) * Hv + hv) * DV + n) * DK;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(hp + 32 * b + 8 * j + 4 * lg);
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hp + 32 * b + 8 * j + 4 * lg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[b][4 * j + e] = x[e];
+        for (int e = 0; e < 4; ++e) h[b][4 * j + e] = (float)x[e];
       }
   }
-  for (int c = cb; c < ce; ++c) {
-    const int L = clen[c];
-    const size_t hc = (size_t)hv * nc + c;
-    // store the start state (transposed: [dv][dk])
-    float* ho = h0w + (((size_t)c * Hv + hv) * DV + n) * DK;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = h[b][4 * j + e];
-        *reinterpret_cast<f32x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
-      }
-    // vn = u - w h0: B operand of k-step a = -h0 registers 8(a%2)..+7 of block a/2
-    // (w's columns are stored in the matching swap23 order)
-    bf16x8 hb[DK / 16];
-#pragma unroll
-    for (int a = 0; a < DK / 16; ++a)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) hb[a][s] = (bf16)(-h[a >> 1][8 * (a & 1) + s]);
-    f32x16 vn[2];
-    const float* uc = u + hc * kCh * DV;
-    const bf16* wc = wp + hc * kCh * DK;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) vn[mb][i] = uc[(size_t)(32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3)) * DV + n];
-#pragma unroll
-      for (int a = 0; a < DK / 16; ++a)
-        vn[mb] = mfma32x32x16(load8(wc + (size_t)(32 * mb + lc) * DK + 16 * a + 8 * lg), hb[a], vn[mb]);
+  const StateBuf<DK, DV> sb0{w0, k0, u0}, sb1{w1, k1, u1};
+  auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
+  auto out_ptrs = [&](int c, bf16** vo, bf16** ho) {
+    *vo = vnt + (((size_t)hv * nc + c) * DV + n) * kCh;
+    *ho = h0w + (((size_t)c * Hv + hv) * DV + n) * DK;
+  };
+  issue(cb, w0, k0, u0);
+  float gl0 = gl_of(cb), gl1 = 0.0f;
+  for (int c = cb; c < ce; c += 2) {
+    bf16 *vo, *ho;
+    wait_dma();
+    __syncthreads();
+    if (c + 1 < ce) {
+      issue(c + 1, w1, k1, u1);
+      gl1 = gl_of(c + 1);
     }
-    // vn, transposed [dv][64], for the output stage
-    bf16* vo = vnt + (hc * DV + n) * kCh;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
-        *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+    out_ptrs(c, &vo, &ho);
+    gdn_state_chunk<DK, DV>(sb0, gl0, lg, lc, n, h, vo, ho);
+    if (c + 1 < ce) {
+      wait_dma();
+      __syncthreads();
+      if (c + 2 < ce) {
+        issue(c + 2, w0, k0, u0);
+        gl0 = gl_of(c + 2);
       }
-    // h = exp(gc_last) h0 + k^T (exp(gc_last - gc) vn). Contraction over the
-    // chunk rows in the order whose k-step a, slot s is row
-    // 16a + 8(s/4) + 4(lane/32) + s%4 = vn register 8(a%2)+s of block a/2.
-    const float* gcc = gcw + hc * kCh;
-    const float gl = gcc[L - 1];
-    const float al = expf(gl);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) h[b] *= al;
-    bf16x8 vb[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int r = 16 * a + 8 * (s >> 2) + 4 * lg + (s & 3);
-        vb[a][s] = (bf16)(r < L ? vn[a >> 1][8 * (a & 1) + s] * expf(gl - gcc[r]) : 0.0f);
-      }
-    const bf16* kc = kt + ((size_t)hk * nc + c) * DK * kCh;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const bf16* kp = kc + (size_t)(32 * b + lc) * kCh + 16 * a + 4 * lg;
-        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(kp), *reinterpret_cast<const bf16x4*>(kp + 8));
-        h[b] = mfma32x32x16(A, vb[a], h[b]);
-      }
+      out_ptrs(c + 1, &vo, &ho);
+      gdn_state_chunk<DK, DV>(sb1, gl1, lg, lc, n, h, vo, ho);
+    }
   }
 }
 
@@ -470,7 +626,7 @@ template <int DK, int DV, typename Tio>
 __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
                                                       const int* __restrict__ cstart, const int* __restrict__ clen,
                                                       int nc, int H, int Hv, const float* __restrict__ gcw,
-                                                      const bf16* __restrict__ vnt, const float* __restrict__ h0w,
+                                                      const bf16* __restrict__ vnt, const bf16* __restrict__ h0w,
                                                       Tio* __restrict__ o) {
   constexpr int NDW = DV / 64;  // 32-wide dv blocks per wave
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -501,17 +657,10 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
 #pragma unroll
     for (int bb = 0; bb < NDW; ++bb) {
       const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
-      const float* hp = h0w + (((size_t)c * Hv + hv) * DV + d) * DK;
+      const bf16* hp = h0w + (((size_t)c * Hv + hv) * DV + d) * DK;
 #pragma unroll
       for (int a = 0; a < DK / 16; ++a) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(hp + 16 * a + 8 * lg);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(hp + 16 * a + 8 * lg + 4);
-        bf16x8 A;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          A[e] = (bf16)x0[e];
-          A[4 + e] = (bf16)x1[e];
-        }
+        const bf16x8 A = load8(hp + 16 * a + 8 * lg);
         acc[bb] = mfma32x32x16(A, qs[a], acc[bb]);
       }
     }
@@ -586,7 +735,7 @@ void gdn_launch(const void* q, const void* k, const void* v, const float* g, con
   bf16* wp = reinterpret_cast<bf16*>(ws + L.w);
   bf16* kt = reinterpret_cast<bf16*>(ws + L.kt);
   bf16* vnt = reinterpret_cast<bf16*>(ws + L.vnt);
-  float* h0w = reinterpret_cast<float*>(ws + L.h0);
+  bf16* h0w = reinterpret_cast<bf16*>(ws + L.h0);
   const int* cstart = plan + pv.off_cstart;
   const int* clen = plan + pv.off_clen;
   {
@@ -600,8 +749,8 @@ void gdn_launch(const void* q, const void* k, const void* v, const float* g, con
     for (int l = 0; l < pv.nl; ++l) {
       const int n = loff[l + 1] - loff[l];
       hipLaunchKernelGGL((gdn_state_kernel<DK, DV>), dim3(n, Hv), dim3(64 * (DV / 32)), 0, st,
-                         plan + pv.off_lchains, loff[l], plan + pv.off_chain, plan + pv.off_cpar, clen, pv.nc, H, Hv,
-                         gcw, u, wp, kt, vnt, h0w);
+                         plan + pv.off_lchains, loff[l], plan + pv.off_chain, plan + pv.off_cpar, pv.nc, Hv, gcw, u,
+                         wp, kt, vnt, h0w);
     }
   }
   {
@@ -646,7 +795,7 @@ extern "C" int tree_conv_fwd(const void* x, ta_dtype dt, int32_t T, int32_t C, i
   if (activation != 0 && activation != 1) return fail(TA_EINVAL, "tree_conv_fwd: activation must be 0 or 1");
   if (!al16(x) || !al16(y)) return fail(TA_EINVAL, "tree_conv_fwd: x and y must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(T, (C / 8 + kConvThreads - 1) / kConvThreads);
+  const dim3 grid((T + kConvTB - 1) / kConvTB, (C / 8 + kConvThreads - 1) / kConvThreads);
   {
     ProfScope ps("conv_fwd", st);
     if (dt == TA_BF16)
@@ -678,8 +827,9 @@ extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t
   clear_error();
   if (!x || !dy || !weight || !parent || !pos || !subtree_end || !dx || !dweight || !workspace)
     return fail(TA_EINVAL, "tree_conv_bwd: NULL pointer argument");
-  if (T < 1 || C < 8 || C % 8 != 0 || K < 1 || K > kConvMaxK)
-    return fail(TA_EINVAL, "tree_conv_bwd: need T >= 1, C a positive multiple of 8, 1 <= K <= %d (T=%d C=%d K=%d)",
+  if (T < 1 || T >= (1 << 28) || C < 8 || C % 8 != 0 || K < 1 || K > kConvMaxK)
+    return fail(TA_EINVAL,
+                "tree_conv_bwd: need 1 <= T < 2^28, C a positive multiple of 8, 1 <= K <= %d (T=%d C=%d K=%d)",
                 kConvMaxK, T, C, K);
   if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_conv_bwd: bad dtype %d", (int)dt);
   if (activation != 0 && activation != 1) return fail(TA_EINVAL, "tree_conv_bwd: activation must be 0 or 1");
@@ -699,13 +849,13 @@ extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t
       hipLaunchKernelGGL(conv_bwd_g_kernel<bf16>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
                          static_cast<const bf16*>(x), static_cast<const bf16*>(dy), weight, bias, parent, T, C, K,
                          activation, gbuf, part);
-      hipLaunchKernelGGL(conv_bwd_dx_kernel<bf16>, dim3(T, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
+      hipLaunchKernelGGL(conv_bwd_dx_kernel<bf16>, dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
                          subtree_end, T, C, K, static_cast<bf16*>(dx));
     } else {
       hipLaunchKernelGGL(conv_bwd_g_kernel<float>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
                          static_cast<const float*>(x), static_cast<const float*>(dy), weight, bias, parent, T, C, K,
                          activation, gbuf, part);
-      hipLaunchKernelGGL(conv_bwd_dx_kernel<float>, dim3(T, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
+      hipLaunchKernelGGL(conv_bwd_dx_kernel<float>, dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
                          subtree_end, T, C, K, static_cast<float*>(dx));
     }
     hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, st, part, nblk, C, K, dweight,
