@@ -23,8 +23,8 @@
 // chain / level schedule):
 //   1. prep (all chunks at once): gc = in-chunk cumulative log decay,
 //      M = strictly-lower (beta k) k^T * exp(gc_i - gc_j) (bf16 MFMA),
-//      [u | w] = (I + M)^-1 [beta v | beta k exp(gc)] by forward substitution
-//      (one thread per right-hand-side column, the column in registers)
+//      T = (I + M)^-1 in float32 by 16 x 16 blocks, [u | w] = T [beta v |
+//      beta k exp(gc)] (bf16 MFMA)
 //   2. state (one launch per level; a workgroup walks one chain): starting
 //      from the parent's end state, per chunk h0 is stored, vn = u - w h0
 //      and h = exp(gc_last) h0 + kd^T vn with kd = k exp(gc_last - gc), both
@@ -88,9 +88,6 @@ __device__ __forceinline__ void st8f(float* p, const float* f) {
   *reinterpret_cast<f32x4*>(p) = a;
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
-// one element, rounded to bf16 as the matrix products see it
-__device__ __forceinline__ float rd_bf(const bf16* p) { return (float)*p; }
-__device__ __forceinline__ float rd_bf(const float* p) { return (float)(bf16)*p; }
 
 __device__ __forceinline__ float sigmoidf(float a) { return 1.0f / (1.0f + expf(-a)); }
 
@@ -364,6 +361,18 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
 }
 
 // Stage 1: per (chunk, v-head). 256 threads.
+//   gc, beta, the decay to the chunk end; M = strictly-lower (beta k) k^T *
+//   exp(gc_i - gc_j) (bf16 MFMA); T = (I + M)^-1 in float32 by 16 x 16
+//   blocks; then [u | w] = T [beta v | beta k e^gc] as a bf16 MFMA product
+//   with the right-hand side transposed in LDS.
+template <int DK, int DV>
+struct PrepLds {
+  static constexpr int NCOL = DK + DV;      // right-hand-side columns
+  static constexpr int KS_B = kCh * (DK + 8) * 2;
+  static constexpr int TS_B = kCh * (kCh + 4) * 4;
+  static constexpr int KT_B = KS_B > TS_B ? KS_B : TS_B;  // k rows, then T (same storage)
+};
+
 template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k, const Tin* __restrict__ v,
                                                        const float* __restrict__ g, const float* __restrict__ beta,
@@ -371,11 +380,18 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
                                                        int nc, int H, int Hv, float* __restrict__ gcw,
                                                        float* __restrict__ u, bf16* __restrict__ wp,
                                                        bf16* __restrict__ kt) {
+  typedef PrepLds<DK, DV> PL;
+  constexpr int NCOL = PL::NCOL;
   __shared__ float gcs[kCh];
   __shared__ float bs[kCh];
   __shared__ float dec[kCh];
+  __shared__ float egs[kCh];
   __shared__ __attribute__((aligned(16))) float Ms[kCh][kCh + 4];
-  __shared__ __attribute__((aligned(16))) bf16 ks[kCh][DK + 8];
+  __shared__ __attribute__((aligned(16))) char kt_raw[PL::KT_B];
+  __shared__ __attribute__((aligned(16))) bf16 rt[NCOL][kCh + 8];  // right-hand side, transposed
+  __shared__ float pscr[3][16][17];                                 // partial sums of the block inverse
+  bf16 (*ks)[DK + 8] = reinterpret_cast<bf16 (*)[DK + 8]>(kt_raw);
+  float (*ts)[kCh + 4] = reinterpret_cast<float (*)[kCh + 4]>(kt_raw);
   const int c = blockIdx.x, hv = blockIdx.y;
   const int hk = hv / (Hv / H);
   const int t0 = cstart[c], L = clen[c];
@@ -392,6 +408,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
     gcw[((size_t)hv * nc + c) * kCh + lane] = gv;
     const float glast = __shfl(gv, 63);  // g is zero past L, so lane 63 holds gc of the last row
     dec[lane] = lane < L ? expf(glast - gv) : 0.0f;
+    egs[lane] = lane < L ? expf(gv) : 0.0f;
   }
   for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
     const int r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
@@ -421,42 +438,95 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
       kto[idx] = (bf16)((float)ks[r][kk] * dec[r]);
     }
   }
+  // right-hand side, transposed: rt[col][row] = beta v (col < DV), beta k e^gc.
+  // Rows are read 8 columns at a time (16-byte loads along the row).
+  for (int idx = tid; idx < kCh * (NCOL / 8); idx += 256) {
+    const int r = idx / (NCOL / 8), cg = 8 * (idx % (NCOL / 8));
+    bf16x8 x8;
+    float sc;
+    if (cg < DV) {
+      x8 = r < L ? load8(v + ((size_t)(t0 + r) * Hv + hv) * DV + cg) : zero8();
+      sc = bs[r];
+    } else {
+      x8 = *reinterpret_cast<const bf16x8*>(&ks[r][cg - DV]);
+      sc = bs[r] * egs[r];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rt[cg + e][r] = (bf16)((float)x8[e] * sc);
+  }
   __syncthreads();
-  // forward substitution, one right-hand-side column per thread: x starts as
-  // the right-hand side and row r becomes x_r = rhs_r - sum_{j<r} M[r][j] x_j.
-  // The compiler barrier per row keeps only that row's LDS reads in flight
-  // (hoisting all of them would need ~2000 registers).
-  const int col = tid;
-  if (col < DV + DK) {
-    float x[kCh];
-    if (col < DV) {
+  // T = (I + M)^-1 by 16 x 16 blocks (T is unit lower triangular):
+  //   T_ii = (I + M_ii)^-1 by forward substitution, one lane per column;
+  //   T_ij = -T_ii sum_{j <= q < i} M_iq T_qj, one block diagonal at a time.
+  for (int idx = tid; idx < kCh * (kCh + 4); idx += 256) (&ts[0][0])[idx] = 0.0f;
+  __syncthreads();
+  if (wv == 0) {
+    const int bd = 16 * (lane >> 4), j = lane & 15;
+    float x[16];
 #pragma unroll
-      for (int r = 0; r < kCh; ++r) x[r] = r < L ? bs[r] * rd_bf(v + ((size_t)(t0 + r) * Hv + hv) * DV + col) : 0.0f;
-    } else {
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == j ? 1.0f : 0.0f;
 #pragma unroll
-      for (int r = 0; r < kCh; ++r) x[r] = bs[r] * (float)ks[r][col - DV] * expf(gcs[r]);
-    }
-#pragma unroll
-    for (int r = 1; r < kCh; ++r) {
-      asm volatile("" ::: "memory");
-      float acc = x[r];
-#pragma unroll
-      for (int j = 0; j < r; j += 4) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(&Ms[r][j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j + e < r) acc = fmaf(-m4[e], x[j + e], acc);
-      }
+      for (int q = 0; q < r; ++q) acc = fmaf(-Ms[bd + r][bd + q], x[q], acc);
       x[r] = acc;
+      ts[bd + r][bd + j] = acc;
     }
-    if (col < DV) {
-      float* uo = u + ((size_t)hv * nc + c) * kCh * DV + col;
+  }
+  __syncthreads();
+  const int er = tid >> 4, ec = tid & 15;  // element (row, column) of a 16 x 16 block
 #pragma unroll
-      for (int r = 0; r < kCh; ++r) uo[(size_t)r * DV] = x[r];
-    } else {
-      bf16* wo = wp + ((size_t)hv * nc + c) * kCh * DK + swap23(col - DV);
+  for (int d = 1; d < 4; ++d) {
+    float part[3];
 #pragma unroll
-      for (int r = 0; r < kCh; ++r) wo[(size_t)r * DK] = (bf16)x[r];
+    for (int bi = 0; bi < 4 - d; ++bi) {
+      const int bi_ = bi + d, bj = bi;
+      float acc = 0.0f;
+      for (int q = 16 * bj; q < 16 * bi_; ++q) acc = fmaf(Ms[16 * bi_ + er][q], ts[q][16 * bj + ec], acc);
+      part[bi] = acc;
+    }
+    // every thread holds its element of each partial sum; exchange them through LDS
+#pragma unroll
+    for (int bi = 0; bi < 4 - d; ++bi) pscr[bi][er][ec] = part[bi];
+    __syncthreads();
+#pragma unroll
+    for (int bi = 0; bi < 4 - d; ++bi) {
+      const int bi_ = bi + d, bj = bi;
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc = fmaf(ts[16 * bi_ + er][16 * bi_ + q], pscr[bi][q][ec], acc);
+      ts[16 * bi_ + er][16 * bj + ec] = -acc;
+    }
+    __syncthreads();
+  }
+  // [u | w] = T rt^T: 32x32 output blocks (2 row blocks x NCOL/32 column
+  // blocks), column blocks dealt to the waves in turn
+  constexpr int NCB = NCOL / 32;
+  for (int cb = wv; cb < NCB; cb += 4) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int a = 0; a < kCh / 16; ++a) {
+        const f32x4 t0v = *reinterpret_cast<const f32x4*>(&ts[32 * mb + lc][16 * a + 8 * lg]);
+        const f32x4 t1v = *reinterpret_cast<const f32x4*>(&ts[32 * mb + lc][16 * a + 8 * lg + 4]);
+        bf16x8 A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          A[e] = (bf16)t0v[e];
+          A[4 + e] = (bf16)t1v[e];
+        }
+        acc = mfma32x32x16(A, *reinterpret_cast<const bf16x8*>(&rt[32 * cb + lc][16 * a + 8 * lg]), acc);
+      }
+      const int col = 32 * cb + lc;
+      if (col < DV) {
+        float* uo = u + ((size_t)hv * nc + c) * kCh * DV + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) uo[(size_t)(32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3)) * DV] = acc[i];
+      } else {
+        bf16* wo = wp + ((size_t)hv * nc + c) * kCh * DK + swap23(col - DV);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wo[(size_t)(32 * mb + 8 * (i >> 2) + 4 * lg + (i & 3)) * DK] = (bf16)acc[i];
+      }
     }
   }
 }
