@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
   for (int k = 0; k < NV; ++k) {
     const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
     if (vi < nvec) {
-      x[k] = reinterpret_cast<const vec*>(row)[vi];
+      x[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(row) + vi);  // read once: streamed
 #pragma unroll
       for (int s = 0; s < EPV; ++s) mx = fmaxf(mx, to_f32(x[k][s]));
     }
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
 #pragma unroll
       for (int s = 0; s < EPV; ++s)
         g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
-      reinterpret_cast<vec*>(drow)[vi] = g;
+      __builtin_nontemporal_store(g, reinterpret_cast<vec*>(drow) + vi);  // written once: streamed
     }
   }
   __syncthreads();
