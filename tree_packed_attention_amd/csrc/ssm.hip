@@ -117,31 +117,77 @@ __device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int 
 }
 
 // weights of channels c0..c0+7 in tap order m (tap m multiplies the m-th ancestor)
+template <int KM>
 __device__ __forceinline__ void conv_weights(const float* __restrict__ w, int c0, int K, float (*wr)[8]) {
 #pragma unroll
-  for (int m = 0; m < kConvMaxK; ++m)
+  for (int m = 0; m < KM; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) wr[m][e] = m < K ? w[(size_t)(c0 + e) * K + (K - 1 - m)] : 0.0f;
 }
 
+// Eight channels of one row, kept in the input precision.
 template <typename Tio>
-__device__ __forceinline__ void conv_pre(const Tio* __restrict__ x, const float (*wr)[8], const float* br,
-                                         const int* anc, int K, int C, int c0, float* a) {
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = load8(p); }
+  __device__ __forceinline__ void zero() { v = zero8(); }
+  __device__ __forceinline__ void get(float* f) const {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = br[e];
+    for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4{}; }
+  __device__ __forceinline__ void get(float* f) const {
 #pragma unroll
-  for (int m = 0; m < kConvMaxK; ++m) {
-    const int s = m < K ? anc[m] : -1;
-    if (s >= 0) {
-      float xv[8];
-      ld8f(x + (size_t)s * C + c0, xv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xv[e], a[e]);
+    for (int e = 0; e < 4; ++e) {
+      f[e] = a[e];
+      f[4 + e] = b[e];
     }
   }
-}
+};
 
-template <typename Tio>
+// A tile of kConvTB consecutive tokens [t0, t0 + kConvTB) and the KM - 1
+// rows before it, loaded up front (independent loads). On a chain (every
+// token of a node but its first) the m-th ancestor of t is t - m, which the
+// tile holds; other taps are loaded.
+template <typename Tio, int KM>
+struct ConvTile {
+  static constexpr int NR = kConvTB + KM - 1;
+  Raw8<Tio> rows[NR];  // rows[r] = x_{t0 - (KM - 1) + r}
+  __device__ __forceinline__ void load(const Tio* __restrict__ x, int t0, int T, int C, int c0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int t = t0 - (KM - 1) + r;
+      if (t >= 0 && t < T)
+        rows[r].load(x + (size_t)t * C + c0);
+      else
+        rows[r].zero();
+    }
+  }
+  // input of tap m of tile token i (ancestor s, -1 past a root)
+  __device__ __forceinline__ void tap(const Tio* __restrict__ x, int s, int t, int i, int m, int C, int c0,
+                                      float* xv) const {
+    if (s < 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
+    } else if (s == t - m) {
+      rows[i + KM - 1 - m].get(xv);
+    } else {
+      ld8f(x + (size_t)s * C + c0, xv);
+    }
+  }
+};
+
+template <typename Tio, int KM>
 __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __restrict__ x, const float* __restrict__ w,
                                                                 const float* __restrict__ bias,
                                                                 const int* __restrict__ par, int T, int C, int K,
@@ -149,28 +195,44 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __res
   __shared__ int anc[kConvTB][kConvMaxK];
   const int t0 = blockIdx.x * kConvTB;
   conv_ancestors(par, t0, kConvTB, T, K, anc);
-  __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
-  if (c0 >= C) return;
-  float wr[kConvMaxK][8], br[8];
-  conv_weights(w, c0, K, wr);
+  const bool cok = c0 < C;
+  ConvTile<Tio, KM> tile;
+  if (cok) tile.load(x, t0, T, C, c0);
+  __syncthreads();
+  if (!cok) return;
+  float wr[KM][8], br[8];
+  conv_weights<KM>(w, c0, K, wr);
 #pragma unroll
   for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
-  const int n = min(kConvTB, T - t0);
-  for (int i = 0; i < n; ++i) {
-    float a[8];
-    conv_pre(x, wr, br, anc[i], K, C, c0, a);
-    if (act) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+  for (int i = 0; i < kConvTB; ++i) {
+    const int t = t0 + i;
+    if (t < T) {
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = br[e];
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        if (m < K) {
+          float xv[8];
+          tile.tap(x, anc[i][m], t, i, m, C, c0, xv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xv[e], a[e]);
+        }
+      }
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+      }
+      st8f(y + (size_t)t * C + c0, a);
     }
-    st8f(y + (size_t)(t0 + i) * C + c0, a);
   }
 }
 
 // g = dy * act'(a) for a block of kConvTokBlock tokens, plus that block's
 // partial sums of dw (per tap) and db.
-template <typename Tio>
+template <typename Tio, int KM>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     const Tio* __restrict__ x, const Tio* __restrict__ dy, const float* __restrict__ w,
     const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, float* __restrict__ gbuf,
@@ -181,41 +243,54 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
   __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
-  float wr[kConvMaxK][8], br[8];
-  conv_weights(w, c0, K, wr);
+  float wr[KM][8], br[8];
+  conv_weights<KM>(w, c0, K, wr);
 #pragma unroll
   for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
-  float dw[kConvMaxK][8], db[8];
+  float dw[KM][8], db[8];
 #pragma unroll
-  for (int m = 0; m < kConvMaxK; ++m)
+  for (int m = 0; m < KM; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) dw[m][e] = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) db[e] = 0.0f;
-  const int n = min(kConvTokBlock, T - tb);
-  for (int i = 0; i < n; ++i) {
-    const int t = tb + i;
-    float a[8], g[8];
-    conv_pre(x, wr, br, anc[i], K, C, c0, a);
-    ld8f(dy + (size_t)t * C + c0, g);
-    if (act) {
+  for (int sub = 0; sub < kConvTokBlock; sub += kConvTB) {
+    const int ts = tb + sub;
+    if (ts >= T) break;
+    ConvTile<Tio, KM> tile;
+    tile.load(x, ts, T, C, c0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = sigmoidf(a[e]);
-        g[e] *= s * (1.0f + a[e] * (1.0f - s));
-      }
-    }
-    st8f(gbuf + (size_t)t * C + c0, g);
+    for (int i = 0; i < kConvTB; ++i) {
+      const int t = ts + i;
+      if (t < T) {
+        float a[8], g[8], xt[KM][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) db[e] += g[e];
+        for (int e = 0; e < 8; ++e) a[e] = br[e];
 #pragma unroll
-    for (int m = 0; m < kConvMaxK; ++m) {
-      const int s = m < K ? anc[i][m] : -1;
-      if (s >= 0) {
-        float xv[8];
-        ld8f(x + (size_t)s * C + c0, xv);
+        for (int m = 0; m < KM; ++m) {
+          if (m < K) {
+            tile.tap(x, anc[sub + i][m], t, i, m, C, c0, xt[m]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dw[m][e] = fmaf(g[e], xv[e], dw[m][e]);
+            for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xt[m][e], a[e]);
+          }
+        }
+        ld8f(dy + (size_t)t * C + c0, g);
+        if (act) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoidf(a[e]);
+            g[e] *= sg * (1.0f + a[e] * (1.0f - sg));
+          }
+        }
+        st8f(gbuf + (size_t)t * C + c0, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) db[e] += g[e];
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+          if (m < K) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dw[m][e] = fmaf(g[e], xt[m][e], dw[m][e]);
+          }
       }
     }
   }
@@ -224,7 +299,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
 #pragma unroll
-    for (int m = 0; m < kConvMaxK; ++m)
+    for (int m = 0; m < KM; ++m)
       if (m < K) pp[(size_t)e * (K + 1) + (K - 1 - m)] = dw[m][e];
     pp[(size_t)e * (K + 1) + K] = db[e];
   }
@@ -235,7 +310,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
 // token K or more levels down is skipped together with its subtree. One
 // thread per token lists (token, depth) pairs in LDS; a token with more than
 // kConvMaxDesc of them is walked again by the channel threads.
-template <typename Tio>
+template <typename Tio, int KM>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* __restrict__ gbuf,
                                                                    const float* __restrict__ w,
                                                                    const int* __restrict__ pos,
@@ -266,8 +341,8 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* 
   __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
-  float wr[kConvMaxK][8];
-  conv_weights(w, c0, K, wr);
+  float wr[KM][8];
+  conv_weights<KM>(w, c0, K, wr);
   const int n = min(kConvTB, T - t0);
   for (int i = 0; i < n; ++i) {
     const int j = t0 + i;
@@ -282,7 +357,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* 
         const int t = code >> 3, dd = code & 7;
         ld8f(gbuf + (size_t)t * C + c0, g);
 #pragma unroll
-        for (int m = 1; m < kConvMaxK; ++m)
+        for (int m = 1; m < KM; ++m)
           if (m == dd) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
@@ -296,7 +371,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* 
         if (dd < K) {
           ld8f(gbuf + (size_t)t * C + c0, g);
 #pragma unroll
-          for (int m = 1; m < kConvMaxK; ++m)
+          for (int m = 1; m < KM; ++m)
             if (m == dd) {
 #pragma unroll
               for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
@@ -847,6 +922,37 @@ int gdn_dispatch(int dk, int dv, const void* q, const void* k, const void* v, co
 
 bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// kernels are instantiated for up to 4 taps (the common K) and up to 8
+template <typename Tio>
+void conv_fwd_launch(int K, dim3 grid, hipStream_t st, const Tio* x, const float* w, const float* b, const int* par,
+                     int T, int C, int act, Tio* y) {
+  if (K <= 4)
+    hipLaunchKernelGGL((conv_fwd_kernel<Tio, 4>), grid, dim3(kConvThreads), 0, st, x, w, b, par, T, C, K, act, y);
+  else
+    hipLaunchKernelGGL((conv_fwd_kernel<Tio, kConvMaxK>), grid, dim3(kConvThreads), 0, st, x, w, b, par, T, C, K,
+                       act, y);
+}
+
+template <typename Tio, int KM>
+void conv_bwd_launch_k(int K, int nblk, int cy, hipStream_t st, const Tio* x, const Tio* dy, const float* w,
+                       const float* b, const int* par, const int* pos, const int* se, int T, int C, int act,
+                       float* gbuf, float* part, Tio* dx) {
+  hipLaunchKernelGGL((conv_bwd_g_kernel<Tio, KM>), dim3(nblk, cy), dim3(kConvThreads), 0, st, x, dy, w, b, par, T, C,
+                     K, act, gbuf, part);
+  hipLaunchKernelGGL((conv_bwd_dx_kernel<Tio, KM>), dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st,
+                     gbuf, w, pos, se, T, C, K, dx);
+}
+
+template <typename Tio>
+void conv_bwd_launch(int K, int nblk, int cy, hipStream_t st, const Tio* x, const Tio* dy, const float* w,
+                     const float* b, const int* par, const int* pos, const int* se, int T, int C, int act, float* gbuf,
+                     float* part, Tio* dx) {
+  if (K <= 4)
+    conv_bwd_launch_k<Tio, 4>(K, nblk, cy, st, x, dy, w, b, par, pos, se, T, C, act, gbuf, part, dx);
+  else
+    conv_bwd_launch_k<Tio, kConvMaxK>(K, nblk, cy, st, x, dy, w, b, par, pos, se, T, C, act, gbuf, part, dx);
+}
+
 }  // namespace
 }  // namespace ta
 
@@ -869,11 +975,11 @@ extern "C" int tree_conv_fwd(const void* x, ta_dtype dt, int32_t T, int32_t C, i
   {
     ProfScope ps("conv_fwd", st);
     if (dt == TA_BF16)
-      hipLaunchKernelGGL(conv_fwd_kernel<bf16>, grid, dim3(kConvThreads), 0, st, static_cast<const bf16*>(x), weight,
-                         bias, parent, T, C, K, activation, static_cast<bf16*>(y));
+      conv_fwd_launch<bf16>(K, grid, st, static_cast<const bf16*>(x), weight, bias, parent, T, C, activation,
+                            static_cast<bf16*>(y));
     else
-      hipLaunchKernelGGL(conv_fwd_kernel<float>, grid, dim3(kConvThreads), 0, st, static_cast<const float*>(x),
-                         weight, bias, parent, T, C, K, activation, static_cast<float*>(y));
+      conv_fwd_launch<float>(K, grid, st, static_cast<const float*>(x), weight, bias, parent, T, C, activation,
+                             static_cast<float*>(y));
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TA_EHIP, "tree_conv_fwd: kernel launch failed: %s", hipGetErrorString(e));
@@ -915,19 +1021,12 @@ extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t
   const int cy = (C / 8 + kConvThreads - 1) / kConvThreads;
   {
     ProfScope ps("conv_bwd", st);
-    if (dt == TA_BF16) {
-      hipLaunchKernelGGL(conv_bwd_g_kernel<bf16>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
-                         static_cast<const bf16*>(x), static_cast<const bf16*>(dy), weight, bias, parent, T, C, K,
-                         activation, gbuf, part);
-      hipLaunchKernelGGL(conv_bwd_dx_kernel<bf16>, dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
-                         subtree_end, T, C, K, static_cast<bf16*>(dx));
-    } else {
-      hipLaunchKernelGGL(conv_bwd_g_kernel<float>, dim3(nblk, cy), dim3(kConvThreads), 0, st,
-                         static_cast<const float*>(x), static_cast<const float*>(dy), weight, bias, parent, T, C, K,
-                         activation, gbuf, part);
-      hipLaunchKernelGGL(conv_bwd_dx_kernel<float>, dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st, gbuf, weight, pos,
-                         subtree_end, T, C, K, static_cast<float*>(dx));
-    }
+    if (dt == TA_BF16)
+      conv_bwd_launch<bf16>(K, nblk, cy, st, static_cast<const bf16*>(x), static_cast<const bf16*>(dy), weight, bias,
+                            parent, pos, subtree_end, T, C, activation, gbuf, part, static_cast<bf16*>(dx));
+    else
+      conv_bwd_launch<float>(K, nblk, cy, st, static_cast<const float*>(x), static_cast<const float*>(dy), weight,
+                             bias, parent, pos, subtree_end, T, C, activation, gbuf, part, static_cast<float*>(dx));
     hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, st, part, nblk, C, K, dweight,
                        dbias);
   }
