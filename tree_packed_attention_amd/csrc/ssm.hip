@@ -514,9 +514,10 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
     }
   }
   // right-hand side, transposed: rt[col][row] = beta v (col < DV), beta k e^gc.
-  // Rows are read 8 columns at a time (16-byte loads along the row).
+  // Lanes take consecutive rows, 8 columns each (16-byte loads along a row),
+  // so each transposed LDS store covers 64 contiguous bytes.
   for (int idx = tid; idx < kCh * (NCOL / 8); idx += 256) {
-    const int r = idx / (NCOL / 8), cg = 8 * (idx % (NCOL / 8));
+    const int r = idx % kCh, cg = 8 * (idx / kCh);
     bf16x8 x8;
     float sc;
     if (cg < DV) {
