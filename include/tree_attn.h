@@ -335,7 +335,7 @@ int tree_partition(const int32_t* node_start, const int32_t* node_end, const int
  * Gradients are summed in a fixed order (bitwise reproducible). The backward
  * gathers each token's descendants at most K-1 levels down from the
  * preorder range (t, subtree_end[t]) and pos.
- * Limits: T >= 1, C a positive multiple of 8, 1 <= K <= 8.
+ * Limits: T >= 1 (backward: T < 2^28), C a positive multiple of 8, 1 <= K <= 8.
  * workspace (backward): >= tree_conv_workspace_bytes(T, C, K) bytes, 256-byte
  * aligned. Errors: TA_EINVAL, TA_EHIP.
  * ---------------------------------------------------------------------- */
