@@ -252,18 +252,22 @@ def partition_leg():
             "tokens_with_boundaries": int(p["T"])}
 
 
+# The files the attention kernels' device code is compiled from: the counter
+# summaries are valid while these are unchanged.
+ATTN_DEVICE_SOURCES = ("attention.hip", "ta_device.h", "ta_lds.h")
+
+
 def measured_traffic(kernel):
     """Calibrated HBM bytes per dispatch of `kernel` from the committed
-    rocprofv3 counter summaries, if they were taken on the current library
-    sources (else None)."""
+    rocprofv3 counter summaries, if they were taken on the current sources of
+    the attention kernels (else None)."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
-    for fn in sorted(glob.glob(os.path.join(ROOT, "tree_packed_attention_amd", "csrc", "*"))):
-        if fn.endswith((".hip", ".cpp", ".h")):
-            with open(fn, "rb") as fh:
-                h.update(fh.read())
+    for name in ATTN_DEVICE_SOURCES:
+        with open(os.path.join(ROOT, "tree_packed_attention_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
     sha = h.hexdigest()[:16]
     for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(fn) as fh:

@@ -17,5 +17,8 @@ attention  per-branch causal attention with RoPE (forward and backward), a
 logprob    log-softmax gather, weighted loss and the scatter-added gradient
            on shared logit rows; occurrence-form and unique-form entries
 tiles      (q-tile, k-tile) classification counts from subtree ends
+ssm        tree-routed gated delta rule (per-token recurrence, its reverse
+           mode, the per-branch and chunked forms) and the tree causal conv1d
+partition  the partition planner's cut and pack, with a brute-force minimum
 """
-from . import pack, attention, logprob, tiles  # noqa: F401
+from . import pack, attention, logprob, tiles, ssm, partition  # noqa: F401

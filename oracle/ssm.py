@@ -21,7 +21,10 @@ Gated delta rule (per v-head; state h is [dk, dv], alpha_t = exp(g_t)):
   h_t = alpha_t (I - beta_t k_t k_t^T) h_{par(t)} + beta_t k_t v_t^T,  h_{-1} = 0
   o_t = h_t^T q_t
 q/k head of v-head j: j // (Hv / H). q and k are taken as given (any
-normalisation or scaling is the caller's).
+normalisation or scaling is the caller's). The backward (gdn_tree_backward)
+is reverse mode of this recurrence; the pages give no backward of their own
+(training differentiates their forward), and it is pinned by finite
+differences.
 
 Tree conv (depthwise, kernel K, weight w [C, K], bias b [C]):
   a_t = b + sum_{n=0}^{K-1} w[:, K-1-n] * x_{anc_n(t)}   (anc_0 = t, zero past a root)
@@ -196,6 +199,57 @@ def gdn_tree(q, k, v, g, beta, par, return_states=False):
         if return_states:
             states[t] = h
     return (o, states) if return_states else o
+
+
+def gdn_tree_backward(q, k, v, g, beta, par, do):
+    """Gradients (dq, dk, dv, dg, dbeta) of sum(do * o) for gdn_tree, by
+    reverse mode of the same per-token recurrence. Tokens are visited in
+    reverse DFS order, so every child has already sent the gradient of its
+    start state h_{par(t)} back to its parent (siblings add theirs, which is
+    how a state shared by several branches collects its gradient). Per token,
+    with hh = alpha h_par, delta = beta (v - hh^T k), h = hh + k delta^T and
+    o = h^T q:
+      dh     = (sum of the children's dh_par) + q do^T,   dq = h do
+      ddelta = dh^T k,   dk = dh delta + hh (-beta ddelta),
+      dv     = beta ddelta,   dbeta = ddelta . (v - hh^T k)
+      dhh    = dh + k (-beta ddelta)^T,   dg = <dhh, hh>,   dh_par = alpha dhh
+    dq and dk of a q/k head sum over the v-heads that read it."""
+    H = np.asarray(q).shape[1]
+    qr, kr, vv, gg, bb = _heads(q, k, v, g, beta)
+    T, Hv, dk = kr.shape
+    dv = vv.shape[2]
+    do = np.asarray(do, np.float64)
+    par = np.asarray(par)
+    _, states = gdn_tree(q, k, v, g, beta, par, return_states=True)
+    dH = np.zeros((T, Hv, dk, dv))
+    dqr = np.zeros((T, Hv, dk))
+    dkr = np.zeros((T, Hv, dk))
+    dvv = np.zeros((T, Hv, dv))
+    dg = np.zeros((T, Hv))
+    dbeta = np.zeros((T, Hv))
+    for t in range(T - 1, -1, -1):
+        p = int(par[t])
+        hp = states[p] if p >= 0 else np.zeros((Hv, dk, dv))
+        a = np.exp(gg[t])
+        hh = hp * a[:, None, None]
+        resid = vv[t] - np.einsum("hk,hkv->hv", kr[t], hh)
+        delta = bb[t][:, None] * resid
+        h = states[t]
+        dh = dH[t] + qr[t][:, :, None] * do[t][:, None, :]
+        dqr[t] = np.einsum("hkv,hv->hk", h, do[t])
+        ddelta = np.einsum("hkv,hk->hv", dh, kr[t])
+        dkv = -bb[t][:, None] * ddelta
+        dkr[t] = np.einsum("hkv,hv->hk", dh, delta) + np.einsum("hkv,hv->hk", hh, dkv)
+        dvv[t] = bb[t][:, None] * ddelta
+        dbeta[t] = np.sum(ddelta * resid, axis=1)
+        dhh = dh + kr[t][:, :, None] * dkv[:, None, :]
+        dg[t] = np.sum(dhh * hh, axis=(1, 2))
+        if p >= 0:
+            dH[p] += dhh * a[:, None, None]
+    r = Hv // H
+    dq = dqr.reshape(T, H, r, dk).sum(axis=2)
+    dk_ = dkr.reshape(T, H, r, dk).sum(axis=2)
+    return dq, dk_, dvv, dg, dbeta
 
 
 def gdn_branches(q, k, v, g, beta, par):

@@ -107,6 +107,77 @@ def test_pages_chunk_form_equals_the_recurrence(seed):
     assert np.max(np.abs(o - oc)) < 1e-10
 
 
+def _gdn_loss(ins, par, do):
+    return float(np.sum(OS.gdn_tree(*ins, par) * do))
+
+
+def test_gdn_backward_finite_differences_every_entry():
+    """Central differences of sum(do * o) against every gradient entry, on a
+    small forest with forks and two v-heads sharing one q/k head (their dq and
+    dk add up)."""
+    seqs, groups = workloads.random_forest(5, [12, 7], max_depth=3, seg_lo=1, seg_hi=4)
+    p = OP.pack(seqs, groups)
+    T = p["T"]
+    rng = np.random.default_rng(0)
+    q, k, v, g, beta = _gdn_inputs(T, 1, 2, 3, 2, 9)
+    q = q * 1.3
+    do = rng.standard_normal((T, 2, 2))
+    grads = OS.gdn_tree_backward(q, k, v, g, beta, p["par"], do)
+    ins = [q, k, v, g, beta]
+    eps = 1e-6
+    for n, (x, gx) in enumerate(zip(ins, grads)):
+        assert gx.shape == x.shape
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp = [a.copy() for a in ins]
+            xm = [a.copy() for a in ins]
+            xp[n][idx] += eps
+            xm[n][idx] -= eps
+            fd[idx] = (_gdn_loss(xp, p["par"], do) - _gdn_loss(xm, p["par"], do)) / (2 * eps)
+        assert np.max(np.abs(fd - gx)) < 1e-7 * (1 + np.max(np.abs(gx))), n
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gdn_backward_directional_derivative(seed):
+    """One random direction per input at a larger size (dk 8, dv 6, four
+    v-heads on two q/k heads, deeper forest): <grad, dir> equals the central
+    difference of the loss along dir."""
+    p = _forest(30 + seed, budgets=(45, 30), lo=1, hi=9)
+    T = p["T"]
+    q, k, v, g, beta = _gdn_inputs(T, 2, 4, 8, 6, 40 + seed)
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal((T, 4, 6))
+    grads = OS.gdn_tree_backward(q, k, v, g, beta, p["par"], do)
+    ins = [q, k, v, g, beta]
+    eps = 1e-5
+    for n, gx in enumerate(grads):
+        d = rng.standard_normal(ins[n].shape)
+        xp = [a.copy() for a in ins]
+        xm = [a.copy() for a in ins]
+        xp[n] = xp[n] + eps * d
+        xm[n] = xm[n] - eps * d
+        fd = (_gdn_loss(xp, p["par"], do) - _gdn_loss(xm, p["par"], do)) / (2 * eps)
+        assert abs(fd - np.sum(gx * d)) < 1e-7 * (1 + abs(fd)), n
+
+
+def test_gdn_backward_full_forgetting_closed_form():
+    """alpha = 0: o_t = beta_t (q_t . k_t) v_t, so dv_t = beta_t (q_t . k_t)
+    do_t, dq_t = beta_t (v_t . do_t) k_t, dbeta_t = (q_t . k_t)(v_t . do_t),
+    and nothing flows to the parent (dg = 0 because the state before the
+    decay is multiplied by zero)."""
+    p = _forest(4)
+    T = p["T"]
+    q, k, v, g, beta = _gdn_inputs(T, 1, 1, 5, 3, 4)
+    do = np.random.default_rng(1).standard_normal((T, 1, 3))
+    dq, dk, dv, dg, db = OS.gdn_tree_backward(q, k, v, np.full_like(g, -np.inf), beta, p["par"], do)
+    qk = np.sum(q[:, 0] * k[:, 0], axis=1)
+    vd = np.sum(v[:, 0] * do[:, 0], axis=1)
+    assert np.max(np.abs(dv[:, 0] - (beta[:, 0] * qk)[:, None] * do[:, 0])) < 1e-12
+    assert np.max(np.abs(dq[:, 0] - (beta[:, 0] * vd)[:, None] * k[:, 0])) < 1e-12
+    assert np.max(np.abs(db[:, 0] - qk * vd)) < 1e-12
+    assert np.max(np.abs(dg)) == 0.0
+
+
 # ----------------------------------------------------------------- conv
 
 
