@@ -156,8 +156,9 @@ def ssm_leg(seqs, groups, dev, steps):
     """Tree SSM kernels on the same packed batch, at the shape of a hybrid
     model's linear-attention layer: 16 q/k heads and 32 v heads of 128, conv
     width 2*16*128 + 32*128 = 8192 channels, K = 4, bf16. Times the tree conv
-    forward and backward and the tree-routed gated delta rule forward, each
-    against its algorithmic HBM bytes (inputs read once, outputs written once)."""
+    forward and backward and the tree-routed gated delta rule forward and
+    backward, each against its algorithmic HBM bytes (inputs read once,
+    outputs written once)."""
     import numpy as np
     import torch
 
@@ -172,7 +173,8 @@ def ssm_leg(seqs, groups, dev, steps):
     plan_ms = (time.perf_counter() - t0) * 1e3
     plan_dev = torch.from_numpy(plan).to(dev)
     q, k, v, g, beta = workloads.gdn_inputs(T, H, Hv, d, d, "bf16", 3, device=dev)
-    gws = torch.empty(ta.library().tree_gdn_workspace_bytes(H, Hv, d, d, int(plan[0])), dtype=torch.uint8, device=dev)
+    gws = ta.gdn_workspace(q, v, plan, backward=True)
+    gdo = workloads.gdn_dout(T, Hv, d, "bf16", 3, device=dev)
     x, dy, w, b = workloads.conv_inputs(T, C, K, "bf16", 3, device=dev)
     par = torch.from_numpy(p["parent"]).to(dev)
     pos = torch.from_numpy(p["pos"]).to(dev)
@@ -194,9 +196,12 @@ def ssm_leg(seqs, groups, dev, steps):
         return dt, {n: round(tot / max(c, 1), 4) for n, (tot, c) in ks.items()}
 
     gdn_s, gdn_k = timed(lambda: ta.tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=plan_dev, workspace=gws))
+    # the backward reads the forward's chunk states from the workspace (left by the last forward above)
+    gdnb_s, gdnb_k = timed(lambda: ta.tree_gdn_bwd(q, k, v, g, beta, gdo, plan, gws, plan_dev=plan_dev))
     cf_s, _ = timed(lambda: ta.tree_conv_fwd(x, w, b, par, 1))
     cb_s, _ = timed(lambda: ta.tree_conv_bwd(x, dy, w, b, par, pos, se, 1, workspace=cws))
     gdn_bytes = T * (2 * H * d * 2 + 2 * Hv * d * 2 + 8 * Hv)
+    gdnb_bytes = T * (4 * H * d * 2 + 3 * Hv * d * 2 + 16 * Hv)
     cf_bytes, cb_bytes = 2.0 * T * C * 2, 3.0 * T * C * 2
     nc = int(plan[0])
     gdn_flop = nc * Hv * (6.0 * 64 * d * d + 64 * 64 * 4.0 * d)
@@ -204,6 +209,8 @@ def ssm_leg(seqs, groups, dev, steps):
             "chunks": nc, "chains": int(plan[1]), "levels": int(plan[2]), "plan_ms_host": round(plan_ms, 3),
             "gdn_fwd_ms": round(gdn_s * 1e3, 4), "gdn_fwd_gbps": round(gdn_bytes / gdn_s / 1e9, 1),
             "gdn_fwd_tflops_chunked": round(gdn_flop / gdn_s / 1e12, 2), "gdn_kernel_ms": gdn_k,
+            "gdn_bwd_ms": round(gdnb_s * 1e3, 4), "gdn_bwd_gbps": round(gdnb_bytes / gdnb_s / 1e9, 1),
+            "gdn_bwd_kernel_ms": gdnb_k,
             "conv_fwd_ms": round(cf_s * 1e3, 4), "conv_fwd_gbps": round(cf_bytes / cf_s / 1e9, 1),
             "conv_bwd_ms": round(cb_s * 1e3, 4), "conv_bwd_gbps": round(cb_bytes / cb_s / 1e9, 1),
             "hbm_peak_gbps": PEAK_HBM_GBPS}
@@ -423,7 +430,8 @@ def main():
     if not args.no_ssm:
         print("[bench] tree SSM leg ...", flush=True)
         ssm = ssm_leg(seqs, groups, dev, max(3, args.steps // 2))
-        print(f"[bench] gdn fwd {ssm['gdn_fwd_ms']:.3f} ms, conv fwd {ssm['conv_fwd_ms']:.3f} ms "
+        print(f"[bench] gdn fwd {ssm['gdn_fwd_ms']:.3f} ms, gdn bwd {ssm['gdn_bwd_ms']:.3f} ms {ssm['gdn_bwd_kernel_ms']}, "
+              f"conv fwd {ssm['conv_fwd_ms']:.3f} ms "
               f"({ssm['conv_fwd_gbps']:.0f} GB/s), conv bwd {ssm['conv_bwd_ms']:.3f} ms", flush=True)
 
     part = partition_leg()

@@ -367,7 +367,8 @@ int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t T, int32_t
  * sizes filled in. Layout: header [n_chunks, n_chains, n_levels, chunk, T,
  * 0, 0, 0], chunk_start[n_chunks], chunk_len[n_chunks],
  * chunk_parent[n_chunks], chain_begin[n_chains + 1], chains by level
- * [n_chains], level_off[n_levels + 1].
+ * [n_chains], level_off[n_levels + 1], child_off[n_chunks + 1],
+ * child_chains[n_chains] (the chains starting under chunk c, increasing).
  * Errors: TA_EINVAL (non-contiguous nodes, bad parent, chunk out of range),
  * TA_ECAPACITY.
  * ---------------------------------------------------------------------- */
@@ -403,6 +404,43 @@ size_t tree_gdn_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, i
 int tree_gdn_fwd(const void* q, const void* k, const void* v, ta_dtype dt,
                  const float* g, const float* beta, int32_t T, int32_t H, int32_t Hv, int32_t dk, int32_t dv,
                  const int32_t* plan, const int32_t* plan_host, void* o,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_gdn_bwd  (DEVICE)
+ *
+ * Gradients of sum(dout * o) for tree_gdn_fwd ("Tree Training" §3.2, Eq.
+ * 10; App. A.2 gives the forward, which training differentiates): dq, dk
+ * (summed over the v-heads that read each q/k head), dv, dg, dbeta. A
+ * chunk's start state is its parent chunk's end state, so the gradient of a
+ * chunk's end state is the sum of the start-state gradients of its child
+ * chunks (siblings share one state and add their gradients, in increasing
+ * chain order). Computed per chunk in reverse WY form: a parallel pass forms
+ * the chunk-local terms, a reverse state pass (levels deepest first, each
+ * chain from its last chunk back) carries the state gradient in float32, and
+ * two parallel passes form the input gradients with bf16 matrix products and
+ * float32 accumulation. Every sum is taken in a fixed order (bitwise
+ * reproducible).
+ * q, k, v, g, beta, plan, plan_host, T, H, Hv, dk, dv, dt: exactly as given
+ * to the tree_gdn_fwd call whose outputs are differentiated.
+ * dout: device [T][Hv][dv] in dt. dq, dk_out: device [T][H][dk] in dt;
+ * dv_out: device [T][Hv][dv] in dt; dg, dbeta: device float32 [T][Hv]. All
+ * 16-byte aligned, none overlapping another.
+ * workspace: >= tree_gdn_bwd_workspace_bytes(H, Hv, dk, dv, n_chunks,
+ * n_chains) bytes, 256-byte aligned, and the one that tree_gdn_fwd call
+ * filled (its first tree_gdn_workspace_bytes bytes hold the forward's
+ * chunk states and WY factors, which are read, not recomputed), unchanged
+ * since. Asynchronous on `stream`.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED (dk, dv), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t tree_gdn_bwd_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, int32_t n_chunks,
+                                    int32_t n_chains);
+
+int tree_gdn_bwd(const void* q, const void* k, const void* v, ta_dtype dt,
+                 const float* g, const float* beta, const void* dout,
+                 int32_t T, int32_t H, int32_t Hv, int32_t dk, int32_t dv,
+                 const int32_t* plan, const int32_t* plan_host,
+                 void* dq, void* dk_out, void* dv_out, float* dg, float* dbeta,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -2,7 +2,9 @@
 
 tree_conv_fwd / tree_conv_bwd against oracle.ssm.tree_conv(_backward);
 tree_gdn_fwd against oracle.ssm.gdn_tree (the per-token recurrence routed
-through par). Inputs are the bf16 / fp32 values the kernels receive.
+through par); tree_gdn_bwd against oracle.ssm.gdn_tree_backward (reverse
+mode of that recurrence). Inputs are the bf16 / fp32 values the kernels
+receive.
 
 Tolerances (none are stated for these kernels; they follow the attention
 ones): outputs max |err| / max(1, |ref|) <= 2e-2, gradients relative L2 <=
@@ -37,7 +39,11 @@ def out_err(a, b):
 
 
 def rel_l2(a, b):
-    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(np.asarray(b)))
+    """Relative L2 error; the absolute one where the reference is all zero
+    (a single token's decay gradient is exactly zero)."""
+    nb = np.linalg.norm(np.asarray(b))
+    d = np.linalg.norm(np.asarray(a) - np.asarray(b))
+    return float(d / nb) if nb > 0 else float(d)
 
 
 def _pack(seqs, groups):
@@ -193,3 +199,66 @@ def test_gdn_deterministic():
     *_, inp, o1 = _gdn_case(seqs, groups, 2, 4, 128, 128, "bf16", 64)
     *_, o2 = _gdn_case(seqs, groups, 2, 4, 128, 128, "bf16", 64)
     assert torch.equal(o1, o2)
+
+
+# ----------------------------------------------------------------- gated delta rule, backward
+
+GRAD_NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+def _gdn_bwd_case(seqs, groups, H, Hv, dk, dv, dtype, chunk, seed=17):
+    p, po = _pack(seqs, groups)
+    plan = ta.tree_gdn_plan(p["node_start"], p["node_end"], p["node_parent"], chunk)
+    q, k, v, g, beta = workloads.gdn_inputs(p["T"], H, Hv, dk, dv, dtype, seed, device="cuda")
+    do = workloads.gdn_dout(p["T"], Hv, dv, dtype, seed, device="cuda")
+    ws = ta.gdn_workspace(q, v, plan, backward=True)
+    ta.tree_gdn_fwd(q, k, v, g, beta, plan, workspace=ws)
+    grads = ta.tree_gdn_bwd(q, k, v, g, beta, do, plan, ws)
+    torch.cuda.synchronize()
+    return po, plan, (q, k, v, g, beta, do), grads
+
+
+def _check_grads(tag, got, ref):
+    for name, a, b in zip(GRAD_NAMES, got, ref):
+        a = host(a)
+        rl = rel_l2(a, b)
+        mx = float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1.0 if not np.any(b) else 1e-30))
+        print(f"{tag} {name}: rel-l2 {rl:.2e} max-err/max-ref {mx:.2e}", flush=True)
+        assert rl <= GRAD_TOL, name
+        assert mx <= 2 * GRAD_TOL, name
+
+
+@pytest.mark.parametrize("case", list(GDN_CASES))
+def test_gdn_bwd_matches_oracle(case):
+    make, H, Hv, dk, dv, dtype, chunk = GDN_CASES[case]
+    seqs, groups = make()
+    print(f"\n[case] gdn bwd {case}", flush=True)
+    po, plan, (q, k, v, g, beta, do), grads = _gdn_bwd_case(seqs, groups, H, Hv, dk, dv, dtype, chunk)
+    ref = OS.gdn_tree_backward(host(q), host(k), host(v), host(g), host(beta), po["par"], host(do))
+    _check_grads(case, grads, ref)
+
+
+def test_gdn_bwd_multistep_full_size_tree():
+    """The multistep batch (T = 28672) with 16 q/k and 32 v heads of 128,
+    bf16. The oracle runs whole tree 3 on q/k head 7 and the two v-heads that
+    read it (14, 15), which gives that head's dq and dk in full."""
+    seqs, groups = workloads.sequences("multistep")
+    H, Hv, d = 16, 32, 128
+    po, plan, (q, k, v, g, beta, do), grads = _gdn_bwd_case(seqs, groups, H, Hv, d, d, "bf16", 64, seed=3)
+    ts, te = int(po["tree_start"][3]), int(po["tree_start"][4])
+    par = po["par"][ts:te].copy()
+    par[par >= 0] -= ts
+    hk, hvs = 7, slice(14, 16)
+    ref = OS.gdn_tree_backward(host(q[ts:te, hk:hk + 1]), host(k[ts:te, hk:hk + 1]), host(v[ts:te, hvs]),
+                               host(g[ts:te, hvs]), host(beta[ts:te, hvs]), par, host(do[ts:te, hvs]))
+    dq, dk_, dv_, dg, db = grads
+    got = (dq[ts:te, hk:hk + 1], dk_[ts:te, hk:hk + 1], dv_[ts:te, hvs], dg[ts:te, hvs], db[ts:te, hvs])
+    _check_grads(f"tree 3 ({te - ts} tokens), q/k head {hk}", got, ref)
+
+
+def test_gdn_bwd_deterministic():
+    seqs, groups = workloads.random_forest(12, [500, 300])
+    *_, g1 = _gdn_bwd_case(seqs, groups, 2, 4, 128, 128, "bf16", 16)
+    *_, g2 = _gdn_bwd_case(seqs, groups, 2, 4, 128, 128, "bf16", 16)
+    for name, a, b in zip(GRAD_NAMES, g1, g2):
+        assert torch.equal(a, b), name

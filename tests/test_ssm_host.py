@@ -20,8 +20,10 @@ def _decode(plan):
     cb = plan[o:o + nch + 1]; o += nch + 1
     lc = plan[o:o + nch]; o += nch
     lo = plan[o:o + nl + 1]; o += nl + 1
+    co = plan[o:o + nc + 1]; o += nc + 1
+    cc = plan[o:o + nch]; o += nch
     assert o == len(plan)
-    return dict(nc=nc, nch=nch, nl=nl, chunk=chunk, T=T, cs=cs, cl=cl, cp=cp, cb=cb, lc=lc, lo=lo)
+    return dict(nc=nc, nch=nch, nl=nl, chunk=chunk, T=T, cs=cs, cl=cl, cp=cp, cb=cb, lc=lc, lo=lo, co=co, cc=cc)
 
 
 @pytest.mark.parametrize("seed,chunk", [(1, 64), (2, 16), (3, 5), (4, 1), (5, 64)])
@@ -55,6 +57,11 @@ def test_plan_matches_its_definition(seed, chunk):
     for l in range(p["nl"]):
         got = p["lc"][p["lo"][l]:p["lo"][l + 1]]
         assert list(got) == [ch for ch in range(p["nch"]) if level[ch] == l]
+    # child chains of every chunk, in increasing order
+    for c in range(p["nc"]):
+        got = p["cc"][p["co"][c]:p["co"][c + 1]]
+        assert list(got) == [ch for ch in range(p["nch"]) if p["cp"][p["cb"][ch]] == c]
+    assert p["co"][-1] == sum(1 for ch in range(p["nch"]) if p["cp"][p["cb"][ch]] >= 0)
 
 
 def test_plan_errors():
@@ -98,6 +105,20 @@ def test_ssm_argument_validation():
     bad = plan.copy()
     bad[3] = 99
     assert lib.tree_gdn_fwd(*gargs(ph=bad.ctypes.data_as(ctypes.c_void_p))) == ta.TA_EINVAL
+    # backward: its workspace holds the forward's plus its own
+    gb = lib.tree_gdn_bwd_workspace_bytes(2, 4, 64, 64, int(plan[0]), int(plan[1]))
+    assert gb > gw
+    assert lib.tree_gdn_bwd_workspace_bytes(2, 4, 64, 64, int(plan[0]), int(plan[0]) + 1) == 0
+    bw = lambda T=10, H=2, Hv=4, dk=64, dv=64, ph=pp, ws=gb, dq=bogus: (
+        bogus, bogus, bogus, ta.TA_BF16, bogus, bogus, bogus, T, H, Hv, dk, dv, bogus, ph, dq, bogus, bogus, bogus,
+        bogus, bogus, ws, None)
+    assert lib.tree_gdn_bwd(*bw(dk=96)) == ta.TA_EUNSUPPORTED
+    assert lib.tree_gdn_bwd(*bw(Hv=3)) == ta.TA_EINVAL
+    assert lib.tree_gdn_bwd(*bw(T=11)) == ta.TA_EINVAL and "plan" in ta.last_error()
+    assert lib.tree_gdn_bwd(*bw(ws=gw)) == ta.TA_EINVAL and "workspace" in ta.last_error()
+    assert lib.tree_gdn_bwd(*bw(dq=None)) == ta.TA_EINVAL
+    assert lib.tree_gdn_bwd(*bw(dq=ctypes.c_void_p(0x1008))) == ta.TA_EINVAL
+    assert lib.tree_gdn_bwd(*bw(ph=bad.ctypes.data_as(ctypes.c_void_p))) == ta.TA_EINVAL
 
 
 # ----------------------------------------------------------------- partition planner

@@ -14,6 +14,8 @@ The names follow the C ABI in include/tree_attn.h:
   tree_partition(node_start, node_end, node_parent, capacity)  host partition plan -> dict
   tree_gdn_plan(node_start, node_end, node_parent)  host chunk schedule -> int32 numpy plan
   tree_gdn_fwd(q, k, v, g, beta, plan, ...)        tree-routed gated delta rule -> o
+  tree_gdn_bwd(q, k, v, g, beta, do, plan, ws)     its gradients -> (dq, dk, dv, dg, dbeta)
+  gdn_workspace(q, v, plan, backward=False)        workspace for tree_gdn_fwd (and tree_gdn_bwd)
   TreeAttention                                    torch.autograd.Function over fwd/bwd
 
 The library must be built first (python tree_packed_attention_amd/build.py);
@@ -53,6 +55,8 @@ EXPORTS = (
     "tree_gdn_plan",
     "tree_gdn_workspace_bytes",
     "tree_gdn_fwd",
+    "tree_gdn_bwd_workspace_bytes",
+    "tree_gdn_bwd",
     "tree_attn_profile_enable",
     "tree_attn_profile_read",
 )
@@ -129,6 +133,11 @@ _lib.tree_gdn_workspace_bytes.restype = _sz
 _lib.tree_gdn_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
 _lib.tree_gdn_fwd.restype = ctypes.c_int
 _lib.tree_gdn_fwd.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]
+_lib.tree_gdn_bwd_workspace_bytes.restype = _sz
+_lib.tree_gdn_bwd_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.tree_gdn_bwd.restype = ctypes.c_int
+_lib.tree_gdn_bwd.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p,
+                              _p, _p, _p, _sz, _p]
 _lib.tree_tile_stats.restype = ctypes.c_int
 _lib.tree_tile_stats.argtypes = [_p, _i32, _i32, _i32] + [ctypes.POINTER(ctypes.c_int64)] * 4
 _lib.tree_attn_profile_enable.restype = ctypes.c_int
@@ -525,6 +534,19 @@ def tree_gdn_plan(node_start, node_end, node_parent, chunk=64):
     return plan
 
 
+def gdn_workspace(q, v, plan, backward=False):
+    """Device workspace for tree_gdn_fwd; with backward=True also large
+    enough for tree_gdn_bwd (pass the same buffer to both)."""
+    torch = _torch()
+    H, dk = q.shape[1], q.shape[2]
+    Hv, dv = v.shape[1], v.shape[2]
+    if backward:
+        nbytes = _lib.tree_gdn_bwd_workspace_bytes(H, Hv, dk, dv, int(plan[0]), int(plan[1]))
+    else:
+        nbytes = _lib.tree_gdn_workspace_bytes(H, Hv, dk, dv, int(plan[0]))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+
+
 def tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=None, workspace=None):
     """q, k [T, H, dk]; v [T, Hv, dv] (bf16 / f32); g, beta [T, Hv] f32; plan from tree_gdn_plan -> o [T, Hv, dv]."""
     torch = _torch()
@@ -544,6 +566,30 @@ def tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=None, workspace=None):
                            _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
     _check(rc)
     return o
+
+
+def tree_gdn_bwd(q, k, v, g, beta, do, plan, workspace, plan_dev=None):
+    """Gradients of sum(do * o) for the tree_gdn_fwd call that filled
+    `workspace` (from gdn_workspace(..., backward=True)) with the same inputs
+    and plan -> (dq, dk, dv, dg, dbeta)."""
+    torch = _torch()
+    T, H, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev = q.device
+    plan = np.ascontiguousarray(plan, dtype=np.int32)
+    if plan_dev is None:
+        plan_dev = torch.from_numpy(plan).to(dev)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    rc = _lib.tree_gdn_bwd(_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, dev), _dev_ptr(v, "v", q.dtype, dev), _dt(q),
+                           _dev_ptr(g, "g", torch.float32, dev), _dev_ptr(beta, "beta", torch.float32, dev),
+                           _dev_ptr(do, "do", q.dtype, dev), T, H, Hv, dk, dv,
+                           _dev_ptr(plan_dev, "plan", torch.int32, dev), _np_ptr(plan), _dev_ptr(dq, "dq"),
+                           _dev_ptr(dk_, "dk"), _dev_ptr(dv_, "dv"), _dev_ptr(dg, "dg"), _dev_ptr(dbeta, "dbeta"),
+                           _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return dq, dk_, dv_, dg, dbeta
 
 
 def _make_autograd():

@@ -435,6 +435,96 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
   return L;
 }
 
+// Backward workspace, after the forward's (chunk-local like it):
+//   dvlt [Hv][nc][dv][64] f32    (P^T dO)^T
+//   kgl  [Hv][nc][64][dk] bf16   k e^(gl - gc), swap23 columns
+//   qgt  [Hv][nc][dk][64] bf16   (q e^gc)^T
+//   wt   [Hv][nc][dk][64] bf16   w^T
+//   dot  [Hv][nc][dv][64] bf16   dO^T
+//   dvnt [Hv][nc][dv][64] bf16   dvn^T
+//   dhe  [nc][Hv][dv][dk] bf16   end-state gradient of each chunk, transposed
+//   dwt  [Hv][nc][dk][64] bf16   dw^T
+//   dgca [Hv][nc][64] f32        decay gradient, output / state part
+//   dka  [H][nc][64][dk] f32     dk, output / state part
+//   dhead [nch][Hv][dv][dk] f32  start-state gradient of each chain, transposed
+struct GdnBwdLayout {
+  size_t dvlt, kgl, qgt, wt, dot, dvnt, dhe, dwt, dgca, dka, dhead, total;
+};
+
+GdnBwdLayout gdn_bwd_layout(int H, int Hv, int dk, int dv, int nc, int nch) {
+  GdnBwdLayout L{};
+  size_t o = gdn_layout(H, Hv, dk, dv, nc).total;
+  const size_t hn = (size_t)Hv * nc;
+  auto take = [&](size_t* at, size_t bytes) {
+    *at = o;
+    o = al256(o + bytes);
+  };
+  take(&L.dvlt, hn * dv * kCh * 4);
+  take(&L.kgl, hn * kCh * dk * 2);
+  take(&L.qgt, hn * dk * kCh * 2);
+  take(&L.wt, hn * dk * kCh * 2);
+  take(&L.dot, hn * dv * kCh * 2);
+  take(&L.dvnt, hn * dv * kCh * 2);
+  take(&L.dhe, hn * dv * dk * 2);
+  take(&L.dwt, hn * dk * kCh * 2);
+  take(&L.dgca, hn * kCh * 4);
+  take(&L.dka, (size_t)H * nc * kCh * dk * 4);
+  take(&L.dhead, (size_t)nch * Hv * dv * dk * 4);
+  L.total = o;
+  return L;
+}
+
+// T = (I + M)^-1 for a unit lower-triangular 64 x 64 system, by 16 x 16
+// blocks: T_ii = (I + M_ii)^-1 by forward substitution (one lane per
+// column), then T_ij = -T_ii sum_{j <= q < i} M_iq T_qj one block diagonal
+// at a time. mval(r, q) returns M[r][q] (read for q < r only); ts is
+// cleared here. All 256 threads of the workgroup take part; ts is complete
+// when it returns.
+template <class MV>
+__device__ __forceinline__ void unit_lower_inverse(MV mval, float (*ts)[kCh + 4], float (*pscr)[16][17], int tid) {
+  const int wv = tid >> 6, lane = tid & 63;
+  for (int idx = tid; idx < kCh * (kCh + 4); idx += 256) (&ts[0][0])[idx] = 0.0f;
+  __syncthreads();
+  if (wv == 0) {
+    const int bd = 16 * (lane >> 4), j = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == j ? 1.0f : 0.0f;
+#pragma unroll
+      for (int q = 0; q < r; ++q) acc = fmaf(-mval(bd + r, bd + q), x[q], acc);
+      x[r] = acc;
+      ts[bd + r][bd + j] = acc;
+    }
+  }
+  __syncthreads();
+  const int er = tid >> 4, ec = tid & 15;  // element (row, column) of a 16 x 16 block
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    float part[3];
+#pragma unroll
+    for (int bi = 0; bi < 4 - d; ++bi) {
+      const int bi_ = bi + d, bj = bi;
+      float acc = 0.0f;
+      for (int q = 16 * bj; q < 16 * bi_; ++q) acc = fmaf(mval(16 * bi_ + er, q), ts[q][16 * bj + ec], acc);
+      part[bi] = acc;
+    }
+    // every thread holds its element of each partial sum; exchange them through LDS
+#pragma unroll
+    for (int bi = 0; bi < 4 - d; ++bi) pscr[bi][er][ec] = part[bi];
+    __syncthreads();
+#pragma unroll
+    for (int bi = 0; bi < 4 - d; ++bi) {
+      const int bi_ = bi + d, bj = bi;
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc = fmaf(ts[16 * bi_ + er][16 * bi_ + q], pscr[bi][q][ec], acc);
+      ts[16 * bi_ + er][16 * bj + ec] = -acc;
+    }
+    __syncthreads();
+  }
+}
+
 // Stage 1: per (chunk, v-head). 256 threads.
 //   gc, beta, the decay to the chunk end; M = strictly-lower (beta k) k^T *
 //   exp(gc_i - gc_j) (bf16 MFMA); T = (I + M)^-1 in float32 by 16 x 16
@@ -531,49 +621,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
     for (int e = 0; e < 8; ++e) rt[cg + e][r] = (bf16)((float)x8[e] * sc);
   }
   __syncthreads();
-  // T = (I + M)^-1 by 16 x 16 blocks (T is unit lower triangular):
-  //   T_ii = (I + M_ii)^-1 by forward substitution, one lane per column;
-  //   T_ij = -T_ii sum_{j <= q < i} M_iq T_qj, one block diagonal at a time.
-  for (int idx = tid; idx < kCh * (kCh + 4); idx += 256) (&ts[0][0])[idx] = 0.0f;
-  __syncthreads();
-  if (wv == 0) {
-    const int bd = 16 * (lane >> 4), j = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = r == j ? 1.0f : 0.0f;
-#pragma unroll
-      for (int q = 0; q < r; ++q) acc = fmaf(-Ms[bd + r][bd + q], x[q], acc);
-      x[r] = acc;
-      ts[bd + r][bd + j] = acc;
-    }
-  }
-  __syncthreads();
-  const int er = tid >> 4, ec = tid & 15;  // element (row, column) of a 16 x 16 block
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    float part[3];
-#pragma unroll
-    for (int bi = 0; bi < 4 - d; ++bi) {
-      const int bi_ = bi + d, bj = bi;
-      float acc = 0.0f;
-      for (int q = 16 * bj; q < 16 * bi_; ++q) acc = fmaf(Ms[16 * bi_ + er][q], ts[q][16 * bj + ec], acc);
-      part[bi] = acc;
-    }
-    // every thread holds its element of each partial sum; exchange them through LDS
-#pragma unroll
-    for (int bi = 0; bi < 4 - d; ++bi) pscr[bi][er][ec] = part[bi];
-    __syncthreads();
-#pragma unroll
-    for (int bi = 0; bi < 4 - d; ++bi) {
-      const int bi_ = bi + d, bj = bi;
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc = fmaf(ts[16 * bi_ + er][16 * bi_ + q], pscr[bi][q][ec], acc);
-      ts[16 * bi_ + er][16 * bj + ec] = -acc;
-    }
-    __syncthreads();
-  }
+  unit_lower_inverse([&](int r, int q) { return Ms[r][q]; }, ts, pscr, tid);
   // [u | w] = T rt^T: 32x32 output blocks (2 row blocks x NCOL/32 column
   // blocks), column blocks dealt to the waves in turn
   constexpr int NCB = NCOL / 32;
@@ -850,9 +898,793 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
   }
 }
 
+// ---------------------------------------------------------------- gated delta rule, backward
+//
+// Per chunk (L rows, local cumulative log decay gc, gl = gc of the last
+// row), with P = (q k^T) exp(gc_i - gc_j) on j <= i, qg = q e^gc,
+// kd = k e^(gl - gc), T = (I + M)^-1 and the forward's u, w, vn, h0:
+//   o    = qg h0 + P vn,   h_end = e^gl h0 + kd^T vn,   vn = u - w h0,
+//   u    = T (beta v),     w     = T (beta k e^gc).
+// Given dO and the end-state gradient dh_end (the sum of the child chunks'
+// start-state gradients):
+//   dvn  = P^T dO + kd dh_end
+//   dh0  = qg^T dO - w^T dvn + e^gl dh_end               (to the parent)
+//   dq   = dS k + e^gc (dO h0^T),   dS = (dO vn^T) exp(gc_i - gc_j), j <= i
+//   dk   = dS^T q + e^(gl-gc) (vn dh_end^T) + [WY part]
+//   dw   = -dvn h0^T,  dbv = T^T dvn,  dbk = T^T dw,
+//   dM   = -(dbv u^T + dbk w^T) on j < i,   M_ij = beta_i (k_i . k_j) exp(gc_i - gc_j)
+//   dv   = beta dbv,   dbeta = v.dbv + e^gc k.dbk + sum_j dM_ij (k_i.k_j) exp(gc_i - gc_j)
+//   dk  += beta e^gc dbk + (G + G^T) k,   G_ij = beta_i dM_ij exp(gc_i - gc_j)
+// and dgc collects the derivative of every exp(gc ...) factor; dg is its
+// reverse cumulative sum inside the chunk.
+//   1. prep (all chunks): P^T dO, and the state pass's operands kd (rows,
+//      swap23 columns), qg^T, w^T, dO^T;
+//   2. state (levels deepest first, each chain from its last chunk back):
+//      dh in MFMA accumulators as h in the forward; stores dh_end and dvn;
+//   3. out (per chunk and q/k head, looping over its v-heads): dq, the
+//      P / h0 / h_end parts of dk and dgc, and dw;
+//   4. wy (per chunk and q/k head): T again, dbv, dbk, dM, dv, dbeta, the
+//      rest of dk and dgc, dg.
+
+__device__ __forceinline__ int crow(int i, int lg) { return 8 * (i >> 2) + 4 * lg + (i & 3); }
+
+__device__ __forceinline__ float sum32(float x) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// 8 elements along the contraction index k0..k0+7: of row r (contiguous) or
+// of column c (stride ld)
+__device__ __forceinline__ bf16x8 row8(const bf16* X, int ld, int r, int k0) {
+  return *reinterpret_cast<const bf16x8*>(X + r * ld + k0);
+}
+__device__ __forceinline__ bf16x8 col8(const bf16* X, int ld, int c, int k0) {
+  bf16x8 v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = X[(k0 + s) * ld + c];
+  return v;
+}
+__device__ __forceinline__ bf16x8 col8f(const float* X, int ld, int c, int k0) {
+  bf16x8 v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = (bf16)X[(k0 + s) * ld + c];
+  return v;
+}
+
+// Stage B1, per (chunk, v-head), 256 threads: dvl^T[e][j] = sum_i dO[i][e]
+// P[i][j] (wave: key block w % 2, dv blocks from w / 2), plus the state
+// pass operands.
+template <int DK, int DV, typename Tio>
+__global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
+                                                           const Tio* __restrict__ dout, const int* __restrict__ cstart,
+                                                           const int* __restrict__ clen, int nc, int H, int Hv,
+                                                           const float* __restrict__ gcw, const bf16* __restrict__ wp,
+                                                           float* __restrict__ dvlt, bf16* __restrict__ kgl,
+                                                           bf16* __restrict__ qgt, bf16* __restrict__ wt,
+                                                           bf16* __restrict__ dot) {
+  __shared__ __attribute__((aligned(16))) bf16 qs[kCh][DK + 8];
+  __shared__ __attribute__((aligned(16))) bf16 ks[kCh][DK + 8];
+  __shared__ __attribute__((aligned(16))) bf16 dT[DV][kCh + 8];
+  __shared__ float gcs[kCh], egs[kCh], decs[kCh];
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int hk = hv / (Hv / H);
+  const int t0 = cstart[c], L = clen[c];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const size_t hc = (size_t)hv * nc + c;
+  if (tid < kCh) {
+    const float gv = gcw[hc * kCh + tid], gl = gcw[hc * kCh + kCh - 1];
+    gcs[tid] = gv;
+    egs[tid] = tid < L ? expf(gv) : 0.0f;
+    decs[tid] = tid < L ? expf(gl - gv) : 0.0f;
+  }
+  __syncthreads();
+  // q and k rows into LDS; (q e^gc)^T out. Lanes take consecutive rows, so
+  // each transposed store covers 128 contiguous bytes.
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int i = idx % kCh, d0 = 8 * (idx / kCh);
+    const bf16x8 qv = i < L ? load8(q + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+    const bf16x8 kv = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+    *reinterpret_cast<bf16x8*>(&qs[i][d0]) = qv;
+    *reinterpret_cast<bf16x8*>(&ks[i][d0]) = kv;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qgt[(hc * DK + d0 + s) * kCh + i] = (bf16)((float)qv[s] * egs[i]);
+  }
+  // w^T (w is stored with swap23 columns: position p holds column swap23(p))
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int i = idx % kCh, p0 = 8 * (idx / kCh);
+    const bf16x8 wv8 = load8(wp + (hc * kCh + i) * DK + p0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wt[(hc * DK + swap23(p0 + s)) * kCh + i] = wv8[s];
+  }
+  // dO^T, in LDS and out
+  for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
+    const int i = idx % kCh, e0 = 8 * (idx / kCh);
+    const bf16x8 d8 = i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      dT[e0 + s][i] = d8[s];
+      dot[(hc * DV + e0 + s) * kCh + i] = d8[s];
+    }
+  }
+  __syncthreads();
+  // kd rows with swap23 columns (the A operand of dvn += kd dh)
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int i = idx / (DK / 8), p0 = 8 * (idx % (DK / 8));
+    bf16x8 o8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o8[s] = (bf16)((float)ks[i][swap23(p0 + s)] * decs[i]);
+    *reinterpret_cast<bf16x8*>(kgl + (hc * kCh + i) * DK + p0) = o8;
+  }
+  // P^T dO: S from q rows and k columns; P from the C registers is the B
+  // operand of the contraction over i (swap23 row order, dO^T read to match)
+  constexpr int NDW = DV / 64;
+  const int kb = wv & 1, j = 32 * kb + lc;
+  f32x16 acc[NDW];
+#pragma unroll
+  for (int m = 0; m < NDW; ++m) acc[m] = f32x16{};
+  for (int qb = kb; qb < 2; ++qb) {
+    f32x16 sv = f32x16{};
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+      sv = mfma32x32x16(row8(&qs[0][0], DK + 8, 32 * qb + lc, 16 * a + 8 * lg),
+                        row8(&ks[0][0], DK + 8, j, 16 * a + 8 * lg), sv);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * qb + crow(r, lg);
+      pb[r >> 3][r & 7] = (bf16)((j <= i && i < L) ? sv[r] * expf(gcs[i] - gcs[j]) : 0.0f);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int a2 = 2 * qb + h2;
+#pragma unroll
+      for (int m = 0; m < NDW; ++m) {
+        const int e = 32 * ((wv >> 1) + 2 * m) + lc;
+        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(&dT[e][16 * a2 + 4 * lg]),
+                             *reinterpret_cast<const bf16x4*>(&dT[e][16 * a2 + 8 + 4 * lg]));
+        acc[m] = mfma32x32x16(A, pb[h2], acc[m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NDW; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 32 * ((wv >> 1) + 2 * m) + crow(r, lg);
+      dvlt[(hc * DV + e) * kCh + j] = acc[m][r];
+    }
+}
+
+// Stage B2: one workgroup per (chain of this level, v-head), levels deepest
+// first; wave s owns dv columns [32 s, 32 s + 32). dh (dk x 32 per wave) in
+// MFMA C registers like the forward's h. Per chunk, from its end-state
+// gradient: store it, dvn = dvl + kd dh (B from the C registers), store
+// dvn^T, dh = e^gl dh + qg^T dO - w^T dvn. The next chunk back (kd, qg^T,
+// w^T) streams into LDS meanwhile.
+template <int DK>
+struct BStateBuf {
+  bf16* kg;
+  bf16* qt;
+  bf16* wt;
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, float gl, int lg, int lc,
+                                                    f32x16 (&dh)[DK / 32], const float* __restrict__ dvl_row,
+                                                    const bf16* __restrict__ do_row, bf16* __restrict__ vo,
+                                                    bf16* __restrict__ ho) {
+  constexpr int NB = DK / 32;
+  // dvl and dO of this lane's column, issued first
+  f32x4 dl[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) dl[mb][j4] = *reinterpret_cast<const f32x4*>(dvl_row + 32 * mb + 8 * j4 + 4 * lg);
+  bf16x8 db[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    db[a] = cat(*reinterpret_cast<const bf16x4*>(do_row + 16 * a + 4 * lg),
+                *reinterpret_cast<const bf16x4*>(do_row + 16 * a + 8 + 4 * lg));
+  // the end-state gradient (bf16, [dv][dk] like the forward's start states)
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (bf16)dh[b][4 * j + e];
+      *reinterpret_cast<bf16x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
+    }
+  bf16x8 hb[DK / 16];
+#pragma unroll
+  for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) hb[a][s] = (bf16)dh[a >> 1][8 * (a & 1) + s];
+  f32x16 vn[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vn[mb][4 * j4 + e] = dl[mb][j4][e];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a)
+      vn[mb] = mfma32x32x16(lds128(sb.kg + toff<DK>(32 * mb + lc, 16 * a + 8 * lg)), hb[a], vn[mb]);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
+      *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+    }
+  const float al = expf(gl);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dh[b] *= al;
+  bf16x8 vb[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) vb[a][s] = (bf16)(-vn[a >> 1][8 * (a & 1) + s]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bf16* qt = sb.qt + (b >> 1) * 64 * kCh;
+    const bf16* wt = sb.wt + (b >> 1) * 64 * kCh;
+    const int rr = 32 * (b & 1) + lc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const bf16x8 Aq = cat(*reinterpret_cast<const bf16x4*>(qt + toff<kCh>(rr, 16 * a + 4 * lg)),
+                            *reinterpret_cast<const bf16x4*>(qt + toff<kCh>(rr, 16 * a + 8 + 4 * lg)));
+      dh[b] = mfma32x32x16(Aq, db[a], dh[b]);
+      const bf16x8 Aw = cat(*reinterpret_cast<const bf16x4*>(wt + toff<kCh>(rr, 16 * a + 4 * lg)),
+                            *reinterpret_cast<const bf16x4*>(wt + toff<kCh>(rr, 16 * a + 8 + 4 * lg)));
+      dh[b] = mfma32x32x16(Aw, vb[a], dh[b]);
+    }
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DV / 32)) void gdn_bwd_state_kernel(
+    const int* __restrict__ level_chains, int lvl0, const int* __restrict__ chain_begin,
+    const int* __restrict__ child_off, const int* __restrict__ child_chains, int nc, int Hv,
+    const float* __restrict__ gcw, const float* __restrict__ dvlt, const bf16* __restrict__ kgl,
+    const bf16* __restrict__ qgt, const bf16* __restrict__ wt, const bf16* __restrict__ dot, bf16* __restrict__ dvnt,
+    bf16* __restrict__ dhe, float* __restrict__ dhead) {
+  constexpr int NW = DV / 32;
+  constexpr int NB = DK / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 g0[kCh * DK];
+  __shared__ __attribute__((aligned(1024))) bf16 g1[kCh * DK];
+  __shared__ __attribute__((aligned(1024))) bf16 q0[DK * kCh];
+  __shared__ __attribute__((aligned(1024))) bf16 q1[DK * kCh];
+  __shared__ __attribute__((aligned(1024))) bf16 x0[DK * kCh];
+  __shared__ __attribute__((aligned(1024))) bf16 x1[DK * kCh];
+  const int ch = level_chains[lvl0 + blockIdx.x];
+  const int hv = blockIdx.y;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lg = lane >> 5, lc = lane & 31;
+  const int n = 32 * wv + lc;  // dv column of this lane
+  const int cb = chain_begin[ch], ce = chain_begin[ch + 1];
+  TileDma<DK, false, NW> gdma;
+  TileDma<kCh, false, NW> tdma;
+  gdma.init(wv, lane);
+  tdma.init(wv, lane);
+  auto issue = [&](int c, bf16* gb, bf16* qb, bf16* xb) {
+    const size_t hc = (size_t)hv * nc + c;
+    gdma.issue(kgl + hc * kCh * DK, gb, wv);
+#pragma unroll
+    for (int t = 0; t < DK / 64; ++t) {
+      tdma.issue(qgt + (hc * DK + 64 * t) * kCh, qb + t * 64 * kCh, wv);
+      tdma.issue(wt + (hc * DK + 64 * t) * kCh, xb + t * 64 * kCh, wv);
+    }
+  };
+  f32x16 dh[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dh[b] = f32x16{};
+  // add the start-state gradients of the chains that begin under chunk c
+  auto add_children = [&](int c) {
+    for (int x = child_off[c]; x < child_off[c + 1]; ++x) {
+      const float* hp = dhead + (((size_t)child_chains[x] * Hv + hv) * DV + n) * DK;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(hp + 32 * b + 8 * j4 + 4 * lg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dh[b][4 * j4 + e] += v[e];
+        }
+    }
+  };
+  const BStateBuf<DK> sb0{g0, q0, x0}, sb1{g1, q1, x1};
+  auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
+  auto run = [&](const BStateBuf<DK>& sb, int c, float gl) {
+    const size_t hc = (size_t)hv * nc + c;
+    gdn_bwd_state_chunk<DK, DV>(sb, gl, lg, lc, dh, dvlt + (hc * DV + n) * kCh, dot + (hc * DV + n) * kCh,
+                                dvnt + (hc * DV + n) * kCh, dhe + (((size_t)c * Hv + hv) * DV + n) * DK);
+  };
+  add_children(ce - 1);
+  issue(ce - 1, g0, q0, x0);
+  float gl0 = gl_of(ce - 1), gl1 = 0.0f;
+  for (int c = ce - 1; c >= cb; c -= 2) {
+    wait_dma();
+    __syncthreads();
+    if (c - 1 >= cb) {
+      issue(c - 1, g1, q1, x1);
+      gl1 = gl_of(c - 1);
+    }
+    run(sb0, c, gl0);
+    if (c - 1 >= cb) {
+      add_children(c - 1);
+      wait_dma();
+      __syncthreads();
+      if (c - 2 >= cb) {
+        issue(c - 2, g0, q0, x0);
+        gl0 = gl_of(c - 2);
+      }
+      run(sb1, c - 1, gl1);
+      if (c - 2 >= cb) add_children(c - 2);
+    }
+  }
+  // dh is the start-state gradient of the chain's first chunk
+  float* hp = dhead + (((size_t)ch * Hv + hv) * DV + n) * DK;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = dh[b][4 * j4 + e];
+      *reinterpret_cast<f32x4*>(hp + 32 * b + 8 * j4 + 4 * lg) = v;
+    }
+}
+
+// Stage B3, per (chunk, q/k head), 256 threads, looping over the v-heads
+// that read the head. Output blocks of 64 x D results: wave w takes row
+// block w % 2 and column blocks w / 2 + 2 m.
+template <int DK, int DV>
+struct BwdOutLds {
+  bf16 q[kCh][DK + 8];
+  bf16 k[kCh][DK + 8];
+  bf16 dO[kCh][DV + 8];
+  bf16 vnT[DV][kCh + 8];
+  bf16 dvnT[DV][kCh + 8];
+  bf16 hb[DV][DK + 8];  // h0, then dh_end, as [dv][dk]
+  bf16 dS[kCh][kCh + 8];
+  float E[kCh][kCh + 1];  // dP * P, for the decay gradient
+  float gc[kCh], eg[kCh], dec[kCh];
+  float rs[2][kCh], rz[2][kCh];
+  float red[4];
+};
+
+template <int DK, int DV, typename Tio>
+__global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
+                                                          const Tio* __restrict__ dout, const int* __restrict__ cstart,
+                                                          const int* __restrict__ clen, int nc, int H, int Hv,
+                                                          const float* __restrict__ gcw, const bf16* __restrict__ vnt,
+                                                          const bf16* __restrict__ h0w, const bf16* __restrict__ dvnt,
+                                                          const bf16* __restrict__ dhe, Tio* __restrict__ dq,
+                                                          float* __restrict__ dka, float* __restrict__ dgca,
+                                                          bf16* __restrict__ dwt) {
+  __shared__ __attribute__((aligned(16))) BwdOutLds<DK, DV> sm;
+  constexpr int NBK = DK / 64;
+  const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
+  const int t0 = cstart[c], L = clen[c];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int rb = wv & 1;
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int i = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+    *reinterpret_cast<bf16x8*>(&sm.q[i][d0]) = i < L ? load8(q + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+    *reinterpret_cast<bf16x8*>(&sm.k[i][d0]) = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+  }
+  f32x16 aq[NBK], ak[NBK];
+#pragma unroll
+  for (int m = 0; m < NBK; ++m) aq[m] = ak[m] = f32x16{};
+  for (int mv = 0; mv < r; ++mv) {
+    const int hv = hk * r + mv;
+    const size_t hc = (size_t)hv * nc + c;
+    __syncthreads();
+    if (tid < kCh) {
+      const float gv = gcw[hc * kCh + tid], gl = gcw[hc * kCh + kCh - 1];
+      sm.gc[tid] = gv;
+      sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
+      sm.dec[tid] = tid < L ? expf(gl - gv) : 0.0f;
+    }
+    for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
+      const int i = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
+      *reinterpret_cast<bf16x8*>(&sm.dO[i][e0]) =
+          i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
+      const int e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
+      *reinterpret_cast<bf16x8*>(&sm.vnT[e][i0]) = load8(vnt + (hc * DV + e) * kCh + i0);
+      *reinterpret_cast<bf16x8*>(&sm.dvnT[e][i0]) = load8(dvnt + (hc * DV + e) * kCh + i0);
+    }
+    const bf16* h0p = h0w + ((size_t)c * Hv + hv) * DV * DK;
+    for (int idx = tid; idx < DV * (DK / 8); idx += 256) {
+      const int e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+      *reinterpret_cast<bf16x8*>(&sm.hb[e][d0]) = load8(h0p + (size_t)e * DK + d0);
+    }
+    __syncthreads();
+    // S = q k^T and dP = dO vn^T on the three lower 32 x 32 blocks
+    if (wv < 3) {
+      const int qb = wv == 0 ? 0 : 1, kb = wv == 2 ? 1 : 0;
+      f32x16 sv = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a)
+        sv = mfma32x32x16(row8(&sm.q[0][0], DK + 8, 32 * qb + lc, 16 * a + 8 * lg),
+                          row8(&sm.k[0][0], DK + 8, 32 * kb + lc, 16 * a + 8 * lg), sv);
+#pragma unroll
+      for (int a = 0; a < DV / 16; ++a)
+        dp = mfma32x32x16(row8(&sm.dO[0][0], DV + 8, 32 * qb + lc, 16 * a + 8 * lg),
+                          col8(&sm.vnT[0][0], kCh + 8, 32 * kb + lc, 16 * a + 8 * lg), dp);
+      const int j = 32 * kb + lc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = 32 * qb + crow(x, lg);
+        const bool ok = j <= i && i < L;
+        const float gam = ok ? expf(sm.gc[i] - sm.gc[j]) : 0.0f;
+        sm.dS[i][j] = (bf16)(dp[x] * gam);
+        sm.E[i][j] = dp[x] * sv[x] * gam;
+      }
+    } else {
+      for (int idx = lane; idx < 32 * 32; idx += 64) {
+        sm.dS[idx >> 5][32 + (idx & 31)] = (bf16)0.0f;
+        sm.E[idx >> 5][32 + (idx & 31)] = 0.0f;
+      }
+    }
+    __syncthreads();
+    // dq += dS k + e^gc (dO h0^T); dk += dS^T q; dw = -dvn h0^T
+    float pq[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pq[x] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NBK; ++m) {
+      const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+      for (int a = 0; a < 2 * (rb + 1); ++a)
+        aq[m] = mfma32x32x16(row8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                             col8(&sm.k[0][0], DK + 8, col, 16 * a + 8 * lg), aq[m]);
+      for (int a = 2 * rb; a < 4; ++a)
+        ak[m] = mfma32x32x16(col8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                             col8(&sm.q[0][0], DK + 8, col, 16 * a + 8 * lg), ak[m]);
+      f32x16 x = f32x16{}, y = f32x16{};
+#pragma unroll
+      for (int a = 0; a < DV / 16; ++a) {
+        const bf16x8 hB = col8(&sm.hb[0][0], DK + 8, col, 16 * a + 8 * lg);
+        x = mfma32x32x16(row8(&sm.dO[0][0], DV + 8, 32 * rb + lc, 16 * a + 8 * lg), hB, x);
+        y = mfma32x32x16(col8(&sm.dvnT[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), hB, y);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 16; ++i4) {
+        const int row = 32 * rb + crow(i4, lg);
+        const float xv = x[i4] * sm.eg[row];
+        aq[m][i4] += xv;
+        pq[i4] += xv * (float)sm.q[row][col];
+      }
+      bf16* wo = dwt + (hc * DK + col) * kCh + 32 * rb;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(-y[4 * j4 + e]);
+        *reinterpret_cast<bf16x4*>(wo + 8 * j4 + 4 * lg) = o4;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float t = sum32(pq[x]);
+      if (lc == 0) sm.rs[wv >> 1][32 * rb + crow(x, lg)] = t;
+    }
+    __syncthreads();
+    // dh_end replaces h0; s = <dh_end, h0>
+    float sp = 0.0f;
+    const bf16* dhp = dhe + ((size_t)c * Hv + hv) * DV * DK;
+    for (int idx = tid; idx < DV * (DK / 8); idx += 256) {
+      const int e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+      const bf16x8 nv = load8(dhp + (size_t)e * DK + d0);
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&sm.hb[e][d0]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sp += (float)nv[s] * (float)ov[s];
+      *reinterpret_cast<bf16x8*>(&sm.hb[e][d0]) = nv;
+    }
+    sp = sum32(sp);
+    sp += __shfl_xor(sp, 32);
+    if (lane == 0) sm.red[wv] = sp;
+    __syncthreads();
+    // kd-part: x = e^(gl - gc) (vn dh_end^T); dk += x; z_i = sum_d x_id k_id
+    float pz[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pz[x] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NBK; ++m) {
+      const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+      f32x16 x = f32x16{};
+#pragma unroll
+      for (int a = 0; a < DV / 16; ++a)
+        x = mfma32x32x16(col8(&sm.vnT[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                         col8(&sm.hb[0][0], DK + 8, col, 16 * a + 8 * lg), x);
+#pragma unroll
+      for (int i4 = 0; i4 < 16; ++i4) {
+        const int row = 32 * rb + crow(i4, lg);
+        const float xv = x[i4] * sm.dec[row];
+        ak[m][i4] += xv;
+        pz[i4] += xv * (float)sm.k[row][col];
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float t = sum32(pz[x]);
+      if (lc == 0) sm.rz[wv >> 1][32 * rb + crow(x, lg)] = t;
+    }
+    __syncthreads();
+    if (tid < kCh) {
+      const int i = tid;
+      float r1 = 0.0f, c1 = 0.0f;
+      for (int j = 0; j < kCh; ++j) {
+        r1 += sm.E[i][j];
+        c1 += sm.E[j][i];
+      }
+      const float z = sm.rz[0][i] + sm.rz[1][i];
+      float d = r1 - c1 + sm.rs[0][i] + sm.rs[1][i] - z;
+      float zs = z;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) zs += __shfl_xor(zs, o);
+      if (i == L - 1) {
+        const float sdot = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+        d += zs + expf(sm.gc[kCh - 1]) * sdot;
+      }
+      dgca[hc * kCh + i] = d;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NBK; ++m) {
+    const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+#pragma unroll
+    for (int i4 = 0; i4 < 16; ++i4) {
+      const int row = 32 * rb + crow(i4, lg);
+      if (row < L) dq[((size_t)(t0 + row) * H + hk) * DK + col] = from_f32<Tio>(aq[m][i4]);
+      dka[(((size_t)hk * nc + c) * kCh + row) * DK + col] = ak[m][i4];
+    }
+  }
+}
+
+template <int DK, int DV>
+struct BwdWyLds {
+  bf16 k[kCh][DK + 8];
+  float Kg[kCh][kCh + 4];  // (k_i . k_j) exp(gc_i - gc_j) on j < i; then G
+  float Ts[kCh][kCh + 4];  // T; then dM * Kg
+  bf16 dvnT[DV][kCh + 8];  // dvn^T, then dbv^T
+  bf16 dwT[DK][kCh + 8];   // dw^T, then dbk^T
+  bf16 u[kCh][DV + 8];
+  bf16 w[kCh][DK + 8];     // swap23 column order, as stored by the forward
+  float pscr[3][16][17];
+  float gc[kCh], bs[kCh], eg[kCh];
+  float r1[2][kCh], r2[2][kCh];
+};
+
+template <int DK, int DV, typename Tio>
+__global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
+    const Tio* __restrict__ k, const Tio* __restrict__ v, const float* __restrict__ beta,
+    const int* __restrict__ cstart, const int* __restrict__ clen, int nc, int H, int Hv,
+    const float* __restrict__ gcw, const float* __restrict__ u, const bf16* __restrict__ wp,
+    const bf16* __restrict__ dvnt, const bf16* __restrict__ dwt, const float* __restrict__ dka,
+    const float* __restrict__ dgca, Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dg,
+    float* __restrict__ dbeta) {
+  __shared__ __attribute__((aligned(16))) BwdWyLds<DK, DV> sm;
+  constexpr int NBK = DK / 64, NBV = DV / 64;
+  const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
+  const int t0 = cstart[c], L = clen[c];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int rb = wv & 1;
+  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+    const int i = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+    *reinterpret_cast<bf16x8*>(&sm.k[i][d0]) = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+  }
+  f32x16 ak[NBK];
+#pragma unroll
+  for (int m = 0; m < NBK; ++m) ak[m] = f32x16{};
+  for (int mv = 0; mv < r; ++mv) {
+    const int hv = hk * r + mv;
+    const size_t hc = (size_t)hv * nc + c;
+    __syncthreads();
+    if (tid < kCh) {
+      const float gv = gcw[hc * kCh + tid];
+      sm.gc[tid] = gv;
+      sm.bs[tid] = tid < L ? beta[(size_t)(t0 + tid) * Hv + hv] : 0.0f;
+      sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
+    }
+    for (int idx = tid; idx < DV * (kCh / 8); idx += 256) {
+      const int e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
+      *reinterpret_cast<bf16x8*>(&sm.dvnT[e][i0]) = load8(dvnt + (hc * DV + e) * kCh + i0);
+    }
+    for (int idx = tid; idx < DK * (kCh / 8); idx += 256) {
+      const int d = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
+      *reinterpret_cast<bf16x8*>(&sm.dwT[d][i0]) = load8(dwt + (hc * DK + d) * kCh + i0);
+    }
+    for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
+      const int i = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
+      *reinterpret_cast<bf16x8*>(&sm.u[i][e0]) = load8(u + (hc * kCh + i) * DV + e0);
+    }
+    for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
+      const int i = idx / (DK / 8), p0 = 8 * (idx % (DK / 8));
+      *reinterpret_cast<bf16x8*>(&sm.w[i][p0]) = load8(wp + (hc * kCh + i) * DK + p0);
+    }
+    __syncthreads();
+    // Kg on the three lower blocks; the upper block stays zero
+    if (wv < 3) {
+      const int mb = wv == 0 ? 0 : 1, nb = wv == 2 ? 1 : 0;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a)
+        acc = mfma32x32x16(row8(&sm.k[0][0], DK + 8, 32 * mb + lc, 16 * a + 8 * lg),
+                           row8(&sm.k[0][0], DK + 8, 32 * nb + lc, 16 * a + 8 * lg), acc);
+      const int j = 32 * nb + lc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = 32 * mb + crow(x, lg);
+        sm.Kg[i][j] = j < i ? acc[x] * expf(sm.gc[i] - sm.gc[j]) : 0.0f;
+      }
+    } else {
+      for (int idx = lane; idx < 32 * 32; idx += 64) sm.Kg[idx >> 5][32 + (idx & 31)] = 0.0f;
+    }
+    __syncthreads();
+    unit_lower_inverse([&](int a, int b) { return sm.bs[a] * sm.Kg[a][b]; }, sm.Ts, sm.pscr, tid);
+    // dbv = T^T dvn, dbk = T^T dw (T[i][j] = 0 for i < j: rows j of block rb
+    // need i >= 32 rb)
+    float pv[16], pk[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pv[x] = pk[x] = 0.0f;
+    f32x16 bv[NBV], bk[NBK];
+#pragma unroll
+    for (int m = 0; m < NBV; ++m) {
+      const int e = 32 * ((wv >> 1) + 2 * m) + lc;
+      f32x16 acc = f32x16{};
+      for (int a = 2 * rb; a < 4; ++a)
+        acc = mfma32x32x16(col8f(&sm.Ts[0][0], kCh + 4, 32 * rb + lc, 16 * a + 8 * lg),
+                           row8(&sm.dvnT[0][0], kCh + 8, e, 16 * a + 8 * lg), acc);
+      bv[m] = acc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = 32 * rb + crow(x, lg);
+        if (j < L) {
+          const size_t off = ((size_t)(t0 + j) * Hv + hv) * DV + e;
+          dv[off] = from_f32<Tio>(sm.bs[j] * acc[x]);
+          pv[x] += acc[x] * (float)v[off];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NBK; ++m) {
+      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+      f32x16 acc = f32x16{};
+      for (int a = 2 * rb; a < 4; ++a)
+        acc = mfma32x32x16(col8f(&sm.Ts[0][0], kCh + 4, 32 * rb + lc, 16 * a + 8 * lg),
+                           row8(&sm.dwT[0][0], kCh + 8, d, 16 * a + 8 * lg), acc);
+      bk[m] = acc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = 32 * rb + crow(x, lg);
+        ak[m][x] += sm.bs[j] * sm.eg[j] * acc[x];
+        pk[x] += acc[x] * (float)sm.k[j][d];
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float a1 = sum32(pv[x]), a2 = sum32(pk[x]);
+      if (lc == 0) {
+        sm.r1[wv >> 1][32 * rb + crow(x, lg)] = a1;
+        sm.r2[wv >> 1][32 * rb + crow(x, lg)] = a2;
+      }
+    }
+    __syncthreads();
+    // dbv^T and dbk^T replace dvn^T and dw^T
+#pragma unroll
+    for (int m = 0; m < NBV; ++m) {
+      const int e = 32 * ((wv >> 1) + 2 * m) + lc;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = (bf16)bv[m][4 * j4 + x];
+        *reinterpret_cast<bf16x4*>(&sm.dvnT[e][32 * rb + 8 * j4 + 4 * lg]) = o4;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NBK; ++m) {
+      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = (bf16)bk[m][4 * j4 + x];
+        *reinterpret_cast<bf16x4*>(&sm.dwT[d][32 * rb + 8 * j4 + 4 * lg]) = o4;
+      }
+    }
+    __syncthreads();
+    // dM = -(dbv u^T + dbk w^T) on the lower blocks; a = dM * Kg replaces T,
+    // G = beta_i dM exp(gc_i - gc_j) replaces Kg (each thread rewrites only
+    // the elements it read)
+    if (wv < 3) {
+      const int mb = wv == 0 ? 0 : 1, nb = wv == 2 ? 1 : 0;
+      const int i0 = 32 * mb + lc, j0 = 32 * nb + lc;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int a = 0; a < DV / 16; ++a)
+        acc = mfma32x32x16(col8(&sm.dvnT[0][0], kCh + 8, i0, 16 * a + 8 * lg),
+                           row8(&sm.u[0][0], DV + 8, j0, 16 * a + 8 * lg), acc);
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a) {
+        bf16x8 A;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) A[s] = sm.dwT[swap23(16 * a + 8 * lg + s)][i0];
+        acc = mfma32x32x16(A, row8(&sm.w[0][0], DK + 8, j0, 16 * a + 8 * lg), acc);
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = 32 * mb + crow(x, lg);
+        const bool ok = j0 < i && i < L;
+        const float dm = ok ? -acc[x] : 0.0f;
+        const float kg = sm.Kg[i][j0];
+        sm.Ts[i][j0] = dm * kg;
+        sm.Kg[i][j0] = ok ? sm.bs[i] * dm * expf(sm.gc[i] - sm.gc[j0]) : 0.0f;
+      }
+    } else {
+      for (int idx = lane; idx < 32 * 32; idx += 64) sm.Ts[idx >> 5][32 + (idx & 31)] = 0.0f;
+    }
+    __syncthreads();
+    // dk += (G + G^T) k
+#pragma unroll
+    for (int m = 0; m < NBK; ++m) {
+      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+      const int i = 32 * rb + lc;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x8 A;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int j = 16 * a + 8 * lg + s;
+          A[s] = (bf16)(sm.Kg[i][j] + sm.Kg[j][i]);
+        }
+        ak[m] = mfma32x32x16(A, col8(&sm.k[0][0], DK + 8, d, 16 * a + 8 * lg), ak[m]);
+      }
+    }
+    if (tid < kCh) {
+      const int i = tid;
+      float ra = 0.0f, cb = 0.0f;
+      for (int j = 0; j < kCh; ++j) {
+        ra += sm.Ts[i][j];
+        cb += sm.bs[j] * sm.Ts[j][i];
+      }
+      const float zk = sm.r2[0][i] + sm.r2[1][i];
+      const float db = (sm.r1[0][i] + sm.r1[1][i]) + sm.eg[i] * zk + ra;
+      float x = i < L ? dgca[hc * kCh + i] + sm.bs[i] * sm.eg[i] * zk + sm.bs[i] * ra - cb : 0.0f;
+      // dg_t = sum of dgc_i over i >= t in the chunk
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_down(x, o);
+        if (i + o < 64) x += y;
+      }
+      if (i < L) {
+        dg[(size_t)(t0 + i) * Hv + hv] = x;
+        dbeta[(size_t)(t0 + i) * Hv + hv] = db;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NBK; ++m) {
+    const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int row = 32 * rb + crow(x, lg);
+      if (row < L)
+        dk[((size_t)(t0 + row) * H + hk) * DK + d] =
+            from_f32<Tio>(ak[m][x] + dka[(((size_t)hk * nc + c) * kCh + row) * DK + d]);
+    }
+  }
+}
+
 struct PlanView {
   int nc, nch, nl, chunk, T;
-  int off_cstart, off_clen, off_cpar, off_chain, off_lchains, off_loff;
+  int off_cstart, off_clen, off_cpar, off_chain, off_lchains, off_loff, off_coff, off_cch;
 };
 
 bool plan_view(const int32_t* ph, PlanView* v) {
@@ -869,6 +1701,8 @@ bool plan_view(const int32_t* ph, PlanView* v) {
   v->off_chain = v->off_cpar + v->nc;
   v->off_lchains = v->off_chain + v->nch + 1;
   v->off_loff = v->off_lchains + v->nch;
+  v->off_coff = v->off_loff + v->nl + 1;
+  v->off_cch = v->off_coff + v->nc + 1;
   return true;
 }
 
@@ -919,6 +1753,74 @@ int gdn_dispatch(int dk, int dv, const void* q, const void* k, const void* v, co
   else
     gdn_launch<64, 64, Tio>(q, k, v, g, beta, H, Hv, plan, ph, pv, o, ws, L, st);
   return TA_OK;
+}
+
+template <int DK, int DV, typename Tio>
+void gdn_bwd_launch(const void* q, const void* k, const void* v, const float* beta, const void* dout, int H, int Hv,
+                    const int32_t* plan, const int32_t* ph, const PlanView& pv, void* dq, void* dk, void* dv,
+                    float* dg, float* dbeta, char* ws, const GdnLayout& F, const GdnBwdLayout& B, hipStream_t st) {
+  const float* gcw = reinterpret_cast<const float*>(ws + F.gc);
+  const float* u = reinterpret_cast<const float*>(ws + F.u);
+  const bf16* wp = reinterpret_cast<const bf16*>(ws + F.w);
+  const bf16* vnt = reinterpret_cast<const bf16*>(ws + F.vnt);
+  const bf16* h0w = reinterpret_cast<const bf16*>(ws + F.h0);
+  float* dvlt = reinterpret_cast<float*>(ws + B.dvlt);
+  bf16* kgl = reinterpret_cast<bf16*>(ws + B.kgl);
+  bf16* qgt = reinterpret_cast<bf16*>(ws + B.qgt);
+  bf16* wt = reinterpret_cast<bf16*>(ws + B.wt);
+  bf16* dot = reinterpret_cast<bf16*>(ws + B.dot);
+  bf16* dvnt = reinterpret_cast<bf16*>(ws + B.dvnt);
+  bf16* dhe = reinterpret_cast<bf16*>(ws + B.dhe);
+  bf16* dwt = reinterpret_cast<bf16*>(ws + B.dwt);
+  float* dgca = reinterpret_cast<float*>(ws + B.dgca);
+  float* dka = reinterpret_cast<float*>(ws + B.dka);
+  float* dhead = reinterpret_cast<float*>(ws + B.dhead);
+  const int* cstart = plan + pv.off_cstart;
+  const int* clen = plan + pv.off_clen;
+  const Tio* qq = static_cast<const Tio*>(q);
+  const Tio* kk = static_cast<const Tio*>(k);
+  const Tio* dd = static_cast<const Tio*>(dout);
+  {
+    ProfScope ps("gdn_bwd_prep", st);
+    hipLaunchKernelGGL((gdn_bwd_prep_kernel<DK, DV, Tio>), dim3(pv.nc, Hv), dim3(256), 0, st, qq, kk, dd, cstart, clen,
+                       pv.nc, H, Hv, gcw, wp, dvlt, kgl, qgt, wt, dot);
+  }
+  {
+    ProfScope ps("gdn_bwd_state", st);
+    const int32_t* loff = ph + pv.off_loff;
+    for (int l = pv.nl - 1; l >= 0; --l) {
+      const int n = loff[l + 1] - loff[l];
+      hipLaunchKernelGGL((gdn_bwd_state_kernel<DK, DV>), dim3(n, Hv), dim3(64 * (DV / 32)), 0, st,
+                         plan + pv.off_lchains, loff[l], plan + pv.off_chain, plan + pv.off_coff, plan + pv.off_cch,
+                         pv.nc, Hv, gcw, dvlt, kgl, qgt, wt, dot, dvnt, dhe, dhead);
+    }
+  }
+  {
+    ProfScope ps("gdn_bwd_out", st);
+    hipLaunchKernelGGL((gdn_bwd_out_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(256), 0, st, qq, kk, dd, cstart, clen,
+                       pv.nc, H, Hv, gcw, vnt, h0w, dvnt, dhe, static_cast<Tio*>(dq), dka, dgca, dwt);
+  }
+  {
+    ProfScope ps("gdn_bwd_wy", st);
+    hipLaunchKernelGGL((gdn_bwd_wy_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(256), 0, st, kk,
+                       static_cast<const Tio*>(v), beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, dvnt, dwt, dka, dgca,
+                       static_cast<Tio*>(dk), static_cast<Tio*>(dv), dg, dbeta);
+  }
+}
+
+template <typename Tio>
+void gdn_bwd_dispatch(int dk_, int dv_, const void* q, const void* k, const void* v, const float* beta,
+                      const void* dout, int H, int Hv, const int32_t* plan, const int32_t* ph, const PlanView& pv,
+                      void* dq, void* dk, void* dv, float* dg, float* dbeta, char* ws, const GdnLayout& F,
+                      const GdnBwdLayout& B, hipStream_t st) {
+  if (dk_ == 128 && dv_ == 128)
+    gdn_bwd_launch<128, 128, Tio>(q, k, v, beta, dout, H, Hv, plan, ph, pv, dq, dk, dv, dg, dbeta, ws, F, B, st);
+  else if (dk_ == 128 && dv_ == 64)
+    gdn_bwd_launch<128, 64, Tio>(q, k, v, beta, dout, H, Hv, plan, ph, pv, dq, dk, dv, dg, dbeta, ws, F, B, st);
+  else if (dk_ == 64 && dv_ == 128)
+    gdn_bwd_launch<64, 128, Tio>(q, k, v, beta, dout, H, Hv, plan, ph, pv, dq, dk, dv, dg, dbeta, ws, F, B, st);
+  else
+    gdn_bwd_launch<64, 64, Tio>(q, k, v, beta, dout, H, Hv, plan, ph, pv, dq, dk, dv, dg, dbeta, ws, F, B, st);
 }
 
 bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
@@ -1072,5 +1974,49 @@ extern "C" int tree_gdn_fwd(const void* q, const void* k, const void* v, ta_dtyp
     gdn_dispatch<float>(dk, dv, q, k, v, g, beta, H, Hv, plan, plan_host, pv, o, ws, L, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TA_EHIP, "tree_gdn_fwd: kernel launch failed: %s", hipGetErrorString(e));
+  return TA_OK;
+}
+
+extern "C" size_t tree_gdn_bwd_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, int32_t n_chunks,
+                                               int32_t n_chains) {
+  if (H < 1 || Hv < 1 || dk < 1 || dv < 1 || n_chunks < 1 || n_chains < 1 || n_chains > n_chunks) return 0;
+  return gdn_bwd_layout(H, Hv, dk, dv, n_chunks, n_chains).total;
+}
+
+extern "C" int tree_gdn_bwd(const void* q, const void* k, const void* v, ta_dtype dt, const float* g,
+                            const float* beta, const void* dout, int32_t T, int32_t H, int32_t Hv, int32_t dk,
+                            int32_t dv, const int32_t* plan, const int32_t* plan_host, void* dq, void* dk_out,
+                            void* dv_out, float* dg, float* dbeta, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!q || !k || !v || !g || !beta || !dout || !plan || !plan_host || !dq || !dk_out || !dv_out || !dg || !dbeta ||
+      !workspace)
+    return fail(TA_EINVAL, "tree_gdn_bwd: NULL pointer argument");
+  if (T < 1 || H < 1 || Hv < H || Hv % H != 0)
+    return fail(TA_EINVAL, "tree_gdn_bwd: need T >= 1, H >= 1 and Hv a multiple of H (T=%d H=%d Hv=%d)", T, H, Hv);
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(TA_EUNSUPPORTED, "tree_gdn_bwd: dk and dv must be 64 or 128 (dk=%d dv=%d)", dk, dv);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "tree_gdn_bwd: bad dtype %d", (int)dt);
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(dout) || !al16(dq) || !al16(dk_out) || !al16(dv_out) || !al16(dg) ||
+      !al16(dbeta))
+    return fail(TA_EINVAL, "tree_gdn_bwd: tensors must be 16-byte aligned");
+  PlanView pv;
+  if (!plan_view(plan_host, &pv)) return fail(TA_EINVAL, "tree_gdn_bwd: plan header is not a tree_gdn_plan output");
+  if (pv.T != T) return fail(TA_EINVAL, "tree_gdn_bwd: the plan covers %d tokens, T = %d", pv.T, T);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TA_EINVAL, "tree_gdn_bwd: workspace must be 256-byte aligned");
+  const GdnLayout F = gdn_layout(H, Hv, dk, dv, pv.nc);
+  const GdnBwdLayout B = gdn_bwd_layout(H, Hv, dk, dv, pv.nc, pv.nch);
+  if (ws_bytes < B.total)
+    return fail(TA_EINVAL, "tree_gdn_bwd: workspace too small (%zu < %zu bytes)", ws_bytes, B.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (dt == TA_BF16)
+    gdn_bwd_dispatch<bf16>(dk, dv, q, k, v, beta, dout, H, Hv, plan, plan_host, pv, dq, dk_out, dv_out, dg, dbeta,
+                           ws, F, B, st);
+  else
+    gdn_bwd_dispatch<float>(dk, dv, q, k, v, beta, dout, H, Hv, plan, plan_host, pv, dq, dk_out, dv_out, dg, dbeta,
+                            ws, F, B, st);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TA_EHIP, "tree_gdn_bwd: kernel launch failed: %s", hipGetErrorString(e));
   return TA_OK;
 }

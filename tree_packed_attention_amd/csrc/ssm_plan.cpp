@@ -14,7 +14,11 @@
 //
 // Blob (int32): header [n_chunks, n_chains, n_levels, chunk, T, 0, 0, 0],
 // then chunk_start[n_chunks], chunk_len[n_chunks], chunk_parent[n_chunks],
-// chain_begin[n_chains + 1], level_chains[n_chains], level_off[n_levels + 1].
+// chain_begin[n_chains + 1], level_chains[n_chains], level_off[n_levels + 1],
+// child_off[n_chunks + 1], child_chains[n_chains]: the chains that start
+// under chunk c are child_chains[child_off[c] .. child_off[c + 1]), in
+// increasing order (the backward sums their start-state gradients into c's
+// end-state gradient in that order).
 #include <cstdint>
 #include <vector>
 
@@ -69,7 +73,21 @@ extern "C" int tree_gdn_plan(const int32_t* node_start, const int32_t* node_end,
     std::vector<int32_t> fill(level_off.begin(), level_off.end() - 1);
     for (int32_t ch = 0; ch < nch; ++ch) level_chains[fill[level[ch]]++] = ch;
   }
-  const int64_t need = 8 + 3ll * nc + (nch + 1) + nch + (nl + 1);
+  std::vector<int32_t> child_off(nc + 1, 0), child_chains;
+  for (int32_t ch = 0; ch < nch; ++ch) {
+    const int32_t p = cpar[chain_begin[ch]];
+    if (p >= 0) ++child_off[p + 1];
+  }
+  for (int32_t c = 0; c < nc; ++c) child_off[c + 1] += child_off[c];
+  child_chains.assign(nch, -1);
+  {
+    std::vector<int32_t> fill(child_off.begin(), child_off.end() - 1);
+    for (int32_t ch = 0; ch < nch; ++ch) {
+      const int32_t p = cpar[chain_begin[ch]];
+      if (p >= 0) child_chains[fill[p]++] = ch;
+    }
+  }
+  const int64_t need = 8 + 3ll * nc + (nch + 1) + nch + (nl + 1) + (nc + 1) + nch;
   sizes->n_chunks = nc;
   sizes->n_chains = nch;
   sizes->n_levels = nl;
@@ -85,5 +103,7 @@ extern "C" int tree_gdn_plan(const int32_t* node_start, const int32_t* node_end,
   for (int32_t v : chain_begin) *o++ = v;
   for (int32_t v : level_chains) *o++ = v;
   for (int32_t v : level_off) *o++ = v;
+  for (int32_t v : child_off) *o++ = v;
+  for (int32_t v : child_chains) *o++ = v;
   return TA_OK;
 }

@@ -277,6 +277,15 @@ def gdn_inputs(T, H, Hv, dk, dv, dtype, seed, device="cpu"):
     return (q.to(dt).to(device), k.to(dt).to(device), v.to(dt).to(device), g.to(device), beta.to(device))
 
 
+def gdn_dout(T, Hv, dv, dtype, seed, device="cpu"):
+    """Output gradient for the gated delta rule backward: N(0, 1) [T, Hv, dv]."""
+    import torch
+
+    gen = torch.Generator().manual_seed(seed + 5500)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return torch.randn(T, Hv, dv, generator=gen).to(dt).to(device)
+
+
 def conv_inputs(T, C, K, dtype, seed, device="cpu"):
     """Tree conv inputs: x and dy N(0, 1) [T, C], weight N(0, 0.25) [C, K],
     bias N(0, 0.01) [C]."""
