@@ -43,6 +43,7 @@
 //   kd  [Hv][nc][dk][64] bf16   (k^T exp(gc_last - gc), zero past the length)
 //   vnt [Hv][nc][dv][64] bf16
 //   h0  [nc][Hv][dv][dk] bf16   (start state of each chunk, transposed)
+//   tt  [Hv][nc][64][64] bf16   ((I + M)^-1 transposed, for the backward)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* __res
 constexpr int kCh = 64;  // chunk rows (the plan's chunk size is at most this)
 
 struct GdnLayout {
-  size_t gc, u, w, kt, vnt, h0, total;
+  size_t gc, u, w, kt, vnt, h0, tt, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -431,6 +432,8 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
   o = al256(o + (size_t)Hv * nc * dv * kCh * 2);
   L.h0 = o;
   o = al256(o + (size_t)nc * Hv * dv * dk * 2);
+  L.tt = o;
+  o = al256(o + (size_t)Hv * nc * kCh * kCh * 2);
   L.total = o;
   return L;
 }
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
                                                        const int* __restrict__ cstart, const int* __restrict__ clen,
                                                        int nc, int H, int Hv, float* __restrict__ gcw,
                                                        float* __restrict__ u, bf16* __restrict__ wp,
-                                                       bf16* __restrict__ kt) {
+                                                       bf16* __restrict__ kt, bf16* __restrict__ tt) {
   typedef PrepLds<DK, DV> PL;
   constexpr int NCOL = PL::NCOL;
   __shared__ float gcs[kCh];
@@ -622,6 +625,12 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
   }
   __syncthreads();
   unit_lower_inverse([&](int r, int q) { return Ms[r][q]; }, ts, pscr, tid);
+  // T^T for the backward (bf16, the precision its products read T in)
+  {
+    bf16* tto = tt + ((size_t)hv * nc + c) * kCh * kCh;
+#pragma unroll 4
+    for (int idx = tid; idx < kCh * kCh; idx += 256) tto[idx] = (bf16)ts[idx % kCh][idx / kCh];
+  }
   // [u | w] = T rt^T: 32x32 output blocks (2 row blocks x NCOL/32 column
   // blocks), column blocks dealt to the waves in turn
   constexpr int NCB = NCOL / 32;
@@ -952,6 +961,31 @@ __device__ __forceinline__ bf16x8 col8f(const float* X, int ld, int c, int k0) {
   return v;
 }
 
+// A [R][C] row-major tile (global row stride gs, rows past rows_valid read
+// as zero) bound for LDS rows of stride ls: issue() starts all of this
+// thread's loads, commit() stores them, so a workgroup keeps every load of a
+// tile (and of the tiles issued with it) in flight at once.
+template <int R, int C, typename Tsrc>
+struct TileLoad {
+  static_assert((R * (C / 8)) % 256 == 0, "whole rounds of 256 threads");
+  static constexpr int N = R * (C / 8) / 256;
+  bf16x8 x[N];
+  __device__ __forceinline__ void issue(const Tsrc* __restrict__ g, size_t gs, int tid, int rows_valid) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int idx = tid + 256 * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
+      x[it] = r < rows_valid ? load8(g + r * gs + c) : zero8();
+    }
+  }
+  __device__ __forceinline__ void commit(bf16* l, int ls, int tid) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int idx = tid + 256 * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
+      *reinterpret_cast<bf16x8*>(l + r * ls + c) = x[it];
+    }
+  }
+};
+
 // Stage B1, per (chunk, v-head), 256 threads: dvl^T[e][j] = sum_i dO[i][e]
 // P[i][j] (wave: key block w % 2, dv blocks from w / 2), plus the state
 // pass operands.
@@ -981,8 +1015,9 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
   __syncthreads();
   // q and k rows into LDS; (q e^gc)^T out. Lanes take consecutive rows, so
   // each transposed store covers 128 contiguous bytes.
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int i = idx % kCh, d0 = 8 * (idx / kCh);
+#pragma unroll
+  for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, i = idx % kCh, d0 = 8 * (idx / kCh);
     const bf16x8 qv = i < L ? load8(q + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
     const bf16x8 kv = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
     *reinterpret_cast<bf16x8*>(&qs[i][d0]) = qv;
@@ -991,15 +1026,17 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
     for (int s = 0; s < 8; ++s) qgt[(hc * DK + d0 + s) * kCh + i] = (bf16)((float)qv[s] * egs[i]);
   }
   // w^T (w is stored with swap23 columns: position p holds column swap23(p))
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int i = idx % kCh, p0 = 8 * (idx / kCh);
+#pragma unroll
+  for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, i = idx % kCh, p0 = 8 * (idx / kCh);
     const bf16x8 wv8 = load8(wp + (hc * kCh + i) * DK + p0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) wt[(hc * DK + swap23(p0 + s)) * kCh + i] = wv8[s];
   }
   // dO^T, in LDS and out
-  for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
-    const int i = idx % kCh, e0 = 8 * (idx / kCh);
+#pragma unroll
+  for (int it = 0; it < kCh * (DV / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, i = idx % kCh, e0 = 8 * (idx / kCh);
     const bf16x8 d8 = i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -1009,8 +1046,9 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
   }
   __syncthreads();
   // kd rows with swap23 columns (the A operand of dvn += kd dh)
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int i = idx / (DK / 8), p0 = 8 * (idx % (DK / 8));
+#pragma unroll
+  for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, i = idx / (DK / 8), p0 = 8 * (idx % (DK / 8));
     bf16x8 o8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) o8[s] = (bf16)((float)ks[i][swap23(p0 + s)] * decs[i]);
@@ -1273,10 +1311,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
   const int t0 = cstart[c], L = clen[c];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int rb = wv & 1;
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int i = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
-    *reinterpret_cast<bf16x8*>(&sm.q[i][d0]) = i < L ? load8(q + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
-    *reinterpret_cast<bf16x8*>(&sm.k[i][d0]) = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+  {
+    TileLoad<kCh, DK, Tio> lq, lk;
+    lq.issue(q + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
+    lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
+    lq.commit(&sm.q[0][0], DK + 8, tid);
+    lk.commit(&sm.k[0][0], DK + 8, tid);
   }
   f32x16 aq[NBK], ak[NBK];
 #pragma unroll
@@ -1291,19 +1331,18 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
       sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
       sm.dec[tid] = tid < L ? expf(gl - gv) : 0.0f;
     }
-    for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
-      const int i = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
-      *reinterpret_cast<bf16x8*>(&sm.dO[i][e0]) =
-          i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
-      const int e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
-      *reinterpret_cast<bf16x8*>(&sm.vnT[e][i0]) = load8(vnt + (hc * DV + e) * kCh + i0);
-      *reinterpret_cast<bf16x8*>(&sm.dvnT[e][i0]) = load8(dvnt + (hc * DV + e) * kCh + i0);
-    }
-    const bf16* h0p = h0w + ((size_t)c * Hv + hv) * DV * DK;
-    for (int idx = tid; idx < DV * (DK / 8); idx += 256) {
-      const int e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
-      *reinterpret_cast<bf16x8*>(&sm.hb[e][d0]) = load8(h0p + (size_t)e * DK + d0);
-    }
+    TileLoad<kCh, DV, Tio> ldo;
+    TileLoad<DV, kCh, bf16> lvn, ldvn;
+    TileLoad<DV, DK, bf16> lh0, ldh;
+    ldo.issue(dout + ((size_t)t0 * Hv + hv) * DV, (size_t)Hv * DV, tid, L);
+    lvn.issue(vnt + hc * DV * kCh, kCh, tid, DV);
+    ldvn.issue(dvnt + hc * DV * kCh, kCh, tid, DV);
+    lh0.issue(h0w + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
+    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);  // committed once h0 is no longer read
+    ldo.commit(&sm.dO[0][0], DV + 8, tid);
+    lvn.commit(&sm.vnT[0][0], kCh + 8, tid);
+    ldvn.commit(&sm.dvnT[0][0], kCh + 8, tid);
+    lh0.commit(&sm.hb[0][0], DK + 8, tid);
     __syncthreads();
     // S = q k^T and dP = dO vn^T on the three lower 32 x 32 blocks
     if (wv < 3) {
@@ -1375,17 +1414,16 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
       if (lc == 0) sm.rs[wv >> 1][32 * rb + crow(x, lg)] = t;
     }
     __syncthreads();
-    // dh_end replaces h0; s = <dh_end, h0>
+    // dh_end replaces h0 (each thread rewrites the elements it reads); s = <dh_end, h0>
     float sp = 0.0f;
-    const bf16* dhp = dhe + ((size_t)c * Hv + hv) * DV * DK;
-    for (int idx = tid; idx < DV * (DK / 8); idx += 256) {
-      const int e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
-      const bf16x8 nv = load8(dhp + (size_t)e * DK + d0);
+#pragma unroll
+    for (int it = 0; it < ldh.N; ++it) {
+      const int idx = tid + 256 * it, e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
       const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&sm.hb[e][d0]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sp += (float)nv[s] * (float)ov[s];
-      *reinterpret_cast<bf16x8*>(&sm.hb[e][d0]) = nv;
+      for (int s = 0; s < 8; ++s) sp += (float)ldh.x[it][s] * (float)ov[s];
     }
+    ldh.commit(&sm.hb[0][0], DK + 8, tid);
     sp = sum32(sp);
     sp += __shfl_xor(sp, 32);
     if (lane == 0) sm.red[wv] = sp;
@@ -1450,34 +1488,38 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
 template <int DK, int DV>
 struct BwdWyLds {
   bf16 k[kCh][DK + 8];
-  float Kg[kCh][kCh + 4];  // (k_i . k_j) exp(gc_i - gc_j) on j < i; then G
-  float Ts[kCh][kCh + 4];  // T; then dM * Kg
-  bf16 dvnT[DV][kCh + 8];  // dvn^T, then dbv^T
-  bf16 dwT[DK][kCh + 8];   // dw^T, then dbk^T
-  bf16 u[kCh][DV + 8];
-  bf16 w[kCh][DK + 8];     // swap23 column order, as stored by the forward
-  float pscr[3][16][17];
+  bf16 tt[kCh][kCh + 8];    // T^T
+  bf16 gs[kCh][kCh + 8];    // G + G^T
+  bf16 dbvT[DV][kCh + 8];
+  bf16 dbkT[DK][kCh + 8];
   float gc[kCh], bs[kCh], eg[kCh];
-  float r1[2][kCh], r2[2][kCh];
+  float r1[2][kCh], r2[2][kCh];  // row sums v.dbv, k.dbk (by column half)
+  float ra[3][kCh], cs[3][kCh];  // row sums of a = dM Kg, column sums of beta a (by lower block)
 };
+
+// The three lower 32 x 32 blocks of a 64 x 64 chunk matrix, one per wave
+// 0-2: (row block, column block).
+__device__ __forceinline__ int lower_mb(int wv) { return wv == 0 ? 0 : 1; }
+__device__ __forceinline__ int lower_nb(int wv) { return wv == 2 ? 1 : 0; }
 
 template <int DK, int DV, typename Tio>
 __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     const Tio* __restrict__ k, const Tio* __restrict__ v, const float* __restrict__ beta,
     const int* __restrict__ cstart, const int* __restrict__ clen, int nc, int H, int Hv,
     const float* __restrict__ gcw, const float* __restrict__ u, const bf16* __restrict__ wp,
-    const bf16* __restrict__ dvnt, const bf16* __restrict__ dwt, const float* __restrict__ dka,
-    const float* __restrict__ dgca, Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dg,
-    float* __restrict__ dbeta) {
+    const bf16* __restrict__ ttw, const bf16* __restrict__ dvnt, const bf16* __restrict__ dwt,
+    const float* __restrict__ dka, const float* __restrict__ dgca, Tio* __restrict__ dk, Tio* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
   __shared__ __attribute__((aligned(16))) BwdWyLds<DK, DV> sm;
   constexpr int NBK = DK / 64, NBV = DV / 64;
   const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
   const int t0 = cstart[c], L = clen[c];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const int rb = wv & 1;
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int i = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
-    *reinterpret_cast<bf16x8*>(&sm.k[i][d0]) = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
+  {
+    TileLoad<kCh, DK, Tio> lk;
+    lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
+    lk.commit(&sm.k[0][0], DK + 8, tid);
   }
   f32x16 ak[NBK];
 #pragma unroll
@@ -1486,85 +1528,85 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     const int hv = hk * r + mv;
     const size_t hc = (size_t)hv * nc + c;
     __syncthreads();
-    if (tid < kCh) {
-      const float gv = gcw[hc * kCh + tid];
-      sm.gc[tid] = gv;
-      sm.bs[tid] = tid < L ? beta[(size_t)(t0 + tid) * Hv + hv] : 0.0f;
-      sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
-    }
-    for (int idx = tid; idx < DV * (kCh / 8); idx += 256) {
-      const int e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
-      *reinterpret_cast<bf16x8*>(&sm.dvnT[e][i0]) = load8(dvnt + (hc * DV + e) * kCh + i0);
-    }
-    for (int idx = tid; idx < DK * (kCh / 8); idx += 256) {
-      const int d = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
-      *reinterpret_cast<bf16x8*>(&sm.dwT[d][i0]) = load8(dwt + (hc * DK + d) * kCh + i0);
-    }
-    for (int idx = tid; idx < kCh * (DV / 8); idx += 256) {
-      const int i = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
-      *reinterpret_cast<bf16x8*>(&sm.u[i][e0]) = load8(u + (hc * kCh + i) * DV + e0);
-    }
-    for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-      const int i = idx / (DK / 8), p0 = 8 * (idx % (DK / 8));
-      *reinterpret_cast<bf16x8*>(&sm.w[i][p0]) = load8(wp + (hc * kCh + i) * DK + p0);
+    {
+      TileLoad<kCh, kCh, bf16> ltt;
+      ltt.issue(ttw + hc * kCh * kCh, kCh, tid, kCh);
+      if (tid < kCh) {
+        const float gv = gcw[hc * kCh + tid];
+        sm.gc[tid] = gv;
+        sm.bs[tid] = tid < L ? beta[(size_t)(t0 + tid) * Hv + hv] : 0.0f;
+        sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
+      }
+      ltt.commit(&sm.tt[0][0], kCh + 8, tid);
     }
     __syncthreads();
-    // Kg on the three lower blocks; the upper block stays zero
+    // Kg = (k_i . k_j) exp(gc_i - gc_j) on j < i, kept in registers (waves 0-2)
+    f32x16 kgr = f32x16{};
     if (wv < 3) {
-      const int mb = wv == 0 ? 0 : 1, nb = wv == 2 ? 1 : 0;
-      f32x16 acc = f32x16{};
-#pragma unroll
+      const int mb = lower_mb(wv), nb = lower_nb(wv), j = 32 * nb + lc;
+#pragma unroll 4
       for (int a = 0; a < DK / 16; ++a)
-        acc = mfma32x32x16(row8(&sm.k[0][0], DK + 8, 32 * mb + lc, 16 * a + 8 * lg),
-                           row8(&sm.k[0][0], DK + 8, 32 * nb + lc, 16 * a + 8 * lg), acc);
-      const int j = 32 * nb + lc;
+        kgr = mfma32x32x16(row8(&sm.k[0][0], DK + 8, 32 * mb + lc, 16 * a + 8 * lg),
+                           row8(&sm.k[0][0], DK + 8, j, 16 * a + 8 * lg), kgr);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int i = 32 * mb + crow(x, lg);
-        sm.Kg[i][j] = j < i ? acc[x] * expf(sm.gc[i] - sm.gc[j]) : 0.0f;
+        kgr[x] = j < i ? kgr[x] * expf(sm.gc[i] - sm.gc[j]) : 0.0f;
       }
-    } else {
-      for (int idx = lane; idx < 32 * 32; idx += 64) sm.Kg[idx >> 5][32 + (idx & 31)] = 0.0f;
     }
-    __syncthreads();
-    unit_lower_inverse([&](int a, int b) { return sm.bs[a] * sm.Kg[a][b]; }, sm.Ts, sm.pscr, tid);
-    // dbv = T^T dvn, dbk = T^T dw (T[i][j] = 0 for i < j: rows j of block rb
-    // need i >= 32 rb)
+    // dbv = T^T dvn, dbk = T^T dw; T[i][j] = 0 for i < j, so rows j of block
+    // rb need i >= 32 rb. The right-hand sides are read from HBM / L2 rows.
     float pv[16], pk[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) pv[x] = pk[x] = 0.0f;
-    f32x16 bv[NBV], bk[NBK];
 #pragma unroll
     for (int m = 0; m < NBV; ++m) {
       const int e = 32 * ((wv >> 1) + 2 * m) + lc;
-      f32x16 acc = f32x16{};
-      for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(col8f(&sm.Ts[0][0], kCh + 4, 32 * rb + lc, 16 * a + 8 * lg),
-                           row8(&sm.dvnT[0][0], kCh + 8, e, 16 * a + 8 * lg), acc);
-      bv[m] = acc;
+      const bf16* brow = dvnt + (hc * DV + e) * kCh;
+      float vv[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int j = 32 * rb + crow(x, lg);
-        if (j < L) {
-          const size_t off = ((size_t)(t0 + j) * Hv + hv) * DV + e;
-          dv[off] = from_f32<Tio>(sm.bs[j] * acc[x]);
-          pv[x] += acc[x] * (float)v[off];
-        }
+        vv[x] = j < L ? (float)v[((size_t)(t0 + j) * Hv + hv) * DV + e] : 0.0f;
+      }
+      f32x16 acc = f32x16{};
+      for (int a = 2 * rb; a < 4; ++a)
+        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
+                           acc);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = 32 * rb + crow(x, lg);
+        if (j < L) dv[((size_t)(t0 + j) * Hv + hv) * DV + e] = from_f32<Tio>(sm.bs[j] * acc[x]);
+        pv[x] += acc[x] * vv[x];
+      }
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = (bf16)acc[4 * j4 + x];
+        *reinterpret_cast<bf16x4*>(&sm.dbvT[e][32 * rb + 8 * j4 + 4 * lg]) = o4;
       }
     }
 #pragma unroll
     for (int m = 0; m < NBK; ++m) {
       const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+      const bf16* brow = dwt + (hc * DK + d) * kCh;
       f32x16 acc = f32x16{};
       for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(col8f(&sm.Ts[0][0], kCh + 4, 32 * rb + lc, 16 * a + 8 * lg),
-                           row8(&sm.dwT[0][0], kCh + 8, d, 16 * a + 8 * lg), acc);
-      bk[m] = acc;
+        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
+                           acc);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int j = 32 * rb + crow(x, lg);
         ak[m][x] += sm.bs[j] * sm.eg[j] * acc[x];
         pk[x] += acc[x] * (float)sm.k[j][d];
+      }
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = (bf16)acc[4 * j4 + x];
+        *reinterpret_cast<bf16x4*>(&sm.dbkT[d][32 * rb + 8 * j4 + 4 * lg]) = o4;
       }
     }
 #pragma unroll
@@ -1576,84 +1618,62 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
       }
     }
     __syncthreads();
-    // dbv^T and dbk^T replace dvn^T and dw^T
-#pragma unroll
-    for (int m = 0; m < NBV; ++m) {
-      const int e = 32 * ((wv >> 1) + 2 * m) + lc;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        bf16x4 o4;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) o4[x] = (bf16)bv[m][4 * j4 + x];
-        *reinterpret_cast<bf16x4*>(&sm.dvnT[e][32 * rb + 8 * j4 + 4 * lg]) = o4;
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < NBK; ++m) {
-      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        bf16x4 o4;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) o4[x] = (bf16)bk[m][4 * j4 + x];
-        *reinterpret_cast<bf16x4*>(&sm.dwT[d][32 * rb + 8 * j4 + 4 * lg]) = o4;
-      }
-    }
-    __syncthreads();
-    // dM = -(dbv u^T + dbk w^T) on the lower blocks; a = dM * Kg replaces T,
-    // G = beta_i dM exp(gc_i - gc_j) replaces Kg (each thread rewrites only
-    // the elements it read)
+    // dM = -(dbv u^T + dbk w^T) on the lower blocks (u, w rows from HBM / L2);
+    // a = dM Kg and G = beta_i dM exp(gc_i - gc_j) where j < i < L. G goes to
+    // gs at (i, j) and (j, i) by the owner of (i, j); the diagonal is zero.
     if (wv < 3) {
-      const int mb = wv == 0 ? 0 : 1, nb = wv == 2 ? 1 : 0;
+      const int mb = lower_mb(wv), nb = lower_nb(wv);
       const int i0 = 32 * mb + lc, j0 = 32 * nb + lc;
       f32x16 acc = f32x16{};
-#pragma unroll
+      const float* urow = u + (hc * kCh + j0) * DV;
+#pragma unroll 2
       for (int a = 0; a < DV / 16; ++a)
-        acc = mfma32x32x16(col8(&sm.dvnT[0][0], kCh + 8, i0, 16 * a + 8 * lg),
-                           row8(&sm.u[0][0], DV + 8, j0, 16 * a + 8 * lg), acc);
-#pragma unroll
+        acc = mfma32x32x16(col8(&sm.dbvT[0][0], kCh + 8, i0, 16 * a + 8 * lg), load8(urow + 16 * a + 8 * lg), acc);
+      const bf16* wrow = wp + (hc * kCh + j0) * DK;
+#pragma unroll 2
       for (int a = 0; a < DK / 16; ++a) {
         bf16x8 A;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) A[s] = sm.dwT[swap23(16 * a + 8 * lg + s)][i0];
-        acc = mfma32x32x16(A, row8(&sm.w[0][0], DK + 8, j0, 16 * a + 8 * lg), acc);
+        for (int s2 = 0; s2 < 8; ++s2) A[s2] = sm.dbkT[swap23(16 * a + 8 * lg + s2)][i0];
+        acc = mfma32x32x16(A, load8(wrow + 16 * a + 8 * lg), acc);
       }
+      float csum = 0.0f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int i = 32 * mb + crow(x, lg);
         const bool ok = j0 < i && i < L;
-        const float dm = ok ? -acc[x] : 0.0f;
-        const float kg = sm.Kg[i][j0];
-        sm.Ts[i][j0] = dm * kg;
-        sm.Kg[i][j0] = ok ? sm.bs[i] * dm * expf(sm.gc[i] - sm.gc[j0]) : 0.0f;
+        const float dm = -acc[x];
+        const float av = ok ? dm * kgr[x] : 0.0f;
+        const float gv = ok ? sm.bs[i] * dm * expf(sm.gc[i] - sm.gc[j0]) : 0.0f;
+        if (j0 < i) {
+          sm.gs[i][j0] = (bf16)gv;
+          sm.gs[j0][i] = (bf16)gv;
+        } else if (j0 == i) {
+          sm.gs[i][i] = (bf16)0.0f;
+        }
+        const float rs = sum32(av);
+        if (lc == 0) sm.ra[wv][i] = rs;
+        csum += sm.bs[i] * av;
       }
-    } else {
-      for (int idx = lane; idx < 32 * 32; idx += 64) sm.Ts[idx >> 5][32 + (idx & 31)] = 0.0f;
+      csum += __shfl_xor(csum, 32);
+      if (lg == 0) sm.cs[wv][j0] = csum;
     }
     __syncthreads();
     // dk += (G + G^T) k
 #pragma unroll
     for (int m = 0; m < NBK; ++m) {
       const int d = 32 * ((wv >> 1) + 2 * m) + lc;
-      const int i = 32 * rb + lc;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x8 A;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int j = 16 * a + 8 * lg + s;
-          A[s] = (bf16)(sm.Kg[i][j] + sm.Kg[j][i]);
-        }
-        ak[m] = mfma32x32x16(A, col8(&sm.k[0][0], DK + 8, d, 16 * a + 8 * lg), ak[m]);
-      }
+      for (int a = 0; a < 4; ++a)
+        ak[m] = mfma32x32x16(row8(&sm.gs[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                             col8(&sm.k[0][0], DK + 8, d, 16 * a + 8 * lg), ak[m]);
     }
     if (tid < kCh) {
       const int i = tid;
-      float ra = 0.0f, cb = 0.0f;
-      for (int j = 0; j < kCh; ++j) {
-        ra += sm.Ts[i][j];
-        cb += sm.bs[j] * sm.Ts[j][i];
-      }
+      // row sums: rows < 32 lie in block (0,0), rows >= 32 in (1,0) and (1,1);
+      // columns < 32 in (0,0) and (1,0), columns >= 32 in (1,1)
+      const float ra = i < 32 ? sm.ra[0][i] : sm.ra[1][i] + sm.ra[2][i];
+      const float cb = i < 32 ? sm.cs[0][i] + sm.cs[1][i] : sm.cs[2][i];
       const float zk = sm.r2[0][i] + sm.r2[1][i];
       const float db = (sm.r1[0][i] + sm.r1[1][i]) + sm.eg[i] * zk + ra;
       float x = i < L ? dgca[hc * kCh + i] + sm.bs[i] * sm.eg[i] * zk + sm.bs[i] * ra - cb : 0.0f;
@@ -1672,12 +1692,13 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
 #pragma unroll
   for (int m = 0; m < NBK; ++m) {
     const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+    float pa[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pa[x] = dka[(((size_t)hk * nc + c) * kCh + 32 * rb + crow(x, lg)) * DK + d];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int row = 32 * rb + crow(x, lg);
-      if (row < L)
-        dk[((size_t)(t0 + row) * H + hk) * DK + d] =
-            from_f32<Tio>(ak[m][x] + dka[(((size_t)hk * nc + c) * kCh + row) * DK + d]);
+      if (row < L) dk[((size_t)(t0 + row) * H + hk) * DK + d] = from_f32<Tio>(ak[m][x] + pa[x]);
     }
   }
 }
@@ -1716,12 +1737,13 @@ void gdn_launch(const void* q, const void* k, const void* v, const float* g, con
   bf16* kt = reinterpret_cast<bf16*>(ws + L.kt);
   bf16* vnt = reinterpret_cast<bf16*>(ws + L.vnt);
   bf16* h0w = reinterpret_cast<bf16*>(ws + L.h0);
+  bf16* tt = reinterpret_cast<bf16*>(ws + L.tt);
   const int* cstart = plan + pv.off_cstart;
   const int* clen = plan + pv.off_clen;
   {
     ProfScope ps("gdn_prep", st);
     hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, Tio>), dim3(pv.nc, Hv), dim3(256), 0, st, static_cast<const Tio*>(k),
-                       static_cast<const Tio*>(v), g, beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, kt);
+                       static_cast<const Tio*>(v), g, beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, kt, tt);
   }
   {
     ProfScope ps("gdn_state", st);
@@ -1774,6 +1796,7 @@ void gdn_bwd_launch(const void* q, const void* k, const void* v, const float* be
   bf16* dwt = reinterpret_cast<bf16*>(ws + B.dwt);
   float* dgca = reinterpret_cast<float*>(ws + B.dgca);
   float* dka = reinterpret_cast<float*>(ws + B.dka);
+  const bf16* ttw = reinterpret_cast<const bf16*>(ws + F.tt);
   float* dhead = reinterpret_cast<float*>(ws + B.dhead);
   const int* cstart = plan + pv.off_cstart;
   const int* clen = plan + pv.off_clen;
@@ -1803,7 +1826,7 @@ void gdn_bwd_launch(const void* q, const void* k, const void* v, const float* be
   {
     ProfScope ps("gdn_bwd_wy", st);
     hipLaunchKernelGGL((gdn_bwd_wy_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(256), 0, st, kk,
-                       static_cast<const Tio*>(v), beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, dvnt, dwt, dka, dgca,
+                       static_cast<const Tio*>(v), beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, ttw, dvnt, dwt, dka, dgca,
                        static_cast<Tio*>(dk), static_cast<Tio*>(dv), dg, dbeta);
   }
 }
