@@ -334,7 +334,8 @@ int tree_partition(const int32_t* node_start, const int32_t* node_end, const int
  * Backward: dx in dt; dweight float32 [C][K]; dbias float32 [C] or NULL.
  * Gradients are summed in a fixed order (bitwise reproducible). The backward
  * gathers each token's descendants at most K-1 levels down from the
- * preorder range (t, subtree_end[t]) and pos.
+ * preorder range (t, subtree_end[t]) and pos; g = dy * act'(a) passes
+ * between its passes in dt (dweight and dbias use it in float32).
  * Limits: T >= 1 (backward: T < 2^28), C a positive multiple of 8, 1 <= K <= 8.
  * workspace (backward): >= tree_conv_workspace_bytes(T, C, K) bytes, 256-byte
  * aligned. Errors: TA_EINVAL, TA_EHIP.

@@ -232,11 +232,12 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __res
 }
 
 // g = dy * act'(a) for a block of kConvTokBlock tokens, plus that block's
-// partial sums of dw (per tap) and db.
+// partial sums of dw (per tap) and db (from g in float32). g itself is kept
+// in the input precision for the dx pass.
 template <typename Tio, int KM>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     const Tio* __restrict__ x, const Tio* __restrict__ dy, const float* __restrict__ w,
-    const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, float* __restrict__ gbuf,
+    const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, Tio* __restrict__ gbuf,
     float* __restrict__ part) {
   __shared__ int anc[kConvTokBlock][kConvMaxK];
   const int tb = blockIdx.x * kConvTokBlock;
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
 // thread per token lists (token, depth) pairs in LDS; a token with more than
 // kConvMaxDesc of them is walked again by the channel threads.
 template <typename Tio, int KM>
-__global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* __restrict__ gbuf,
+__global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __restrict__ gbuf,
                                                                    const float* __restrict__ w,
                                                                    const int* __restrict__ pos,
                                                                    const int* __restrict__ se, int T, int C, int K,
@@ -387,24 +388,28 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const float* 
   }
 }
 
-// Fixed-order sum of the per-block partials.
+// Fixed-order sum of the per-block partials [nblk][C][K + 1]: one thread
+// per (channel, tap) value, reading consecutive values across the block's
+// threads; eight running sums over block residues, added in a fixed order.
 __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* __restrict__ part, int nblk, int C, int K,
                                                               float* __restrict__ dw, float* __restrict__ db) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
-  float acc[kConvMaxK + 1];
+  const int V = C * (K + 1);
+  const int vi = blockIdx.x * blockDim.x + threadIdx.x;
+  if (vi >= V) return;
+  float acc[8];
 #pragma unroll
-  for (int n = 0; n <= kConvMaxK; ++n) acc[n] = 0.0f;
-  for (int b = 0; b < nblk; ++b) {
-    const float* pp = part + ((size_t)b * C + c) * (K + 1);
+  for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
+  int b = 0;
+  for (; b + 8 <= nblk; b += 8)
 #pragma unroll
-    for (int n = 0; n <= kConvMaxK; ++n)
-      if (n <= K) acc[n] += pp[n];
-  }
-#pragma unroll
-  for (int n = 0; n < kConvMaxK; ++n)
-    if (n < K) dw[(size_t)c * K + n] = acc[n];
-  if (db) db[c] = acc[K];
+    for (int r = 0; r < 8; ++r) acc[r] += part[(size_t)(b + r) * V + vi];
+  for (int r = 0; b < nblk; ++b, ++r) acc[r] += part[(size_t)b * V + vi];
+  const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  const int c = vi / (K + 1), n = vi % (K + 1);
+  if (n < K)
+    dw[(size_t)c * K + n] = sum;
+  else if (db)
+    db[c] = sum;
 }
 
 // ---------------------------------------------------------------- gated delta rule
@@ -1862,7 +1867,7 @@ void conv_fwd_launch(int K, dim3 grid, hipStream_t st, const Tio* x, const float
 template <typename Tio, int KM>
 void conv_bwd_launch_k(int K, int nblk, int cy, hipStream_t st, const Tio* x, const Tio* dy, const float* w,
                        const float* b, const int* par, const int* pos, const int* se, int T, int C, int act,
-                       float* gbuf, float* part, Tio* dx) {
+                       Tio* gbuf, float* part, Tio* dx) {
   hipLaunchKernelGGL((conv_bwd_g_kernel<Tio, KM>), dim3(nblk, cy), dim3(kConvThreads), 0, st, x, dy, w, b, par, T, C,
                      K, act, gbuf, part);
   hipLaunchKernelGGL((conv_bwd_dx_kernel<Tio, KM>), dim3((T + kConvTB - 1) / kConvTB, cy), dim3(kConvThreads), 0, st,
@@ -1871,7 +1876,7 @@ void conv_bwd_launch_k(int K, int nblk, int cy, hipStream_t st, const Tio* x, co
 
 template <typename Tio>
 void conv_bwd_launch(int K, int nblk, int cy, hipStream_t st, const Tio* x, const Tio* dy, const float* w,
-                     const float* b, const int* par, const int* pos, const int* se, int T, int C, int act, float* gbuf,
+                     const float* b, const int* par, const int* pos, const int* se, int T, int C, int act, Tio* gbuf,
                      float* part, Tio* dx) {
   if (K <= 4)
     conv_bwd_launch_k<Tio, 4>(K, nblk, cy, st, x, dy, w, b, par, pos, se, T, C, act, gbuf, part, dx);
@@ -1941,7 +1946,6 @@ extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t
   const size_t need = tree_conv_workspace_bytes(T, C, K);
   if (ws_bytes < need) return fail(TA_EINVAL, "tree_conv_bwd: workspace too small (%zu < %zu bytes)", ws_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* gbuf = static_cast<float*>(workspace);
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + conv_ws_part_off(T, C));
   const int nblk = (T + kConvTokBlock - 1) / kConvTokBlock;
   const int cy = (C / 8 + kConvThreads - 1) / kConvThreads;
@@ -1949,12 +1953,14 @@ extern "C" int tree_conv_bwd(const void* x, const void* dy, ta_dtype dt, int32_t
     ProfScope ps("conv_bwd", st);
     if (dt == TA_BF16)
       conv_bwd_launch<bf16>(K, nblk, cy, st, static_cast<const bf16*>(x), static_cast<const bf16*>(dy), weight, bias,
-                            parent, pos, subtree_end, T, C, activation, gbuf, part, static_cast<bf16*>(dx));
+                            parent, pos, subtree_end, T, C, activation, static_cast<bf16*>(workspace), part,
+                            static_cast<bf16*>(dx));
     else
       conv_bwd_launch<float>(K, nblk, cy, st, static_cast<const float*>(x), static_cast<const float*>(dy), weight,
-                             bias, parent, pos, subtree_end, T, C, activation, gbuf, part, static_cast<float*>(dx));
-    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((C + 255) / 256), dim3(256), 0, st, part, nblk, C, K, dweight,
-                       dbias);
+                             bias, parent, pos, subtree_end, T, C, activation, static_cast<float*>(workspace), part,
+                             static_cast<float*>(dx));
+    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((C * (K + 1) + 255) / 256), dim3(256), 0, st, part, nblk, C, K,
+                       dweight, dbias);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TA_EHIP, "tree_conv_bwd: kernel launch failed: %s", hipGetErrorString(e));
