@@ -942,10 +942,19 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
 
 __device__ __forceinline__ int crow(int i, int lg) { return 8 * (i >> 2) + 4 * lg + (i & 3); }
 
+// Sum over the 32 lanes of each half-wave (lanes 0-31 and 32-63): quad
+// exchanges and row rotations by DPP, then the two 16-lane rows swapped by a
+// swizzle (no memory access).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum32(float x) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dppf<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dppf<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dppf<0x124>(x);  // row_ror 4
+  x += dppf<0x128>(x);  // row_ror 8
+  return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // lane ^ 16
 }
 
 // 8 elements along the contraction index k0..k0+7: of row r (contiguous) or
@@ -970,22 +979,22 @@ __device__ __forceinline__ bf16x8 col8f(const float* X, int ld, int c, int k0) {
 // as zero) bound for LDS rows of stride ls: issue() starts all of this
 // thread's loads, commit() stores them, so a workgroup keeps every load of a
 // tile (and of the tiles issued with it) in flight at once.
-template <int R, int C, typename Tsrc>
+template <int R, int C, typename Tsrc, int NT = 256>
 struct TileLoad {
-  static_assert((R * (C / 8)) % 256 == 0, "whole rounds of 256 threads");
-  static constexpr int N = R * (C / 8) / 256;
+  static_assert((R * (C / 8)) % NT == 0, "whole rounds of the workgroup's threads");
+  static constexpr int N = R * (C / 8) / NT;
   bf16x8 x[N];
   __device__ __forceinline__ void issue(const Tsrc* __restrict__ g, size_t gs, int tid, int rows_valid) {
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-      const int idx = tid + 256 * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
+      const int idx = tid + NT * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
       x[it] = r < rows_valid ? load8(g + r * gs + c) : zero8();
     }
   }
   __device__ __forceinline__ void commit(bf16* l, int ls, int tid) const {
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-      const int idx = tid + 256 * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
+      const int idx = tid + NT * it, r = idx / (C / 8), c = 8 * (idx % (C / 8));
       *reinterpret_cast<bf16x8*>(l + r * ls + c) = x[it];
     }
   }
@@ -1497,18 +1506,22 @@ struct BwdWyLds {
   bf16 gs[kCh][kCh + 8];    // G + G^T
   bf16 dbvT[DV][kCh + 8];
   bf16 dbkT[DK][kCh + 8];
+  float dmw[3][16][64];     // the dbk w^T half of dM, per lower block, in C-register order
   float gc[kCh], bs[kCh], eg[kCh];
-  float r1[2][kCh], r2[2][kCh];  // row sums v.dbv, k.dbk (by column half)
-  float ra[3][kCh], cs[3][kCh];  // row sums of a = dM Kg, column sums of beta a (by lower block)
+  float r1[4][kCh], r2[4][kCh];  // row sums v.dbv, k.dbk, by column block
+  float ra[3][kCh], cs[3][kCh];  // row sums of a = dM Kg, column sums of beta a, by lower block
 };
 
-// The three lower 32 x 32 blocks of a 64 x 64 chunk matrix, one per wave
-// 0-2: (row block, column block).
-__device__ __forceinline__ int lower_mb(int wv) { return wv == 0 ? 0 : 1; }
-__device__ __forceinline__ int lower_nb(int wv) { return wv == 2 ? 1 : 0; }
+// The three lower 32 x 32 blocks of a 64 x 64 chunk matrix: (row block,
+// column block) of block 0, 1, 2.
+__device__ __forceinline__ int lower_mb(int b) { return b == 0 ? 0 : 1; }
+__device__ __forceinline__ int lower_nb(int b) { return b == 2 ? 1 : 0; }
 
+// Eight waves; wave w owns output block (row block w % 2, column block w / 2)
+// of the 64 x D results (dbv, dbk, dk). Waves 0-2 own the lower blocks of the
+// chunk matrices (Kg, dM); waves 4-6 form the w-half of dM for them.
 template <int DK, int DV, typename Tio>
-__global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
+__global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     const Tio* __restrict__ k, const Tio* __restrict__ v, const float* __restrict__ beta,
     const int* __restrict__ cstart, const int* __restrict__ clen, int nc, int H, int Hv,
     const float* __restrict__ gcw, const float* __restrict__ u, const bf16* __restrict__ wp,
@@ -1516,25 +1529,24 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     const float* __restrict__ dka, const float* __restrict__ dgca, Tio* __restrict__ dk, Tio* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
   __shared__ __attribute__((aligned(16))) BwdWyLds<DK, DV> sm;
-  constexpr int NBK = DK / 64, NBV = DV / 64;
   const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
   const int t0 = cstart[c], L = clen[c];
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
-  const int rb = wv & 1;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int rb = wv & 1, cb = wv >> 1;
+  const bool own_v = cb < DV / 32, own_k = cb < DK / 32;
   {
-    TileLoad<kCh, DK, Tio> lk;
+    TileLoad<kCh, DK, Tio, 512> lk;
     lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
     lk.commit(&sm.k[0][0], DK + 8, tid);
   }
-  f32x16 ak[NBK];
-#pragma unroll
-  for (int m = 0; m < NBK; ++m) ak[m] = f32x16{};
+  f32x16 ak = f32x16{};
   for (int mv = 0; mv < r; ++mv) {
     const int hv = hk * r + mv;
     const size_t hc = (size_t)hv * nc + c;
     __syncthreads();
     {
-      TileLoad<kCh, kCh, bf16> ltt;
+      TileLoad<kCh, kCh, bf16, 512> ltt;
       ltt.issue(ttw + hc * kCh * kCh, kCh, tid, kCh);
       if (tid < kCh) {
         const float gv = gcw[hc * kCh + tid];
@@ -1548,8 +1560,8 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     // Kg = (k_i . k_j) exp(gc_i - gc_j) on j < i, kept in registers (waves 0-2)
     f32x16 kgr = f32x16{};
     if (wv < 3) {
-      const int mb = lower_mb(wv), nb = lower_nb(wv), j = 32 * nb + lc;
-#pragma unroll 4
+      const int mb = lower_mb(wv), j = 32 * lower_nb(wv) + lc;
+#pragma unroll
       for (int a = 0; a < DK / 16; ++a)
         kgr = mfma32x32x16(row8(&sm.k[0][0], DK + 8, 32 * mb + lc, 16 * a + 8 * lg),
                            row8(&sm.k[0][0], DK + 8, j, 16 * a + 8 * lg), kgr);
@@ -1559,14 +1571,10 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
         kgr[x] = j < i ? kgr[x] * expf(sm.gc[i] - sm.gc[j]) : 0.0f;
       }
     }
-    // dbv = T^T dvn, dbk = T^T dw; T[i][j] = 0 for i < j, so rows j of block
-    // rb need i >= 32 rb. The right-hand sides are read from HBM / L2 rows.
-    float pv[16], pk[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) pv[x] = pk[x] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NBV; ++m) {
-      const int e = 32 * ((wv >> 1) + 2 * m) + lc;
+    // dbv = T^T dvn (block rb, cb), dv = beta dbv; T[i][j] = 0 for i < j, so
+    // rows j of block rb need i >= 32 rb. Right-hand sides are HBM / L2 rows.
+    if (own_v) {
+      const int e = 32 * cb + lc;
       const bf16* brow = dvnt + (hc * DV + e) * kCh;
       float vv[16];
 #pragma unroll
@@ -1578,11 +1586,16 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
       for (int a = 2 * rb; a < 4; ++a)
         acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
                            acc);
+      float pv[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int j = 32 * rb + crow(x, lg);
         if (j < L) dv[((size_t)(t0 + j) * Hv + hv) * DV + e] = from_f32<Tio>(sm.bs[j] * acc[x]);
-        pv[x] += acc[x] * vv[x];
+        pv[x] = sum32(acc[x] * vv[x]);
+      }
+      if (lc == 0) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sm.r1[cb][32 * rb + crow(x, lg)] = pv[x];
       }
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
@@ -1592,19 +1605,24 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
         *reinterpret_cast<bf16x4*>(&sm.dbvT[e][32 * rb + 8 * j4 + 4 * lg]) = o4;
       }
     }
-#pragma unroll
-    for (int m = 0; m < NBK; ++m) {
-      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+    // dbk = T^T dw; dk += beta e^gc dbk
+    if (own_k) {
+      const int d = 32 * cb + lc;
       const bf16* brow = dwt + (hc * DK + d) * kCh;
       f32x16 acc = f32x16{};
       for (int a = 2 * rb; a < 4; ++a)
         acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
                            acc);
+      float pk[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int j = 32 * rb + crow(x, lg);
-        ak[m][x] += sm.bs[j] * sm.eg[j] * acc[x];
-        pk[x] += acc[x] * (float)sm.k[j][d];
+        ak[x] += sm.bs[j] * sm.eg[j] * acc[x];
+        pk[x] = sum32(acc[x] * (float)sm.k[j][d]);
+      }
+      if (lc == 0) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sm.r2[cb][32 * rb + crow(x, lg)] = pk[x];
       }
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
@@ -1614,40 +1632,41 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
         *reinterpret_cast<bf16x4*>(&sm.dbkT[d][32 * rb + 8 * j4 + 4 * lg]) = o4;
       }
     }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const float a1 = sum32(pv[x]), a2 = sum32(pk[x]);
-      if (lc == 0) {
-        sm.r1[wv >> 1][32 * rb + crow(x, lg)] = a1;
-        sm.r2[wv >> 1][32 * rb + crow(x, lg)] = a2;
-      }
-    }
     __syncthreads();
-    // dM = -(dbv u^T + dbk w^T) on the lower blocks (u, w rows from HBM / L2);
-    // a = dM Kg and G = beta_i dM exp(gc_i - gc_j) where j < i < L. G goes to
-    // gs at (i, j) and (j, i) by the owner of (i, j); the diagonal is zero.
-    if (wv < 3) {
-      const int mb = lower_mb(wv), nb = lower_nb(wv);
-      const int i0 = 32 * mb + lc, j0 = 32 * nb + lc;
-      f32x16 acc = f32x16{};
-      const float* urow = u + (hc * kCh + j0) * DV;
-#pragma unroll 2
-      for (int a = 0; a < DV / 16; ++a)
-        acc = mfma32x32x16(col8(&sm.dbvT[0][0], kCh + 8, i0, 16 * a + 8 * lg), load8(urow + 16 * a + 8 * lg), acc);
+    // dM = -(dbv u^T + dbk w^T) on the lower blocks: waves 4-6 form the w
+    // half and hand it over through LDS; u, w rows come from HBM / L2
+    f32x16 dmacc = f32x16{};
+    if (wv >= 4 && wv < 7) {
+      const int bl = wv - 4;
+      const int i0 = 32 * lower_mb(bl) + lc, j0 = 32 * lower_nb(bl) + lc;
       const bf16* wrow = wp + (hc * kCh + j0) * DK;
-#pragma unroll 2
+#pragma unroll 4
       for (int a = 0; a < DK / 16; ++a) {
         bf16x8 A;
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) A[s2] = sm.dbkT[swap23(16 * a + 8 * lg + s2)][i0];
-        acc = mfma32x32x16(A, load8(wrow + 16 * a + 8 * lg), acc);
+        dmacc = mfma32x32x16(A, load8(wrow + 16 * a + 8 * lg), dmacc);
       }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sm.dmw[bl][x][lane] = dmacc[x];
+    } else if (wv < 3) {
+      const int j0 = 32 * lower_nb(wv) + lc, i0 = 32 * lower_mb(wv) + lc;
+      const float* urow = u + (hc * kCh + j0) * DV;
+#pragma unroll 4
+      for (int a = 0; a < DV / 16; ++a)
+        dmacc = mfma32x32x16(col8(&sm.dbvT[0][0], kCh + 8, i0, 16 * a + 8 * lg), load8(urow + 16 * a + 8 * lg), dmacc);
+    }
+    __syncthreads();
+    // a = dM Kg and G = beta_i dM exp(gc_i - gc_j) where j < i < L. G goes to
+    // gs at (i, j) and (j, i) by the owner of (i, j); the diagonal is zero.
+    if (wv < 3) {
+      const int mb = lower_mb(wv), j0 = 32 * lower_nb(wv) + lc;
       float csum = 0.0f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int i = 32 * mb + crow(x, lg);
         const bool ok = j0 < i && i < L;
-        const float dm = -acc[x];
+        const float dm = -(dmacc[x] + sm.dmw[wv][x][lane]);
         const float av = ok ? dm * kgr[x] : 0.0f;
         const float gv = ok ? sm.bs[i] * dm * expf(sm.gc[i] - sm.gc[j0]) : 0.0f;
         if (j0 < i) {
@@ -1665,23 +1684,26 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     }
     __syncthreads();
     // dk += (G + G^T) k
-#pragma unroll
-    for (int m = 0; m < NBK; ++m) {
-      const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+    if (own_k) {
+      const int d = 32 * cb + lc;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        ak[m] = mfma32x32x16(row8(&sm.gs[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
-                             col8(&sm.k[0][0], DK + 8, d, 16 * a + 8 * lg), ak[m]);
+        ak = mfma32x32x16(row8(&sm.gs[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                          col8(&sm.k[0][0], DK + 8, d, 16 * a + 8 * lg), ak);
     }
     if (tid < kCh) {
       const int i = tid;
-      // row sums: rows < 32 lie in block (0,0), rows >= 32 in (1,0) and (1,1);
-      // columns < 32 in (0,0) and (1,0), columns >= 32 in (1,1)
+      // row sums: rows < 32 lie in lower block 0, rows >= 32 in blocks 1 and
+      // 2; columns < 32 in blocks 0 and 1, columns >= 32 in block 2
       const float ra = i < 32 ? sm.ra[0][i] : sm.ra[1][i] + sm.ra[2][i];
-      const float cb = i < 32 ? sm.cs[0][i] + sm.cs[1][i] : sm.cs[2][i];
-      const float zk = sm.r2[0][i] + sm.r2[1][i];
-      const float db = (sm.r1[0][i] + sm.r1[1][i]) + sm.eg[i] * zk + ra;
-      float x = i < L ? dgca[hc * kCh + i] + sm.bs[i] * sm.eg[i] * zk + sm.bs[i] * ra - cb : 0.0f;
+      const float cbs = i < 32 ? sm.cs[0][i] + sm.cs[1][i] : sm.cs[2][i];
+      float zv = 0.0f, zk = 0.0f;
+#pragma unroll
+      for (int q = 0; q < DV / 32; ++q) zv += sm.r1[q][i];
+#pragma unroll
+      for (int q = 0; q < DK / 32; ++q) zk += sm.r2[q][i];
+      const float db = zv + sm.eg[i] * zk + ra;
+      float x = i < L ? dgca[hc * kCh + i] + sm.bs[i] * sm.eg[i] * zk + sm.bs[i] * ra - cbs : 0.0f;
       // dg_t = sum of dgc_i over i >= t in the chunk
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -1694,16 +1716,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
       }
     }
   }
-#pragma unroll
-  for (int m = 0; m < NBK; ++m) {
-    const int d = 32 * ((wv >> 1) + 2 * m) + lc;
+  if (own_k) {
+    const int d = 32 * cb + lc;
     float pa[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) pa[x] = dka[(((size_t)hk * nc + c) * kCh + 32 * rb + crow(x, lg)) * DK + d];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int row = 32 * rb + crow(x, lg);
-      if (row < L) dk[((size_t)(t0 + row) * H + hk) * DK + d] = from_f32<Tio>(ak[m][x] + pa[x]);
+      if (row < L) dk[((size_t)(t0 + row) * H + hk) * DK + d] = from_f32<Tio>(ak[x] + pa[x]);
     }
   }
 }
@@ -1830,7 +1851,7 @@ void gdn_bwd_launch(const void* q, const void* k, const void* v, const float* be
   }
   {
     ProfScope ps("gdn_bwd_wy", st);
-    hipLaunchKernelGGL((gdn_bwd_wy_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(256), 0, st, kk,
+    hipLaunchKernelGGL((gdn_bwd_wy_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(512), 0, st, kk,
                        static_cast<const Tio*>(v), beta, cstart, clen, pv.nc, H, Hv, gcw, u, wp, ttw, dvnt, dwt, dka, dgca,
                        static_cast<Tio*>(dk), static_cast<Tio*>(dv), dg, dbeta);
   }
