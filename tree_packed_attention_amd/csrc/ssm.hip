@@ -1292,9 +1292,15 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_bwd_state_kernel(
     }
 }
 
-// Stage B3, per (chunk, q/k head), 256 threads, looping over the v-heads
-// that read the head. Output blocks of 64 x D results: wave w takes row
-// block w % 2 and column blocks w / 2 + 2 m.
+// The three lower 32 x 32 blocks of a 64 x 64 chunk matrix: (row block,
+// column block) of block 0, 1, 2.
+__device__ __forceinline__ int lower_mb(int b) { return b == 0 ? 0 : 1; }
+__device__ __forceinline__ int lower_nb(int b) { return b == 2 ? 1 : 0; }
+
+// Stage B3, per (chunk, q/k head), looping over the v-heads that read the
+// head. Eight waves; wave w owns output block (row block w % 2, column block
+// w / 2) of the 64 x dk results (dq, dk, dw); waves 0-2 own the lower blocks
+// of the chunk matrices (S, dS), waves 4-6 form dP for them.
 template <int DK, int DV>
 struct BwdOutLds {
   bf16 q[kCh][DK + 8];
@@ -1304,14 +1310,15 @@ struct BwdOutLds {
   bf16 dvnT[DV][kCh + 8];
   bf16 hb[DV][DK + 8];  // h0, then dh_end, as [dv][dk]
   bf16 dS[kCh][kCh + 8];
-  float E[kCh][kCh + 1];  // dP * P, for the decay gradient
+  float dpx[3][16][64];  // dP of the lower blocks, C-register order
   float gc[kCh], eg[kCh], dec[kCh];
-  float rs[2][kCh], rz[2][kCh];
-  float red[4];
+  float rs[4][kCh], rz[4][kCh];  // by column block
+  float er[3][kCh], ec[3][kCh];  // row / column sums of dP * P, by lower block
+  float red[8];
 };
 
 template <int DK, int DV, typename Tio>
-__global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
+__global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict__ q, const Tio* __restrict__ k,
                                                           const Tio* __restrict__ dout, const int* __restrict__ cstart,
                                                           const int* __restrict__ clen, int nc, int H, int Hv,
                                                           const float* __restrict__ gcw, const bf16* __restrict__ vnt,
@@ -1320,21 +1327,21 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
                                                           float* __restrict__ dka, float* __restrict__ dgca,
                                                           bf16* __restrict__ dwt) {
   __shared__ __attribute__((aligned(16))) BwdOutLds<DK, DV> sm;
-  constexpr int NBK = DK / 64;
   const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
   const int t0 = cstart[c], L = clen[c];
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
-  const int rb = wv & 1;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  const int rb = wv & 1, cb = wv >> 1;
+  const bool own = cb < DK / 32;
+  const int col = 32 * cb + lc;  // dk column of this lane's output block
   {
-    TileLoad<kCh, DK, Tio> lq, lk;
+    TileLoad<kCh, DK, Tio, 512> lq, lk;
     lq.issue(q + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
     lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
     lq.commit(&sm.q[0][0], DK + 8, tid);
     lk.commit(&sm.k[0][0], DK + 8, tid);
   }
-  f32x16 aq[NBK], ak[NBK];
-#pragma unroll
-  for (int m = 0; m < NBK; ++m) aq[m] = ak[m] = f32x16{};
+  f32x16 aq = f32x16{}, ak = f32x16{};
   for (int mv = 0; mv < r; ++mv) {
     const int hv = hk * r + mv;
     const size_t hc = (size_t)hv * nc + c;
@@ -1345,73 +1352,84 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
       sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
       sm.dec[tid] = tid < L ? expf(gl - gv) : 0.0f;
     }
-    TileLoad<kCh, DV, Tio> ldo;
-    TileLoad<DV, kCh, bf16> lvn, ldvn;
-    TileLoad<DV, DK, bf16> lh0, ldh;
+    TileLoad<kCh, DV, Tio, 512> ldo;
+    TileLoad<DV, kCh, bf16, 512> lvn, ldvn;
+    TileLoad<DV, DK, bf16, 512> lh0, ldh;
     ldo.issue(dout + ((size_t)t0 * Hv + hv) * DV, (size_t)Hv * DV, tid, L);
     lvn.issue(vnt + hc * DV * kCh, kCh, tid, DV);
     ldvn.issue(dvnt + hc * DV * kCh, kCh, tid, DV);
     lh0.issue(h0w + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
-    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);  // committed once h0 is no longer read
     ldo.commit(&sm.dO[0][0], DV + 8, tid);
     lvn.commit(&sm.vnT[0][0], kCh + 8, tid);
     ldvn.commit(&sm.dvnT[0][0], kCh + 8, tid);
     lh0.commit(&sm.hb[0][0], DK + 8, tid);
     __syncthreads();
-    // S = q k^T and dP = dO vn^T on the three lower 32 x 32 blocks
-    if (wv < 3) {
-      const int qb = wv == 0 ? 0 : 1, kb = wv == 2 ? 1 : 0;
-      f32x16 sv = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int a = 0; a < DK / 16; ++a)
-        sv = mfma32x32x16(row8(&sm.q[0][0], DK + 8, 32 * qb + lc, 16 * a + 8 * lg),
-                          row8(&sm.k[0][0], DK + 8, 32 * kb + lc, 16 * a + 8 * lg), sv);
+    // S = q k^T on the lower blocks (waves 0-2); dP = dO vn^T (waves 4-6)
+    f32x16 sv = f32x16{};
+    if (wv >= 4 && wv < 7) {
+      const int bl = wv - 4;
+      f32x16 dp = f32x16{};
 #pragma unroll
       for (int a = 0; a < DV / 16; ++a)
-        dp = mfma32x32x16(row8(&sm.dO[0][0], DV + 8, 32 * qb + lc, 16 * a + 8 * lg),
-                          col8(&sm.vnT[0][0], kCh + 8, 32 * kb + lc, 16 * a + 8 * lg), dp);
-      const int j = 32 * kb + lc;
+        dp = mfma32x32x16(row8(&sm.dO[0][0], DV + 8, 32 * lower_mb(bl) + lc, 16 * a + 8 * lg),
+                          col8(&sm.vnT[0][0], kCh + 8, 32 * lower_nb(bl) + lc, 16 * a + 8 * lg), dp);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sm.dpx[bl][x][lane] = dp[x];
+    } else if (wv < 3) {
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a)
+        sv = mfma32x32x16(row8(&sm.q[0][0], DK + 8, 32 * lower_mb(wv) + lc, 16 * a + 8 * lg),
+                          row8(&sm.k[0][0], DK + 8, 32 * lower_nb(wv) + lc, 16 * a + 8 * lg), sv);
+    } else if (wv == 3) {
+      for (int idx = lane; idx < 32 * 32; idx += 64) sm.dS[idx >> 5][32 + (idx & 31)] = (bf16)0.0f;
+    }
+    __syncthreads();
+    // dS = dP exp(gc_i - gc_j) on j <= i < L; E = dP * P summed by rows and columns
+    if (wv < 3) {
+      const int mb = lower_mb(wv), j = 32 * lower_nb(wv) + lc;
+      float csum = 0.0f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int i = 32 * qb + crow(x, lg);
+        const int i = 32 * mb + crow(x, lg);
         const bool ok = j <= i && i < L;
         const float gam = ok ? expf(sm.gc[i] - sm.gc[j]) : 0.0f;
-        sm.dS[i][j] = (bf16)(dp[x] * gam);
-        sm.E[i][j] = dp[x] * sv[x] * gam;
+        const float dp = sm.dpx[wv][x][lane];
+        sm.dS[i][j] = (bf16)(dp * gam);
+        const float e = dp * sv[x] * gam;
+        const float rsum = sum32(e);
+        if (lc == 0) sm.er[wv][i] = rsum;
+        csum += e;
       }
-    } else {
-      for (int idx = lane; idx < 32 * 32; idx += 64) {
-        sm.dS[idx >> 5][32 + (idx & 31)] = (bf16)0.0f;
-        sm.E[idx >> 5][32 + (idx & 31)] = 0.0f;
-      }
+      csum += __shfl_xor(csum, 32);
+      if (lg == 0) sm.ec[wv][j] = csum;
     }
     __syncthreads();
     // dq += dS k + e^gc (dO h0^T); dk += dS^T q; dw = -dvn h0^T
-    float pq[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) pq[x] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NBK; ++m) {
-      const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+    if (own) {
       for (int a = 0; a < 2 * (rb + 1); ++a)
-        aq[m] = mfma32x32x16(row8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
-                             col8(&sm.k[0][0], DK + 8, col, 16 * a + 8 * lg), aq[m]);
+        aq = mfma32x32x16(row8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                          col8(&sm.k[0][0], DK + 8, col, 16 * a + 8 * lg), aq);
       for (int a = 2 * rb; a < 4; ++a)
-        ak[m] = mfma32x32x16(col8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
-                             col8(&sm.q[0][0], DK + 8, col, 16 * a + 8 * lg), ak[m]);
+        ak = mfma32x32x16(col8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                          col8(&sm.q[0][0], DK + 8, col, 16 * a + 8 * lg), ak);
       f32x16 x = f32x16{}, y = f32x16{};
-#pragma unroll
+#pragma unroll 2
       for (int a = 0; a < DV / 16; ++a) {
         const bf16x8 hB = col8(&sm.hb[0][0], DK + 8, col, 16 * a + 8 * lg);
         x = mfma32x32x16(row8(&sm.dO[0][0], DV + 8, 32 * rb + lc, 16 * a + 8 * lg), hB, x);
         y = mfma32x32x16(col8(&sm.dvnT[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), hB, y);
       }
+      float pq[16];
 #pragma unroll
       for (int i4 = 0; i4 < 16; ++i4) {
         const int row = 32 * rb + crow(i4, lg);
         const float xv = x[i4] * sm.eg[row];
-        aq[m][i4] += xv;
-        pq[i4] += xv * (float)sm.q[row][col];
+        aq[i4] += xv;
+        pq[i4] = sum32(xv * (float)sm.q[row][col]);
+      }
+      if (lc == 0) {
+#pragma unroll
+        for (int i4 = 0; i4 < 16; ++i4) sm.rs[cb][32 * rb + crow(i4, lg)] = pq[i4];
       }
       bf16* wo = dwt + (hc * DK + col) * kCh + 32 * rb;
 #pragma unroll
@@ -1422,20 +1440,16 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
         *reinterpret_cast<bf16x4*>(wo + 8 * j4 + 4 * lg) = o4;
       }
     }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const float t = sum32(pq[x]);
-      if (lc == 0) sm.rs[wv >> 1][32 * rb + crow(x, lg)] = t;
-    }
+    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
     __syncthreads();
     // dh_end replaces h0 (each thread rewrites the elements it reads); s = <dh_end, h0>
     float sp = 0.0f;
 #pragma unroll
     for (int it = 0; it < ldh.N; ++it) {
-      const int idx = tid + 256 * it, e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+      const int idx = tid + 512 * it, e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
       const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&sm.hb[e][d0]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sp += (float)ldh.x[it][s] * (float)ov[s];
+      for (int s2 = 0; s2 < 8; ++s2) sp += (float)ldh.x[it][s2] * (float)ov[s2];
     }
     ldh.commit(&sm.hb[0][0], DK + 8, tid);
     sp = sum32(sp);
@@ -1443,58 +1457,57 @@ __global__ __launch_bounds__(256) void gdn_bwd_out_kernel(const Tio* __restrict_
     if (lane == 0) sm.red[wv] = sp;
     __syncthreads();
     // kd-part: x = e^(gl - gc) (vn dh_end^T); dk += x; z_i = sum_d x_id k_id
-    float pz[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) pz[x] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NBK; ++m) {
-      const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+    if (own) {
       f32x16 x = f32x16{};
-#pragma unroll
+#pragma unroll 4
       for (int a = 0; a < DV / 16; ++a)
         x = mfma32x32x16(col8(&sm.vnT[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
                          col8(&sm.hb[0][0], DK + 8, col, 16 * a + 8 * lg), x);
+      float pz[16];
 #pragma unroll
       for (int i4 = 0; i4 < 16; ++i4) {
         const int row = 32 * rb + crow(i4, lg);
         const float xv = x[i4] * sm.dec[row];
-        ak[m][i4] += xv;
-        pz[i4] += xv * (float)sm.k[row][col];
+        ak[i4] += xv;
+        pz[i4] = sum32(xv * (float)sm.k[row][col]);
       }
-    }
+      if (lc == 0) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const float t = sum32(pz[x]);
-      if (lc == 0) sm.rz[wv >> 1][32 * rb + crow(x, lg)] = t;
+        for (int i4 = 0; i4 < 16; ++i4) sm.rz[cb][32 * rb + crow(i4, lg)] = pz[i4];
+      }
     }
     __syncthreads();
     if (tid < kCh) {
       const int i = tid;
-      float r1 = 0.0f, c1 = 0.0f;
-      for (int j = 0; j < kCh; ++j) {
-        r1 += sm.E[i][j];
-        c1 += sm.E[j][i];
+      // rows < 32 lie in lower block 0, rows >= 32 in blocks 1 and 2;
+      // columns < 32 in blocks 0 and 1, columns >= 32 in block 2
+      const float r1 = i < 32 ? sm.er[0][i] : sm.er[1][i] + sm.er[2][i];
+      const float c1 = i < 32 ? sm.ec[0][i] + sm.ec[1][i] : sm.ec[2][i];
+      float rq = 0.0f, z = 0.0f;
+#pragma unroll
+      for (int q4 = 0; q4 < DK / 32; ++q4) {
+        rq += sm.rs[q4][i];
+        z += sm.rz[q4][i];
       }
-      const float z = sm.rz[0][i] + sm.rz[1][i];
-      float d = r1 - c1 + sm.rs[0][i] + sm.rs[1][i] - z;
+      float d = r1 - c1 + rq - z;
       float zs = z;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) zs += __shfl_xor(zs, o);
       if (i == L - 1) {
-        const float sdot = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+        float sdot = 0.0f;
+#pragma unroll
+        for (int w8 = 0; w8 < 8; ++w8) sdot += sm.red[w8];
         d += zs + expf(sm.gc[kCh - 1]) * sdot;
       }
       dgca[hc * kCh + i] = d;
     }
   }
-#pragma unroll
-  for (int m = 0; m < NBK; ++m) {
-    const int col = 32 * ((wv >> 1) + 2 * m) + lc;
+  if (own) {
 #pragma unroll
     for (int i4 = 0; i4 < 16; ++i4) {
       const int row = 32 * rb + crow(i4, lg);
-      if (row < L) dq[((size_t)(t0 + row) * H + hk) * DK + col] = from_f32<Tio>(aq[m][i4]);
-      dka[(((size_t)hk * nc + c) * kCh + row) * DK + col] = ak[m][i4];
+      if (row < L) dq[((size_t)(t0 + row) * H + hk) * DK + col] = from_f32<Tio>(aq[i4]);
+      dka[(((size_t)hk * nc + c) * kCh + row) * DK + col] = ak[i4];
     }
   }
 }
@@ -1511,11 +1524,6 @@ struct BwdWyLds {
   float r1[4][kCh], r2[4][kCh];  // row sums v.dbv, k.dbk, by column block
   float ra[3][kCh], cs[3][kCh];  // row sums of a = dM Kg, column sums of beta a, by lower block
 };
-
-// The three lower 32 x 32 blocks of a 64 x 64 chunk matrix: (row block,
-// column block) of block 0, 1, 2.
-__device__ __forceinline__ int lower_mb(int b) { return b == 0 ? 0 : 1; }
-__device__ __forceinline__ int lower_nb(int b) { return b == 2 ? 1 : 0; }
 
 // Eight waves; wave w owns output block (row block w % 2, column block w / 2)
 // of the 64 x D results (dbv, dbk, dk). Waves 0-2 own the lower blocks of the
@@ -1846,7 +1854,7 @@ void gdn_bwd_launch(const void* q, const void* k, const void* v, const float* be
   }
   {
     ProfScope ps("gdn_bwd_out", st);
-    hipLaunchKernelGGL((gdn_bwd_out_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(256), 0, st, qq, kk, dd, cstart, clen,
+    hipLaunchKernelGGL((gdn_bwd_out_kernel<DK, DV, Tio>), dim3(pv.nc, H), dim3(512), 0, st, qq, kk, dd, cstart, clen,
                        pv.nc, H, Hv, gcw, vnt, h0w, dvnt, dhe, static_cast<Tio*>(dq), dka, dgca, dwt);
   }
   {
