@@ -1512,9 +1512,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, typename Tio>
 struct BwdWyLds {
   bf16 k[kCh][DK + 8];
+  bf16 vs[kCh][DV + 8];    // v rows of the v-head
+  Tio dvs[kCh][DV + 8];    // dv rows, staged for row stores
   bf16 tt[kCh][kCh + 8];    // T^T
   bf16 gs[kCh][kCh + 8];    // G + G^T
   bf16 dbvT[DV][kCh + 8];
@@ -1536,7 +1538,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     const bf16* __restrict__ ttw, const bf16* __restrict__ dvnt, const bf16* __restrict__ dwt,
     const float* __restrict__ dka, const float* __restrict__ dgca, Tio* __restrict__ dk, Tio* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
-  __shared__ __attribute__((aligned(16))) BwdWyLds<DK, DV> sm;
+  __shared__ __attribute__((aligned(16))) BwdWyLds<DK, DV, Tio> sm;
   const int c = blockIdx.x, hk = blockIdx.y, r = Hv / H;
   const int t0 = cstart[c], L = clen[c];
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1555,7 +1557,9 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     __syncthreads();
     {
       TileLoad<kCh, kCh, bf16, 512> ltt;
+      TileLoad<kCh, DV, Tio, 512> lv;
       ltt.issue(ttw + hc * kCh * kCh, kCh, tid, kCh);
+      lv.issue(v + ((size_t)t0 * Hv + hv) * DV, (size_t)Hv * DV, tid, L);
       if (tid < kCh) {
         const float gv = gcw[hc * kCh + tid];
         sm.gc[tid] = gv;
@@ -1563,13 +1567,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
         sm.eg[tid] = tid < L ? expf(gv) : 0.0f;
       }
       ltt.commit(&sm.tt[0][0], kCh + 8, tid);
+      lv.commit(&sm.vs[0][0], DV + 8, tid);
     }
     __syncthreads();
     // Kg = (k_i . k_j) exp(gc_i - gc_j) on j < i, kept in registers (waves 0-2)
     f32x16 kgr = f32x16{};
     if (wv < 3) {
       const int mb = lower_mb(wv), j = 32 * lower_nb(wv) + lc;
-#pragma unroll
+#pragma unroll 4
       for (int a = 0; a < DK / 16; ++a)
         kgr = mfma32x32x16(row8(&sm.k[0][0], DK + 8, 32 * mb + lc, 16 * a + 8 * lg),
                            row8(&sm.k[0][0], DK + 8, j, 16 * a + 8 * lg), kgr);
@@ -1584,12 +1589,6 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     if (own_v) {
       const int e = 32 * cb + lc;
       const bf16* brow = dvnt + (hc * DV + e) * kCh;
-      float vv[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int j = 32 * rb + crow(x, lg);
-        vv[x] = j < L ? (float)v[((size_t)(t0 + j) * Hv + hv) * DV + e] : 0.0f;
-      }
       f32x16 acc = f32x16{};
       for (int a = 2 * rb; a < 4; ++a)
         acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
@@ -1598,8 +1597,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int j = 32 * rb + crow(x, lg);
-        if (j < L) dv[((size_t)(t0 + j) * Hv + hv) * DV + e] = from_f32<Tio>(sm.bs[j] * acc[x]);
-        pv[x] = sum32(acc[x] * vv[x]);
+        sm.dvs[j][e] = from_f32<Tio>(sm.bs[j] * acc[x]);
+        pv[x] = sum32(acc[x] * (float)sm.vs[j][e]);
       }
       if (lc == 0) {
 #pragma unroll
@@ -1641,6 +1640,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
       }
     }
     __syncthreads();
+    // dv rows out (rows past the chunk are not written)
+#pragma unroll
+    for (int it = 0; it < kCh * (DV / 8) / 512; ++it) {
+      const int idx = tid + 512 * it, j = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
+      if (j < L) {
+        Tio* o = dv + ((size_t)(t0 + j) * Hv + hv) * DV + e0;
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) o[q8] = sm.dvs[j][e0 + q8];
+      }
+    }
     // dM = -(dbv u^T + dbk w^T) on the lower blocks: waves 4-6 form the w
     // half and hand it over through LDS; u, w rows come from HBM / L2
     f32x16 dmacc = f32x16{};
