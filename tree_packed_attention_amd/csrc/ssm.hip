@@ -605,10 +605,15 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
   }
   // kd^T = (k exp(gc_last - gc))^T, chunk-local, for the state pass
   {
+    // 16 bytes per lane, eight lanes per 128-byte row of kd^T
     bf16* kto = kt + ((size_t)hv * nc + c) * DK * kCh;
-    for (int idx = tid; idx < DK * kCh; idx += 256) {
-      const int kk = idx / kCh, r = idx % kCh;
-      kto[idx] = (bf16)((float)ks[r][kk] * dec[r]);
+#pragma unroll
+    for (int it = 0; it < DK * (kCh / 8) / 256; ++it) {
+      const int idx = tid + 256 * it, kk = idx / (kCh / 8), r0 = 8 * (idx % (kCh / 8));
+      bf16x8 o8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = (bf16)((float)ks[r0 + e][kk] * dec[r0 + e]);
+      *reinterpret_cast<bf16x8*>(kto + (size_t)kk * kCh + r0) = o8;
     }
   }
   // right-hand side, transposed: rt[col][row] = beta v (col < DV), beta k e^gc.
@@ -1013,6 +1018,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
                                                            bf16* __restrict__ dot) {
   __shared__ __attribute__((aligned(16))) bf16 qs[kCh][DK + 8];
   __shared__ __attribute__((aligned(16))) bf16 ks[kCh][DK + 8];
+  __shared__ __attribute__((aligned(16))) bf16 ws_[kCh][DK + 8];
   __shared__ __attribute__((aligned(16))) bf16 dT[DV][kCh + 8];
   __shared__ float gcs[kCh], egs[kCh], decs[kCh];
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -1020,45 +1026,51 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
   const int t0 = cstart[c], L = clen[c];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
   const size_t hc = (size_t)hv * nc + c;
-  if (tid < kCh) {
-    const float gv = gcw[hc * kCh + tid], gl = gcw[hc * kCh + kCh - 1];
-    gcs[tid] = gv;
-    egs[tid] = tid < L ? expf(gv) : 0.0f;
-    decs[tid] = tid < L ? expf(gl - gv) : 0.0f;
+  {
+    TileLoad<kCh, DK, Tio> lq, lk;
+    TileLoad<kCh, DK, bf16> lw;
+    lq.issue(q + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
+    lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
+    lw.issue(wp + hc * kCh * DK, DK, tid, kCh);
+    if (tid < kCh) {
+      const float gv = gcw[hc * kCh + tid], gl = gcw[hc * kCh + kCh - 1];
+      gcs[tid] = gv;
+      egs[tid] = tid < L ? expf(gv) : 0.0f;
+      decs[tid] = tid < L ? expf(gl - gv) : 0.0f;
+    }
+    lq.commit(&qs[0][0], DK + 8, tid);
+    lk.commit(&ks[0][0], DK + 8, tid);
+    lw.commit(&ws_[0][0], DK + 8, tid);
   }
-  __syncthreads();
-  // q and k rows into LDS; (q e^gc)^T out. Lanes take consecutive rows, so
-  // each transposed store covers 128 contiguous bytes.
-#pragma unroll
-  for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx % kCh, d0 = 8 * (idx / kCh);
-    const bf16x8 qv = i < L ? load8(q + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
-    const bf16x8 kv = i < L ? load8(k + ((size_t)(t0 + i) * H + hk) * DK + d0) : zero8();
-    *reinterpret_cast<bf16x8*>(&qs[i][d0]) = qv;
-    *reinterpret_cast<bf16x8*>(&ks[i][d0]) = kv;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qgt[(hc * DK + d0 + s) * kCh + i] = (bf16)((float)qv[s] * egs[i]);
-  }
-  // w^T (w is stored with swap23 columns: position p holds column swap23(p))
-#pragma unroll
-  for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx % kCh, p0 = 8 * (idx / kCh);
-    const bf16x8 wv8 = load8(wp + (hc * kCh + i) * DK + p0);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) wt[(hc * DK + swap23(p0 + s)) * kCh + i] = wv8[s];
-  }
-  // dO^T, in LDS and out
+  // dO^T into LDS (lanes over rows, so each transposed LDS store covers 64
+  // contiguous bytes)
 #pragma unroll
   for (int it = 0; it < kCh * (DV / 8) / 256; ++it) {
     const int idx = tid + 256 * it, i = idx % kCh, e0 = 8 * (idx / kCh);
     const bf16x8 d8 = i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      dT[e0 + s][i] = d8[s];
-      dot[(hc * DV + e0 + s) * kCh + i] = d8[s];
-    }
+    for (int s = 0; s < 8; ++s) dT[e0 + s][i] = d8[s];
   }
   __syncthreads();
+  // transposed outputs, 16 bytes per lane, eight lanes per 128-byte row:
+  // (q e^gc)^T and w^T (w's position p holds column swap23(p)), dO^T
+#pragma unroll
+  for (int it = 0; it < DK * (kCh / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, d = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
+    bf16x8 qo, wo;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qo[s] = (bf16)((float)qs[i0 + s][d] * egs[i0 + s]);
+      wo[s] = ws_[i0 + s][swap23(d)];
+    }
+    *reinterpret_cast<bf16x8*>(qgt + (hc * DK + d) * kCh + i0) = qo;
+    *reinterpret_cast<bf16x8*>(wt + (hc * DK + d) * kCh + i0) = wo;
+  }
+#pragma unroll
+  for (int it = 0; it < DV * (kCh / 8) / 256; ++it) {
+    const int idx = tid + 256 * it, e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
+    *reinterpret_cast<bf16x8*>(dot + (hc * DV + e) * kCh + i0) = *reinterpret_cast<const bf16x8*>(&dT[e][i0]);
+  }
   // kd rows with swap23 columns (the A operand of dvn += kd dh)
 #pragma unroll
   for (int it = 0; it < kCh * (DK / 8) / 256; ++it) {
