@@ -223,22 +223,29 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
 // 64-key tiles of the forward / dQ pass and the 128-key tiles of the dK/dV
 // pass, whose work (the number of 64-row query blocks from row Lq on it can
 // see) is also recorded.
-__device__ __forceinline__ int2 key_range_minmax(const int* __restrict__ se, int T, int j0, int n) {
-  int mn = INT_MAX, mx = 0;
-  for (int j = j0; j < j0 + n; ++j) {
-    const int s = j < T ? se[j] : 0;
-    mn = min(mn, s);
-    mx = max(mx, s);
+__device__ __forceinline__ int2 wave_minmax(int2 m) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    m.x = min(m.x, __shfl_xor(m.x, o));
+    m.y = max(m.y, __shfl_xor(m.y, o));
   }
-  return make_int2(mn, mx);
+  return m;
 }
+// One wave per 128-key tile (and its two 64-key halves); subtree ends past T
+// count as 0, so a tile holding the end of the sequence is never "full".
 __global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict__ se, int T, int Lq, int nk64,
                                                           int nk128, int2* __restrict__ kmm64,
                                                           int2* __restrict__ kmm128, int* __restrict__ work) {
-  const int kt = blockIdx.x * blockDim.x + threadIdx.x;
-  if (kt < nk64) kmm64[kt] = key_range_minmax(se, T, kt * kFwdBK, kFwdBK);
-  if (kt < nk128) {
-    const int2 m = key_range_minmax(se, T, kt * kBwdBK, kBwdBK);
+  const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (kt >= nk128) return;
+  const int lane = threadIdx.x & 63;
+  const int ja = kt * kBwdBK + lane, jb = ja + kFwdBK;
+  const int sa = ja < T ? se[ja] : 0, sb = jb < T ? se[jb] : 0;
+  const int2 ma = wave_minmax(make_int2(sa, sa)), mb = wave_minmax(make_int2(sb, sb));
+  if (lane == 0) {
+    kmm64[2 * kt] = ma;
+    if (2 * kt + 1 < nk64) kmm64[2 * kt + 1] = mb;
+    const int2 m = make_int2(min(ma.x, mb.x), max(ma.y, mb.y));
     kmm128[kt] = m;
     work[kt] = max((m.y + kBwdBQ - 1) / kBwdBQ - max(kt * kBwdBK, Lq) / kBwdBQ, 0);  // queries start at Lq
   }
@@ -290,20 +297,25 @@ __global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ wor
   const int n = blockIdx.x == 0 ? n0 : n1;
   int* __restrict__ order = blockIdx.x == 0 ? order0 : order1;
   __shared__ int hist[1024];
-  hist[threadIdx.x] = 0;
+  __shared__ int scan[1024];
+  const int t = threadIdx.x;
+  hist[t] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[min(work[i], 1023)], 1);
+  for (int i = t; i < n; i += blockDim.x) atomicAdd(&hist[min(work[i], 1023)], 1);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int b = 1023; b >= 0; --b) {
-      const int c = hist[b];
-      hist[b] = acc;
-      acc += c;
-    }
+  // start of each bin, heaviest bin first: an inclusive scan over bins in
+  // descending order (thread t holds bin 1023 - t), made exclusive
+  const int cnt = hist[1023 - t];
+  int v = cnt;
+  for (int o = 1; o < 1024; o <<= 1) {
+    scan[t] = v;
+    __syncthreads();
+    if (t >= o) v += scan[t - o];
+    __syncthreads();
   }
+  hist[1023 - t] = v - cnt;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) order[atomicAdd(&hist[min(work[i], 1023)], 1)] = i;
+  for (int i = t; i < n; i += blockDim.x) order[atomicAdd(&hist[min(work[i], 1023)], 1)] = i;
 }
 
 // Loads 8 elements [c, c+8) of a caller row; zero past the row end or for
@@ -1121,7 +1133,8 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
   }
   ProfScope ps("tile_plan", st);
   static_assert(kFwdRows == kFwdBQ, "the forward shares the dQ pass's query-tile plan");
-  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk64 + 255) / 256), dim3(256), 0, st, at<const int>(ws, L.off_sep),
+  static_assert(kBwdBK == 2 * kFwdBK, "a 128-key tile is two 64-key tiles");
+  hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk128 + 3) / 4), dim3(256), 0, st, at<const int>(ws, L.off_sep),
                      L.Tc, L.Lq, L.nk64, L.nk128, at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128),
                      at<int>(ws, L.off_kwork));
   hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.Tc, L.Lq,
