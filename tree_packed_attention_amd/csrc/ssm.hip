@@ -90,7 +90,13 @@ __device__ __forceinline__ void st8f(float* p, const float* f) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
-__device__ __forceinline__ float sigmoidf(float a) { return 1.0f / (1.0f + expf(-a)); }
+// Logistic function from the hardware exp2 and reciprocal (each about 1 ulp in
+// float32): the full-precision expf and IEEE division would make the conv
+// kernels instruction-bound. Large |a| saturates to 0 or 1 (exp2 overflows to
+// inf, whose reciprocal is 0).
+__device__ __forceinline__ float sigmoidf(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+}
 
 // ---------------------------------------------------------------- tree conv
 
@@ -100,21 +106,46 @@ constexpr int kConvTB = 16;          // tokens per forward / dx workgroup
 constexpr int kConvTokBlock = 128;   // tokens per dw / db partial (g pass)
 constexpr int kConvMaxDesc = 48;     // listed descendants per token in the dx pass
 
-// Ancestor table of tokens [t0, t0 + n): anc[i][m] = m-th ancestor of
-// t0 + i (m < K), -1 past a root or for tokens past T. One thread per token
-// walks its parents, so the row loads that follow are independent.
-__device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int t0, int n, int T, int K,
-                                               int (*anc)[kConvMaxK]) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+// Ancestor table of tokens [t0, t0 + N): anc[i][m] = m-th ancestor of
+// t0 + i (m < K), -1 past a root or for tokens past T. The parents of the
+// window [t0 - (kConvMaxK - 1), t0 + N) are read in one parallel pass into
+// pl (LDS, N + kConvMaxK - 1 entries); one thread per token then walks its
+// parents there, reading HBM only where a node's first token points outside
+// the window. All threads of the workgroup call it (it holds a barrier).
+template <int N>
+__device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int t0, int T, int K,
+                                               int (*anc)[kConvMaxK], int* pl) {
+  const int base = t0 - (kConvMaxK - 1);
+  for (int r = threadIdx.x; r < N + kConvMaxK - 1; r += blockDim.x) {
+    const int t = base + r;
+    pl[r] = (t >= 0 && t < T) ? par[t] : -1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
     int s = t0 + i < T ? t0 + i : -1;
 #pragma unroll
     for (int m = 0; m < kConvMaxK; ++m) {
       if (m < K) {
         anc[i][m] = s;
-        if (s >= 0) s = par[s];
+        if (s >= 0) s = s >= base ? pl[s - base] : par[s];
       }
     }
   }
+}
+
+// Whether every tap of the tokens [t0, t0 + n) in the ancestor table is on a
+// chain (anc[i][m] = t0 + i - m for m < K) and every token is below T: then
+// the kernels take all inputs from the tile without per-tap checks.
+__device__ __forceinline__ bool conv_tile_is_chain(const int (*anc)[kConvMaxK], int t0, int n, int T, int K) {
+  bool ok = true;
+  if (threadIdx.x < n) {
+    const int i = threadIdx.x;
+    ok = t0 + i < T;
+#pragma unroll
+    for (int m = 0; m < kConvMaxK; ++m)
+      if (m < K) ok = ok && anc[i][m] == t0 + i - m;
+  }
+  return __syncthreads_and(ok) != 0;
 }
 
 // weights of channels c0..c0+7 in tap order m (tap m multiplies the m-th ancestor)
@@ -174,6 +205,19 @@ struct ConvTile {
         rows[r].zero();
     }
   }
+  // a_i += sum over taps of w_m x_{t-m}, for a tile whose every tap is on a
+  // chain (the m-th ancestor of t is t - m): all inputs are in the tile
+  __device__ __forceinline__ void chain_taps(int i, int K, const float (*wr)[8], float* a) const {
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      if (m < K) {
+        float xv[8];
+        rows[i + KM - 1 - m].get(xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xv[e], a[e]);
+      }
+    }
+  }
   // input of tap m of tile token i (ancestor s, -1 past a root)
   __device__ __forceinline__ void tap(const Tio* __restrict__ x, int s, int t, int i, int m, int C, int c0,
                                       float* xv) const {
@@ -194,18 +238,38 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __res
                                                                 const int* __restrict__ par, int T, int C, int K,
                                                                 int act, Tio* __restrict__ y) {
   __shared__ int anc[kConvTB][kConvMaxK];
+  __shared__ int pl[kConvTB + kConvMaxK - 1];
   const int t0 = blockIdx.x * kConvTB;
-  conv_ancestors(par, t0, kConvTB, T, K, anc);
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   const bool cok = c0 < C;
+  // rows, weights and bias are all in flight while the ancestor table forms
   ConvTile<Tio, KM> tile;
-  if (cok) tile.load(x, t0, T, C, c0);
-  __syncthreads();
-  if (!cok) return;
   float wr[KM][8], br[8];
-  conv_weights<KM>(w, c0, K, wr);
+  if (cok) {
+    tile.load(x, t0, T, C, c0);
+    conv_weights<KM>(w, c0, K, wr);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+    for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+  }
+  conv_ancestors<kConvTB>(par, t0, T, K, anc, pl);
+  __syncthreads();
+  const bool chain = conv_tile_is_chain(anc, t0, kConvTB, T, K);
+  if (!cok) return;
+  if (chain) {
+#pragma unroll
+    for (int i = 0; i < kConvTB; ++i) {
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = br[e];
+      tile.chain_taps(i, K, wr, a);
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = a[e] * sigmoidf(a[e]);
+      }
+      st8f(y + (size_t)(t0 + i) * C + c0, a);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kConvTB; ++i) {
     const int t = t0 + i;
@@ -240,15 +304,19 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     const float* __restrict__ bias, const int* __restrict__ par, int T, int C, int K, int act, Tio* __restrict__ gbuf,
     float* __restrict__ part) {
   __shared__ int anc[kConvTokBlock][kConvMaxK];
+  __shared__ int pl[kConvTokBlock + kConvMaxK - 1];
   const int tb = blockIdx.x * kConvTokBlock;
-  conv_ancestors(par, tb, kConvTokBlock, T, K, anc);
-  __syncthreads();
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
-  if (c0 >= C) return;
   float wr[KM][8], br[8];
-  conv_weights<KM>(w, c0, K, wr);
+  if (c0 < C) {
+    conv_weights<KM>(w, c0, K, wr);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+    for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+  }
+  conv_ancestors<kConvTokBlock>(par, tb, T, K, anc, pl);
+  __syncthreads();
+  const bool chain = conv_tile_is_chain(anc, tb, kConvTokBlock, T, K);
+  if (c0 >= C) return;
   float dw[KM][8], db[8];
 #pragma unroll
   for (int m = 0; m < KM; ++m)
@@ -271,7 +339,11 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
 #pragma unroll
         for (int m = 0; m < KM; ++m) {
           if (m < K) {
-            tile.tap(x, anc[sub + i][m], t, i, m, C, c0, xt[m]);
+            // a chain block takes every input from the tile, without per-tap checks
+            if (chain)
+              tile.rows[i + KM - 1 - m].get(xt[m]);
+            else
+              tile.tap(x, anc[sub + i][m], t, i, m, C, c0, xt[m]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xt[m][e], a[e]);
           }
@@ -321,6 +393,9 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
   __shared__ int dlist[kConvTB][kConvMaxDesc];
   __shared__ int dcount[kConvTB];
   const int t0 = blockIdx.x * kConvTB;
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  float wr[KM][8];
+  if (c0 < C) conv_weights<KM>(w, c0, K, wr);
   for (int i = threadIdx.x; i < kConvTB; i += blockDim.x) {
     const int j = t0 + i;
     int cnt = 0;
@@ -341,10 +416,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
     dcount[i] = cnt;
   }
   __syncthreads();
-  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
-  float wr[KM][8];
-  conv_weights<KM>(w, c0, K, wr);
   const int n = min(kConvTB, T - t0);
   for (int i = 0; i < n; ++i) {
     const int j = t0 + i;
