@@ -390,33 +390,74 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
                                                                    const int* __restrict__ pos,
                                                                    const int* __restrict__ se, int T, int C, int K,
                                                                    Tio* __restrict__ dx) {
+  constexpr int NWIN = kConvTB + kConvMaxK;  // pos / se of [t0, t0 + NWIN) staged in LDS
   __shared__ int dlist[kConvTB][kConvMaxDesc];
   __shared__ int dcount[kConvTB];
+  __shared__ int pw[NWIN], sw[NWIN];
   const int t0 = blockIdx.x * kConvTB;
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   float wr[KM][8];
   if (c0 < C) conv_weights<KM>(w, c0, K, wr);
+  for (int r = threadIdx.x; r < NWIN; r += blockDim.x) {
+    const int t = t0 + r;
+    pw[r] = t < T ? pos[t] : 0;
+    sw[r] = t < T ? se[t] : 0;
+  }
+  __syncthreads();
+  // the walk reads LDS inside the window and HBM past it
+  auto pos_at = [&](int t) { return t - t0 < NWIN ? pw[t - t0] : pos[t]; };
+  auto se_at = [&](int t) { return t - t0 < NWIN ? sw[t - t0] : se[t]; };
   for (int i = threadIdx.x; i < kConvTB; i += blockDim.x) {
     const int j = t0 + i;
     int cnt = 0;
     if (j < T) {
-      const int pj = pos[j], end = se[j];
+      const int pj = pw[i], end = sw[i];
       int t = j + 1;
       while (t < end) {
-        const int dd = pos[t] - pj;
+        const int dd = pos_at(t) - pj;
         if (dd < K) {
           if (cnt < kConvMaxDesc) dlist[i][cnt] = (t << 3) | dd;
           ++cnt;
           ++t;
         } else {
-          t = se[t];
+          t = se_at(t);
         }
       }
     }
     dcount[i] = cnt;
   }
-  __syncthreads();
+  // chain tile: every token j has exactly the descendants j + 1 .. j + K - 1
+  // (depths 1 .. K - 1) within K - 1 levels, so dx_j = sum_m w_m g_{j+m}
+  // from a tile of g rows loaded up front
+  bool ch = true;
+  if (threadIdx.x < kConvTB) {
+    const int i = threadIdx.x, j = t0 + i;
+    ch = j < T && dcount[i] == K - 1;
+    for (int q = 0; q < K - 1 && ch; ++q) ch = dlist[i][q] == (((j + q + 1) << 3) | (q + 1));
+  }
+  const bool chain = __syncthreads_and(ch) != 0;
   if (c0 >= C) return;
+  if (chain) {
+    ConvTile<Tio, KM> gt;  // gt.rows[r] = g_{t0 + r}
+    gt.load(gbuf, t0 + KM - 1, T, C, c0);
+#pragma unroll
+    for (int i = 0; i < kConvTB; ++i) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        if (m < K) {
+          float g[8];
+          gt.rows[i + m].get(g);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
+        }
+      }
+      st8f(dx + (size_t)(t0 + i) * C + c0, acc);
+    }
+    return;
+  }
   const int n = min(kConvTB, T - t0);
   for (int i = 0; i < n; ++i) {
     const int j = t0 + i;
