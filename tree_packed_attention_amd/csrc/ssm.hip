@@ -10,13 +10,16 @@
 //   delta  h_t = alpha_t (I - beta_t k_t k_t^T) h_{par(t)} + beta_t k_t v_t^T,
 //          o_t = h_t^T q_t,  alpha_t = exp(g_t)
 //
-// Conv: a workgroup takes a tile of tokens; one thread per token first
-// lists its K-1 ancestors in LDS, then every thread (8 channels) loads the
-// ancestor rows independently. The backward forms g = dy * act'(a) once,
-// gathers dx_j over the descendants of j at most K-1 levels below it (listed
-// per token in LDS by a walk of the preorder range (j, se[j]) that jumps over
-// every deeper subtree), and reduces dw / db over token blocks in a fixed
-// order.
+// Conv: a workgroup takes a tile of tokens and every thread 8 channels. The
+// tile's rows and the K-1 rows before it are loaded up front; one thread per
+// token lists its K-1 ancestors in LDS (walking parents read into LDS for the
+// tile window), and taps whose ancestor is not the row before are loaded
+// apart. A tile on a chain (every tap's ancestor is t - m) skips the
+// per-tap checks. The backward forms g = dy * act'(a) once, gathers dx_j over
+// the descendants of j at most K-1 levels below it (listed per token in LDS
+// by a walk of the preorder range (j, se[j]) that jumps over every deeper
+// subtree; on a chain they are j + 1 .. j + K - 1 and come from a tile of g
+// rows), and reduces dw / db over token blocks in a fixed order.
 //
 // Gated delta rule, per v-head, in chunks of <= 64 tokens inside tree nodes
 // (the host plan, tree_gdn_plan, gives chunk ranges, chunk parents and the
@@ -35,6 +38,8 @@
 //      gc_j), j <= i) vn
 // The start state of a chunk's first child chunk is the chunk's end state, so
 // a chain that starts under chunk p loads the stored start state of p + 1.
+// The backward (tree_gdn_bwd) runs the same routing in reverse: see the
+// section "gated delta rule, backward" below.
 //
 // Workspace (chunk-local, rows past a chunk's length are zero):
 //   gc  [Hv][nc][64] f32        (past the chunk length: the last value)
