@@ -114,6 +114,27 @@ def test_conv_multistep_full_size_channel_slice():
     assert rel_l2(host(dw[cs]), rdw) <= 1e-4 and rel_l2(host(db[cs]), rdb) <= 1e-4
 
 
+def test_conv_max_size_tree():
+    """The largest tree (agentic_l: 131072 tokens, depth up to 5842, forks at
+    every level) at 256 channels, K = 4, bf16, SiLU: every token against the
+    oracle."""
+    seqs, groups = workloads.sequences("agentic_l")
+    p, po = _pack(seqs, groups)
+    T, C, K = p["T"], 256, 4
+    x, dy, w, b = workloads.conv_inputs(T, C, K, "bf16", 4, device="cuda")
+    par = torch.from_numpy(p["parent"]).cuda()
+    y = ta.tree_conv_fwd(x, w, b, par, 1)
+    dx, dw, db = ta.tree_conv_bwd(x, dy, w, b, par, torch.from_numpy(p["pos"]).cuda(),
+                                  torch.from_numpy(p["subtree_end"]).cuda(), 1)
+    torch.cuda.synchronize()
+    print(f"\n[case] conv agentic_l T={T}", flush=True)
+    ry, _ = OS.tree_conv(host(x), host(w), host(b), po["par"])
+    rdx, rdw, rdb = OS.tree_conv_backward(host(x), host(w), host(b), po["par"], host(dy))
+    assert out_err(host(y), ry) <= OUT_TOL
+    assert rel_l2(host(dx), rdx) <= GRAD_TOL
+    assert rel_l2(host(dw), rdw) <= 1e-4 and rel_l2(host(db), rdb) <= 1e-4
+
+
 def test_conv_bwd_deterministic():
     seqs, groups = workloads.random_forest(8, [400, 300])
     p, _ = _pack(seqs, groups)
@@ -220,7 +241,7 @@ def _gdn_bwd_case(seqs, groups, H, Hv, dk, dv, dtype, chunk, seed=17):
 
 def _check_grads(tag, got, ref):
     for name, a, b in zip(GRAD_NAMES, got, ref):
-        a = host(a)
+        a = host(a) if isinstance(a, torch.Tensor) else np.asarray(a)
         rl = rel_l2(a, b)
         mx = float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1.0 if not np.any(b) else 1e-30))
         print(f"{tag} {name}: rel-l2 {rl:.2e} max-err/max-ref {mx:.2e}", flush=True)
@@ -262,3 +283,49 @@ def test_gdn_bwd_deterministic():
     *_, g2 = _gdn_bwd_case(seqs, groups, 2, 4, 128, 128, "bf16", 16)
     for name, a, b in zip(GRAD_NAMES, g1, g2):
         assert torch.equal(a, b), name
+
+
+def _leaf_path(par, leaf):
+    path = [int(leaf)]
+    while par[path[-1]] >= 0:
+        path.append(int(par[path[-1]]))
+    return np.array(path[::-1])
+
+
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_gdn_max_size_tree_one_path(chunk):
+    """The largest tree (agentic_l: 131072 tokens, 204 nodes, 124 chains on 7
+    levels) with dO nonzero on one root-to-leaf path only. The outputs of the
+    path and every gradient are then those of that path run alone as one
+    sequence (the oracle's per-token recurrence on it); every token off the
+    path gets exactly zero gradient, since no output it reaches has a
+    gradient (no leakage between sibling branches)."""
+    seqs, groups = workloads.sequences("agentic_l")
+    p, po = _pack(seqs, groups)
+    par = po["par"]
+    T, H, Hv, d = p["T"], 2, 4, 64
+    plan = ta.tree_gdn_plan(p["node_start"], p["node_end"], p["node_parent"], chunk)
+    q, k, v, g, beta = workloads.gdn_inputs(T, H, Hv, d, d, "bf16", 5, device="cuda")
+    has_child = np.zeros(T, bool)
+    has_child[par[par >= 0]] = True
+    leaves = np.nonzero(~has_child)[0]
+    path = _leaf_path(par, leaves[len(leaves) // 3])
+    on = torch.zeros(T, dtype=torch.bool)
+    on[torch.from_numpy(path)] = True
+    do = workloads.gdn_dout(T, Hv, d, "bf16", 5, device="cuda")
+    do[~on.cuda()] = 0
+    ws = ta.gdn_workspace(q, v, plan, backward=True)
+    o = ta.tree_gdn_fwd(q, k, v, g, beta, plan, workspace=ws)
+    grads = ta.tree_gdn_bwd(q, k, v, g, beta, do, plan, ws)
+    torch.cuda.synchronize()
+    print(f"\n[case] agentic_l chunk {chunk}: {int(plan[0])} chunks, {int(plan[1])} chains, {int(plan[2])} levels, "
+          f"path of {len(path)} tokens", flush=True)
+    chain = np.arange(len(path)) - 1
+    sel = lambda t: host(t[torch.from_numpy(path).cuda()])
+    ro = OS.gdn_tree(sel(q), sel(k), sel(v), sel(g), sel(beta), chain)
+    assert out_err(sel(o), ro) <= OUT_TOL and rel_l2(sel(o), ro) <= 1e-2
+    ref = OS.gdn_tree_backward(sel(q), sel(k), sel(v), sel(g), sel(beta), chain, sel(do))
+    _check_grads(f"agentic_l chunk {chunk} path", [sel(x) for x in grads], ref)
+    off = ~on.cuda()
+    for name, x in zip(GRAD_NAMES, grads):
+        assert float(x[off].abs().max()) == 0.0, name
