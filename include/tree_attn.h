@@ -397,7 +397,10 @@ int tree_gdn_plan(const int32_t* node_start, const int32_t* node_end, const int3
  * host memory (its header and level table drive the launches).
  * dk, dv in {64, 128}; Hv a multiple of H.
  * workspace: >= tree_gdn_workspace_bytes(H, Hv, dk, dv, n_chunks) bytes,
- * 256-byte aligned. Asynchronous on `stream`; one launch per chain level.
+ * 256-byte aligned; a workspace of tree_gdn_bwd_workspace_bytes serves as
+ * well and is what a later tree_gdn_bwd of this call needs (the forward
+ * leaves its chunk states and WY factors there). Asynchronous on `stream`;
+ * one launch per chain level.
  * Errors: TA_EINVAL, TA_EUNSUPPORTED (dk, dv), TA_EHIP.
  * ---------------------------------------------------------------------- */
 size_t tree_gdn_workspace_bytes(int32_t H, int32_t Hv, int32_t dk, int32_t dv, int32_t n_chunks);
