@@ -334,9 +334,15 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
     if (ts >= T) break;
     ConvTile<Tio, KM> tile;
     tile.load(x, ts, T, C, c0);
+    // dy one token ahead, from a clamped (always valid) row, so its load is
+    // issued before the current token's g store: stores share the wait
+    // counter with loads, and a load issued after a store waits for it too
+    Raw8<Tio> dcur, dnext;
+    dcur.load(dy + (size_t)min(ts, T - 1) * C + c0);
 #pragma unroll
     for (int i = 0; i < kConvTB; ++i) {
       const int t = ts + i;
+      if (i + 1 < kConvTB) dnext.load(dy + (size_t)min(t + 1, T - 1) * C + c0);
       if (t < T) {
         float a[8], g[8], xt[KM][8];
 #pragma unroll
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
             for (int e = 0; e < 8; ++e) a[e] = fmaf(wr[m][e], xt[m][e], a[e]);
           }
         }
-        ld8f(dy + (size_t)t * C + c0, g);
+        dcur.get(g);
         if (act) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -371,6 +377,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_g_kernel(
             for (int e = 0; e < 8; ++e) dw[m][e] = fmaf(g[e], xt[m][e], dw[m][e]);
           }
       }
+      dcur = dnext;
     }
   }
   // partials [block][c][K + 1]: taps in weight order (index K-1-m), then db
