@@ -1542,6 +1542,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
     }
     __syncthreads();
     // dq += dS k + e^gc (dO h0^T); dk += dS^T q; dw = -dvn h0^T
+    f32x16 y = f32x16{};
     if (own) {
       for (int a = 0; a < 2 * (rb + 1); ++a)
         aq = mfma32x32x16(row8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
@@ -1549,7 +1550,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
       for (int a = 2 * rb; a < 4; ++a)
         ak = mfma32x32x16(col8(&sm.dS[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
                           col8(&sm.q[0][0], DK + 8, col, 16 * a + 8 * lg), ak);
-      f32x16 x = f32x16{}, y = f32x16{};
+      f32x16 x = f32x16{};
 #pragma unroll 2
       for (int a = 0; a < DV / 16; ++a) {
         const bf16x8 hB = col8(&sm.hb[0][0], DK + 8, col, 16 * a + 8 * lg);
@@ -1568,6 +1569,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
 #pragma unroll
         for (int i4 = 0; i4 < 16; ++i4) sm.rs[cb][32 * rb + crow(i4, lg)] = pq[i4];
       }
+    }
+    // dh_end loads first, then the dw stores (a load issued after a store
+    // would wait for it)
+    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
+    if (own) {
       bf16* wo = dwt + (hc * DK + col) * kCh + 32 * rb;
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
@@ -1577,7 +1583,6 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
         *reinterpret_cast<bf16x4*>(wo + 8 * j4 + 4 * lg) = o4;
       }
     }
-    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
     __syncthreads();
     // dh_end replaces h0 (each thread rewrites the elements it reads); s = <dh_end, h0>
     float sp = 0.0f;
@@ -1777,16 +1782,6 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
       }
     }
     __syncthreads();
-    // dv rows out (rows past the chunk are not written)
-#pragma unroll
-    for (int it = 0; it < kCh * (DV / 8) / 512; ++it) {
-      const int idx = tid + 512 * it, j = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
-      if (j < L) {
-        Tio* o = dv + ((size_t)(t0 + j) * Hv + hv) * DV + e0;
-#pragma unroll
-        for (int q8 = 0; q8 < 8; ++q8) o[q8] = sm.dvs[j][e0 + q8];
-      }
-    }
     // dM = -(dbv u^T + dbk w^T) on the lower blocks: waves 4-6 form the w
     // half and hand it over through LDS; u, w rows come from HBM / L2
     f32x16 dmacc = f32x16{};
@@ -1837,6 +1832,17 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
       if (lg == 0) sm.cs[wv][j0] = csum;
     }
     __syncthreads();
+    // dv rows out (rows past the chunk are not written), after the dM phase's
+    // row loads: a load issued after a store would wait for it
+#pragma unroll
+    for (int it = 0; it < kCh * (DV / 8) / 512; ++it) {
+      const int idx = tid + 512 * it, j = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
+      if (j < L) {
+        Tio* o = dv + ((size_t)(t0 + j) * Hv + hv) * DV + e0;
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) o[q8] = sm.dvs[j][e0 + q8];
+      }
+    }
     // dk += (G + G^T) k
     if (own_k) {
       const int d = 32 * cb + lc;
