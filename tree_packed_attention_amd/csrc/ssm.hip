@@ -46,8 +46,8 @@
 //   u   [Hv][nc][64][dv] f32
 //   w   [Hv][nc][64][dk] bf16   (columns in swap23 order within each 16)
 //   kd  [Hv][nc][dk][64] bf16   (k^T exp(gc_last - gc), zero past the length)
-//   vnt [Hv][nc][dv][64] bf16
-//   h0  [nc][Hv][dv][dk] bf16   (start state of each chunk, transposed)
+//   vnt [Hv][nc] x (dv x 64) bf16, column-grouped (vn^T; cr_off below)
+//   h0  [nc][Hv] x (dv x dk) bf16, column-grouped (start state of each chunk)
 //   tt  [Hv][nc][64][64] bf16   ((I + M)^-1 transposed, for the backward)
 #include <hip/hip_runtime.h>
 
@@ -574,8 +574,8 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
 //   qgt  [Hv][nc][dk][64] bf16   (q e^gc)^T
 //   wt   [Hv][nc][dk][64] bf16   w^T
 //   dot  [Hv][nc][dv][64] bf16   dO^T
-//   dvnt [Hv][nc][dv][64] bf16   dvn^T
-//   dhe  [nc][Hv][dv][dk] bf16   end-state gradient of each chunk, transposed
+//   dvnt [Hv][nc] x (dv x 64) bf16, column-grouped   dvn^T
+//   dhe  [nc][Hv] x (dv x dk) bf16, column-grouped   end-state gradient of each chunk
 //   dwt  [Hv][nc][dk][64] bf16   dw^T
 //   dgca [Hv][nc][64] f32        decay gradient, output / state part
 //   dka  [H][nc][64][dk] f32     dk, output / state part
@@ -606,6 +606,40 @@ GdnBwdLayout gdn_bwd_layout(int H, int Hv, int dk, int dv, int nc, int nch) {
   L.total = o;
   return L;
 }
+
+// Column-grouped layout of the chunk states and of the transposed chunk rows
+// (h0 and dh_end: columns dv, rows dk; vn^T and dvn^T: columns dv, rows the
+// chunk's 64): 32-column groups, then 32-row blocks, 8-row groups, the 32
+// columns and 8 rows. A wave's stores from MFMA C registers (lane = column,
+// 4 consecutive rows) are contiguous 512-byte runs, and 8 consecutive rows
+// of a column are 16 contiguous bytes. Offset of (column e, row r) within
+// one C x R block:
+template <int R>
+__device__ __forceinline__ int cr_off(int e, int r) {
+  return (((e >> 5) * (R / 32) + (r >> 5)) * 4 + ((r & 31) >> 3)) * 256 + (e & 31) * 8 + (r & 7);
+}
+
+// A C x R block in the column-grouped layout into LDS rows of stride ls
+// (l[e * ls + r]), read in its memory order (coalesced): issue() starts the
+// loads, commit() stores them.
+template <int C, int R, int NT>
+struct CrTileLoad {
+  static_assert((C * R / 8) % NT == 0, "whole rounds of the workgroup's threads");
+  static constexpr int N = C * R / 8 / NT;
+  bf16x8 x[N];
+  __device__ __forceinline__ void issue(const bf16* __restrict__ g, int tid) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) x[it] = load8(g + (size_t)(tid + NT * it) * 8);
+  }
+  __device__ __forceinline__ void commit(bf16* l, int ls, int tid) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int idx = tid + NT * it;
+      const int ec = idx & 31, gg = (idx >> 5) & 3, rb = (idx >> 7) % (R / 32), eg = (idx >> 7) / (R / 32);
+      *reinterpret_cast<bf16x8*>(l + (32 * eg + ec) * ls + 32 * rb + 8 * gg) = x[it];
+    }
+  }
+};
 
 // T = (I + M)^-1 for a unit lower-triangular 64 x 64 system, by 16 x 16
 // blocks: T_ii = (I + M_ii)^-1 by forward substitution (one lane per
@@ -816,7 +850,7 @@ template <int DK, int DV>
 __device__ __forceinline__ void gdn_state_chunk(const StateBuf<DK, DV>& sb, float gl, int lg, int lc, int n,
                                                 f32x16 (&h)[DK / 32], bf16* __restrict__ vo, bf16* __restrict__ ho) {
   constexpr int NB = DK / 32;
-  // store the start state (bf16, transposed: [dv][dk])
+  // store the start state (bf16, column-grouped: column n, rows of dk)
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -824,7 +858,7 @@ __device__ __forceinline__ void gdn_state_chunk(const StateBuf<DK, DV>& sb, floa
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (bf16)h[b][4 * j + e];
-      *reinterpret_cast<bf16x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
+      *reinterpret_cast<bf16x4*>(ho + cr_off<DK>(n, 32 * b + 8 * j + 4 * lg)) = x;
     }
   // vn = u - w h0: B operand of k-step a = -h0 registers 8(a%2)..+7 of block a/2
   // (w's columns are stored in the matching swap23 order)
@@ -842,7 +876,7 @@ __device__ __forceinline__ void gdn_state_chunk(const StateBuf<DK, DV>& sb, floa
     for (int a = 0; a < DK / 16; ++a)
       vn[mb] = mfma32x32x16(lds128(sb.w + toff<DK>(32 * mb + lc, 16 * a + 8 * lg)), hb[a], vn[mb]);
   }
-  // vn, transposed [dv][64], for the output stage
+  // vn^T (column-grouped: column n, the chunk's rows), for the output stage
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -850,7 +884,7 @@ __device__ __forceinline__ void gdn_state_chunk(const StateBuf<DK, DV>& sb, floa
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
-      *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+      *reinterpret_cast<bf16x4*>(vo + cr_off<kCh>(n, 32 * mb + 8 * j + 4 * lg)) = x;
     }
   // h = exp(gc_last) h0 + kd^T vn. Contraction over the chunk rows in the
   // order whose k-step a, slot s is row 16a + 8(s/4) + 4(lane/32) + s%4 =
@@ -915,12 +949,12 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_state_kernel(
     for (int b = 0; b < NB; ++b) h[b] = f32x16{};
   } else {
     // the start state of p's first child chunk p + 1 is p's end state
-    const bf16* hp = h0w + (((size_t)(p + 1) * Hv + hv) * DV + n) * DK;
+    const bf16* hp = h0w + ((size_t)(p + 1) * Hv + hv) * DV * DK;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hp + 32 * b + 8 * j + 4 * lg);
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hp + cr_off<DK>(n, 32 * b + 8 * j + 4 * lg));
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[b][4 * j + e] = (float)x[e];
       }
@@ -928,8 +962,8 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_state_kernel(
   const StateBuf<DK, DV> sb0{w0, k0, u0}, sb1{w1, k1, u1};
   auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
   auto out_ptrs = [&](int c, bf16** vo, bf16** ho) {
-    *vo = vnt + (((size_t)hv * nc + c) * DV + n) * kCh;
-    *ho = h0w + (((size_t)c * Hv + hv) * DV + n) * DK;
+    *vo = vnt + ((size_t)hv * nc + c) * DV * kCh;
+    *ho = h0w + ((size_t)c * Hv + hv) * DV * DK;
   };
   issue(cb, w0, k0, u0);
   float gl0 = gl_of(cb), gl1 = 0.0f;
@@ -995,10 +1029,10 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
 #pragma unroll
     for (int bb = 0; bb < NDW; ++bb) {
       const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
-      const bf16* hp = h0w + (((size_t)c * Hv + hv) * DV + d) * DK;
+      const bf16* hp = h0w + ((size_t)c * Hv + hv) * DV * DK;
 #pragma unroll
       for (int a = 0; a < DK / 16; ++a) {
-        const bf16x8 A = load8(hp + 16 * a + 8 * lg);
+        const bf16x8 A = load8(hp + cr_off<DK>(d, 16 * a + 8 * lg));
         acc[bb] = mfma32x32x16(A, qs[a], acc[bb]);
       }
     }
@@ -1023,8 +1057,9 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
 #pragma unroll
       for (int bb = 0; bb < NDW; ++bb) {
         const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
-        const bf16* vp = vnt + (hc * DV + d) * kCh + 16 * a2 + 4 * lg;
-        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 8));
+        const bf16* vp = vnt + hc * DV * kCh;
+        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 4 * lg)),
+                             *reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 8 + 4 * lg)));
         acc[bb] = mfma32x32x16(A, pb[h2], acc[bb]);
       }
     }
@@ -1259,7 +1294,7 @@ struct BStateBuf {
 };
 
 template <int DK, int DV>
-__device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, float gl, int lg, int lc,
+__device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, float gl, int lg, int lc, int n,
                                                     f32x16 (&dh)[DK / 32], const float* __restrict__ dvl_row,
                                                     const bf16* __restrict__ do_row, bf16* __restrict__ vo,
                                                     bf16* __restrict__ ho) {
@@ -1275,7 +1310,7 @@ __device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, flo
   for (int a = 0; a < 4; ++a)
     db[a] = cat(*reinterpret_cast<const bf16x4*>(do_row + 16 * a + 4 * lg),
                 *reinterpret_cast<const bf16x4*>(do_row + 16 * a + 8 + 4 * lg));
-  // the end-state gradient (bf16, [dv][dk] like the forward's start states)
+  // the end-state gradient (bf16, column-grouped like the forward's start states)
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -1283,7 +1318,7 @@ __device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, flo
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (bf16)dh[b][4 * j + e];
-      *reinterpret_cast<bf16x4*>(ho + 32 * b + 8 * j + 4 * lg) = x;
+      *reinterpret_cast<bf16x4*>(ho + cr_off<DK>(n, 32 * b + 8 * j + 4 * lg)) = x;
     }
   bf16x8 hb[DK / 16];
 #pragma unroll
@@ -1308,7 +1343,7 @@ __device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, flo
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (bf16)vn[mb][4 * j + e];
-      *reinterpret_cast<bf16x4*>(vo + 32 * mb + 8 * j + 4 * lg) = x;
+      *reinterpret_cast<bf16x4*>(vo + cr_off<kCh>(n, 32 * mb + 8 * j + 4 * lg)) = x;
     }
   const float al = expf(gl);
 #pragma unroll
@@ -1390,8 +1425,8 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_bwd_state_kernel(
   auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
   auto run = [&](const BStateBuf<DK>& sb, int c, float gl) {
     const size_t hc = (size_t)hv * nc + c;
-    gdn_bwd_state_chunk<DK, DV>(sb, gl, lg, lc, dh, dvlt + (hc * DV + n) * kCh, dot + (hc * DV + n) * kCh,
-                                dvnt + (hc * DV + n) * kCh, dhe + (((size_t)c * Hv + hv) * DV + n) * DK);
+    gdn_bwd_state_chunk<DK, DV>(sb, gl, lg, lc, n, dh, dvlt + (hc * DV + n) * kCh, dot + (hc * DV + n) * kCh,
+                                dvnt + hc * DV * kCh, dhe + ((size_t)c * Hv + hv) * DV * DK);
   };
   add_children(ce - 1);
   issue(ce - 1, g0, q0, x0);
@@ -1490,12 +1525,12 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
       sm.dec[tid] = tid < L ? expf(gl - gv) : 0.0f;
     }
     TileLoad<kCh, DV, Tio, 512> ldo;
-    TileLoad<DV, kCh, bf16, 512> lvn, ldvn;
-    TileLoad<DV, DK, bf16, 512> lh0, ldh;
+    CrTileLoad<DV, kCh, 512> lvn, ldvn;
+    CrTileLoad<DV, DK, 512> lh0, ldh;
     ldo.issue(dout + ((size_t)t0 * Hv + hv) * DV, (size_t)Hv * DV, tid, L);
-    lvn.issue(vnt + hc * DV * kCh, kCh, tid, DV);
-    ldvn.issue(dvnt + hc * DV * kCh, kCh, tid, DV);
-    lh0.issue(h0w + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
+    lvn.issue(vnt + hc * DV * kCh, tid);
+    ldvn.issue(dvnt + hc * DV * kCh, tid);
+    lh0.issue(h0w + ((size_t)c * Hv + hv) * DV * DK, tid);
     ldo.commit(&sm.dO[0][0], DV + 8, tid);
     lvn.commit(&sm.vnT[0][0], kCh + 8, tid);
     ldvn.commit(&sm.dvnT[0][0], kCh + 8, tid);
@@ -1572,7 +1607,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
     }
     // dh_end loads first, then the dw stores (a load issued after a store
     // would wait for it)
-    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, DK, tid, DV);
+    ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, tid);
     if (own) {
       bf16* wo = dwt + (hc * DK + col) * kCh + 32 * rb;
 #pragma unroll
@@ -1588,7 +1623,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
     float sp = 0.0f;
 #pragma unroll
     for (int it = 0; it < ldh.N; ++it) {
-      const int idx = tid + 512 * it, e = idx / (DK / 8), d0 = 8 * (idx % (DK / 8));
+      const int idx = tid + 512 * it;
+      const int e = 32 * ((idx >> 7) / (DK / 32)) + (idx & 31), d0 = 32 * ((idx >> 7) % (DK / 32)) + 8 * ((idx >> 5) & 3);
       const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&sm.hb[e][d0]);
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) sp += (float)ldh.x[it][s2] * (float)ov[s2];
@@ -1730,11 +1766,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     // rows j of block rb need i >= 32 rb. Right-hand sides are HBM / L2 rows.
     if (own_v) {
       const int e = 32 * cb + lc;
-      const bf16* brow = dvnt + (hc * DV + e) * kCh;
+      const bf16* dvb = dvnt + hc * DV * kCh;
       f32x16 acc = f32x16{};
       for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
-                           acc);
+        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                           load8(dvb + cr_off<kCh>(e, 16 * a + 8 * lg)), acc);
       float pv[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
