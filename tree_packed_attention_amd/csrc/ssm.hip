@@ -569,11 +569,11 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
 }
 
 // Backward workspace, after the forward's (chunk-local like it):
-//   dvlt [Hv][nc][dv][64] f32    (P^T dO)^T
+//   dvlt [Hv][nc] x (dv x 64) f32, column-grouped   (P^T dO)^T
 //   kgl  [Hv][nc][64][dk] bf16   k e^(gl - gc), swap23 columns
 //   qgt  [Hv][nc][dk][64] bf16   (q e^gc)^T
 //   wt   [Hv][nc][dk][64] bf16   w^T
-//   dot  [Hv][nc][dv][64] bf16   dO^T
+//   dot  [Hv][nc] x (dv x 64) bf16, column-grouped  dO^T
 //   dvnt [Hv][nc] x (dv x 64) bf16, column-grouped   dvn^T
 //   dhe  [nc][Hv] x (dv x dk) bf16, column-grouped   end-state gradient of each chunk
 //   dwt  [Hv][nc][dk][64] bf16   dw^T
@@ -1226,10 +1226,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
     *reinterpret_cast<bf16x8*>(qgt + (hc * DK + d) * kCh + i0) = qo;
     *reinterpret_cast<bf16x8*>(wt + (hc * DK + d) * kCh + i0) = wo;
   }
+  // dO^T in the column-grouped layout, written in its memory order
 #pragma unroll
   for (int it = 0; it < DV * (kCh / 8) / 256; ++it) {
-    const int idx = tid + 256 * it, e = idx / (kCh / 8), i0 = 8 * (idx % (kCh / 8));
-    *reinterpret_cast<bf16x8*>(dot + (hc * DV + e) * kCh + i0) = *reinterpret_cast<const bf16x8*>(&dT[e][i0]);
+    const int idx = tid + 256 * it;
+    const int e = 32 * (idx >> 8) + (idx & 31), i0 = 32 * ((idx >> 7) & 1) + 8 * ((idx >> 5) & 3);
+    *reinterpret_cast<bf16x8*>(dot + hc * DV * kCh + (size_t)idx * 8) = *reinterpret_cast<const bf16x8*>(&dT[e][i0]);
   }
   // kd rows with swap23 columns (the A operand of dvn += kd dh)
 #pragma unroll
@@ -1276,7 +1278,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int e = 32 * ((wv >> 1) + 2 * m) + crow(r, lg);
-      dvlt[(hc * DV + e) * kCh + j] = acc[m][r];
+      dvlt[hc * DV * kCh + cr_off<kCh>(e, j)] = acc[m][r];
     }
 }
 
@@ -1304,12 +1306,13 @@ __device__ __forceinline__ void gdn_bwd_state_chunk(const BStateBuf<DK>& sb, flo
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) dl[mb][j4] = *reinterpret_cast<const f32x4*>(dvl_row + 32 * mb + 8 * j4 + 4 * lg);
+    for (int j4 = 0; j4 < 4; ++j4)
+      dl[mb][j4] = *reinterpret_cast<const f32x4*>(dvl_row + cr_off<kCh>(n, 32 * mb + 8 * j4 + 4 * lg));
   bf16x8 db[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
-    db[a] = cat(*reinterpret_cast<const bf16x4*>(do_row + 16 * a + 4 * lg),
-                *reinterpret_cast<const bf16x4*>(do_row + 16 * a + 8 + 4 * lg));
+    db[a] = cat(*reinterpret_cast<const bf16x4*>(do_row + cr_off<kCh>(n, 16 * a + 4 * lg)),
+                *reinterpret_cast<const bf16x4*>(do_row + cr_off<kCh>(n, 16 * a + 8 + 4 * lg)));
   // the end-state gradient (bf16, column-grouped like the forward's start states)
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -1425,7 +1428,7 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_bwd_state_kernel(
   auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
   auto run = [&](const BStateBuf<DK>& sb, int c, float gl) {
     const size_t hc = (size_t)hv * nc + c;
-    gdn_bwd_state_chunk<DK, DV>(sb, gl, lg, lc, n, dh, dvlt + (hc * DV + n) * kCh, dot + (hc * DV + n) * kCh,
+    gdn_bwd_state_chunk<DK, DV>(sb, gl, lg, lc, n, dh, dvlt + hc * DV * kCh, dot + hc * DV * kCh,
                                 dvnt + hc * DV * kCh, dhe + ((size_t)c * Hv + hv) * DV * DK);
   };
   add_children(ce - 1);
