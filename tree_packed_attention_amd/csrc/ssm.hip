@@ -576,7 +576,7 @@ GdnLayout gdn_layout(int H, int Hv, int dk, int dv, int nc) {
 //   dot  [Hv][nc] x (dv x 64) bf16, column-grouped  dO^T
 //   dvnt [Hv][nc] x (dv x 64) bf16, column-grouped   dvn^T
 //   dhe  [nc][Hv] x (dv x dk) bf16, column-grouped   end-state gradient of each chunk
-//   dwt  [Hv][nc][dk][64] bf16   dw^T
+//   dwt  [Hv][nc] x (dk x 64) bf16, column-grouped   dw^T
 //   dgca [Hv][nc][64] f32        decay gradient, output / state part
 //   dka  [H][nc][64][dk] f32     dk, output / state part
 //   dhead [nch][Hv][dv][dk] f32  start-state gradient of each chain, transposed
@@ -1612,13 +1612,13 @@ __global__ __launch_bounds__(512) void gdn_bwd_out_kernel(const Tio* __restrict_
     // would wait for it)
     ldh.issue(dhe + ((size_t)c * Hv + hv) * DV * DK, tid);
     if (own) {
-      bf16* wo = dwt + (hc * DK + col) * kCh + 32 * rb;
+      bf16* wo = dwt + hc * DK * kCh;
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (bf16)(-y[4 * j4 + e]);
-        *reinterpret_cast<bf16x4*>(wo + 8 * j4 + 4 * lg) = o4;
+        *reinterpret_cast<bf16x4*>(wo + cr_off<kCh>(col, 32 * rb + 8 * j4 + 4 * lg)) = o4;
       }
     }
     __syncthreads();
@@ -1796,11 +1796,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     // dbk = T^T dw; dk += beta e^gc dbk
     if (own_k) {
       const int d = 32 * cb + lc;
-      const bf16* brow = dwt + (hc * DK + d) * kCh;
+      const bf16* dwb = dwt + hc * DK * kCh;
       f32x16 acc = f32x16{};
       for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), load8(brow + 16 * a + 8 * lg),
-                           acc);
+        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
+                           load8(dwb + cr_off<kCh>(d, 16 * a + 8 * lg)), acc);
       float pk[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
