@@ -318,6 +318,19 @@ __global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ wor
   for (int i = t; i < n; i += blockDim.x) order[atomicAdd(&hist[min(work[i], 1023)], 1)] = i;
 }
 
+// Stores 8 floats as elements [0, 8) of a caller row (one 16- or 32-byte
+// store; the row start is 16-byte aligned).
+__device__ __forceinline__ void store_row8(bf16* p, const float* f) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)f[e];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void store_row8(float* p, const float* f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
 // Loads 8 elements [c, c+8) of a caller row; zero past the row end or for
 // rows past T.
 template <typename Tio>
@@ -745,27 +758,38 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     }
   }
 
+  // Epilogue through LDS. The lane holds dQ'^T column qrow, rows
+  // d = 32b + 8(i/4) + 4lg + i%4; per-lane stores of single elements would
+  // touch a cache line per lane. Each wave stages its 32 rows scaled, as
+  // [d][row] float32, in one tile buffer (the tiles are no longer read), then
+  // a lane forms its row's output 8 columns at a time with the RoPE partner
+  // d + D/2 (R(pos)^T) and writes 16-byte pieces.
+  static_assert(DP * 32 * 4 <= TILE * 2, "a wave's dQ' rows must fit in one tile buffer");
+  __syncthreads();
+  float* ep = reinterpret_cast<float*>(w < 2 ? (w == 0 ? kb0 : kb1) : (w == 2 ? vb0 : vb1));
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ep[(32 * b + 8 * (i >> 2) + 4 * lg + (i & 3)) * 32 + lc] = acc[b][i] * scale;
+  __syncthreads();
   if (qok) {
-    // lane holds dQ'^T column qrow, rows d = 32b + 8(i/4) + 4lg + i%4; the
-    // RoPE partner d + D/2 sits in the same lane (D/2 is a multiple of 8).
     constexpr int half = D / 2;
+    constexpr int NP = half / 8;  // 8-column pieces per half row
     const float2* csr = cs + (size_t)qrow * half;
     Tio* out = dq + ((size_t)own * Hq + h) * D;
+    for (int c = lg; c < NP; c += 2) {
+      const int d0 = 8 * c;
+      float o1[8], o2[8];
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * b + 8 * (i >> 2) + 4 * lg + (i & 3);
-        if (d < half) {
-          const int dp2 = d + half;
-          const int b2 = dp2 >> 5, a2 = (dp2 & 31) >> 3;
-          const float g1 = acc[b][i] * scale;
-          const float g2 = acc[b2][4 * a2 + (i & 3)] * scale;
-          const float2 c = csr[d];
-          out[d] = from_f32<Tio>(g1 * c.x + g2 * c.y);
-          out[dp2] = from_f32<Tio>(g2 * c.x - g1 * c.y);
-        }
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const float g1 = ep[(d0 + s2) * 32 + lc], g2 = ep[(d0 + half + s2) * 32 + lc];
+        const float2 cc = csr[d0 + s2];
+        o1[s2] = g1 * cc.x + g2 * cc.y;
+        o2[s2] = g2 * cc.x - g1 * cc.y;
       }
+      store_row8(out + d0, o1);
+      store_row8(out + d0 + half, o2);
+    }
   }
 }
 
