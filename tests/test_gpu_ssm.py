@@ -60,6 +60,7 @@ CONV_CASES = {
                                 "bf16", 1),
     "forest_f32_no_act": (lambda: workloads.random_forest(4, [150, 77]), 40, 4, "f32", 0),
     "forest_k2_f32": (lambda: workloads.random_forest(5, [90]), 24, 2, "f32", 1),
+    "forest_k1_bf16": (lambda: workloads.random_forest(7, [150, 60]), 48, 1, "bf16", 1),
     "chain_k8_bf16": (lambda: ([list(range(300))], [0]), 2056, 8, "bf16", 1),
     "single_token": (lambda: ([[7]], None), 8, 4, "f32", 1),
     "deep_tree": (lambda: workloads.random_tree(11, 6, 1500, 16, 200), 128, 4, "bf16", 1),
