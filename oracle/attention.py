@@ -13,7 +13,7 @@ here unpacks every root-to-leaf path, runs textbook causal attention on it
 maps the rows back. RoPE is applied to q and k at each token's position on
 its path ("Trie packing" Step 1, "Tree Training" §3.2 Eq. 9), in the
 rotate-half convention with base theta (the pages name RoPE but fix neither
-convention nor base; this reading is listed in the design doc).
+convention nor base, so this is a reading).
 
 Everything is float64. bf16 inputs are widened exactly.
 

@@ -18,7 +18,7 @@ What it follows
   every sequence into a plain trie, merge single-child chains into one node,
   then give every node its (start, end) range in preorder.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 * children are visited in first-insertion order;
 * a node boundary falls at a fork and also right after a token where some
   input sequence ends (the Prefix Tree Merge example keeps [6,7] and [8,9]

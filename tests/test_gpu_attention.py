@@ -1,6 +1,6 @@
 """GPU parity of tree_attn_fwd / tree_attn_bwd against the float64 oracle.
 
-Tolerances (BASELINE target): O and LSE max-abs <= 2e-2; dQ, dK, dV relative
+Tolerances (the stated targets): O and LSE max-abs <= 2e-2; dQ, dK, dV relative
 L2 <= 5e-2. Small cases compare every element with the per-branch oracle;
 full-size workloads compare every element of selected trees / kv groups, or
 sampled rows and keys plus identities that hold at any size.

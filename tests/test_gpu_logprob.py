@@ -1,6 +1,6 @@
 """GPU parity of tree_logprob against the float64 oracle.
 
-Tolerances (mirroring the attention ones, a reading listed in the design doc):
+Tolerances (mirroring the attention ones):
 logp, row lse and loss max-abs <= 2e-2 (loss relative for large M); dlogits
 relative L2 <= 5e-2. Tighter internal checks: logp max-abs <= 1e-3 for
 float32 logits.
