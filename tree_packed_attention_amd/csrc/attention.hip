@@ -55,6 +55,17 @@
 #ifndef TA_FWD_WAVES
 #define TA_FWD_WAVES 4  // forward workgroup: TA_FWD_WAVES waves x 32 query rows
 #endif
+// LDS operand reads issued this many reads ahead of the MFMAs that use them
+// (0: left to the compiler), per kernel
+#ifndef TA_LA_FWD
+#define TA_LA_FWD 0
+#endif
+#ifndef TA_LA_DQ
+#define TA_LA_DQ 4
+#endif
+#ifndef TA_LA_DKDV
+#define TA_LA_DKDV 4
+#endif
 
 namespace ta {
 namespace {
@@ -63,6 +74,32 @@ __device__ __forceinline__ void sched_hint() {
 #if TA_IGLP >= 0
   __builtin_amdgcn_iglp_opt(TA_IGLP);
 #endif
+}
+
+// Issue order for one straight-line product: the first L LDS reads, then
+// after each MFMA the next reads in turn, so every operand is requested
+// about L reads before the MFMA that consumes it instead of just before it
+// (the compiler's default under register pressure). MF MFMAs and RD LDS
+// reads in all; the region is the enclosing basic block.
+template <int MF, int RD, int PER>
+struct LdsAheadTail {
+  static __device__ __forceinline__ void emit() {
+    if constexpr (MF > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int r = RD < PER ? RD : PER;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+      LdsAheadTail<MF - 1, RD - r, PER>::emit();
+    }
+  }
+};
+template <int L, int MF, int RD>
+__device__ __forceinline__ void lds_ahead() {
+  if constexpr (L > 0) {
+    constexpr int pre = L < RD ? L : RD;
+    constexpr int per = (RD + MF - 1) / MF;
+    __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+    LdsAheadTail<MF, RD - pre, per>::emit();
+  }
 }
 
 constexpr int kFwdBQ = 128;  // query rows per forward / dQ workgroup (4 waves x 32)
@@ -418,6 +455,7 @@ __device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const i
       for (int nb = 0; nb < kNB; ++nb) s[mb][nb] = mfma32x32x16(a, qop[nb][k], s[mb][nb]);
     }
   }
+  lds_ahead<TA_LA_FWD, 2 * KS * kNB, 2 * KS>();
   if (!full) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -624,6 +662,7 @@ __device__ __forceinline__ void dq_tile(const bf16* kb, const bf16* vb, const in
       s = mfma32x32x16(lds128(kb + off), qop[k], s);
       dp = mfma32x32x16(lds128(vb + off), dop[k], dp);
     }
+    lds_ahead<TA_LA_DQ, 2 * KS, 2 * KS>();
     bf16x8 db8[2];
     if (full) {
 #pragma unroll
@@ -655,6 +694,7 @@ __device__ __forceinline__ void dq_tile(const bf16* kb, const bf16* vb, const in
         const bf16x8 a = cat(lds_read_tr(kb + ad.tr[b] + r0), lds_read_tr(kb + ad.tr[b] + r0 + 8 * DP));
         acc[b] = mfma32x32x16(a, db8[t2], acc[b]);
       }
+    lds_ahead<TA_LA_DQ, 2 * NDB, 4 * NDB>();
   }
 }
 
@@ -839,6 +879,7 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
   for (int k = 0; k < KS; ++k)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) x[mb] = mfma32x32x16(lds128(xs + ad.op[k] + 32 * mb * DP), op[k], x[mb]);
+  lds_ahead<TA_LA_DKDV, 2 * KS, 2 * KS>();
   if (m == 0) __builtin_amdgcn_s_setprio(0);
   // a[2 mb + t2] is the A operand (keys x 16 query rows) of the second product.
   bf16x8 a[4];
@@ -892,6 +933,7 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
         acc[b] = mfma32x32x16(a[2 * mb + t2], bt, acc[b]);
       }
     }
+  lds_ahead<TA_LA_DKDV, 4 * NDB, 8 * NDB>();
 }
 
 template <int DP, typename Tio>
