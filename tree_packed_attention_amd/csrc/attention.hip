@@ -873,14 +873,13 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
       x[mb][4 * q4 + 2] = v.z;
       x[mb][4 * q4 + 3] = v.w;
     }
-  // role 0's products go first on the SIMD's shared MFMA pipe
+  // role 0's products and softmax go first on the SIMD
   if (m == 0) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int k = 0; k < KS; ++k)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) x[mb] = mfma32x32x16(lds128(xs + ad.op[k] + 32 * mb * DP), op[k], x[mb]);
   lds_ahead<TA_LA_DKDV, 2 * KS, 2 * KS>();
-  if (m == 0) __builtin_amdgcn_s_setprio(0);
   // a[2 mb + t2] is the A operand (keys x 16 query rows) of the second product.
   bf16x8 a[4];
   if (m == 0) {
@@ -905,6 +904,9 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
       }
 #pragma unroll
     for (int j = 0; j < 4; ++j) xch[64 * j] = a[j];
+    // the priority stays raised through the exponentials, which the dP-wave
+    // waits for
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   if (m == 1) {
