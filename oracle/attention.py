@@ -289,3 +289,126 @@ def backward_keys(q, k, v, do, par, keys, kv_heads=None, scale=None, theta=10000
                     acc_k[b] += ds_ij * qi[h] * scale
         dk[a] = rope_transpose(acc_k[None], [depth_j], theta)[0]
     return dk, dv
+
+
+# ----------------------------------------------------------------------------
+# Whole-tree ancestor-chain formulation (for element-wise checks at full size)
+#
+# Every packed query row attends to exactly its ancestor-or-self chain (the
+# "Trie packing" page, Step 2; "Tree Training" §3.2, Attention Mask), with
+# RoPE at its depth. The rows of a chain segment (a run of consecutive tokens
+# each of whose parent is the token before it; in preorder the first child of
+# a token directly follows it) share the ancestors of the segment's first
+# token, so one textbook causal attention over [those ancestors ; the
+# segment] with the segment's rows as queries computes them all. Gradients
+# are the textbook ones, scatter-added to the keys of every chain they belong
+# to ("Trie packing", "Same chain rule", Step 3). No path splitting is needed:
+# each packed row is a query exactly once. A long segment is taken in blocks
+# of at most `block` query rows, each over the segment's context plus the
+# segment rows before and in the block, which bounds the masked part.
+
+
+def chain_segments(par):
+    """(start, end) of the maximal runs t with par[t] == t - 1, in order."""
+    par = np.asarray(par)
+    starts = [t for t in range(len(par)) if t == 0 or par[t] != t - 1]
+    return list(zip(starts, starts[1:] + [len(par)]))
+
+
+def chain_blocks(par, block):
+    """(segment start, block start, block end): every chain segment cut into
+    consecutive blocks of at most `block` rows."""
+    return [(s, b, min(b + block, e)) for s, e in chain_segments(par) for b in range(s, e, block)]
+
+
+def depths(par):
+    """Depth of every token (0 at a root), from the parent links."""
+    par = np.asarray(par)
+    dep = np.zeros(len(par), dtype=np.int64)
+    for t in range(len(par)):
+        if par[t] >= 0:
+            dep[t] = dep[par[t]] + 1
+    return dep
+
+
+def _block_keys(par, s, b, e):
+    """Keys of query rows [b, e) of the segment starting at s: the ancestors
+    of s (root first), then rows s .. e - 1; and the number before row b."""
+    ctx = ancestors_or_self(par, int(par[s])) if par[s] >= 0 else np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.asarray(ctx, dtype=np.int64), np.arange(s, e, dtype=np.int64)]), len(ctx) + b - s
+
+
+def _segment_probs(qr_h, kr_h, n_ctx, scale):
+    """Causal softmax of one segment's rows over [context ; segment]."""
+    S = (qr_h @ kr_h.T) * scale
+    R, L = S.shape
+    # row r sees key columns 0 .. n_ctx + r
+    S[np.arange(L)[None, :] > (n_ctx + np.arange(R))[:, None]] = -np.inf
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return E / l, (m + np.log(l))[:, 0]
+
+
+def _chain_heads(Hq, Hkv, kv_heads, q_heads):
+    G = Hq // Hkv
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    heads = [h for hk in kv_heads for h in range(hk * G, (hk + 1) * G)]
+    if q_heads is not None:
+        heads = [h for h in heads if h in set(q_heads)]
+    return kv_heads, heads, [kv_heads.index(h // G) for h in heads]
+
+
+def forward_chains(q, k, v, par, kv_heads=None, scale=None, theta=10000.0, block=256, q_heads=None):
+    """O and LSE of every row for the q heads of the given kv groups (or
+    only those of them listed in q_heads). Returns O [T, n_heads, d] and
+    LSE [n_heads, T], heads in increasing order."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    kv_heads, heads, slot = _chain_heads(Hq, Hkv, kv_heads, q_heads)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    dep = depths(par)
+    qr = rope(_f64(q[:, heads]), dep, theta)
+    kr = rope(_f64(k[:, kv_heads]), dep, theta)
+    vv = _f64(v[:, kv_heads])
+    O = np.zeros((T, len(heads), d))
+    LSE = np.zeros((len(heads), T))
+    for s, b0, e in chain_blocks(par, block):
+        idx, n_ctx = _block_keys(par, s, b0, e)
+        for a, b in enumerate(slot):
+            P, lse = _segment_probs(qr[b0:e, a], kr[idx, b], n_ctx, scale)
+            O[b0:e, a] = P @ vv[idx, b]
+            LSE[a, b0:e] = lse
+    return O, LSE
+
+
+def backward_chains(q, k, v, do, par, kv_heads=None, scale=None, theta=10000.0, block=256, q_heads=None):
+    """dQ of every row (the q heads of the given kv groups) and dK, dV of
+    every key (those kv groups), for the upstream gradient do. With q_heads,
+    only those heads are taken: the caller's do must be zero on the other
+    heads of the groups, which then contribute nothing to dK and dV.
+    Returns dq [T, n_heads, d], dk and dv [T, len(kv_heads), d]."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    kv_heads, heads, slot = _chain_heads(Hq, Hkv, kv_heads, q_heads)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    dep = depths(par)
+    qr = rope(_f64(q[:, heads]), dep, theta)
+    kr = rope(_f64(k[:, kv_heads]), dep, theta)
+    vv = _f64(v[:, kv_heads])
+    dov = _f64(do[:, heads])
+    dqr = np.zeros((T, len(heads), d))
+    dkr = np.zeros((T, len(kv_heads), d))
+    dv = np.zeros((T, len(kv_heads), d))
+    for s, b0, e in chain_blocks(par, block):
+        idx, n_ctx = _block_keys(par, s, b0, e)
+        for a, b in enumerate(slot):
+            P, _ = _segment_probs(qr[b0:e, a], kr[idx, b], n_ctx, scale)
+            o = P @ vv[idx, b]
+            dOr = dov[b0:e, a]
+            D = np.sum(dOr * o, axis=1, keepdims=True)
+            dS = P * (dOr @ vv[idx, b].T - D)
+            dqr[b0:e, a] = (dS @ kr[idx, b]) * scale
+            dkr[idx, b] += (dS.T @ qr[b0:e, a]) * scale
+            dv[idx, b] += P.T @ dOr
+    return rope_transpose(dqr, dep, theta), rope_transpose(dkr, dep, theta), dv

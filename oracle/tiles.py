@@ -57,3 +57,31 @@ def tile_visible_counts(vis, BQ, BK):
         for kt in range(nk):
             out[qt, kt] = vis[qt * BQ:(qt + 1) * BQ, kt * BK:(kt + 1) * BK].sum()
     return out
+
+
+def tile_counts_per_qtile(se, T, BQ, BK):
+    """Per query tile (rows [qt*BQ, min(qt*BQ+BQ, T))): the number of causal
+    key tiles that are non-empty and the number that are full, under the
+    rule of tile_stats. Returns two int64 arrays of length ceil(T / BQ)."""
+    se = np.asarray(se, dtype=np.int64)
+    nq = -(-T // BQ)
+    nk = -(-T // BK)
+    pad = np.zeros(nk * BK, dtype=np.int64)
+    pad[:T] = se[:T]
+    nonempty = np.zeros(nq, dtype=np.int64)
+    full = np.zeros(nq, dtype=np.int64)
+    for qt in range(nq):
+        i0 = qt * BQ
+        i1 = min(i0 + BQ, T)
+        for kt in range(nk):
+            j0 = kt * BK
+            j1 = j0 + BK
+            if j0 > i1 - 1:
+                continue
+            blk = pad[j0:j1]
+            if blk.max() <= i0:
+                continue
+            nonempty[qt] += 1
+            if j1 - 1 <= i0 and blk.min() >= i1:
+                full[qt] += 1
+    return nonempty, full

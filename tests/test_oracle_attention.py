@@ -164,3 +164,51 @@ def test_gqa_group_sum():
     dqg, dkg, dvg = OA.backward_branches(np.repeat(q, G, 1), k, v, np.repeat(do, G, 1), p["par"], p["pos"])
     assert np.allclose(dkg, G * dk1, atol=1e-12) and np.allclose(dvg, G * dv1, atol=1e-12)
     assert np.allclose(dqg, np.repeat(dq1, G, 1), atol=1e-12)
+
+
+def test_chain_formulation_equals_branches():
+    """The whole-tree ancestor-chain formulation (each packed row as a query
+    once, over its own chain) equals the per-branch oracle on random trees,
+    forward and backward, including a GQA group sum and a scale and theta
+    other than the defaults."""
+    rng = np.random.default_rng(123)
+    for trial in range(25):
+        seqs, groups = workloads.random_small_forest(rng, n_seqs_max=6, len_max=9, vocab=3, n_groups_max=3)
+        p = OP.pack(seqs, groups)
+        T = p["T"]
+        Hq, Hkv, d = (4, 2, 16) if trial % 2 else (2, 1, 8)
+        q, k, v, do = (rng.standard_normal(s) for s in ((T, Hq, d), (T, Hkv, d), (T, Hkv, d), (T, Hq, d)))
+        scale, theta = (None, 10000.0) if trial % 3 else (0.3, 500.0)
+        O, L = OA.forward_branches(q, k, v, p["par"], p["pos"], scale=scale, theta=theta)
+        dq, dk, dv = OA.backward_branches(q, k, v, do, p["par"], p["pos"], scale=scale, theta=theta)
+        blk = (2, 3, 256)[trial % 3]  # blocks shorter than the segments, too
+        O2, L2 = OA.forward_chains(q, k, v, p["par"], scale=scale, theta=theta, block=blk)
+        dq2, dk2, dv2 = OA.backward_chains(q, k, v, do, p["par"], scale=scale, theta=theta, block=blk)
+        for a, b in ((O, O2), (L, L2), (dq, dq2), (dk, dk2), (dv, dv2)):
+            assert np.max(np.abs(a - b)) < 1e-9
+        # one kv group alone: its q heads, its keys
+        hk = Hkv - 1
+        O3, L3 = OA.forward_chains(q, k, v, p["par"], kv_heads=[hk], scale=scale, theta=theta)
+        _, dk3, dv3 = OA.backward_chains(q, k, v, do, p["par"], kv_heads=[hk], scale=scale, theta=theta)
+        G = Hq // Hkv
+        assert np.max(np.abs(O3 - O[:, hk * G:(hk + 1) * G])) < 1e-9
+        assert np.max(np.abs(dk3[:, 0] - dk[:, hk])) < 1e-9 and np.max(np.abs(dv3[:, 0] - dv[:, hk])) < 1e-9
+        # an upstream gradient on one q head of the group only: the listed
+        # head alone gives the group's dK, dV (the per-branch oracle sees the
+        # zero gradients of the other heads)
+        h1 = hk * G + G - 1
+        do1 = np.zeros_like(do)
+        do1[:, h1] = do[:, h1]
+        _, dk4, dv4 = OA.backward_branches(q, k, v, do1, p["par"], p["pos"], scale=scale, theta=theta)
+        dq5, dk5, dv5 = OA.backward_chains(q, k, v, do1, p["par"], kv_heads=[hk], q_heads=[h1], scale=scale,
+                                           theta=theta)
+        O5, _ = OA.forward_chains(q, k, v, p["par"], kv_heads=[hk], q_heads=[h1], scale=scale, theta=theta)
+        assert np.max(np.abs(dk5[:, 0] - dk4[:, hk])) < 1e-9 and np.max(np.abs(dv5[:, 0] - dv4[:, hk])) < 1e-9
+        assert np.max(np.abs(dq5[:, 0] - dq[:, h1])) < 1e-9 and np.max(np.abs(O5[:, 0] - O[:, h1])) < 1e-9
+
+
+def test_chain_segments_and_depths():
+    p = OP.pack(*workloads.sequences("ex_a"))
+    # A B C D | E | F G  (E's parent is C, F's parent is B)
+    assert OA.chain_segments(p["par"]) == [(0, 4), (4, 5), (5, 7)]
+    assert np.array_equal(OA.depths(p["par"]), p["pos"])

@@ -39,3 +39,23 @@ def test_classification_is_conservative_and_complete(BQ, BK):
                     partial += 1
         assert OT.tile_stats(se, T, BQ, BK) == (full, partial, empty, causal)
         assert causal == sum(min(nk, -(-min(qt * BQ + BQ, T) // BK)) for qt in range(nq))
+
+
+@pytest.mark.parametrize("BQ,BK", [(4, 2), (8, 4), (3, 5)])
+def test_per_query_tile_counts_brute_force(BQ, BK):
+    """Per query tile: a key tile is counted non-empty iff it holds a visible
+    pair, and full iff every one of its BQ' x BK pairs is visible (key columns
+    past T count as not visible)."""
+    rng = np.random.default_rng(7 * BQ + BK)
+    for _ in range(120):
+        seqs, groups = workloads.random_small_forest(rng, n_seqs_max=7, len_max=9, vocab=3, n_groups_max=3)
+        p = OP.pack(seqs, groups)
+        T = p["T"]
+        cnt = OT.tile_visible_counts(OP.visibility_dense(p["par"]), BQ, BK)
+        ne, fu = OT.tile_counts_per_qtile(p["se"], T, BQ, BK)
+        for qt in range(cnt.shape[0]):
+            rows = min(qt * BQ + BQ, T) - qt * BQ
+            assert ne[qt] == int((cnt[qt] > 0).sum())
+            assert fu[qt] == int((cnt[qt] == rows * BK).sum())
+        f, pa, e, c = OT.tile_stats(p["se"], T, BQ, BK)
+        assert (int(ne.sum()), int(fu.sum())) == (f + pa, f)
