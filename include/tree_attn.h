@@ -23,8 +23,10 @@
  *   - Device tensors are contiguous and token-major: q, o, dout, dq are
  *     [T][Hq][d]; k, v, dk, dv are [T][Hkv][d]; lse is [Hq][T] float32.
  *     Query head h uses kv head h / (Hq / Hkv).
- *   - The library keeps no state besides the error string and the opt-in
- *     profiling table below: calls on different streams with separate
+ *   - The library keeps no state besides the thread-local error string and
+ *     the opt-in, process-wide kernel timing table (tree_attn_profile_*,
+ *     the one piece of shared state; while it is enabled the library creates
+ *     HIP events inside its calls): calls on different streams with separate
  *     workspaces may run concurrently.
  */
 #ifndef TREE_ATTN_H
@@ -135,10 +137,15 @@ int tree_pack(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
  * d must be 16, 64 or 128 (else TA_EUNSUPPORTED). 1 <= T <= 2^22,
  * Hq % Hkv == 0, Hq <= 256.
  * pos, subtree_end: device int32 [T] as produced by tree_pack (a forest of
- * trees is fine; subtree ends must satisfy i < subtree_end[i] <= T).
+ * trees is fine; subtree ends must satisfy i < subtree_end[i] <= T). Only
+ * the device sees these values: a subtree end outside (i, T] is clamped into
+ * that range (so no access leaves the buffers and every row sees at least
+ * itself) and sets TA_STATUS_SUBTREE_END in the workspace status word; the
+ * outputs are then those of the clamped mask.
  * workspace: device memory of at least tree_attn_workspace_bytes(...) bytes,
  * 256-byte aligned; contents are scratch between calls except under
- * TA_REUSE_PREP.
+ * TA_REUSE_PREP and the status word at its start (see
+ * tree_attn_workspace_status).
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_EHIP (launch failure).
  * ---------------------------------------------------------------------- */
 size_t tree_attn_workspace_bytes(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t with_bwd);
@@ -154,6 +161,41 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const int32_t* pos, const int32_t* subtree_end,
                   float softmax_scale, float rope_theta, int32_t flags,
                   void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_attn_workspace_status  (HOST, reads device memory)
+ *
+ * Data errors that only the device can see (the conventions of the C ABI:
+ * arguments are validated on the host, metadata values are not). Every prep
+ * pass (tree_attn_fwd, tree_attn_gw_fwd, and a backward without
+ * TA_REUSE_PREP) clears the int32 status word at the start of its workspace
+ * and sets bits in it; the word then stays as it is until the next prep pass
+ * on that workspace. This call enqueues a copy of the word to *status (host
+ * memory) on `stream` and waits for the stream.
+ *   TA_STATUS_SUBTREE_END  some subtree_end[i] was outside (i, T] and clamped
+ * Errors: TA_EINVAL (NULL pointer), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+enum { TA_STATUS_SUBTREE_END = 1 };
+
+int tree_attn_workspace_status(const void* workspace, int32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_attn_plan_counts  (HOST, reads device memory)
+ *
+ * The tile plan the device built in `workspace` during the last prep pass,
+ * per 128-row query tile: nonempty[t] = key tiles of 64 the forward and dQ
+ * passes visit for query tile t (tiles the plan skips hold no visible pair),
+ * full[t] = those among them whose every pair is visible (no masking). The
+ * classification is the one tree_tile_stats counts on the host, at BQ = 128,
+ * BK = 64. T, past_len, Hq, Hkv, d: as given to the call that filled the
+ * workspace (past_len = 0 for tree_attn_fwd); n_qtiles must equal
+ * ceil((ceil(past_len / 128) * 128 + T) / 256) * 2. Query tiles of cached rows
+ * and of padding report 0. Copies on `stream` into host memory and waits.
+ * Errors: TA_EINVAL (shape, size, NULL), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+int tree_attn_plan_counts(const void* workspace, size_t ws_bytes, int32_t T, int32_t past_len, int32_t Hq,
+                          int32_t Hkv, int32_t d, int32_t n_qtiles, int32_t* nonempty, int32_t* full,
+                          void* stream);
 
 /* ------------------------------------------------------------------------
  * Tree-masked attention across a partition boundary (DEVICE)
@@ -330,7 +372,11 @@ int tree_partition(const int32_t* node_start, const int32_t* node_end, const int
  * anc_0(t) = t, anc_{n+1}(t) = parent[anc_n(t)]; terms past a root are zero.
  * x, y, dy, dx: device [T][C] in dt (TA_BF16 or TA_F32), 16-byte aligned;
  * weight: device float32 [C][K]; bias: device float32 [C] or NULL.
- * parent, pos, subtree_end: device int32 [T] from tree_pack.
+ * parent, pos, subtree_end: device int32 [T] from tree_pack. Only the device
+ * reads them: a parent not in [-1, t) is read as -1 (no parent), a subtree
+ * end outside (t, T] is clamped into it and a descendant at depth <= the
+ * token's own is skipped, so malformed metadata gives meaningless values but
+ * no access outside [0, T) and no endless walk.
  * Backward: dx in dt; dweight float32 [C][K]; dbias float32 [C] or NULL.
  * Gradients are summed in a fixed order (bitwise reproducible). The backward
  * gathers each token's descendants at most K-1 levels down from the

@@ -38,7 +38,7 @@ def _compare(p, o):
     assert (p["T"], p["n_nodes"], p["n_trees"]) == (o["T"], o["n_nodes"], o["n_trees"])
 
 
-@pytest.mark.parametrize("name", ["ex_a", "ex_b", "short", "multistep", "agentic"])
+@pytest.mark.parametrize("name", ["ex_a", "ex_b", "short", "multistep", "agentic", "agentic_l"])
 def test_pack_bit_exact_workloads(name):
     seqs, groups = workloads.sequences(name)
     _compare(ta.tree_pack(seqs, groups), OP.pack(seqs, groups))
@@ -103,9 +103,17 @@ def test_tile_stats_errors():
     assert e.value.code == ta.TA_EINVAL
 
 
+def _gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0  # counts devices without initialising one
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="passes dangling device pointers: run only where no GPU is visible")
 def test_device_entry_points_validate_before_hip():
     """Bad arguments are rejected on the host: these calls pass dangling
-    pointers on purpose, which would fault if any HIP work were issued."""
+    pointers on purpose, which would fault if any HIP work were issued, so
+    the test runs only on a host without a GPU."""
     lib = ta.library()
     bogus = ctypes.c_void_p(0x1000)
     ws_need = lib.tree_attn_workspace_bytes(100, 4, 2, 64, 0)
@@ -179,3 +187,13 @@ def test_device_entry_points_validate_before_hip():
     assert lib.tree_logprob_ppo(*pargs(adv=None)) == ta.TA_EINVAL and "advantage" in ta.last_error()
     assert lib.tree_logprob_ppo(*pargs(old=None)) == ta.TA_EINVAL
     assert lib.tree_logprob_ppo(*pargs(ws=lw - 1)) == ta.TA_EINVAL
+    # read-back of the device tile plan: shape checks before any copy
+    pc = lambda n=2, T=100, ws=ws_need, ne=bogus: lib.tree_attn_plan_counts(bogus, ws, T, 0, 4, 2, 64, n, ne, bogus,
+                                                                           None)
+    assert pc(n=3) == ta.TA_EINVAL and "n_qtiles" in ta.last_error()
+    assert pc(T=0) == ta.TA_EINVAL
+    assert pc(ws=ws_need - 1) == ta.TA_EINVAL
+    assert pc(ne=None) == ta.TA_EINVAL
+    st = ctypes.c_int32(0)
+    assert lib.tree_attn_workspace_status(None, ctypes.byref(st), None) == ta.TA_EINVAL
+    assert lib.tree_attn_workspace_status(bogus, None, None) == ta.TA_EINVAL

@@ -2,8 +2,9 @@
 
 Tolerances (the stated targets): O and LSE max-abs <= 2e-2; dQ, dK, dV relative
 L2 <= 5e-2. Small cases compare every element with the per-branch oracle;
-full-size workloads compare every element of selected trees / kv groups, or
-sampled rows and keys plus identities that hold at any size.
+full-size workloads compare every row and key of whole kv groups with the
+whole-tree ancestor-chain oracle (on the largest tree, with the upstream
+gradient on two heads of the group), plus sampled rows on all heads.
 """
 import numpy as np
 import pytest
@@ -100,37 +101,98 @@ def test_short_prompt_group_full():
         assert rel_l2(host(r[name]), ref) <= GRAD_TOL, name
 
 
-def _tree_slice(po, t):
-    ts, te = int(po["tree_start"][t]), int(po["tree_start"][t + 1])
-    par = po["par"][ts:te].copy()
-    par[par >= 0] -= ts
-    return ts, te, par, po["pos"][ts:te]
+def _check_group(r, po, c, hk, q_heads=None):
+    """Every row and key of kv group hk against the whole-tree ancestor-chain
+    oracle: O, LSE and dQ of its q heads (or of those listed), dK and dV."""
+    G = c["Hq"] // c["Hkv"]
+    hs = slice(hk * G, (hk + 1) * G)
+    heads = list(range(hk * G, (hk + 1) * G)) if q_heads is None else list(q_heads)
+    qn, kn, vn, don = host(r["q"][:, hs]), host(r["k"][:, hk:hk + 1]), host(r["v"][:, hk:hk + 1]), host(r["do"][:, hs])
+    rel = [h - hk * G for h in heads]
+    O, LSE = OA.forward_chains(qn, kn, vn, po["par"], q_heads=rel)
+    assert max_abs(host(r["o"][:, heads]), O) <= O_TOL
+    assert max_abs(host(r["lse"][heads]), LSE) <= LSE_TOL
+    dq, dk, dv = OA.backward_chains(qn, kn, vn, don, po["par"], q_heads=rel)
+    errs = dict(dq=rel_l2(host(r["dq"][:, heads]), dq), dk=rel_l2(host(r["dk"][:, hk:hk + 1]), dk),
+                dv=rel_l2(host(r["dv"][:, hk:hk + 1]), dv))
+    print(f"kv group {hk} heads {heads[0]}..{heads[-1]}: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}",
+          flush=True)
+    assert max(errs.values()) <= GRAD_TOL, errs
+    return dk, dv
 
 
-def test_multistep_trees_full_per_group():
-    """Long prompt, multi-step trajectories (4 trees, 28672 tokens, 32q/8kv).
-    Whole trees 0 and 3 for kv groups 0 and 7 against the per-branch oracle."""
+def test_multistep_batch_whole_kv_groups():
+    """Long prompt, multi-step trajectories (4 trees, 28672 tokens, 32q/8kv):
+    every row and key of the whole batch for kv groups 0 and 7."""
     seqs, groups = workloads.sequences("multistep")
     c = workloads.WORKLOADS["multistep"]
     r = run_gpu(seqs, groups, c["Hq"], c["Hkv"], c["d"], c["dtype"], c["seed"])
     po = OP.pack(seqs, groups)
-    G = c["Hq"] // c["Hkv"]
-    for t in (0, 3):
-        ts, te, par, pos = _tree_slice(po, t)
-        for hk in (0, c["Hkv"] - 1):
-            hs = slice(hk * G, (hk + 1) * G)
-            qn = host(r["q"][ts:te, hs])
-            kn = host(r["k"][ts:te, hk:hk + 1])
-            vn = host(r["v"][ts:te, hk:hk + 1])
-            don = host(r["do"][ts:te, hs])
-            O, LSE = OA.forward_branches(qn, kn, vn, par, pos)
-            assert max_abs(host(r["o"][ts:te, hs]), O) <= O_TOL
-            assert max_abs(host(r["lse"][hs, ts:te]), LSE) <= LSE_TOL
-            dq, dk, dv = OA.backward_branches(qn, kn, vn, don, par, pos)
-            assert rel_l2(host(r["dq"][ts:te, hs]), dq) <= GRAD_TOL
-            assert rel_l2(host(r["dk"][ts:te, hk:hk + 1]), dk) <= GRAD_TOL
-            assert rel_l2(host(r["dv"][ts:te, hk:hk + 1]), dv) <= GRAD_TOL
-            print(f"tree {t} kv {hk} ok", flush=True)
+    for hk in (0, c["Hkv"] - 1):
+        _check_group(r, po, c, hk)
+
+
+def _heavy_keys(po):
+    """The keys with the most descendants: the root segment and every key
+    whose subtree holds more than a tenth of the tree (the fork points of the
+    upper levels)."""
+    size = po["se"] - np.arange(po["T"])
+    return np.nonzero(size > po["T"] // 10)[0]
+
+
+def test_random_agentic_tree_whole_kv_group():
+    """Random agentic tree (32768 tokens, depth <= 6, 64q/8kv, d=128) at full
+    size: every row and key of kv group 0 (its 8 q heads) element-wise,
+    including the root segment and fork keys that gather gradients from
+    thousands of descendants."""
+    seqs, groups = workloads.sequences("agentic")
+    c = workloads.WORKLOADS["agentic"]
+    r = run_gpu(seqs, groups, c["Hq"], c["Hkv"], c["d"], c["dtype"], c["seed"])
+    po = OP.pack(seqs, groups)
+    dk, dv = _check_group(r, po, c, 0)
+    heavy = _heavy_keys(po)
+    assert len(heavy) > 1000
+    assert rel_l2(host(r["dk"][:, :1])[heavy], dk[heavy]) <= GRAD_TOL
+    assert rel_l2(host(r["dv"][:, :1])[heavy], dv[heavy]) <= GRAD_TOL
+
+
+def test_random_agentic_tree_large_whole_kv_group():
+    """Large random tree (131072 tokens, depth <= 10, 64q/8kv, d=128) at full
+    size. The upstream gradient is the workload's on q heads 56 and 63 (the
+    first and last head of kv group 7) and zero on the others, so the
+    oracle needs two heads while the kernels run all 64 over every block:
+    dK and dV of every key of group 7 (root segment and all forks included),
+    O, LSE and dQ of every row of heads 56 and 63, element-wise; dQ of the
+    zero-gradient heads of the group must be exactly zero. Sampled rows check
+    O and LSE on all heads."""
+    seqs, groups = workloads.sequences("agentic_l")
+    c = workloads.WORKLOADS["agentic_l"]
+    p = ta.tree_pack(seqs, groups)
+    T = p["T"]
+    q, k, v, do = workloads.dense_inputs(T, c["Hq"], c["Hkv"], c["d"], c["dtype"], c["seed"], device="cuda")
+    keep = torch.zeros(c["Hq"], dtype=torch.bool, device="cuda")
+    keep[[56, 63]] = True
+    do = do * keep[None, :, None].to(do.dtype)
+    pos = torch.from_numpy(p["pos"]).cuda()
+    se = torch.from_numpy(p["subtree_end"]).cuda()
+    o, lse, ws = ta.tree_attn_fwd(q, k, v, pos, se, with_bwd_workspace=True)
+    dq, dk, dv = ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws, reuse_prep=True)
+    torch.cuda.synchronize()
+    assert ta.tree_attn_workspace_status(ws) == 0
+    r = dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    po = OP.pack(seqs, groups)
+    dkr, dvr = _check_group(r, po, c, 7, q_heads=[56, 63])
+    heavy = _heavy_keys(po)
+    assert len(heavy) > 1000
+    assert rel_l2(host(dk[:, 7:8])[heavy], dkr[heavy]) <= GRAD_TOL
+    assert rel_l2(host(dv[:, 7:8])[heavy], dvr[heavy]) <= GRAD_TOL
+    assert torch.count_nonzero(dq[:, 57:63]) == 0
+    rng = np.random.default_rng(42)
+    rows = _sample_rows(po, 12, rng)
+    O, LSE = OA.forward_rows(_Rows(q, rows), host(k), host(v), po["par"], rows)
+    rt = torch.as_tensor(rows, device="cuda")
+    assert max_abs(host(o[rt]), O) <= O_TOL
+    assert max_abs(host(lse[:, rt]), LSE) <= LSE_TOL
 
 
 class _Rows:
@@ -158,61 +220,36 @@ def _sample_rows(po, n, rng):
     return rows
 
 
-def _small_subtree_keys(po, n, rng, max_sub=48):
-    size = po["se"] - np.arange(po["T"])
-    cand = np.nonzero(size <= max_sub)[0]
-    keys = list(rng.choice(cand, size=min(n, len(cand)), replace=False))
-    # include keys at a node boundary and the last token
-    keys += [int(po["T"] - 1)]
-    return sorted(set(int(x) for x in keys))
+PLAN_CASES = {
+    "forest_ragged": (lambda: workloads.random_forest(3, [333, 250, 97]), 8, 2, 128),
+    "deep_tree": (lambda: workloads.random_tree(11, 6, 1500, 16, 200), 4, 1, 64),
+    "single_token": (lambda: ([[5]], None), 1, 1, 16),
+    "short": (lambda: workloads.sequences("short"), 32, 8, 128),
+    "multistep": (lambda: workloads.sequences("multistep"), 32, 8, 128),
+    "agentic": (lambda: workloads.sequences("agentic"), 64, 8, 128),
+}
 
 
-@pytest.mark.parametrize("name", ["agentic", "agentic_l"])
-def test_random_agentic_tree_sampled(name):
-    """Random agentic trees (32768 tokens, depth <= 6; 131072 tokens, depth
-    <= 10), 64q/8kv, d=128, at full size. Sampled query rows (O, LSE, dQ over
-    all heads), sampled keys (dK, dV), and two identities over all keys."""
-    seqs, groups = workloads.sequences(name)
-    c = workloads.WORKLOADS[name]
-    r = run_gpu(seqs, groups, c["Hq"], c["Hkv"], c["d"], c["dtype"], c["seed"])
-    po = OP.pack(seqs, groups)
-    rng = np.random.default_rng(42)
-    n_rows = 24 if name == "agentic" else 12
-    rows = _sample_rows(po, n_rows, rng)
-    print(f"\n{name}: {len(rows)} rows", flush=True)
-    kn = host(r["k"])
-    vn = host(r["v"])
-    qv = _Rows(r["q"], rows)
-    dov = _Rows(r["do"], rows)
-    O, LSE = OA.forward_rows(qv, kn, vn, po["par"], rows)
-    rt = torch.as_tensor(rows, device="cuda")
-    assert max_abs(host(r["o"][rt]), O) <= O_TOL
-    assert max_abs(host(r["lse"][:, rt]), LSE) <= LSE_TOL
-    dq = OA.backward_rows_dq(qv, kn, vn, dov, po["par"], rows)
-    assert rel_l2(host(r["dq"][rt]), dq) <= GRAD_TOL
-    print(f"{name}: rows ok", flush=True)
+@pytest.mark.parametrize("case", list(PLAN_CASES))
+def test_device_tile_plan_matches_oracle(case):
+    """The tile plan the device builds (per 128-row query tile: 64-key tiles
+    visited and those among them taken unmasked) equals the oracle's
+    classification of every tile, and the status word stays clear."""
+    make, Hq, Hkv, d = PLAN_CASES[case]
+    seqs, groups = make()
+    p = ta.tree_pack(seqs, groups)
+    T = p["T"]
+    q, k, v, _ = workloads.dense_inputs(T, Hq, Hkv, d, "bf16", 1, device="cuda")
+    o, lse, ws = ta.tree_attn_fwd(q, k, v, torch.from_numpy(p["pos"]).cuda(), torch.from_numpy(p["subtree_end"]).cuda())
+    ne, fu = ta.tree_attn_plan_counts(ws, T, Hq, Hkv, d)
+    assert ta.tree_attn_workspace_status(ws) == 0
+    from oracle import tiles as OT
 
-    keys = _small_subtree_keys(po, 4 if name == "agentic" else 3, rng)
-    need = sorted(set(int(i) for j in keys for i in OA.subtree_rows(po["par"], j)))
-    qk = _Rows(r["q"], need)
-    dok = _Rows(r["do"], need)
-    kvh = [0, c["Hkv"] - 1]
-    dk, dv = OA.backward_keys(qk, kn, vn, dok, po["par"], keys, kv_heads=kvh)
-    kt = torch.as_tensor(keys, device="cuda")
-    assert rel_l2(host(r["dk"][kt][:, kvh]), dk) <= GRAD_TOL
-    assert rel_l2(host(r["dv"][kt][:, kvh]), dv) <= GRAD_TOL
-    print(f"{name}: keys ok", flush=True)
-
-    # identities over every key: softmax rows sum to one, so sum_j dV_j equals
-    # the summed upstream gradient of each group; and sum_j dS_ij = 0, so the
-    # re-rotated dK sums to zero.
-    G = c["Hq"] // c["Hkv"]
-    sum_dv = r["dv"].double().sum(0)
-    sum_do = r["do"].double().view(-1, c["Hkv"], G, c["d"]).sum((0, 2))
-    assert rel_l2(sum_dv.cpu().numpy(), sum_do.cpu().numpy()) <= GRAD_TOL
-    dkr = OA.rope(host(r["dk"]).astype(np.float64), po["pos"], 10000.0)
-    ratio = np.linalg.norm(dkr.sum(0)) / np.linalg.norm(dkr, axis=-1).sum()
-    assert ratio < 1e-3, ratio
+    one, ofu = OT.tile_counts_per_qtile(OP.pack(seqs, groups)["se"], T, 128, 64)
+    n = len(one)
+    assert np.array_equal(ne[:n], one) and np.array_equal(fu[:n], ofu)
+    assert not ne[n:].any() and not fu[n:].any()
+    print(case, "non-empty", int(ne.sum()), "full", int(fu.sum()), flush=True)
 
 
 def test_bitwise_deterministic_and_reuse_prep():
@@ -256,10 +293,23 @@ def test_no_rope_and_custom_scale():
     po = OP.pack(seqs, groups)
     # theta = 0 disables RoPE: the oracle rotates by position 0 (identity)
     vis = OP.visibility_dense(po["par"])
-    qn, kn, vn = host(r["q"]), host(r["k"]), host(r["v"])
+    qn, kn, vn, don = host(r["q"]), host(r["k"]), host(r["v"]), host(r["do"])
     O, LSE = OA.forward_dense(qn, kn, vn, vis, np.zeros(po["T"]))
     assert max_abs(host(r["o"]), O) <= O_TOL and max_abs(host(r["lse"]), LSE) <= LSE_TOL
+    # backward without RoPE: the per-branch oracle at theta = 0
+    dq, dk, dv = OA.backward_branches(qn, kn, vn, don, po["par"], po["pos"], theta=0.0)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert rel_l2(host(r[name]), ref) <= GRAD_TOL, name
     q, k, v = r["q"], r["k"], r["v"]
-    o, lse, _ = ta.tree_attn_fwd(q, k, v, r["pos"], r["se"], softmax_scale=0.05)
+    o, lse, ws = ta.tree_attn_fwd(q, k, v, r["pos"], r["se"], softmax_scale=0.05, with_bwd_workspace=True)
     O2, L2 = OA.forward_dense(qn, kn, vn, vis, po["pos"], scale=0.05)
     assert max_abs(host(o), O2) <= O_TOL and max_abs(host(lse), L2) <= LSE_TOL
+    # backward at a scale other than 1/sqrt(d), with RoPE, and with both
+    for theta in (10000.0, 0.0):
+        o, lse, ws = ta.tree_attn_fwd(q, k, v, r["pos"], r["se"], softmax_scale=0.05, rope_theta=theta,
+                                      with_bwd_workspace=True)
+        g = ta.tree_attn_bwd(q, k, v, o, lse, r["do"], r["pos"], r["se"], softmax_scale=0.05, rope_theta=theta,
+                             workspace=ws, reuse_prep=True)
+        ref = OA.backward_branches(qn, kn, vn, don, po["par"], po["pos"], scale=0.05, theta=theta)
+        for name, a, b in zip(("dq", "dk", "dv"), g, ref):
+            assert rel_l2(host(a), b) <= GRAD_TOL, (theta, name)

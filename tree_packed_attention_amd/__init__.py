@@ -34,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
 TA_OK, TA_EINVAL, TA_ECAPACITY, TA_EUNSUPPORTED, TA_EHIP = 0, -1, -2, -3, -4
 TA_BF16, TA_F32 = 0, 1
 TA_REUSE_PREP, TA_ACCUMULATE_PAST = 1, 2
+TA_STATUS_SUBTREE_END = 1
 
 EXPORTS = (
     "tree_attn_last_error",
@@ -59,6 +60,8 @@ EXPORTS = (
     "tree_gdn_bwd",
     "tree_attn_profile_enable",
     "tree_attn_profile_read",
+    "tree_attn_workspace_status",
+    "tree_attn_plan_counts",
 )
 
 
@@ -140,6 +143,10 @@ _lib.tree_gdn_bwd.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _p, _i32, _i32, 
                               _p, _p, _p, _sz, _p]
 _lib.tree_tile_stats.restype = ctypes.c_int
 _lib.tree_tile_stats.argtypes = [_p, _i32, _i32, _i32] + [ctypes.POINTER(ctypes.c_int64)] * 4
+_lib.tree_attn_workspace_status.restype = ctypes.c_int
+_lib.tree_attn_workspace_status.argtypes = [_p, ctypes.POINTER(ctypes.c_int32), _p]
+_lib.tree_attn_plan_counts.restype = ctypes.c_int
+_lib.tree_attn_plan_counts.argtypes = [_p, _sz, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
 _lib.tree_attn_profile_enable.restype = ctypes.c_int
 _lib.tree_attn_profile_enable.argtypes = [_i32]
 _lib.tree_attn_profile_read.restype = ctypes.c_int
@@ -266,6 +273,33 @@ def _dev_ptr(t, name, dtype=None, device=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, name, shape):
+    """Raises ValueError unless tensor t has exactly `shape` (None = any size)."""
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError(f"{name} has shape {got}, expected {tuple('*' if w is None else w for w in shape)}")
+    return t
+
+
+def _check_attn(q, k, v, pos, subtree_end, o=None, lse=None, dout=None, past_len=None):
+    """Shapes of the attention tensors against (T, Hq, Hkv, d) from q and k."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError(f"q and k must be [T, H, d] (got {tuple(q.shape)} and {tuple(k.shape)})")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (T, Hkv, d))
+    _shape(v, "v", (T, Hkv, d))
+    _shape(pos, "pos", (T,))
+    _shape(subtree_end, "subtree_end", (T,))
+    if o is not None:
+        _shape(o, "o", (T, Hq, d))
+    if lse is not None:
+        _shape(lse, "lse", (Hq, T))
+    if dout is not None:
+        _shape(dout, "dout", (T, Hq, d))
+    return T, Hq, Hkv, d
+
+
 def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
@@ -283,8 +317,7 @@ def tree_attn_fwd(q, k, v, pos, subtree_end, softmax_scale=0.0, rope_theta=10000
     reuse_prep=True to skip the RoPE and tile-plan pass there.
     """
     torch = _torch()
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    T, Hq, Hkv, d = _check_attn(q, k, v, pos, subtree_end)
     dev = q.device
     if workspace is None:
         workspace = attn_workspace(T, Hq, Hkv, d, with_bwd_workspace, dev)
@@ -303,8 +336,7 @@ def tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, softmax_scale=0.0, ro
                   workspace=None, reuse_prep=False):
     """Gradients (dq, dk, dv) of sum(o * dout); dk/dv summed over each kv group."""
     torch = _torch()
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    T, Hq, Hkv, d = _check_attn(q, k, v, pos, subtree_end, o=o, lse=lse, dout=dout)
     dev = q.device
     if workspace is None:
         if reuse_prep:
@@ -325,6 +357,30 @@ def tree_attn_bwd(q, k, v, o, lse, dout, pos, subtree_end, softmax_scale=0.0, ro
     return dq, dk, dv
 
 
+def tree_attn_workspace_status(workspace):
+    """Status word of an attention workspace after its last prep pass (0 = no
+    data error; TA_STATUS_SUBTREE_END = a subtree end was clamped). Waits for
+    the current stream."""
+    st = ctypes.c_int32(0)
+    _check(_lib.tree_attn_workspace_status(_dev_ptr(workspace, "workspace"), ctypes.byref(st),
+                                           _stream(workspace.device)))
+    return st.value
+
+
+def tree_attn_plan_counts(workspace, T, Hq, Hkv, d, past_len=0):
+    """Per 128-row query tile: (non-empty, full) 64-key tile counts of the
+    device tile plan in `workspace`, as int32 numpy arrays. Waits for the
+    current stream."""
+    Lq = -(-int(past_len) // 128) * 128
+    nq = -(-(Lq + int(T)) // 256) * 2
+    ne = np.zeros(nq, np.int32)
+    fu = np.zeros(nq, np.int32)
+    _check(_lib.tree_attn_plan_counts(_dev_ptr(workspace, "workspace"), workspace.numel(), int(T), int(past_len),
+                                      int(Hq), int(Hkv), int(d), nq, _np_ptr(ne), _np_ptr(fu),
+                                      _stream(workspace.device)))
+    return ne, fu
+
+
 def gw_workspace(T, past_len, Hq, Hkv, d, with_bwd, device):
     nbytes = _lib.tree_attn_gw_workspace_bytes(T, past_len, Hq, Hkv, d, 1 if with_bwd else 0)
     if nbytes == 0:
@@ -336,6 +392,10 @@ def _past_args(q, k_past, v_past, past_visible):
     torch = _torch()
     dev = q.device
     Lp = k_past.shape[0]
+    d = q.shape[2]
+    _shape(k_past, "k_past", (Lp, None, d))
+    _shape(v_past, "v_past", tuple(k_past.shape))
+    _shape(past_visible, "past_visible", (Lp,))
     if Lp == 0:
         return (None, None, None, 0)
     return (_dev_ptr(k_past, "k_past", q.dtype, dev), _dev_ptr(v_past, "v_past", q.dtype, dev),
@@ -352,8 +412,8 @@ def tree_attn_gw_fwd(q, k, v, pos, subtree_end, pos_offset, k_past, v_past, past
     pos_offset + pos. Returns (o, lse, workspace).
     """
     torch = _torch()
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    T, Hq, Hkv, d = _check_attn(q, k, v, pos, subtree_end)
+    _shape(k_past, "k_past", (None, Hkv, d))
     dev = q.device
     kp, vp, vis, Lp = _past_args(q, k_past, v_past, past_visible)
     if workspace is None:
@@ -376,8 +436,11 @@ def tree_attn_gw_bwd(q, k, v, o, lse, dout, pos, subtree_end, pos_offset, k_past
     with respect to the rotated k_past and v_past. With accumulate=True the
     cached rows' gradients are added to the given dk_past / dv_past."""
     torch = _torch()
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    T, Hq, Hkv, d = _check_attn(q, k, v, pos, subtree_end, o=o, lse=lse, dout=dout)
+    _shape(k_past, "k_past", (None, Hkv, d))
+    for name, t in (("dk_past", dk_past), ("dv_past", dv_past)):
+        if t is not None:
+            _shape(t, name, tuple(k_past.shape))
     dev = q.device
     kp, vp, vis, Lp = _past_args(q, k_past, v_past, past_visible)
     if workspace is None:
@@ -389,6 +452,8 @@ def tree_attn_gw_bwd(q, k, v, o, lse, dout, pos, subtree_end, pos_offset, k_past
             raise ValueError("accumulate needs dk_past and dv_past")
         dk_past = torch.empty(Lp, Hkv, d, dtype=torch.float32, device=dev)
         dv_past = torch.empty(Lp, Hkv, d, dtype=torch.float32, device=dev)
+    _shape(dk_past, "dk_past", (Lp, Hkv, d))
+    _shape(dv_past, "dv_past", (Lp, Hkv, d))
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -407,11 +472,24 @@ def tree_attn_gw_bwd(q, k, v, o, lse, dout, pos, subtree_end, pos_offset, k_past
     return dq, dk, dv, dk_past, dv_past
 
 
+def _check_logprob(logits, src_row, target, weight, *per_entry):
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [R, V] (got {tuple(logits.shape)})")
+    M = src_row.numel()
+    _shape(src_row, "src_row", (M,))
+    _shape(target, "target", (M,))
+    _shape(weight, "weight", (M,))
+    for name, t in per_entry:
+        if t is not None:
+            _shape(t, name, (M,))
+    return logits.shape
+
+
 def tree_logprob(logits, src_row, target, weight, grad_scale=1.0, with_grad=True, with_row_lse=True,
                  workspace=None):
     """Returns (logp [M] f32, row_lse [R] f32 or None, loss [] f32, dlogits [R,V] or None)."""
     torch = _torch()
-    R, V = logits.shape
+    R, V = _check_logprob(logits, src_row, target, weight)
     M = src_row.numel()
     dev = logits.device
     if workspace is None:
@@ -438,7 +516,8 @@ def tree_logprob_ppo(logits, src_row, target, weight, advantage, old_logp, mask=
     """Clipped policy loss per occurrence. Returns (logp [M] f32, row_lse [R] f32 or None, loss [] f32,
     dlogits [R,V] or None)."""
     torch = _torch()
-    R, V = logits.shape
+    R, V = _check_logprob(logits, src_row, target, weight, ("advantage", advantage), ("old_logp", old_logp),
+                          ("mask", mask))
     M = src_row.numel()
     dev = logits.device
     if workspace is None:
@@ -482,11 +561,27 @@ def tree_partition(node_start, node_end, node_parent, capacity):
             "part_cut": part_cut[:P].copy()}
 
 
+def _check_conv(x, weight, bias, parent, pos=None, subtree_end=None, dy=None):
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError(f"x must be [T, C] and weight [C, K] (got {tuple(x.shape)}, {tuple(weight.shape)})")
+    T, C = x.shape
+    K = weight.shape[1]
+    _shape(weight, "weight", (C, K))
+    if bias is not None:
+        _shape(bias, "bias", (C,))
+    _shape(parent, "parent", (T,))
+    for name, t in (("pos", pos), ("subtree_end", subtree_end)):
+        if t is not None:
+            _shape(t, name, (T,))
+    if dy is not None:
+        _shape(dy, "dy", (T, C))
+    return T, C, K
+
+
 def tree_conv_fwd(x, weight, bias, parent, activation=1):
     """x [T, C] (bf16 / f32), weight [C, K] f32, bias [C] f32 or None, parent [T] int32 -> y [T, C]."""
     torch = _torch()
-    T, C = x.shape
-    K = weight.shape[1]
+    T, C, K = _check_conv(x, weight, bias, parent)
     dev = x.device
     y = torch.empty_like(x)
     rc = _lib.tree_conv_fwd(_dev_ptr(x, "x"), _dt(x), T, C, K, _dev_ptr(weight, "weight", torch.float32, dev),
@@ -500,8 +595,7 @@ def tree_conv_fwd(x, weight, bias, parent, activation=1):
 def tree_conv_bwd(x, dy, weight, bias, parent, pos, subtree_end, activation=1, workspace=None):
     """Returns (dx [T, C] like x, dweight [C, K] f32, dbias [C] f32 or None)."""
     torch = _torch()
-    T, C = x.shape
-    K = weight.shape[1]
+    T, C, K = _check_conv(x, weight, bias, parent, pos=pos, subtree_end=subtree_end, dy=dy)
     dev = x.device
     if workspace is None:
         workspace = torch.empty(max(_lib.tree_conv_workspace_bytes(T, C, K), 256), dtype=torch.uint8, device=dev)
@@ -547,11 +641,24 @@ def gdn_workspace(q, v, plan, backward=False):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
 
 
+def _check_gdn(q, k, v, g, beta, do=None):
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError(f"q must be [T, H, dk] and v [T, Hv, dv] (got {tuple(q.shape)}, {tuple(v.shape)})")
+    T, H, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _shape(k, "k", (T, H, dk))
+    _shape(v, "v", (T, Hv, dv))
+    _shape(g, "g", (T, Hv))
+    _shape(beta, "beta", (T, Hv))
+    if do is not None:
+        _shape(do, "do", (T, Hv, dv))
+    return T, H, dk, Hv, dv
+
+
 def tree_gdn_fwd(q, k, v, g, beta, plan, plan_dev=None, workspace=None):
     """q, k [T, H, dk]; v [T, Hv, dv] (bf16 / f32); g, beta [T, Hv] f32; plan from tree_gdn_plan -> o [T, Hv, dv]."""
     torch = _torch()
-    T, H, dk = q.shape
-    Hv, dv = v.shape[1], v.shape[2]
+    T, H, dk, Hv, dv = _check_gdn(q, k, v, g, beta)
     dev = q.device
     plan = np.ascontiguousarray(plan, dtype=np.int32)
     if plan_dev is None:
@@ -573,8 +680,7 @@ def tree_gdn_bwd(q, k, v, g, beta, do, plan, workspace, plan_dev=None):
     `workspace` (from gdn_workspace(..., backward=True)) with the same inputs
     and plan -> (dq, dk, dv, dg, dbeta)."""
     torch = _torch()
-    T, H, dk = q.shape
-    Hv, dv = v.shape[1], v.shape[2]
+    T, H, dk, Hv, dv = _check_gdn(q, k, v, g, beta, do=do)
     dev = q.device
     plan = np.ascontiguousarray(plan, dtype=np.int32)
     if plan_dev is None:

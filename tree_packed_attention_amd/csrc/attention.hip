@@ -11,12 +11,15 @@
 //   q, o, dout, dq  [T][Hq][D] (caller, bf16 or f32)
 //   k, v, dk, dv    [T][Hkv][D]
 //   lse             [Hq][T] f32
-// workspace (Tp = T rounded up to 128, DP = max(D, 32); padding is zero):
+// workspace (Tp = T rounded up to 256, DP = max(D, 32); padding is zero):
+//   status (one int at offset 0)         device-side data errors of the last prep
 //   qr [Hq][Tp][DP], kr, vr [Hkv][Tp][DP]  bf16; q, k rotated by RoPE
 //   sep [Tp]                             subtree ends, 0 past T
 //   cs [Tp][D/2] float2                  cos / sin of every token's angles
 //   kmm64 [nk64], kmm128 [nk128] int2    min / max subtree end per key tile
-//   qcount, qorder [nq]; qlist [nq][nk64] non-empty 64-key tiles per 128-row
+//   qcount, qfull, qorder [nq]           non-empty and full 64-key tiles per
+//                                        128-row query tile, work order
+//   qlist [nq][nk64]                     non-empty 64-key tiles per 128-row
 //                                        query tile (2 * tile + full flag);
 //                                        qorder = query tiles, heaviest first
 //   kwork, korder [nk128]                dK/dV work per 128-key tile, order
@@ -154,6 +157,14 @@ __device__ __forceinline__ void load8f(const float* p, float* x) {  // rotated i
   }
 }
 
+// Status word at the start of the workspace: bits of data errors only the
+// device can see. It is cleared at the start of every prep pass and read by
+// tree_attn_workspace_status.
+constexpr int kStatusSubtreeEnd = 1;  // a subtree end outside (i, T] was clamped
+__global__ __launch_bounds__(64) void status_reset_kernel(int* __restrict__ status) {
+  if (threadIdx.x == 0) *status = 0;
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                         const Tin* __restrict__ v, const int* __restrict__ pos,
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
                                                         int pos_offset, int T, int Tp, int Hq, int Hkv, int D,
                                                         int DP, float theta, bf16* __restrict__ qr,
                                                         bf16* __restrict__ kr, bf16* __restrict__ vr,
-                                                        int* __restrict__ sep, float2* __restrict__ cs) {
+                                                        int* __restrict__ sep, float2* __restrict__ cs,
+                                                        int* __restrict__ status) {
   // Row t of the combined sequence (T = Lq + own tokens, padded to Tp):
   //   t <  Lp        a cached row: key and value copied as given (the key is
   //                  already rotated), no query; visible to every own query
@@ -190,9 +202,16 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
   }
   if (threadIdx.x == 0) {
     int e = 0;
-    if (own)
-      e = se[i] + Lq;
-    else if (t < Lp)
+    if (own) {
+      // a subtree end lies in (i, number of own tokens]; any other value is
+      // clamped into that range (and reported in the status word), so every
+      // tile bound derived from it stays inside the workspace and every row
+      // sees at least itself
+      const int raw = se[i];
+      const int c = min(max(raw, i + 1), T - Lq);
+      if (c != raw) atomicOr(status, kStatusSubtreeEnd);
+      e = c + Lq;
+    } else if (t < Lp)
       e = past_vis[t] ? T : t;
     else if (t < Lq)
       e = t;
@@ -295,18 +314,19 @@ __global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict_
 // queries span [j, T) and masked ones nothing, so for the query rows, which
 // start at Lq after all cached rows, the same test holds.)
 __global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm, int T, int Lq, int BQ, int BK,
-                                                    int nk, int* __restrict__ counts, int* __restrict__ lists) {
+                                                    int nk, int* __restrict__ counts, int* __restrict__ fulls,
+                                                    int* __restrict__ lists) {
   const int qt = blockIdx.x;
   const int lane = threadIdx.x;
   const int i0 = qt * BQ;
-  if (i0 < Lq) {  // rows before Lq (cached keys) have no queries
-    if (lane == 0) counts[qt] = 0;
+  if (i0 < Lq || i0 >= T) {  // rows before Lq (cached keys) and padding rows have no queries
+    if (lane == 0) counts[qt] = fulls[qt] = 0;
     return;
   }
   const int i1 = min(i0 + BQ, T);
   const int nkc = min(nk, (i1 - 1) / BK + 1);
   int* out = lists + (size_t)qt * nk;
-  int n = 0;
+  int n = 0, nf = 0;
   for (int base = 0; base < nkc; base += 64) {
     const int kt = base + lane;
     bool ne = false;
@@ -320,8 +340,12 @@ __global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm
     const int off = __popcll(mask & ((1ull << lane) - 1ull));
     if (ne) out[n + off] = 2 * kt + full;
     n += __popcll(mask);
+    nf += __popcll(__ballot(ne && full));
   }
-  if (lane == 0) counts[qt] = n;
+  if (lane == 0) {
+    counts[qt] = n;
+    fulls[qt] = nf;
+  }
 }
 
 // Tile indices sorted by work, heaviest first (counting sort on the work
@@ -1105,7 +1129,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
 // tokens; Tc = Lq + T rows in all, padded to Tp.
 struct AttnLayout {
   int T, Lp, Lq, Tc, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
-  size_t off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qorder, off_qlist;
+  size_t off_status, off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qfull, off_qorder,
+      off_qlist;
   size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
 
@@ -1132,6 +1157,7 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
     o = align256(o + bytes);
     return at;
   };
+  L.off_status = take(4);  // always offset 0
   L.off_qr = take((size_t)Hq * L.Tp * L.DP * 2);
   L.off_kr = take((size_t)Hkv * L.Tp * L.DP * 2);
   L.off_vr = take((size_t)Hkv * L.Tp * L.DP * 2);
@@ -1140,6 +1166,7 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   L.off_kmm64 = take((size_t)L.nk64 * 8);
   L.off_kmm128 = take((size_t)L.nk128 * 8);
   L.off_qcount = take((size_t)L.nq * 4);
+  L.off_qfull = take((size_t)L.nq * 4);
   L.off_qorder = take((size_t)L.nq * 4);
   L.off_qlist = take((size_t)L.nq * L.nk64 * 4);
   L.off_kwork = take((size_t)L.nk128 * 4);
@@ -1192,12 +1219,13 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
              const Past& past, float theta, char* ws, hipStream_t st) {
   {
     ProfScope ps("rope_prep", st);
+    hipLaunchKernelGGL(status_reset_kernel, dim3(1), dim3(64), 0, st, at<int>(ws, L.off_status));
     hipLaunchKernelGGL(rope_prep_kernel<Tio>, dim3(L.Tp), dim3(256), 0, st, static_cast<const Tio*>(q),
                        static_cast<const Tio*>(k), static_cast<const Tio*>(v), pos, se,
                        static_cast<const Tio*>(past.k), static_cast<const Tio*>(past.v), past.vis, L.Lp, L.Lq,
                        past.pos_offset, L.Tc, L.Tp, L.Hq, L.Hkv, L.D, L.DP, theta, at<bf16>(ws, L.off_qr),
                        at<bf16>(ws, L.off_kr), at<bf16>(ws, L.off_vr), at<int>(ws, L.off_sep),
-                       at<float2>(ws, L.off_cs));
+                       at<float2>(ws, L.off_cs), at<int>(ws, L.off_status));
   }
   ProfScope ps("tile_plan", st);
   static_assert(kFwdRows == kFwdBQ, "the forward shares the dQ pass's query-tile plan");
@@ -1206,7 +1234,8 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
                      L.Tc, L.Lq, L.nk64, L.nk128, at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128),
                      at<int>(ws, L.off_kwork));
   hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.Tc, L.Lq,
-                     kFwdBQ, kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qlist));
+                     kFwdBQ, kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qfull),
+                     at<int>(ws, L.off_qlist));
   hipLaunchKernelGGL(order_kernel, dim3(2), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
                      at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, at<int>(ws, L.off_korder));
   return check_launch("prep");
@@ -1346,6 +1375,36 @@ extern "C" int tree_attn_bwd(const void* q, const void* k, const void* v, const 
   if (flags & TA_ACCUMULATE_PAST) return fail(TA_EINVAL, "tree_attn_bwd: TA_ACCUMULATE_PAST needs cached rows");
   return attn_bwd("tree_attn_bwd", q, k, v, o, lse, dout, dt, T, Hq, Hkv, d, pos, subtree_end, Past{}, 0,
                   softmax_scale, rope_theta, flags, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+extern "C" int tree_attn_workspace_status(const void* workspace, int32_t* status, void* stream) {
+  clear_error();
+  if (!workspace || !status) return fail(TA_EINVAL, "tree_attn_workspace_status: NULL pointer argument");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(TA_EHIP, "tree_attn_workspace_status: %s", hipGetErrorString(hipGetLastError()));
+  return TA_OK;
+}
+
+extern "C" int tree_attn_plan_counts(const void* workspace, size_t ws_bytes, int32_t T, int32_t past_len, int32_t Hq,
+                                     int32_t Hkv, int32_t d, int32_t n_qtiles, int32_t* nonempty, int32_t* full,
+                                     void* stream) {
+  clear_error();
+  if (int rc = validate_shape("tree_attn_plan_counts", T, past_len, Hq, Hkv, d)) return rc;
+  if (!workspace || !nonempty || !full) return fail(TA_EINVAL, "tree_attn_plan_counts: NULL pointer argument");
+  const AttnLayout L = make_layout(T, past_len, Hq, Hkv, d, false);
+  if (ws_bytes < L.total)
+    return fail(TA_EINVAL, "tree_attn_plan_counts: workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  if (n_qtiles != L.nq)
+    return fail(TA_EINVAL, "tree_attn_plan_counts: n_qtiles must be %d (got %d)", L.nq, n_qtiles);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* ws = static_cast<const char*>(workspace);
+  if (hipMemcpyAsync(nonempty, ws + L.off_qcount, (size_t)L.nq * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(full, ws + L.off_qfull, (size_t)L.nq * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(TA_EHIP, "tree_attn_plan_counts: %s", hipGetErrorString(hipGetLastError()));
+  return TA_OK;
 }
 
 extern "C" size_t tree_attn_gw_workspace_bytes(int32_t T, int32_t past_len, int32_t Hq, int32_t Hkv, int32_t d,

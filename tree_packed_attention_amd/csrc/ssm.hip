@@ -117,13 +117,18 @@ constexpr int kConvMaxDesc = 48;     // listed descendants per token in the dx p
 // pl (LDS, N + kConvMaxK - 1 entries); one thread per token then walks its
 // parents there, reading HBM only where a node's first token points outside
 // the window. All threads of the workgroup call it (it holds a barrier).
+// A parent precedes its child in preorder; any other value (malformed
+// metadata) is read as "no parent", so ancestor walks always move to lower
+// indices and stay in bounds.
+__device__ __forceinline__ int sane_parent(int p, int t) { return (p >= 0 && p < t) ? p : -1; }
+
 template <int N>
 __device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int t0, int T, int K,
                                                int (*anc)[kConvMaxK], int* pl) {
   const int base = t0 - (kConvMaxK - 1);
   for (int r = threadIdx.x; r < N + kConvMaxK - 1; r += blockDim.x) {
     const int t = base + r;
-    pl[r] = (t >= 0 && t < T) ? par[t] : -1;
+    pl[r] = (t >= 0 && t < T) ? sane_parent(par[t], t) : -1;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < N; i += blockDim.x) {
@@ -132,7 +137,7 @@ __device__ __forceinline__ void conv_ancestors(const int* __restrict__ par, int 
     for (int m = 0; m < kConvMaxK; ++m) {
       if (m < K) {
         anc[i][m] = s;
-        if (s >= 0) s = s >= base ? pl[s - base] : par[s];
+        if (s >= 0) s = s >= base ? pl[s - base] : sane_parent(par[s], s);
       }
     }
   }
@@ -423,16 +428,20 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
     const int j = t0 + i;
     int cnt = 0;
     if (j < T) {
-      const int pj = pw[i], end = sw[i];
+      // subtree ends are clamped into (t, T] and depths below 1 are skipped,
+      // so malformed metadata can neither leave [0, T) nor stall the walk
+      const int pj = pw[i], end = min(max(sw[i], j + 1), T);
       int t = j + 1;
       while (t < end) {
         const int dd = pos_at(t) - pj;
         if (dd < K) {
-          if (cnt < kConvMaxDesc) dlist[i][cnt] = (t << 3) | dd;
-          ++cnt;
+          if (dd >= 1) {
+            if (cnt < kConvMaxDesc) dlist[i][cnt] = (t << 3) | dd;
+            ++cnt;
+          }
           ++t;
         } else {
-          t = se_at(t);
+          t = max(se_at(t), t + 1);
         }
       }
     }
@@ -491,21 +500,23 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
           }
       }
     } else {
-      const int pj = pos[j], end = se[j];
+      const int pj = pos[j], end = min(max(se[j], j + 1), T);
       int t = j + 1;
       while (t < end) {
         const int dd = pos[t] - pj;
         if (dd < K) {
-          ld8f(gbuf + (size_t)t * C + c0, g);
+          if (dd >= 1) {
+            ld8f(gbuf + (size_t)t * C + c0, g);
 #pragma unroll
-          for (int m = 1; m < KM; ++m)
-            if (m == dd) {
+            for (int m = 1; m < KM; ++m)
+              if (m == dd) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
-            }
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wr[m][e], g[e], acc[e]);
+              }
+          }
           ++t;
         } else {
-          t = se[t];
+          t = max(se[t], t + 1);
         }
       }
     }
