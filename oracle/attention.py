@@ -38,7 +38,11 @@ def _f64(x):
 
 
 def rope_angles(positions, d, theta):
-    """angle[n, k] = position_n * theta^(-2k/d), k < d/2, in float64."""
+    """angle[n, k] = position_n * theta^(-2k/d), k < d/2, in float64.
+    theta <= 0 means no rotation (all angles 0), the library's convention
+    for switching RoPE off."""
+    if theta <= 0:
+        return np.zeros((len(positions), d // 2))
     k = np.arange(d // 2, dtype=np.float64)
     inv_freq = theta ** (-2.0 * k / d)
     return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]

@@ -212,3 +212,19 @@ def test_chain_segments_and_depths():
     # A B C D | E | F G  (E's parent is C, F's parent is B)
     assert OA.chain_segments(p["par"]) == [(0, 4), (4, 5), (5, 7)]
     assert np.array_equal(OA.depths(p["par"]), p["pos"])
+
+
+def test_theta_zero_is_no_rotation():
+    """rope_theta = 0 switches RoPE off: the same as rotating every token by
+    position 0 (the identity) at any base, forward and backward."""
+    rng = np.random.default_rng(8)
+    p = OP.pack(*workloads.random_small_forest(rng, n_seqs_max=5, len_max=8, vocab=3))
+    T = p["T"]
+    q, k, v, do = (rng.standard_normal(s) for s in ((T, 2, 8), (T, 1, 8), (T, 1, 8), (T, 2, 8)))
+    O, L = OA.forward_branches(q, k, v, p["par"], p["pos"], theta=0.0)
+    O2, L2 = OA.forward_dense(q, k, v, OP.visibility_dense(p["par"]), np.zeros(T), theta=10000.0)
+    assert np.max(np.abs(O - O2)) < 1e-12 and np.max(np.abs(L - L2)) < 1e-12
+    x = rng.standard_normal((T, 2, 8))
+    assert np.array_equal(OA.rope(x, p["pos"], 0.0), x) and np.array_equal(OA.rope_transpose(x, p["pos"], 0.0), x)
+    dq, dk, dv = OA.backward_branches(q, k, v, do, p["par"], p["pos"], theta=0.0)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk))
