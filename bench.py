@@ -101,17 +101,14 @@ def gateway_leg(seqs, groups, cfg, dev, steps):
     se = torch.from_numpy(full["subtree_end"]).to(dev)
     assert int(full["pos"][L - 1]) == L - 1 and int(full["subtree_end"][L - 1]) == T  # the prompt is a chain
 
-    # cached prompt K rotated at its positions (what the parent's forward hands over)
-    half = d // 2
-    inv = 10000.0 ** (-torch.arange(half, dtype=torch.float64, device=dev) * 2.0 / d)
-    ang = torch.arange(L, dtype=torch.float64, device=dev)[:, None] * inv[None, :]
-    c, s_ = torch.cos(ang)[:, None, :].float(), torch.sin(ang)[:, None, :].float()
-    kf = k[:L].float()
-    k_past = torch.cat([kf[..., :half] * c - kf[..., half:] * s_, kf[..., half:] * c + kf[..., :half] * s_],
-                       -1).to(torch.bfloat16).contiguous()
-    v_past = v[:L].contiguous()
+    # the parent partition's own tensors (its prompt chain) and the child
+    # partitions' tensors, sliced before the timed region
+    pq, pk, pv, pdo = (t[:L].contiguous() for t in (q, k, v, do))
     vis = torch.ones(L, dtype=torch.uint8, device=dev)
     ppos, pse = pos[:L].contiguous(), torch.full((L,), L, dtype=torch.int32, device=dev)
+    rows = torch.arange(L, dtype=torch.int32, device=dev)  # every prompt token is a cached row
+    k_past = torch.empty(L, Hkv, d, dtype=q.dtype, device=dev)
+    v_past = torch.empty_like(k_past)
     cq, ck, cv, cdo = (t[L:].contiguous() for t in (q, k, v, do))
     cpos, cse = (pos[L:] - L).contiguous(), (se[L:] - L).contiguous()
     ws_full = ta.attn_workspace(T, Hq, Hkv, d, True, dev)
@@ -123,13 +120,17 @@ def gateway_leg(seqs, groups, cfg, dev, steps):
         return o, ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws_full, reuse_prep=True)
 
     def split():
-        o1, l1, _ = ta.tree_attn_fwd(q[:L].contiguous(), k[:L].contiguous(), v_past, ppos, pse, workspace=ws_par)
-        ta.tree_attn_bwd(q[:L].contiguous(), k[:L].contiguous(), v_past, o1, l1, do[:L].contiguous(), ppos, pse,
-                         workspace=ws_par, reuse_prep=True)
+        # parent forward, hand-over of its rotated K and V rows, child
+        # forward and backward through the gateway, parent backward, relay of
+        # the cached rows' float32 gradients into the parent's dK, dV
+        o1, l1, _ = ta.tree_attn_fwd(pq, pk, pv, ppos, pse, workspace=ws_par)
+        ta.tree_attn_gw_export(pk, pv, ppos, rows, 0, 10000.0, k_past=k_past, v_past=v_past)
         o2, l2, _ = ta.tree_attn_gw_fwd(cq, ck, cv, cpos, cse, L, k_past, v_past, vis, workspace=ws_ch)
         g = ta.tree_attn_gw_bwd(cq, ck, cv, o2, l2, cdo, cpos, cse, L, k_past, v_past, vis, workspace=ws_ch,
                                 reuse_prep=True)
-        return o2, g
+        gp = ta.tree_attn_bwd(pq, pk, pv, o1, l1, pdo, ppos, pse, workspace=ws_par, reuse_prep=True)
+        ta.tree_attn_gw_relay(g[3], g[4], rows, ppos, gp[1], gp[2], 0, 10000.0)
+        return o2, (gp, g)
 
     def timed(fn):
         for _ in range(2):
@@ -141,15 +142,19 @@ def gateway_leg(seqs, groups, cfg, dev, steps):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps * 1e3, out
 
-    ms_full, (o_full, _) = timed(unsplit)
-    ms_split, (o_child, _) = timed(split)
+    ms_full, (o_full, g_full) = timed(unsplit)
+    ms_split, (o_child, (gp, gc)) = timed(split)
     P_child = int((cpos.long() + 1).sum().item()) + L * (T - L)
+    rel = lambda a, b: float((a.float() - b.float()).norm() / b.float().norm())
     return {"workload": f"tree 0 (T={T}) split after its {L}-token shared prefix: parent partition = the prefix, "
-                        f"child partitions = the subtrees under it ({T - L} tokens) in one gateway call",
+                        f"child partitions = the subtrees under it ({T - L} tokens) in one gateway call; the split "
+                        f"includes the export of the cached rows and the relay of their gradients",
             "unsplit_ms": round(ms_full, 4), "split_ms": round(ms_split, 4),
             "split_overhead": round(ms_split / ms_full - 1.0, 4),
             "child_visible_pairs": P_child,
-            "max_abs_child_o_vs_unsplit": round(float((o_child.float() - o_full[L:].float()).abs().max()), 5)}
+            "max_abs_child_o_vs_unsplit": round(float((o_child.float() - o_full[L:].float()).abs().max()), 5),
+            "rel_l2_parent_dk_vs_unsplit": round(rel(gp[1], g_full[1][:L]), 5),
+            "rel_l2_parent_dv_vs_unsplit": round(rel(gp[2], g_full[2][:L]), 5)}
 
 
 def ssm_leg(seqs, groups, dev, steps):

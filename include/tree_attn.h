@@ -221,8 +221,9 @@ int tree_attn_plan_counts(const void* workspace, size_t ws_bytes, int32_t T, int
  * past_len: >= 0 (0 gives plain tree attention); T + past_len <= 2^22 - 128.
  * pos_offset: >= 0.
  * dk_past, dv_past: device float32 [past_len][Hkv][d]; dk_past is the
- *   gradient with respect to the rotated k_past (the caller relays it
- *   through the parent's RoPE); rows the bias masks get 0.
+ *   gradient with respect to the rotated k_past (tree_attn_gw_relay takes
+ *   it back through the parent's RoPE); rows the bias masks get 0.
+ * tree_attn_gw_export builds k_past / v_past from the parent's tensors.
  * workspace: >= tree_attn_gw_workspace_bytes(T, past_len, ...) bytes.
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_EHIP. No allocation; asynchronous
  * on `stream`; bitwise reproducible for a fixed TA_ACCUMULATE_PAST order.
@@ -244,6 +245,45 @@ int tree_attn_gw_bwd(const void* q, const void* k, const void* v, const void* o,
                      float softmax_scale, float rope_theta, int32_t flags,
                      void* dq, void* dk, void* dv, float* dk_past, float* dv_past,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tree_attn_gw_export / tree_attn_gw_relay  (DEVICE)
+ *
+ * The two hand-overs across a partition boundary ("Tree Training" App. B.2:
+ * the parent's keys after RoPE and its values are cached for the child
+ * partitions; App. B.5: the gradients of the cached rows, kept in float32,
+ * flow back into the parent's gradients, summed over its children, Eq. 18).
+ * They act on the tensors of one partition (the parent, or any ancestor
+ * partition that holds part of a gateway): k, v, dk, dv [T][Hkv][d] in dt,
+ * pos [T] its own depth positions, pos_offset its own offset (0 for a
+ * partition of tree roots), so token j sits at position pos_offset + pos[j].
+ * rows: device int32 [n_rows], the partition's own token indices that make
+ * up cached rows r = 0 .. n_rows - 1 (for a gateway spread over several
+ * ancestor partitions, call once per partition on the matching slice of
+ * k_past / v_past / dk_past / dv_past).
+ *
+ * export: k_past[r] = R(pos_offset + pos[rows[r]]) k[rows[r]] (rotated in
+ *   float32 exactly as the attention prep rotates its keys, then stored in
+ *   dt), v_past[r] = v[rows[r]]; k_past, v_past [n_rows][Hkv][d] in dt. A row
+ *   index outside [0, T) exports zeros.
+ * relay: dk[rows[r]] += R(...)^T dk_past[r], dv[rows[r]] += dv_past[r], with
+ *   dk_past, dv_past float32 [n_rows][Hkv][d] as tree_attn_gw_bwd returns
+ *   them; each sum is formed in float32 and rounded once to dt. Run it after
+ *   the partition's own tree_attn_bwd / tree_attn_gw_bwd (which overwrite dk,
+ *   dv). rows must be distinct (calls that overlap on one stream and rows are
+ *   ordered; duplicated rows within one call race). A row outside [0, T) is
+ *   skipped.
+ * Asynchronous on `stream`; no allocation. 16-byte alignment is not needed.
+ * Errors: TA_EINVAL (NULL, sizes, dtype, negative theta or offset),
+ * TA_EUNSUPPORTED (d not in {16, 64, 128}), TA_EHIP.
+ * ---------------------------------------------------------------------- */
+int tree_attn_gw_export(const void* k, const void* v, ta_dtype dt, int32_t T, int32_t Hkv, int32_t d,
+                        const int32_t* pos, int32_t pos_offset, float rope_theta, const int32_t* rows,
+                        int32_t n_rows, void* k_past, void* v_past, void* stream);
+
+int tree_attn_gw_relay(const float* dk_past, const float* dv_past, const int32_t* rows, int32_t n_rows,
+                       ta_dtype dt, int32_t T, int32_t Hkv, int32_t d, const int32_t* pos, int32_t pos_offset,
+                       float rope_theta, void* dk, void* dv, void* stream);
 
 /* ------------------------------------------------------------------------
  * tree_logprob  (DEVICE)

@@ -1,7 +1,9 @@
 """GPU parity of tree_attn_gw_fwd / tree_attn_gw_bwd (attention of a child
 partition over cached ancestor rows, "Tree Training" §3.3, App. B.2-B.5)
 against the float64 gateway oracle, which is itself pinned to the unsplit
-tree in test_oracle_gateway.py.
+tree in test_oracle_gateway.py. On the GPU side the cached rows come from
+tree_attn_gw_export and the cached-row gradients go back through
+tree_attn_gw_relay; the oracle does its own RoPE.
 
 Tolerances as for plain tree attention: O and LSE max-abs <= 2e-2; dQ, dK,
 dV, dK_past, dV_past relative L2 <= 5e-2.
@@ -51,14 +53,24 @@ def _setup(seqs, groups, Hq, Hkv, d, dtype, seed, children):
     q, k, v, do = workloads.dense_inputs(len(par), Hq, Hkv, d, dtype, seed)
     sp = GW.split_at(par, children)
     P, e = sp["parent_rows"], sp["past_len"]
-    kp = torch.from_numpy(OA.rope(k[P[:e]].double().numpy(), pos[P[:e]], THETA)).to(q.dtype)
+    # the oracle rotates the cached keys itself; the GPU side takes them from
+    # the parent's tensors with tree_attn_gw_export (see _gpu)
+    kp = torch.from_numpy(OA.rope(k[P[:e]].double().numpy(), pos[P[:e]], THETA))
     vp = v[P[:e]].clone()
     vis = torch.from_numpy(sp["visible"].astype(np.uint8))
     parts = []
     for C, cpar in zip(sp["child_rows"], sp["child_par"]):
         parts.append(dict(q=q[C].contiguous(), k=k[C].contiguous(), v=v[C].contiguous(), do=do[C].contiguous(),
                           par=cpar, pos=GW._depths(cpar).astype(np.int32), se=_subtree_ends(cpar).astype(np.int32)))
-    return dict(sp=sp, k_past=kp, v_past=vp, vis=vis, parts=parts)
+    return dict(sp=sp, k_past=kp, v_past=vp, vis=vis, parts=parts, k=k, v=v, pos=pos.astype(np.int32),
+                past_rows=np.asarray(P[:e], np.int32))
+
+
+def _export(s):
+    """The cached rows as a parent partition hands them over: the library
+    exports them from the whole tree's k and v at the tree's positions."""
+    rows = torch.from_numpy(s["past_rows"]).cuda()
+    return ta.tree_attn_gw_export(s["k"].cuda(), s["v"].cuda(), torch.from_numpy(s["pos"]).cuda(), rows, 0, THETA)
 
 
 def _gpu(part, s, accumulate=False, dk_past=None, dv_past=None):
@@ -66,7 +78,8 @@ def _gpu(part, s, accumulate=False, dk_past=None, dv_past=None):
     pos = torch.from_numpy(part["pos"]).cuda()
     se = torch.from_numpy(part["se"]).cuda()
     q, k, v, do = c(part["q"]), c(part["k"]), c(part["v"]), c(part["do"])
-    kp, vp, vis = c(s["k_past"]), c(s["v_past"]), c(s["vis"])
+    kp, vp = _export(s)
+    vis = c(s["vis"])
     off = s["sp"]["pos_offset"]
     o, lse, ws = ta.tree_attn_gw_fwd(q, k, v, pos, se, off, kp, vp, vis, rope_theta=THETA, with_bwd_workspace=True)
     g = ta.tree_attn_gw_bwd(q, k, v, o, lse, do, pos, se, off, kp, vp, vis, rope_theta=THETA, workspace=ws,
@@ -78,6 +91,9 @@ def _gpu(part, s, accumulate=False, dk_past=None, dv_past=None):
 def _oracle(part, s):
     f = lambda t: t.double().numpy()
     args = (f(part["q"]), f(part["k"]), f(part["v"]))
+    # the oracle's cached keys: rotated in float64 and rounded to the input
+    # precision, as the parent's prep stores them
+    s = dict(s, k_past=s["k_past"].to(part["q"].dtype))
     O, LSE = GW.forward(*args, part["par"], f(s["k_past"]), f(s["v_past"]), s["sp"]["visible"],
                         s["sp"]["pos_offset"], theta=THETA)
     grads = GW.backward(*args, f(part["do"]), part["par"], f(s["k_past"]), f(s["v_past"]), s["sp"]["visible"],
@@ -203,11 +219,15 @@ def test_masked_gateway_rows_get_no_gradient_and_no_weight():
 
 def _run_partitioned(seqs, groups, Hq, Hkv, d, dtype, seed, capacity):
     """Plans the packed tree with tree_partition and runs every partition on
-    the GPU: tree-root partitions through the plain entry points, the others
-    through the gateway of their cut token's ancestors (the cut token
-    included, all visible) at pos_offset = its depth + 1. Gradients of the
-    cached rows are relayed back (un-rotated for dK, Tree Training App. B.5)
-    and summed. Returns the assembled outputs and the plan."""
+    the GPU with its own device tensors, in plan order (parents first):
+    tree-root partitions through the plain entry points, the others through
+    the gateway of their cut token's ancestors (the cut token included, all
+    visible) at pos_offset = its depth + 1. The gateway rows are built with
+    tree_attn_gw_export from each ancestor partition that holds part of the
+    chain, and after every backward their float32 gradients go back with
+    tree_attn_gw_relay into those partitions' dK, dV (Tree Training App. B.2,
+    B.5, Eq. 18). Only library calls touch the data on the GPU side. Returns
+    the assembled outputs and the plan."""
     p = ta.tree_pack(seqs, groups)
     T = p["T"]
     par, pos = p["parent"], p["pos"]
@@ -215,48 +235,129 @@ def _run_partitioned(seqs, groups, Hq, Hkv, d, dtype, seed, capacity):
     plan = ta.tree_partition(p["node_start"], p["node_end"], p["node_parent"], capacity)
     node_of = np.repeat(np.arange(p["n_nodes"]), p["node_end"] - p["node_start"])
     tok_part = plan["node_part"][node_of]
+    loc = -np.ones(T, np.int64)  # token -> index inside its own partition
+    parts = []
+    for b in range(len(plan["part_tokens"])):
+        R = np.nonzero(tok_part == b)[0]
+        loc[R] = np.arange(len(R))
+        inside = (par[R] >= 0) & (tok_part[np.maximum(par[R], 0)] == b)  # parent in this partition
+        lpar = np.where(inside, loc[np.maximum(par[R], 0)], -1)
+        cutn = int(plan["part_cut"][b])
+        off = 0 if cutn < 0 else int(pos[p["node_end"][cutn] - 1]) + 1
+        lpos = (pos[R] - off).astype(np.int32)
+        assert np.all(lpos[lpar < 0] == 0)
+        c = lambda t: t[torch.as_tensor(R)].contiguous().cuda()
+        parts.append(dict(R=R, off=off, cut=cutn, q=c(q), k=c(k), v=c(v), do=c(do),
+                          pos=torch.from_numpy(lpos).cuda(), se=torch.from_numpy(_subtree_ends(lpar).astype(np.int32)).cuda()))
+    relays = []
+    for b, P in enumerate(parts):
+        if P["cut"] < 0:
+            o, lse, ws = ta.tree_attn_fwd(P["q"], P["k"], P["v"], P["pos"], P["se"], rope_theta=THETA,
+                                          with_bwd_workspace=True)
+            g = ta.tree_attn_bwd(P["q"], P["k"], P["v"], o, lse, P["do"], P["pos"], P["se"], rope_theta=THETA,
+                                 workspace=ws, reuse_prep=True)
+        else:
+            A = [int(p["node_end"][P["cut"]] - 1)]
+            while par[A[-1]] >= 0:
+                A.append(int(par[A[-1]]))
+            A = np.array(A[::-1])
+            assert len(A) == P["off"]
+            kp = torch.empty(len(A), Hkv, d, dtype=q.dtype, device="cuda")
+            vp = torch.empty_like(kp)
+            pieces = []  # (ancestor partition, first cached row, local rows)
+            for a in sorted(set(int(x) for x in tok_part[A])):
+                sel = np.nonzero(tok_part[A] == a)[0]
+                assert np.array_equal(sel, np.arange(sel[0], sel[-1] + 1))  # a contiguous run of the chain
+                rows = torch.as_tensor(loc[A[sel]].astype(np.int32)).cuda()
+                Pa = parts[a]
+                ta.tree_attn_gw_export(Pa["k"], Pa["v"], Pa["pos"], rows, Pa["off"], THETA,
+                                       k_past=kp[sel[0]:sel[-1] + 1], v_past=vp[sel[0]:sel[-1] + 1])
+                pieces.append((a, int(sel[0]), int(sel[-1]) + 1, rows))
+            vis = torch.ones(len(A), dtype=torch.uint8).cuda()
+            o, lse, ws = ta.tree_attn_gw_fwd(P["q"], P["k"], P["v"], P["pos"], P["se"], P["off"], kp, vp, vis,
+                                             rope_theta=THETA, with_bwd_workspace=True)
+            g = ta.tree_attn_gw_bwd(P["q"], P["k"], P["v"], o, lse, P["do"], P["pos"], P["se"], P["off"], kp, vp, vis,
+                                    rope_theta=THETA, workspace=ws, reuse_prep=True)
+            relays.append((g[3], g[4], pieces))
+        P.update(o=o, lse=lse, dq=g[0], dk=g[1], dv=g[2])
+    # every partition's own backward has run: relay the cached rows' gradients
+    for dkp, dvp, pieces in relays:
+        for a, r0, r1, rows in pieces:
+            Pa = parts[a]
+            ta.tree_attn_gw_relay(dkp[r0:r1].contiguous(), dvp[r0:r1].contiguous(), rows, Pa["pos"], Pa["dk"],
+                                  Pa["dv"], Pa["off"], THETA)
+    torch.cuda.synchronize()
     O = np.zeros((T, Hq, d))
     LSE = np.zeros((Hq, T))
     dq = np.zeros((T, Hq, d))
     dk = np.zeros((T, Hkv, d))
     dv = np.zeros((T, Hkv, d))
-    for b in range(len(plan["part_tokens"])):
-        R = np.nonzero(tok_part == b)[0]
-        loc = -np.ones(T, np.int64)
-        loc[R] = np.arange(len(R))
-        lpar = np.where(par[R] >= 0, loc[np.maximum(par[R], 0)], -1)
-        lpar[par[R] < 0] = -1
-        cutn = int(plan["part_cut"][b])
-        off = 0 if cutn < 0 else int(pos[p["node_end"][cutn] - 1]) + 1
-        lpos = (pos[R] - off).astype(np.int32)
-        assert np.all(lpos[lpar < 0] == 0)
-        lse_ = _subtree_ends(lpar).astype(np.int32)
-        c = lambda t: t[torch.as_tensor(R)].contiguous().cuda()
-        qb, kb, vb, dob = c(q), c(k), c(v), c(do)
-        pt, st = torch.from_numpy(lpos).cuda(), torch.from_numpy(lse_).cuda()
-        if cutn < 0:
-            o, lse, ws = ta.tree_attn_fwd(qb, kb, vb, pt, st, rope_theta=THETA, with_bwd_workspace=True)
-            g = ta.tree_attn_bwd(qb, kb, vb, o, lse, dob, pt, st, rope_theta=THETA, workspace=ws, reuse_prep=True)
-        else:
-            A = [int(p["node_end"][cutn] - 1)]
-            while par[A[-1]] >= 0:
-                A.append(int(par[A[-1]]))
-            A = np.array(A[::-1])
-            assert len(A) == off
-            kp = torch.from_numpy(OA.rope(k[torch.as_tensor(A)].double().numpy(), pos[A], THETA)).to(q.dtype).cuda()
-            vp = v[torch.as_tensor(A)].contiguous().cuda()
-            vis = torch.ones(len(A), dtype=torch.uint8).cuda()
-            o, lse, ws = ta.tree_attn_gw_fwd(qb, kb, vb, pt, st, off, kp, vp, vis, rope_theta=THETA,
-                                             with_bwd_workspace=True)
-            g = ta.tree_attn_gw_bwd(qb, kb, vb, o, lse, dob, pt, st, off, kp, vp, vis, rope_theta=THETA,
-                                    workspace=ws, reuse_prep=True)
-            dk[A] += OA.rope_transpose(host(g[3]), pos[A], THETA)
-            dv[A] += host(g[4])
-        torch.cuda.synchronize()
-        O[R], LSE[:, R], dq[R] = host(o), host(lse), host(g[0])
-        dk[R] += host(g[1])
-        dv[R] += host(g[2])
+    for P in parts:
+        R = P["R"]
+        O[R], LSE[:, R], dq[R], dk[R], dv[R] = host(P["o"]), host(P["lse"]), host(P["dq"]), host(P["dk"]), host(P["dv"])
     return dict(p=p, plan=plan, q=q, k=k, v=v, do=do, O=O, LSE=LSE, dq=dq, dk=dk, dv=dv)
+
+
+def test_export_is_the_prep_rotation_and_relay_adds_the_rotated_gradient():
+    """tree_attn_gw_export rotates rows at pos_offset + pos as the oracle's
+    RoPE does, and copies the values; the relay adds the transposed rotation
+    of the float32 gradient (checked against its definition on the oracle's
+    rotation). A child partition of one token under a gateway exported from
+    its ancestor chain reproduces that token appended to the unsplit tree."""
+    rng = np.random.default_rng(3)
+    T, Hkv, d, off = 300, 2, 64, 37
+    seqs, groups = workloads.random_forest(12, [T])
+    pk = ta.tree_pack(seqs, groups)
+    T = pk["T"]
+    _, k, v, _ = workloads.dense_inputs(T, 2, Hkv, d, "bf16", 9, device="cuda")
+    pos = torch.from_numpy(pk["pos"]).cuda()
+    rows_np = rng.permutation(T)[:120].astype(np.int32)
+    rows = torch.as_tensor(rows_np).cuda()
+    kp, vp = ta.tree_attn_gw_export(k, v, pos, rows, off, THETA)
+    torch.cuda.synchronize()
+    ref = OA.rope(host(k)[rows_np].astype(np.float64), pk["pos"][rows_np] + off, THETA)
+    assert max_abs(host(kp), ref) <= 2e-2 and torch.equal(vp, v[rows.long()])
+    # relay: dk += R^T g, dv += h, in float32 then rounded once
+    g = torch.randn(120, Hkv, d, device="cuda")
+    h = torch.randn(120, Hkv, d, device="cuda")
+    dk0 = torch.randn(T, Hkv, d, device="cuda").to(torch.bfloat16)
+    dv0 = torch.randn(T, Hkv, d, device="cuda").to(torch.bfloat16)
+    dk, dv = dk0.clone(), dv0.clone()
+    ta.tree_attn_gw_relay(g, h, rows, pos, dk, dv, off, THETA)
+    torch.cuda.synchronize()
+    exp_k = host(dk0).astype(np.float64)
+    exp_v = host(dv0).astype(np.float64)
+    exp_k[rows_np] += OA.rope_transpose(host(g).astype(np.float64), pk["pos"][rows_np] + off, THETA)
+    exp_v[rows_np] += host(h)
+    assert max_abs(host(dk), exp_k) <= 3e-2 and max_abs(host(dv), exp_v) <= 3e-2
+    untouched = np.setdiff1d(np.arange(T), rows_np)
+    assert np.array_equal(host(dk)[untouched], host(dk0)[untouched])
+    # the exported keys are the ones the attention prep rotates: a child of
+    # one token under a gateway of the partition's whole ancestor chain at
+    # this offset sees exactly the rotated keys of the unsplit layout
+    chain = np.array(sorted(set(OP.ancestors_or_self(pk["parent"], T - 1))), np.int32)
+    kc, vc = ta.tree_attn_gw_export(k, v, pos, torch.as_tensor(chain).cuda(), 0, THETA)
+    qx = torch.randn(1, 2, d, device="cuda").to(torch.bfloat16)
+    kx = torch.randn(1, Hkv, d, device="cuda").to(torch.bfloat16)
+    vx = torch.randn(1, Hkv, d, device="cuda").to(torch.bfloat16)
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ox, lx, _ = ta.tree_attn_gw_fwd(qx, kx, vx, one, one + 1, len(chain), kc, vc,
+                                    torch.ones(len(chain), dtype=torch.uint8, device="cuda"), rope_theta=THETA)
+    # the same token appended under T - 1 in the unsplit tree
+    qf = torch.zeros(T + 1, 2, d, dtype=torch.bfloat16, device="cuda")
+    qf[T] = qx[0]
+    kf = torch.cat([k, kx]).contiguous()
+    vf = torch.cat([v, vx]).contiguous()
+    posf = torch.cat([pos, pos[T - 1:T] + 1]).contiguous()
+    sef = torch.from_numpy(np.append(np.where(np.isin(np.arange(T), chain), T + 1, pk["subtree_end"]),
+                                     T + 1).astype(np.int32)).cuda()
+    of, lf, _ = ta.tree_attn_fwd(qf, kf, vf, posf, sef, rope_theta=THETA)
+    torch.cuda.synchronize()
+    # the two runs tile and sum the same visible keys in another order, so
+    # the float32 LSE may differ in its last bits; a key rotated differently
+    # by even one bf16 unit would move it by far more
+    assert torch.equal(ox[0], of[T])
+    assert float((lx[:, 0] - lf[:, T]).abs().max()) <= 1e-5
 
 
 @pytest.mark.parametrize("capacity", [600, 1500])

@@ -62,6 +62,8 @@ EXPORTS = (
     "tree_attn_profile_read",
     "tree_attn_workspace_status",
     "tree_attn_plan_counts",
+    "tree_attn_gw_export",
+    "tree_attn_gw_relay",
 )
 
 
@@ -147,6 +149,10 @@ _lib.tree_attn_workspace_status.restype = ctypes.c_int
 _lib.tree_attn_workspace_status.argtypes = [_p, ctypes.POINTER(ctypes.c_int32), _p]
 _lib.tree_attn_plan_counts.restype = ctypes.c_int
 _lib.tree_attn_plan_counts.argtypes = [_p, _sz, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
+_lib.tree_attn_gw_export.restype = ctypes.c_int
+_lib.tree_attn_gw_export.argtypes = [_p, _p, ctypes.c_int, _i32, _i32, _i32, _p, _i32, _f32, _p, _i32, _p, _p, _p]
+_lib.tree_attn_gw_relay.restype = ctypes.c_int
+_lib.tree_attn_gw_relay.argtypes = [_p, _p, _p, _i32, ctypes.c_int, _i32, _i32, _i32, _p, _i32, _f32, _p, _p, _p]
 _lib.tree_attn_profile_enable.restype = ctypes.c_int
 _lib.tree_attn_profile_enable.argtypes = [_i32]
 _lib.tree_attn_profile_read.restype = ctypes.c_int
@@ -483,6 +489,57 @@ def _check_logprob(logits, src_row, target, weight, *per_entry):
         if t is not None:
             _shape(t, name, (M,))
     return logits.shape
+
+
+def tree_attn_gw_export(k, v, pos, rows, pos_offset=0, rope_theta=10000.0, k_past=None, v_past=None):
+    """Cached gateway rows from one partition's own tokens: k_past[r] = k of
+    rows[r] rotated at pos_offset + pos[rows[r]], v_past[r] = its v. k, v
+    [T, Hkv, d]; pos [T] int32; rows [n] int32 (device). Writes into the given
+    k_past / v_past (e.g. a slice of a larger gateway) or new tensors.
+    Returns (k_past, v_past)."""
+    torch = _torch()
+    if k.dim() != 3:
+        raise ValueError(f"k must be [T, Hkv, d] (got {tuple(k.shape)})")
+    T, Hkv, d = k.shape
+    _shape(v, "v", (T, Hkv, d))
+    _shape(pos, "pos", (T,))
+    n = rows.numel()
+    _shape(rows, "rows", (n,))
+    if k_past is None:
+        k_past = torch.empty(n, Hkv, d, dtype=k.dtype, device=k.device)
+    if v_past is None:
+        v_past = torch.empty(n, Hkv, d, dtype=k.dtype, device=k.device)
+    _shape(k_past, "k_past", (n, Hkv, d))
+    _shape(v_past, "v_past", (n, Hkv, d))
+    dev = k.device
+    _check(_lib.tree_attn_gw_export(_dev_ptr(k, "k"), _dev_ptr(v, "v", k.dtype, dev), _dt(k), T, Hkv, d,
+                                    _dev_ptr(pos, "pos", torch.int32, dev), int(pos_offset), float(rope_theta),
+                                    _dev_ptr(rows, "rows", torch.int32, dev), n,
+                                    _dev_ptr(k_past, "k_past", k.dtype, dev), _dev_ptr(v_past, "v_past", k.dtype, dev),
+                                    _stream(dev)))
+    return k_past, v_past
+
+
+def tree_attn_gw_relay(dk_past, dv_past, rows, pos, dk, dv, pos_offset=0, rope_theta=10000.0):
+    """Adds the float32 gradients of cached rows back into one partition's
+    dk / dv [T, Hkv, d] (in place): dk[rows[r]] += R^T dk_past[r],
+    dv[rows[r]] += dv_past[r], rotated at pos_offset + pos[rows[r]]."""
+    torch = _torch()
+    if dk.dim() != 3:
+        raise ValueError(f"dk must be [T, Hkv, d] (got {tuple(dk.shape)})")
+    T, Hkv, d = dk.shape
+    _shape(dv, "dv", (T, Hkv, d))
+    _shape(pos, "pos", (T,))
+    n = rows.numel()
+    _shape(rows, "rows", (n,))
+    _shape(dk_past, "dk_past", (n, Hkv, d))
+    _shape(dv_past, "dv_past", (n, Hkv, d))
+    dev = dk.device
+    _check(_lib.tree_attn_gw_relay(_dev_ptr(dk_past, "dk_past", torch.float32, dev),
+                                   _dev_ptr(dv_past, "dv_past", torch.float32, dev),
+                                   _dev_ptr(rows, "rows", torch.int32, dev), n, _dt(dk), T, Hkv, d,
+                                   _dev_ptr(pos, "pos", torch.int32, dev), int(pos_offset), float(rope_theta),
+                                   _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv", dk.dtype, dev), _stream(dev)))
 
 
 def tree_logprob(logits, src_row, target, weight, grad_scale=1.0, with_grad=True, with_row_lse=True,

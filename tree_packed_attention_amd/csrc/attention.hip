@@ -165,6 +165,32 @@ __global__ __launch_bounds__(64) void status_reset_kernel(int* __restrict__ stat
   if (threadIdx.x == 0) *status = 0;
 }
 
+// cos / sin of the RoPE angle of position p for rotation pair k (dims k and
+// k + D/2): angle = p * theta^(-2k/D), formed and reduced in float64, then
+// evaluated in float32 on [-pi, pi]. theta <= 0: no rotation. Shared by the
+// prep, the gateway export and the gateway relay, so all rotate bitwise alike.
+__device__ __forceinline__ float2 rope_cs(int p, int k, int D, float theta) {
+  float c = 1.0f, s = 0.0f;
+  if (theta > 0.0f) {
+    const double inv = exp2(-2.0 * (double)k / (double)D * log2((double)theta));
+    const double ang = (double)p * inv;
+    const double twopi = 6.283185307179586476925286766559;
+    const double r = ang - rint(ang / twopi) * twopi;
+    sincosf((float)r, &s, &c);
+  }
+  return make_float2(c, s);
+}
+// (x1, x2) -> R (x1, x2) and its transpose, with explicit fused multiply-adds
+// so every kernel rounds alike
+__device__ __forceinline__ void rope_rot(float x1, float x2, float2 cs, float& y1, float& y2) {
+  y1 = fmaf(x1, cs.x, -x2 * cs.y);
+  y2 = fmaf(x2, cs.x, x1 * cs.y);
+}
+__device__ __forceinline__ void rope_rot_t(float g1, float g2, float2 cs, float& y1, float& y2) {
+  y1 = fmaf(g1, cs.x, g2 * cs.y);
+  y2 = fmaf(g2, cs.x, -g1 * cs.y);
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                         const Tin* __restrict__ v, const int* __restrict__ pos,
@@ -189,16 +215,9 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
   const bool own = t >= Lq && t < T;
   const int i = t - Lq;
   if ((int)threadIdx.x < half) {
-    float c = 1.0f, s = 0.0f;
-    if (own && theta > 0.0f) {
-      const double inv = exp2(-2.0 * (double)threadIdx.x / (double)D * log2((double)theta));
-      const double ang = (double)(pos_offset + pos[i]) * inv;
-      const double twopi = 6.283185307179586476925286766559;
-      const double r = ang - rint(ang / twopi) * twopi;
-      sincosf((float)r, &s, &c);
-    }
-    tab[threadIdx.x] = make_float2(c, s);
-    cs[(size_t)t * half + threadIdx.x] = make_float2(c, s);
+    const float2 c = own ? rope_cs(pos_offset + pos[i], threadIdx.x, D, theta) : make_float2(1.0f, 0.0f);
+    tab[threadIdx.x] = c;
+    cs[(size_t)t * half + threadIdx.x] = c;
   }
   if (threadIdx.x == 0) {
     int e = 0;
@@ -257,9 +276,10 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const Tin* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (rotate) {
-        const float2 c = tab[kk + e];
-        y1[e] = (bf16)(x1[e] * c.x - x2[e] * c.y);
-        y2[e] = (bf16)(x2[e] * c.x + x1[e] * c.y);
+        float r1, r2;
+        rope_rot(x1[e], x2[e], tab[kk + e], r1, r2);
+        y1[e] = (bf16)r1;
+        y2[e] = (bf16)r2;
       } else {
         y1[e] = (bf16)x1[e];
         y2[e] = (bf16)x2[e];
@@ -846,10 +866,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       float o1[8], o2[8];
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
-        const float g1 = ep[(d0 + s2) * 32 + lc], g2 = ep[(d0 + half + s2) * 32 + lc];
-        const float2 cc = csr[d0 + s2];
-        o1[s2] = g1 * cc.x + g2 * cc.y;
-        o2[s2] = g2 * cc.x - g1 * cc.y;
+        rope_rot_t(ep[(d0 + s2) * 32 + lc], ep[(d0 + half + s2) * 32 + lc], csr[d0 + s2], o1[s2], o2[s2]);
       }
       store_row8(out + d0, o1);
       store_row8(out + d0 + half, o2);
@@ -1108,10 +1125,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
         Tio* out = dk + ((size_t)(j - Lq) * Hkv + hk) * D;
         const float2* csr = cs + (size_t)j * half;
         for (int kk = lane; kk < half; kk += 64) {
-          const float g1 = er[kk], g2 = er[kk + half];
-          const float2 c = csr[kk];
-          out[kk] = from_f32<Tio>(g1 * c.x + g2 * c.y);
-          out[kk + half] = from_f32<Tio>(g2 * c.x - g1 * c.y);
+          float y1, y2;
+          rope_rot_t(er[kk], er[kk + half], csr[kk], y1, y2);
+          out[kk] = from_f32<Tio>(y1);
+          out[kk + half] = from_f32<Tio>(y2);
         }
       } else {
         Tio* out = dv + ((size_t)(j - Lq) * Hkv + hk) * D;
@@ -1119,6 +1136,68 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
       }
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------
+// Partition-boundary hand-over ("Tree Training" App. B.2 and B.5). Export:
+// rows[r] of a partition's own tokens become cached row r of a child's
+// gateway, the key rotated at that token's position (pos_offset + pos), the
+// value as is. Relay: the float32 gradients of cached row r flow back into
+// that token's dk (through R^T) and dv, added in float32 and rounded once.
+// One workgroup per listed row; a row index outside [0, T) exports zeros and
+// relays nothing.
+template <typename Tio>
+__global__ __launch_bounds__(256) void gw_export_kernel(const Tio* __restrict__ k, const Tio* __restrict__ v,
+                                                        const int* __restrict__ pos, const int* __restrict__ rows,
+                                                        int T, int Hkv, int D, int pos_offset, float theta,
+                                                        Tio* __restrict__ k_past, Tio* __restrict__ v_past) {
+  __shared__ float2 tab[64];
+  const int r = blockIdx.x;
+  const int j = rows[r];
+  const bool ok = j >= 0 && j < T;
+  const int half = D / 2;
+  if ((int)threadIdx.x < half) tab[threadIdx.x] = ok ? rope_cs(pos_offset + pos[j], threadIdx.x, D, theta)
+                                                     : make_float2(1.0f, 0.0f);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < Hkv * half; idx += blockDim.x) {
+    const int hk = idx / half, kk = idx % half;
+    const size_t src = ((size_t)(ok ? j : 0) * Hkv + hk) * D, dst = ((size_t)r * Hkv + hk) * D;
+    float y1 = 0.0f, y2 = 0.0f, v1 = 0.0f, v2 = 0.0f;
+    if (ok) {
+      rope_rot(to_f32(k[src + kk]), to_f32(k[src + kk + half]), tab[kk], y1, y2);
+      v1 = to_f32(v[src + kk]);
+      v2 = to_f32(v[src + kk + half]);
+    }
+    k_past[dst + kk] = from_f32<Tio>(y1);
+    k_past[dst + kk + half] = from_f32<Tio>(y2);
+    v_past[dst + kk] = from_f32<Tio>(v1);
+    v_past[dst + kk + half] = from_f32<Tio>(v2);
+  }
+}
+
+template <typename Tio>
+__global__ __launch_bounds__(256) void gw_relay_kernel(const float* __restrict__ dk_past,
+                                                       const float* __restrict__ dv_past,
+                                                       const int* __restrict__ pos, const int* __restrict__ rows,
+                                                       int T, int Hkv, int D, int pos_offset, float theta,
+                                                       Tio* __restrict__ dk, Tio* __restrict__ dv) {
+  __shared__ float2 tab[64];
+  const int r = blockIdx.x;
+  const int j = rows[r];
+  if (j < 0 || j >= T) return;  // uniform over the workgroup
+  const int half = D / 2;
+  if ((int)threadIdx.x < half) tab[threadIdx.x] = rope_cs(pos_offset + pos[j], threadIdx.x, D, theta);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < Hkv * half; idx += blockDim.x) {
+    const int hk = idx / half, kk = idx % half;
+    const size_t src = ((size_t)r * Hkv + hk) * D, dst = ((size_t)j * Hkv + hk) * D;
+    float g1, g2;
+    rope_rot_t(dk_past[src + kk], dk_past[src + kk + half], tab[kk], g1, g2);
+    dk[dst + kk] = from_f32<Tio>(to_f32(dk[dst + kk]) + g1);
+    dk[dst + kk + half] = from_f32<Tio>(to_f32(dk[dst + kk + half]) + g2);
+    dv[dst + kk] = from_f32<Tio>(to_f32(dv[dst + kk]) + dv_past[src + kk]);
+    dv[dst + kk + half] = from_f32<Tio>(to_f32(dv[dst + kk + half]) + dv_past[src + kk + half]);
   }
 }
 
@@ -1447,4 +1526,61 @@ extern "C" int tree_attn_gw_bwd(const void* q, const void* k, const void* v, con
   past.accumulate = (flags & TA_ACCUMULATE_PAST) ? 1 : 0;
   return attn_bwd("tree_attn_gw_bwd", q, k, v, o, lse, dout, dt, T, Hq, Hkv, d, pos, subtree_end, past, past_len,
                   softmax_scale, rope_theta, flags, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+namespace ta {
+namespace {
+int gw_rows_check(const char* fn, ta_dtype dt, int32_t T, int32_t Hkv, int32_t d, int32_t n_rows) {
+  if (T < 1 || T > kMaxRows) return fail(TA_EINVAL, "%s: T must be in [1, 2^22] (got %d)", fn, T);
+  if (Hkv < 1 || Hkv > 256) return fail(TA_EINVAL, "%s: Hkv must be in [1, 256] (got %d)", fn, Hkv);
+  if (d != 16 && d != 64 && d != 128) return fail(TA_EUNSUPPORTED, "%s: head dim %d not in {16, 64, 128}", fn, d);
+  if (n_rows < 0 || n_rows > kMaxRows) return fail(TA_EINVAL, "%s: n_rows must be in [0, 2^22] (got %d)", fn, n_rows);
+  if (dt != TA_BF16 && dt != TA_F32) return fail(TA_EINVAL, "%s: bad dtype %d", fn, (int)dt);
+  return TA_OK;
+}
+}  // namespace
+}  // namespace ta
+
+extern "C" int tree_attn_gw_export(const void* k, const void* v, ta_dtype dt, int32_t T, int32_t Hkv, int32_t d,
+                                   const int32_t* pos, int32_t pos_offset, float rope_theta, const int32_t* rows,
+                                   int32_t n_rows, void* k_past, void* v_past, void* stream) {
+  clear_error();
+  const char* fn = "tree_attn_gw_export";
+  if (int rc = gw_rows_check(fn, dt, T, Hkv, d, n_rows)) return rc;
+  if (!k || !v || !pos || !rows || !k_past || !v_past) return fail(TA_EINVAL, "%s: NULL pointer argument", fn);
+  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "%s: rope_theta must be >= 0", fn);
+  if (pos_offset < 0) return fail(TA_EINVAL, "%s: pos_offset must be >= 0", fn);
+  if (n_rows == 0) return TA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ProfScope ps("gw_export", st);
+  if (dt == TA_BF16)
+    hipLaunchKernelGGL(gw_export_kernel<bf16>, dim3(n_rows), dim3(256), 0, st, static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), pos, rows, T, Hkv, d, pos_offset, rope_theta,
+                       static_cast<bf16*>(k_past), static_cast<bf16*>(v_past));
+  else
+    hipLaunchKernelGGL(gw_export_kernel<float>, dim3(n_rows), dim3(256), 0, st, static_cast<const float*>(k),
+                       static_cast<const float*>(v), pos, rows, T, Hkv, d, pos_offset, rope_theta,
+                       static_cast<float*>(k_past), static_cast<float*>(v_past));
+  return check_launch(fn);
+}
+
+extern "C" int tree_attn_gw_relay(const float* dk_past, const float* dv_past, const int32_t* rows, int32_t n_rows,
+                                  ta_dtype dt, int32_t T, int32_t Hkv, int32_t d, const int32_t* pos,
+                                  int32_t pos_offset, float rope_theta, void* dk, void* dv, void* stream) {
+  clear_error();
+  const char* fn = "tree_attn_gw_relay";
+  if (int rc = gw_rows_check(fn, dt, T, Hkv, d, n_rows)) return rc;
+  if (!dk_past || !dv_past || !rows || !pos || !dk || !dv) return fail(TA_EINVAL, "%s: NULL pointer argument", fn);
+  if (!(rope_theta >= 0.0f)) return fail(TA_EINVAL, "%s: rope_theta must be >= 0", fn);
+  if (pos_offset < 0) return fail(TA_EINVAL, "%s: pos_offset must be >= 0", fn);
+  if (n_rows == 0) return TA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ProfScope ps("gw_relay", st);
+  if (dt == TA_BF16)
+    hipLaunchKernelGGL(gw_relay_kernel<bf16>, dim3(n_rows), dim3(256), 0, st, dk_past, dv_past, pos, rows, T, Hkv,
+                       d, pos_offset, rope_theta, static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  else
+    hipLaunchKernelGGL(gw_relay_kernel<float>, dim3(n_rows), dim3(256), 0, st, dk_past, dv_past, pos, rows, T, Hkv,
+                       d, pos_offset, rope_theta, static_cast<float*>(dk), static_cast<float*>(dv));
+  return check_launch(fn);
 }
