@@ -17,11 +17,11 @@
 //   sep [Tp]                             subtree ends, 0 past T
 //   cs [Tp][D/2] float2                  cos / sin of every token's angles
 //   kmm64 [nk64], kmm128 [nk128] int2    min / max subtree end per key tile
+//   sbmax [nk64 / 64]                    max subtree end per 4096-key superblock
 //   qcount, qfull, qorder [nq]           non-empty and full 64-key tiles per
-//                                        128-row query tile, work order
-//   qlist [nq][nk64]                     non-empty 64-key tiles per 128-row
-//                                        query tile (2 * tile + full flag);
-//                                        qorder = query tiles, heaviest first
+//                                        128-row query tile, work order (the
+//                                        tile lists themselves are built per
+//                                        workgroup in LDS: O(T) plan storage)
 //   kwork, korder [nk128]                dK/dV work per 128-key tile, order
 //   dd, l2 [Hq][Tp] f32                  -rowsum(dO * O) and -lse / scale
 //   dor [Hq][Tp][DP] bf16                dO, head-major (written by dQ pass)
@@ -327,41 +327,98 @@ __global__ __launch_bounds__(256) void tile_minmax_kernel(const int* __restrict_
   }
 }
 
-// One wave per query tile: the compacted, ascending list of key tiles that
-// hold at least one visible pair. Keys of tile kt cover [j0, max se) without
-// gaps (every key's interval starts inside the tile), so the tile meets query
-// rows [i0, i1) iff j0 <= i1 - 1 and max se > i0. (Cached rows visible to all
-// queries span [j, T) and masked ones nothing, so for the query rows, which
-// start at Lq after all cached rows, the same test holds.)
-__global__ __launch_bounds__(64) void q_plan_kernel(const int2* __restrict__ kmm, int T, int Lq, int BQ, int BK,
-                                                    int nk, int* __restrict__ counts, int* __restrict__ fulls,
-                                                    int* __restrict__ lists) {
+// Superblocks of kSbTiles key tiles (4096 keys): the largest subtree end of
+// each, so the list builder skips 64 empty key tiles with one comparison.
+constexpr int kSbTiles = 64;
+constexpr int kListCap = 256;  // entries of one round of a workgroup's tile list
+// One wave per superblock.
+__global__ __launch_bounds__(256) void sb_max_kernel(const int2* __restrict__ kmm64, int nk64, int nsb,
+                                                     int* __restrict__ sbmax) {
+  const int sb = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sb >= nsb) return;
+  const int lane = threadIdx.x & 63;
+  const int kt = sb * kSbTiles + lane;
+  int m = kt < nk64 ? kmm64[kt].y : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  if (lane == 0) sbmax[sb] = m;
+}
+
+// The non-empty key tiles of query rows [i0, i1), ascending from tile
+// `resume` on, written by one wave as entries 2 * tile + full into list
+// (at most kListCap). Keys of tile kt cover [j0, max se) without gaps (every
+// key's interval starts inside the tile), so the tile meets the rows iff
+// j0 <= i1 - 1 (kt < nkc) and max se > i0; it is full iff j1 - 1 <= i0 and
+// min se >= i1. (Cached rows visible to all queries span [j, T) and masked
+// ones nothing, so for the query rows, which start at Lq after all cached
+// rows, the same test holds.) Returns the number of entries; resume becomes
+// the tile to continue from (nkc when the list is complete). Empty
+// superblocks cost one comparison, so the work is O(nkc / 4096 + entries).
+__device__ __forceinline__ int build_tile_list(const int2* __restrict__ kmm, const int* __restrict__ sbmax, int i0,
+                                               int i1, int nkc, int& resume, int* list, int lane) {
+  const int nsb = (nkc + kSbTiles - 1) / kSbTiles;
+  int n = 0;
+  int kt = resume;
+  while (kt < nkc && n < kListCap) {
+    int sb = kt / kSbTiles;
+    const uint64_t smask = __ballot(sb + lane < nsb && sbmax[sb + lane] > i0);
+    if (smask == 0) {
+      kt = (sb + 64) * kSbTiles;
+      continue;
+    }
+    sb += __builtin_ctzll(smask);
+    kt = max(kt, sb * kSbTiles);
+    const int t = sb * kSbTiles + lane;
+    bool ne = false;
+    int full = 0;
+    if (t >= kt && t < nkc) {
+      const int2 m = kmm[t];
+      ne = m.y > i0;
+      full = (t * kFwdBK + kFwdBK - 1 <= i0) && (m.x >= i1);
+    }
+    const uint64_t mask = __ballot(ne);
+    const int off = n + __popcll(mask & ((1ull << lane) - 1ull));
+    if (ne && off < kListCap) list[off] = 2 * t + full;
+    const int total = n + __popcll(mask);
+    kt = (sb + 1) * kSbTiles;
+    if (total > kListCap) {
+      // the first tile that did not fit is where the next round starts
+      const uint64_t first_out = __ballot(ne && off == kListCap);
+      kt = sb * kSbTiles + __builtin_ctzll(first_out);
+      n = kListCap;
+      break;
+    }
+    n = total;
+  }
+  resume = min(kt, nkc);
+  return n;
+}
+
+// One wave per query tile: how many key tiles the forward and dQ passes
+// visit for it (the lists build_tile_list gives them) and how many of those
+// are full; the counts order the query tiles and are what
+// tree_attn_plan_counts reports.
+__global__ __launch_bounds__(64) void q_count_kernel(const int2* __restrict__ kmm, const int* __restrict__ sbmax,
+                                                     int T, int Lq, int nk, int* __restrict__ counts,
+                                                     int* __restrict__ fulls) {
+  __shared__ int list[kListCap];
   const int qt = blockIdx.x;
   const int lane = threadIdx.x;
-  const int i0 = qt * BQ;
+  const int i0 = qt * kFwdBQ;
   if (i0 < Lq || i0 >= T) {  // rows before Lq (cached keys) and padding rows have no queries
     if (lane == 0) counts[qt] = fulls[qt] = 0;
     return;
   }
-  const int i1 = min(i0 + BQ, T);
-  const int nkc = min(nk, (i1 - 1) / BK + 1);
-  int* out = lists + (size_t)qt * nk;
-  int n = 0, nf = 0;
-  for (int base = 0; base < nkc; base += 64) {
-    const int kt = base + lane;
-    bool ne = false;
-    int full = 0;
-    if (kt < nkc) {
-      const int2 m = kmm[kt];
-      ne = m.y > i0;
-      full = (kt * BK + BK - 1 <= i0) && (m.x >= i1);
-    }
-    const uint64_t mask = __ballot(ne);
-    const int off = __popcll(mask & ((1ull << lane) - 1ull));
-    if (ne) out[n + off] = 2 * kt + full;
-    n += __popcll(mask);
-    nf += __popcll(__ballot(ne && full));
+  const int i1 = min(i0 + kFwdBQ, T);
+  const int nkc = min(nk, (i1 - 1) / kFwdBK + 1);
+  int resume = 0, n = 0, nf = 0;
+  while (resume < nkc) {
+    const int m = build_tile_list(kmm, sbmax, i0, i1, nkc, resume, list, lane);
+    for (int e = lane; e < m; e += 64) nf += list[e] & 1;
+    n += m;
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nf += __shfl_xor(nf, o);
   if (lane == 0) {
     counts[qt] = n;
     fulls[qt] = nf;
@@ -563,9 +620,9 @@ __device__ __forceinline__ void fwd_tile(const bf16* kb, const bf16* vb, const i
 template <int DP, typename Tio>
 __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
-    const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ counts,
-    const int* __restrict__ lists, const int* __restrict__ order, int T, int Lq, int Tp, int Hq, int Hkv, int nq,
-    int nk, float sl2, Tio* __restrict__ o, float* __restrict__ lse) {
+    const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ sbmax,
+    const int* __restrict__ order, int T, int Lq, int Tp, int Hq, int Hkv, int nq, int nk, float sl2,
+    Tio* __restrict__ o, float* __restrict__ lse) {
   // Row indices are those of the combined sequence: Lq cached / padding rows
   // (keys only, no queries) and then the packed tokens; T = Lq + own tokens.
   constexpr int D = DP == 32 ? 16 : DP;  // head dim (16 is padded to 32 for the MFMA shapes)
@@ -581,6 +638,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
   __shared__ __attribute__((aligned(1024))) bf16 vb1[TILE];
   __shared__ __attribute__((aligned(256))) int sb0[64];
   __shared__ __attribute__((aligned(256))) int sb1[64];
+  __shared__ int lst[kListCap + 2];  // this round's key tiles, their count, the next round's start
 
   const int G = Hq / Hkv;
   // kv-head-major: consecutive workgroups (one XCD's share) work on one kv
@@ -591,7 +649,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
   const int hk = lid / (G * nq);
   const int qt = order[(lid / G) % nq];
   const int h = hk * G + gq;
-  if (qt * kFwdRows < Lq) return;  // a tile of cached rows: no queries (Lq is a multiple of the tile)
+  if (qt * kFwdRows < Lq || qt * kFwdRows >= T) return;  // cached rows or padding: no queries
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -627,12 +685,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
     for (int b = 0; b < NDB; ++b) acc[nb][b] = f32x16{};
   }
 
-  const int cnt = counts[qt];
-  const int* lst = lists + (size_t)qt * nk;
   const bf16* kg = kr + (size_t)hk * Tp * DP;
   const bf16* vg = vr + (size_t)hk * Tp * DP;
 
-  if (cnt > 0) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[0] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
   // this wave's own rows [r0, r1): a key tile can be empty or full for them
   // even when it is partial for the whole query tile
   const int r0 = qt * kFwdRows + 32 * kNB * w;
@@ -645,21 +700,40 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
     const bool full = (e & 1) || ((j0 + kFwdBK - 1 <= r0) && (m.x >= r1));
     fwd_tile<DP>(kb, vb, sb, full, j0, qrow, lg, ad, sl2, qop, acc, st);
   };
-  for (int it = 0; it < cnt; it += 2) {
-    {
-      const int e = lst[it];
-      wait_dma();
-      __syncthreads();
-      if (it + 1 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1, w, lane);
-      wave_tile(e, kb0, vb0, sb0);
+  // the query tile's non-empty key tiles, kListCap per round
+  const int i0 = qt * kFwdRows, i1 = min(i0 + kFwdRows, T);
+  const int nkc = min(nk, (i1 - 1) / kFwdBK + 1);
+  int resume = 0;
+  for (;;) {
+    if (w == 0) {
+      const int n = build_tile_list(kmm, sbmax, i0, i1, nkc, resume, lst, lane);
+      if (lane == 0) {
+        lst[kListCap] = n;
+        lst[kListCap + 1] = resume;
+      }
     }
-    if (it + 1 < cnt) {
-      const int e = lst[it + 1];
-      wait_dma();
-      __syncthreads();
-      if (it + 2 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
-      wave_tile(e, kb1, vb1, sb1);
+    __syncthreads();
+    const int cnt = lst[kListCap];
+    resume = lst[kListCap + 1];
+    if (cnt > 0) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[0] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
+    for (int it = 0; it < cnt; it += 2) {
+      {
+        const int e = lst[it];
+        wait_dma();
+        __syncthreads();
+        if (it + 1 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1, w, lane);
+        wave_tile(e, kb0, vb0, sb0);
+      }
+      if (it + 1 < cnt) {
+        const int e = lst[it + 1];
+        wait_dma();
+        __syncthreads();
+        if (it + 2 < cnt) fwd_issue<DP>(kd, vd, kg, vg, sep, (lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0, w, lane);
+        wave_tile(e, kb1, vb1, sb1);
+      }
     }
+    if (resume >= nkc) break;
+    __syncthreads();  // every wave is done with this round's list and tiles
   }
 
 #pragma unroll
@@ -747,7 +821,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const Tio* __restrict__ o, const Tio* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dd, float* __restrict__ l2, bf16* __restrict__ dor, const int* __restrict__ sep,
-    const int* __restrict__ counts, const int* __restrict__ lists, const int* __restrict__ order,
+    const int2* __restrict__ kmm, const int* __restrict__ sbmax, const int* __restrict__ order,
     const float2* __restrict__ cs, int T, int Lq, int Tp, int Hq, int Hkv, int nq, int nk, float sl2, float scale,
     Tio* __restrict__ dq) {
   // Row indices are those of the combined sequence (Lq cached / padding
@@ -763,6 +837,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 vb1[TILE];
   __shared__ __attribute__((aligned(256))) int sb0[64];
   __shared__ __attribute__((aligned(256))) int sb1[64];
+  __shared__ int lst[kListCap + 2];  // this round's key tiles, their count, the next round's start
 
   const int G = Hq / Hkv;
   // kv-head-major: consecutive workgroups (one XCD's share) work on one kv
@@ -814,8 +889,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
 
-  const int cnt = counts[qt];
-  const int* lst = lists + (size_t)qt * nk;
   const bf16* kg = kr + (size_t)hk * Tp * DP;
   const bf16* vg = vr + (size_t)hk * Tp * DP;
   auto issue = [&](int j, bf16* kb, bf16* vb, int* sb) {
@@ -824,22 +897,41 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     if (w == 0) dma4(sep + j + lane, sb);
   };
 
-  if (cnt > 0) issue((lst[0] >> 1) * kFwdBK, kb0, vb0, sb0);
-  for (int it = 0; it < cnt; it += 2) {
-    {
-      const int e = lst[it];
-      wait_dma();
-      __syncthreads();
-      if (it + 1 < cnt) issue((lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1);
-      dq_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
+  // the query tile's non-empty key tiles, kListCap per round (no rows past T:
+  // an empty list)
+  const int i0 = qt * kFwdBQ, i1 = min(i0 + kFwdBQ, T);
+  const int nkc = i0 < T ? min(nk, (i1 - 1) / kFwdBK + 1) : 0;
+  int resume = 0;
+  for (;;) {
+    if (w == 0) {
+      const int n = build_tile_list(kmm, sbmax, i0, i1, nkc, resume, lst, lane);
+      if (lane == 0) {
+        lst[kListCap] = n;
+        lst[kListCap + 1] = resume;
+      }
     }
-    if (it + 1 < cnt) {
-      const int e = lst[it + 1];
-      wait_dma();
-      __syncthreads();
-      if (it + 2 < cnt) issue((lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0);
-      dq_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
+    __syncthreads();
+    const int cnt = lst[kListCap];
+    resume = lst[kListCap + 1];
+    if (cnt > 0) issue((lst[0] >> 1) * kFwdBK, kb0, vb0, sb0);
+    for (int it = 0; it < cnt; it += 2) {
+      {
+        const int e = lst[it];
+        wait_dma();
+        __syncthreads();
+        if (it + 1 < cnt) issue((lst[it + 1] >> 1) * kFwdBK, kb1, vb1, sb1);
+        dq_tile<DP>(kb0, vb0, sb0, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
+      }
+      if (it + 1 < cnt) {
+        const int e = lst[it + 1];
+        wait_dma();
+        __syncthreads();
+        if (it + 2 < cnt) issue((lst[it + 2] >> 1) * kFwdBK, kb0, vb0, sb0);
+        dq_tile<DP>(kb1, vb1, sb1, e & 1, (e >> 1) * kFwdBK, qrow, lg, ad, sl2, lse2, dval, qop, dop, acc);
+      }
     }
+    if (resume >= nkc) break;
+    __syncthreads();  // every wave is done with this round's list and tiles
   }
 
   // Epilogue through LDS. The lane holds dQ'^T column qrow, rows
@@ -1208,8 +1300,9 @@ __global__ __launch_bounds__(256) void gw_relay_kernel(const float* __restrict__
 // tokens; Tc = Lq + T rows in all, padded to Tp.
 struct AttnLayout {
   int T, Lp, Lq, Tc, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
-  size_t off_status, off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_qcount, off_qfull, off_qorder,
-      off_qlist;
+  int nsb;
+  size_t off_status, off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_sbmax, off_qcount, off_qfull,
+      off_qorder;
   size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
 };
 
@@ -1230,6 +1323,7 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   L.nq = L.Tp / kFwdBQ;
   L.nk64 = (L.Tc + kFwdBK - 1) / kFwdBK;
   L.nk128 = (L.Tc + kBwdBK - 1) / kBwdBK;
+  L.nsb = (L.nk64 + kSbTiles - 1) / kSbTiles;
   size_t o = 0;
   auto take = [&o](size_t bytes) {
     const size_t at = o;
@@ -1244,10 +1338,10 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   L.off_cs = take((size_t)L.Tp * (D / 2) * 8);
   L.off_kmm64 = take((size_t)L.nk64 * 8);
   L.off_kmm128 = take((size_t)L.nk128 * 8);
+  L.off_sbmax = take((size_t)L.nsb * 4);
   L.off_qcount = take((size_t)L.nq * 4);
   L.off_qfull = take((size_t)L.nq * 4);
   L.off_qorder = take((size_t)L.nq * 4);
-  L.off_qlist = take((size_t)L.nq * L.nk64 * 4);
   L.off_kwork = take((size_t)L.nk128 * 4);
   L.off_korder = take((size_t)L.nk128 * 4);
   if (with_bwd) {
@@ -1312,9 +1406,11 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
   hipLaunchKernelGGL(tile_minmax_kernel, dim3((L.nk128 + 3) / 4), dim3(256), 0, st, at<const int>(ws, L.off_sep),
                      L.Tc, L.Lq, L.nk64, L.nk128, at<int2>(ws, L.off_kmm64), at<int2>(ws, L.off_kmm128),
                      at<int>(ws, L.off_kwork));
-  hipLaunchKernelGGL(q_plan_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64), L.Tc, L.Lq,
-                     kFwdBQ, kFwdBK, L.nk64, at<int>(ws, L.off_qcount), at<int>(ws, L.off_qfull),
-                     at<int>(ws, L.off_qlist));
+  hipLaunchKernelGGL(sb_max_kernel, dim3((L.nsb + 3) / 4), dim3(256), 0, st, at<const int2>(ws, L.off_kmm64), L.nk64,
+                     L.nsb, at<int>(ws, L.off_sbmax));
+  hipLaunchKernelGGL(q_count_kernel, dim3(L.nq), dim3(64), 0, st, at<const int2>(ws, L.off_kmm64),
+                     at<const int>(ws, L.off_sbmax), L.Tc, L.Lq, L.nk64, at<int>(ws, L.off_qcount),
+                     at<int>(ws, L.off_qfull));
   hipLaunchKernelGGL(order_kernel, dim3(2), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
                      at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, at<int>(ws, L.off_korder));
   return check_launch("prep");
@@ -1325,9 +1421,9 @@ int run_fwd(const AttnLayout& L, float sl2, void* o, float* lse, char* ws, hipSt
   ProfScope ps("attn_fwd", st);
   hipLaunchKernelGGL((attn_fwd_kernel<DP, Tio>), dim3(L.nq * L.Hq), dim3(64 * kFwdWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
-                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_qcount),
-                     at<const int>(ws, L.off_qlist), at<const int>(ws, L.off_qorder), L.Tc, L.Lq, L.Tp, L.Hq, L.Hkv,
-                     L.nq, L.nk64, sl2, static_cast<Tio*>(o), lse);
+                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_sbmax),
+                     at<const int>(ws, L.off_qorder), L.Tc, L.Lq, L.Tp, L.Hq, L.Hkv, L.nq, L.nk64, sl2,
+                     static_cast<Tio*>(o), lse);
   return check_launch("tree_attn_fwd");
 }
 
@@ -1340,7 +1436,7 @@ int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* do
                        at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
                        static_cast<const Tio*>(o), static_cast<const Tio*>(dout), lse, at<float>(ws, L.off_dd),
                        at<float>(ws, L.off_l2), at<bf16>(ws, L.off_dor), at<const int>(ws, L.off_sep),
-                       at<const int>(ws, L.off_qcount), at<const int>(ws, L.off_qlist),
+                       at<const int2>(ws, L.off_kmm64), at<const int>(ws, L.off_sbmax),
                        at<const int>(ws, L.off_qorder), at<const float2>(ws, L.off_cs), L.Tc, L.Lq, L.Tp, L.Hq,
                        L.Hkv, L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
   }
