@@ -319,6 +319,28 @@ int tree_logprob(const void* logits, ta_dtype dt, int64_t R, int64_t V,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * tree_logprob_noalloc  (DEVICE)
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): exactly
+ * tree_logprob, with the same arguments and results, minus the workspace.
+ * Its entry table lives in a fixed 16 MiB device array inside the library,
+ * one per device for the life of the process, so a call needs
+ * tree_logprob_workspace_bytes(R, M) <= 16 MiB (about R + M <= 1.3 million);
+ * larger calls return TA_ECAPACITY without touching the device. The array's
+ * address is resolved on the first call on each device (the device of
+ * `stream`); later calls make no runtime call besides their launches and
+ * allocate nothing. Every call on a device shares that device's array:
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be ordered by the caller. Each call clears what it needs zeroed.
+ * Errors: those of tree_logprob, TA_ECAPACITY, TA_EHIP.
+ * ---------------------------------------------------------------------- */
+int tree_logprob_noalloc(const void* logits, ta_dtype dt, int64_t R, int64_t V,
+                         const int32_t* src_row, const int32_t* target, const float* weight, int64_t M,
+                         float* logp, float* row_lse, float* loss,
+                         void* dlogits, float grad_scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * tree_logprob_ppo  (DEVICE)
  *
  * Per-occurrence clipped policy loss on shared logit rows. The "Trie

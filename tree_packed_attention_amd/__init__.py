@@ -64,6 +64,7 @@ EXPORTS = (
     "tree_attn_plan_counts",
     "tree_attn_gw_export",
     "tree_attn_gw_relay",
+    "tree_logprob_noalloc",
 )
 
 
@@ -120,6 +121,8 @@ _lib.tree_logprob_workspace_bytes.restype = _sz
 _lib.tree_logprob_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tree_logprob.restype = ctypes.c_int
 _lib.tree_logprob.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _f32, _p, _sz, _p]
+_lib.tree_logprob_noalloc.restype = ctypes.c_int
+_lib.tree_logprob_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _f32, _p]
 _lib.tree_logprob_ppo.restype = ctypes.c_int
 _lib.tree_logprob_ppo.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _f32, _p, _p, _p,
                                   _p, _f32, _p, _sz, _p]

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "ta_device.h"
 #include "profile.h"
@@ -490,4 +491,68 @@ extern "C" int tree_logprob_ppo(const void* logits, ta_dtype dt, int64_t R, int6
   EntryRule er{weight, advantage, old_logp, mask, 1.0f - eps_low, 1.0f + eps_high, nullptr};
   return logprob_impl("tree_logprob_ppo", logits, dt, R, V, src_row, target, er, M, logp, row_lse, loss, dlogits,
                       grad_scale, workspace, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------
+// tree_logprob without a workspace argument, for callers that cannot
+// allocate. Its entry table (the workspace of tree_logprob) lives in this
+// fixed array, one per device for the life of the process.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of the scratch array on the device `stream` belongs to
+// (the current device for the null stream), resolved once per device with
+// that device current. Host code never passes `scratch` itself: its name is
+// a host-side stand-in, not a device address.
+int scratch_on(hipStream_t stream, const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TA_EHIP, "%s: no device for the stream: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TA_EUNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return fail(TA_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(TA_EHIP, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(TA_EHIP, "%s: hipGetSymbolAddress of the scratch array: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TA_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_logprob_noalloc(const void* logits, ta_dtype dt, int64_t R, int64_t V, const int32_t* src_row,
+                                    const int32_t* target, const float* weight, int64_t M, float* logp,
+                                    float* row_lse, float* loss, void* dlogits, float grad_scale, void* stream) {
+  clear_error();
+  const char* fn = "tree_logprob_noalloc";
+  if (R >= 1 && M >= 0) {
+    const size_t need = lp_layout(R, M).total;
+    if (need > kNoAllocScratchBytes)
+      return fail(TA_ECAPACITY, "%s: R=%lld rows and M=%lld entries need %zu bytes of scratch, more than the %zu "
+                  "bytes this entry point has (use tree_logprob with a workspace)",
+                  fn, (long long)R, (long long)M, need, kNoAllocScratchBytes);
+  }
+  // sizes out of range: logprob_impl rejects them before it looks at the
+  // (then absent) scratch
+  void* ws = nullptr;
+  if (R >= 1 && R < INT32_MAX && V >= 1 && V < INT32_MAX && M >= 0 && M < INT32_MAX - 1) {
+    if (int rc = scratch_on(static_cast<hipStream_t>(stream), fn, &ws)) return rc;
+  }
+  EntryRule er{weight, nullptr, nullptr, nullptr, 0.0f, 0.0f, nullptr};
+  return logprob_impl(fn, logits, dt, R, V, src_row, target, er, M, logp, row_lse, loss, dlogits, grad_scale, ws,
+                      kNoAllocScratchBytes, stream);
 }
