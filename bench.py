@@ -14,7 +14,12 @@ every row referenced 3 times (its own timed leg, HBM GB/s), per-kernel HIP
 event timings, the roofline of the dominant kernel and the CPU oracle timed
 on a bounded sample.
 
+Legs on the same line: the other attention workloads (short-prompt groups,
+the random agentic trees of 32768 and 131072 tokens), each with forward,
+backward and the whole step timed apart as medians of 20 HIP-event timings.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload multistep]
+    python bench.py --cpu-report    (host-only oracle measurements, no GPU)
 """
 from __future__ import annotations
 
@@ -23,6 +28,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -43,24 +50,52 @@ DESCR = {
 KERNEL_FLOPS = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 
 
-def cpu_baseline(seqs, groups, cfg, n_trees=3, n_groups=2):
-    """The float64 oracle (per-branch fwd + bwd) on the first n_trees trees x
-    the first n_groups kv groups of the workload (a bounded sample)."""
+def host_info():
+    """The host the CPU baseline runs on: cores, CPU model, BLAS, RAM."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal"):
+                    info["ram_gb"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    try:
+        info["nproc"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return info
+
+
+def _oracle_attn(seqs, groups, cfg, n_trees, n_groups, seed=77):
+    """The float64 per-branch oracle, fwd then bwd, on trees 0 .. n_trees-1
+    x kv groups 0 .. n_groups-1 of the workload. Returns (fwd s, bwd s,
+    visible-pair FLOPs (14 d P Hq), tokens)."""
     import workloads
     from oracle import attention as OA
     from oracle import pack as OP
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     po = OP.pack(seqs, groups)
     n_trees = min(n_trees, len(po["tree_start"]) - 1)
     G = cfg["Hq"] // cfg["Hkv"]
     f = lambda t: t.float().numpy()
-    dt, flops, toks = 0.0, 0.0, 0
+    tf = tb = flops = 0.0
+    toks = 0
     for tr in range(n_trees):
         ts, te = int(po["tree_start"][tr]), int(po["tree_start"][tr + 1])
         par = po["par"][ts:te].copy()
@@ -68,15 +103,183 @@ def cpu_baseline(seqs, groups, cfg, n_trees=3, n_groups=2):
         P = int((po["pos"][ts:te] + 1).sum())
         toks += te - ts
         for g in range(n_groups):
-            q, k, v, do = workloads.dense_inputs(te - ts, G, 1, cfg["d"], "bf16", 77 + 100 * tr + g)
+            q, k, v, do = workloads.dense_inputs(te - ts, G, 1, cfg["d"], "bf16", seed + 100 * tr + g)
             t0 = time.perf_counter()
             OA.forward_branches(f(q), f(k), f(v), par, po["pos"][ts:te], check_agree=False)
+            t1 = time.perf_counter()
             OA.backward_branches(f(q), f(k), f(v), f(do), par, po["pos"][ts:te])
-            dt += time.perf_counter() - t0
+            t2 = time.perf_counter()
+            tf += t1 - t0
+            tb += t2 - t1
             flops += 14.0 * cfg["d"] * P * G
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"trees 0..{n_trees - 1} ({toks} tokens) x kv groups 0..{n_groups - 1} ({G} q heads each), "
-                      f"fwd+bwd, float64 NumPy, {dt:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP"}
+    return tf, tb, flops, toks, n_trees
+
+
+def cpu_baseline(seqs, groups, cfg, n_trees=3, n_groups=2):
+    """The float64 oracle as it stands, on the host cores: per-branch fwd +
+    bwd on the first n_trees trees x the first n_groups kv groups of the
+    workload (a bounded sample), plus the oracle packer on the whole batch
+    and the oracle log-prob on 256 rows of the 151936-token vocabulary."""
+    import workloads
+    from oracle import logprob as OL
+    from oracle import pack as OP
+
+    info = host_info()
+    t0 = time.perf_counter()
+    OP.pack(seqs, groups)
+    pack_s = time.perf_counter() - t0
+    tf, tb, flops, toks, nt = _oracle_attn(seqs, groups, cfg, n_trees, n_groups)
+    R, V = 256, 151936
+    src, tgt, w = workloads.repeated_rows_entries(R, V, 3, 5)
+    z = workloads.logits_input(R, V, "bf16", 5).double().numpy()
+    t0 = time.perf_counter()
+    OL.logprob(z, src, tgt, w.astype(np.float32) if hasattr(w, "astype") else w)
+    lp_s = time.perf_counter() - t0
+    G = cfg["Hq"] // cfg["Hkv"]
+    cores = info.get("blas_threads", info.get("nproc", 1))
+    return {"value": flops / (tf + tb) / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"trees 0..{nt - 1} ({toks} tokens) x kv groups 0..{n_groups - 1} ({G} q heads each), "
+                      f"fwd+bwd per branch, float64 NumPy, {tf + tb:.1f} s for {flops / 1e9:.1f} visible-pair GFLOP",
+            "host": info, "stage_s": {"pack_whole_batch": round(pack_s, 3), "attn_fwd_sample": round(tf, 3),
+                                      "attn_bwd_sample": round(tb, 3),
+                                      "logprob_256_rows_fused": round(lp_s, 3)},
+            "logprob_gbps": round(2.0 * R * V * 2 / lp_s / 1e9, 3)}
+
+
+def cpu_report():
+    """Longer host-only oracle measurements (no GPU work): every host core
+    and one thread on the short-prompt batch, per stage; the multistep
+    sample of the default line; the large random tree's attention on kv
+    groups 0 and 7 with the whole-tree ancestor-chain oracle, scaled to all
+    8 groups (labelled extrapolated)."""
+    import workloads
+    from oracle import attention as OA
+    from oracle import pack as OP
+
+    out = {"host": host_info()}
+    for name, nt, ng in (("short", 8, 8), ("multistep", 3, 2)):
+        seqs, groups = workloads.sequences(name)
+        cfg = workloads.WORKLOADS[name]
+        tf, tb, flops, toks, n = _oracle_attn(seqs, groups, cfg, nt, ng)
+        out[name] = {"trees": n, "kv_groups": ng, "tokens": toks, "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+                     "tflops": round(flops / (tf + tb) / 1e12, 5)}
+        print(f"[cpu] {name}: fwd {tf:.2f} s, bwd {tb:.2f} s", flush=True)
+    try:
+        from threadpoolctl import threadpool_limits
+
+        seqs, groups = workloads.sequences("short")
+        cfg = workloads.WORKLOADS["short"]
+        with threadpool_limits(limits=1):
+            tf, tb, flops, toks, n = _oracle_attn(seqs, groups, cfg, 8, 8)
+        out["short_one_thread"] = {"fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+                                   "tflops": round(flops / (tf + tb) / 1e12, 5)}
+        print(f"[cpu] short, one thread: fwd {tf:.2f} s, bwd {tb:.2f} s", flush=True)
+    except ImportError:  # pragma: no cover
+        pass
+    seqs, groups = workloads.sequences("agentic_l")
+    cfg = workloads.WORKLOADS["agentic_l"]
+    po = OP.pack(seqs, groups)
+    T, G = po["T"], cfg["Hq"] // cfg["Hkv"]
+    P = int((po["pos"].astype(np.int64) + 1).sum())
+    q, k, v, do = workloads.dense_inputs(T, cfg["Hq"], cfg["Hkv"], cfg["d"], "bf16", cfg["seed"])
+    tf = tb = 0.0
+    for hk in (0, cfg["Hkv"] - 1):
+        f = lambda t: t.float().numpy()
+        qq, kk, vv, dd = f(q[:, hk * G:(hk + 1) * G]), f(k[:, hk:hk + 1]), f(v[:, hk:hk + 1]), f(do[:, hk * G:(hk + 1) * G])
+        t0 = time.perf_counter()
+        OA.forward_chains(qq, kk, vv, po["par"])
+        t1 = time.perf_counter()
+        OA.backward_chains(qq, kk, vv, dd, po["par"])
+        t2 = time.perf_counter()
+        tf += t1 - t0
+        tb += t2 - t1
+        print(f"[cpu] agentic_l kv group {hk}: fwd {t1 - t0:.1f} s, bwd {t2 - t1:.1f} s", flush=True)
+    scale = cfg["Hkv"] / 2.0
+    out["agentic_l"] = {"kv_groups_run": [0, cfg["Hkv"] - 1], "oracle": "whole-tree ancestor chains",
+                        "fwd_s_extrapolated": round(tf * scale, 1), "bwd_s_extrapolated": round(tb * scale, 1),
+                        "tflops_extrapolated": round(14.0 * cfg["d"] * P * cfg["Hq"] / ((tf + tb) * scale) / 1e12, 5),
+                        "label": "extrapolated: 2 of 8 kv groups run, times scaled by 4"}
+    print(json.dumps(out), flush=True)
+
+
+def tile_report(p):
+    """Tile classification of a packed batch: at 128x64 (the kernels'
+    forward and dQ tiles) and 128x128, over the whole batch and within each
+    tree (cross-tree tiles, all empty, left out)."""
+    import tree_packed_attention_amd as ta
+
+    T, se = p["T"], p["subtree_end"]
+    out = {}
+    for BQ, BK in ((128, 64), (128, 128)):
+        full, partial, empty, causal = ta.tree_tile_stats(se, T, BQ, BK)
+        wf = wp = we = wc = 0
+        ts = p["tree_start"]
+        for t in range(len(ts) - 1):
+            a, b = int(ts[t]), int(ts[t + 1])
+            f_, p_, e_, c_ = ta.tree_tile_stats((se[a:b] - a).astype(np.int32), b - a, BQ, BK)
+            wf, wp, we, wc = wf + f_, wp + p_, we + e_, wc + c_
+        out[f"{BQ}x{BK}"] = {"full": full, "partial": partial, "empty": empty, "causal": causal,
+                             "skip": round(empty / causal, 4),
+                             "within_tree": {"full": wf, "partial": wp, "empty": we, "causal": wc,
+                                             "skip": round(we / max(wc, 1), 4)}}
+    return out
+
+
+def attn_leg(name, dev, reps=20, warmup=3):
+    """One workload: forward, backward and the whole step timed separately
+    with HIP events on the launch stream (median of `reps` after `warmup`),
+    visible-pair TFLOP/s with the backward counted both ways (10 d P Hq,
+    FlashAttention's convention with the recomputed scores, and the strict
+    8 d P Hq), tile classification, per-kernel times."""
+    import torch
+
+    import tree_packed_attention_amd as ta
+    import workloads
+
+    cfg = workloads.WORKLOADS[name]
+    seqs, groups = workloads.sequences(name)
+    p = ta.tree_pack(seqs, groups)
+    T, Hq, Hkv, d = p["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    P = int((p["pos"].astype(np.int64) + 1).sum())
+    q, k, v, do = workloads.dense_inputs(T, Hq, Hkv, d, "bf16", cfg["seed"], device=dev)
+    pos = torch.from_numpy(p["pos"]).to(dev)
+    se = torch.from_numpy(p["subtree_end"]).to(dev)
+    ws = ta.attn_workspace(T, Hq, Hkv, d, True, dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    fwd_ms, bwd_ms, step_ms = [], [], []
+    for i in range(warmup + reps):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        o, lse, _ = ta.tree_attn_fwd(q, k, v, pos, se, workspace=ws)
+        e1.record()
+        ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws, reuse_prep=True)
+        e2.record()
+        e2.synchronize()
+        if i >= warmup:
+            fwd_ms.append(e0.elapsed_time(e1))
+            bwd_ms.append(e1.elapsed_time(e2))
+            step_ms.append(e0.elapsed_time(e2))
+    ta.tree_attn_profile_enable(True)
+    for _ in range(3):
+        o, lse, _ = ta.tree_attn_fwd(q, k, v, pos, se, workspace=ws)
+        ta.tree_attn_bwd(q, k, v, o, lse, do, pos, se, workspace=ws, reuse_prep=True)
+    torch.cuda.synchronize()
+    kern = {n: round(tot / max(c, 1), 4) for n, (tot, c) in ta.tree_attn_profile_read().items()}
+    ta.tree_attn_profile_enable(False)
+    status = ta.tree_attn_workspace_status(ws)
+    del ws, q, k, v, do, o, lse
+    torch.cuda.empty_cache()
+    med = lambda x: float(np.median(x))
+    fm, bm, sm = med(fwd_ms), med(bwd_ms), med(step_ms)
+    u = d * P * Hq
+    return {"workload": DESCR[name], "T": T, "visible_pairs": P, "Hq": Hq, "Hkv": Hkv, "d": d,
+            "trees": p["n_trees"], "reps": reps, "warmup": warmup,
+            "fwd_ms_median": round(fm, 4), "bwd_ms_median": round(bm, 4), "step_ms_median": round(sm, 4),
+            "fwd_tflops": round(4 * u / fm / 1e9, 2), "bwd_tflops": round(10 * u / bm / 1e9, 2),
+            "bwd_tflops_strict_8dPH": round(8 * u / bm / 1e9, 2), "step_tflops": round(14 * u / sm / 1e9, 2),
+            "pct_bf16_peak": round(100.0 * 14 * u / sm / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "packed_tokens_per_s": round(T / (sm * 1e-3), 1), "tiles": tile_report(p), "kernel_ms": kern,
+            "status_word": status}
 
 
 def gateway_leg(seqs, groups, cfg, dev, steps):
@@ -301,9 +504,17 @@ def main():
     ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--no-gateway", action="store_true")
     ap.add_argument("--no-ssm", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the other attention workloads' legs")
+    ap.add_argument("--cpu-report", action="store_true",
+                    help="only the longer host-side oracle measurements (no GPU work), as one JSON line")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run a plain device copy of this many bytes (calibrates HBM counters)")
     args = ap.parse_args()
+    if args.cpu_report:
+        import numpy as np  # noqa: F401
+
+        cpu_report()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding is a design "
               "note, not a built path.", file=sys.stderr)
@@ -361,6 +572,20 @@ def main():
     print(f"[bench] attention step {ms_step:.3f} ms, {value:.1f} TFLOP/s", flush=True)
 
     kernel_ms = {n: tot / max(cnt, 1) for n, (tot, cnt) in kern.items()}
+    del ws
+    torch.cuda.empty_cache()
+    # the same workload again, forward and backward timed apart (medians)
+    head = attn_leg(args.workload, dev)
+    print(f"[bench] {args.workload}: fwd {head['fwd_ms_median']:.3f} ms, bwd {head['bwd_ms_median']:.3f} ms "
+          f"(medians)", flush=True)
+    legs = {}
+    if not args.no_legs:
+        for name in ("short", "multistep", "agentic", "agentic_l"):
+            if name == args.workload:
+                continue
+            legs[name] = attn_leg(name, dev)
+            print(f"[bench] leg {name}: step {legs[name]['step_ms_median']:.3f} ms, "
+                  f"{legs[name]['step_tflops']:.1f} TFLOP/s ({legs[name]['pct_bf16_peak']:.1f} %)", flush=True)
     dom = max((n for n in kernel_ms if n in KERNEL_FLOPS), key=lambda n: kernel_ms[n])
     achieved = KERNEL_FLOPS[dom] * d * P * Hq / (kernel_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -370,8 +595,6 @@ def main():
 
     lp = None
     if not args.no_logprob:
-        del ws
-        torch.cuda.empty_cache()
         R, V = 16384, 151936
         src, tgt, w = workloads.repeated_rows_entries(R, V, 3, 5)
         z = workloads.logits_input(R, V, "bf16", 5, device=dev)
@@ -459,6 +682,10 @@ def main():
         "tiles_128x64": {"full": full, "partial": partial, "empty": empty, "causal": causal,
                          "skip": round(empty / causal, 4)},
         "kernel_ms": {n: round(x, 4) for n, x in kernel_ms.items()},
+        "medians": {k_: head[k_] for k_ in ("fwd_ms_median", "bwd_ms_median", "step_ms_median", "fwd_tflops",
+                                            "bwd_tflops", "bwd_tflops_strict_8dPH", "step_tflops", "pct_bf16_peak",
+                                            "reps", "warmup")},
+        "tiles": head["tiles"], "legs": legs,
         "pack_ms_host": round(pack_ms, 2),
         "roofline": roofline, "tree_logprob": lp, "gateway": gw, "tree_ssm": ssm, "partition": part,
         "cpu_baseline": cpu,
