@@ -472,10 +472,10 @@ def partition_leg():
 ATTN_DEVICE_SOURCES = ("attention.hip", "ta_device.h", "ta_lds.h")
 
 
-def measured_traffic(kernel):
-    """Calibrated HBM bytes per dispatch of `kernel` from the committed
-    rocprofv3 counter summaries, if they were taken on the current sources of
-    the attention kernels (else None)."""
+def measured_traffic(kernel, workload):
+    """Calibrated HBM bytes per dispatch of `kernel` on `workload` from the
+    committed rocprofv3 counter summaries, if they were taken on the current
+    sources of the attention kernels (else None)."""
     import glob
     import hashlib
 
@@ -489,7 +489,8 @@ def measured_traffic(kernel):
             for line in fh:
                 if line.startswith("traffic-json: "):
                     rec = json.loads(line[len("traffic-json: "):])
-                    if rec.get("source_sha") == sha and kernel in rec.get("bytes_per_dispatch", {}):
+                    if (rec.get("source_sha") == sha and rec.get("workload", "multistep") == workload
+                            and kernel in rec.get("bytes_per_dispatch", {})):
                         return int(rec["bytes_per_dispatch"][kernel])
     return None
 
@@ -590,7 +591,7 @@ def main():
     achieved = KERNEL_FLOPS[dom] * d * P * Hq / (kernel_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom + "_kernel"), "traffic_unit": "bytes per launch (HBM, calibrated)",
+                "traffic": measured_traffic(dom + "_kernel", args.workload), "traffic_unit": "bytes per launch (HBM, calibrated)",
                 "flops_per_launch": KERNEL_FLOPS[dom] * d * P * Hq}
 
     lp = None
