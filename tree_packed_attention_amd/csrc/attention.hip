@@ -22,9 +22,12 @@
 //                                        128-row query tile, work order (the
 //                                        tile lists themselves are built per
 //                                        workgroup in LDS: O(T) plan storage)
-//   kwork, korder [nk128]                dK/dV work per 128-key tile, order
+//   kwork, korder [nk128]                query blocks per 128-key tile; scratch
+//   cdesc [nk128 + 32] int4              dK/dV chunks, heaviest first
+//   ktcut [32] int4                      the cut tiles: {tile, chunks, first slot}
 //   dd, l2 [Hq][Tp] f32                  -rowsum(dO * O) and -lse / scale
 //   dor [Hq][Tp][DP] bf16                dO, head-major (written by dQ pass)
+//   kpart [64][Hkv][8][DP/2][64] f32     dK/dV partial sums of cut tiles
 //
 // Products use v_mfma_f32_32x32x16_bf16 with float32 accumulation. The
 // forward and dQ kernels work on S^T (keys x queries): each lane then owns
@@ -428,12 +431,8 @@ __global__ __launch_bounds__(64) void q_count_kernel(const int2* __restrict__ km
 // Tile indices sorted by work, heaviest first (counting sort on the work
 // clipped to 1023). The order within one work value is arbitrary; it only
 // affects scheduling, never results.
-// Workgroup 0 sorts list (work0, n0), workgroup 1 list (work1, n1).
-__global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ work0, int n0, int* __restrict__ order0,
-                                                     const int* __restrict__ work1, int n1, int* __restrict__ order1) {
-  const int* __restrict__ work = blockIdx.x == 0 ? work0 : work1;
-  const int n = blockIdx.x == 0 ? n0 : n1;
-  int* __restrict__ order = blockIdx.x == 0 ? order0 : order1;
+// Run by one workgroup of 1024 threads.
+__device__ __forceinline__ void order_tiles(const int* __restrict__ work, int n, int* __restrict__ order) {
   __shared__ int hist[1024];
   __shared__ int scan[1024];
   const int t = threadIdx.x;
@@ -454,6 +453,126 @@ __global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ wor
   hist[1023 - t] = v - cnt;
   __syncthreads();
   for (int i = t; i < n; i += blockDim.x) order[atomicAdd(&hist[min(work[i], 1023)], 1)] = i;
+}
+
+// dK/dV work split. The work of a 128-key tile is W = G * (its query blocks)
+// iterations of one workgroup. In a tree the root's keys see every query
+// below them, so a few tiles can carry many times the average and, as single
+// workgroups, finish long after the rest. Let total be the sum of W over the
+// tiles of one kv head and C = max(ceil(total / kDkdvSlots), kMinChunk),
+// kDkdvSlots being the dK/dV workgroups one XCD holds at a time (32 CUs x 1):
+// a tile with W > C is cut into S = ceil(W / C) chunks of consecutive
+// iterations, every other tile is one chunk. Each chunk of a cut tile writes
+// its float32 dK / dV accumulators to a partial-sum slot of its own; a second
+// kernel adds the S slots of each cut tile in slot order (the same order on
+// every run) and writes the tile's gradients as an uncut tile does.
+// Bounds: sum over cut tiles of (S - 1) < total / C <= kDkdvSlots, so there
+// are fewer than nk128 + kDkdvSlots chunks; a cut tile has W >= C + 1, so
+// fewer than kDkdvSlots tiles are cut and they use fewer than
+// 2 * kDkdvSlots slots.
+constexpr int kDkdvSlots = 32;
+constexpr int kMinChunk = 64;  // a chunk's fixed cost (operand loads, epilogue) is a few iterations
+constexpr int kSplitSlots = 2 * kDkdvSlots;
+
+__device__ __forceinline__ int chunk_count(int W, int C) { return W > C ? (W + C - 1) / C : 1; }
+
+// Run by one workgroup of 1024 threads. Lists the chunks heaviest first (counting sort on the
+// chunk size relative to C, 1024 bins): cdesc[c] = {tile, index s within the
+// tile, S, first slot of the tile (-1 when S = 1)}, then {-1, 0, 0, 0} up to
+// ncmax; and the cut tiles, ktcut[i] = {tile, S, first slot, 0}, then
+// {-1, 0, 0, 0} up to kDkdvSlots. korder is scratch (nk ints).
+__device__ __forceinline__ void chunk_plan(const int* __restrict__ work, int nk, int G, int* __restrict__ korder,
+                                           int4* __restrict__ cdesc, int ncmax, int4* __restrict__ ktcut) {
+  __shared__ int hist[1024];
+  __shared__ int scan[1024];
+  __shared__ long long part[16];
+  __shared__ int4 sums[1024];
+  const int t = threadIdx.x;
+  long long s = 0;
+  for (int i = t; i < nk; i += blockDim.x) s += (long long)G * work[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if ((t & 63) == 0) part[t >> 6] = s;
+  hist[t] = 0;
+  __syncthreads();
+  long long total = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) total += part[i];
+  // W <= 256 * 2^16 (heads x query blocks), so C fits an int once clipped there
+  const int C = (int)min(max((total + kDkdvSlots - 1) / kDkdvSlots, (long long)kMinChunk), (long long)(1 << 25));
+  auto bin_of = [&](int i) {
+    const int W = G * work[i];
+    const int S = chunk_count(W, C);
+    return (int)((long long)((W + S - 1) / S) * 1023 / C);
+  };
+  for (int i = t; i < nk; i += blockDim.x) atomicAdd(&hist[bin_of(i)], 1);
+  __syncthreads();
+  const int cnt = hist[1023 - t];
+  int v = cnt;
+  for (int o = 1; o < 1024; o <<= 1) {
+    scan[t] = v;
+    __syncthreads();
+    if (t >= o) v += scan[t - o];
+    __syncthreads();
+  }
+  hist[1023 - t] = v - cnt;
+  __syncthreads();
+  for (int i = t; i < nk; i += blockDim.x) korder[atomicAdd(&hist[bin_of(i)], 1)] = i;
+  __syncthreads();
+  // chunks, slots and cut tiles before each position of the order: thread t
+  // owns the positions [p0, p1)
+  const int per = (nk + 1023) / 1024;
+  const int p0 = min(t * per, nk), p1 = min(p0 + per, nk);
+  int4 mine = make_int4(0, 0, 0, 0);
+  for (int p = p0; p < p1; ++p) {
+    const int S = chunk_count(G * work[korder[p]], C);
+    mine.x += S;
+    mine.y += S > 1 ? S : 0;
+    mine.z += S > 1 ? 1 : 0;
+  }
+  int4 acc = mine;
+  for (int o = 1; o < 1024; o <<= 1) {
+    sums[t] = acc;
+    __syncthreads();
+    if (t >= o) {
+      acc.x += sums[t - o].x;
+      acc.y += sums[t - o].y;
+      acc.z += sums[t - o].z;
+    }
+    __syncthreads();
+  }
+  int c = acc.x - mine.x, slot = acc.y - mine.y, ci = acc.z - mine.z;
+  for (int p = p0; p < p1; ++p) {
+    const int kt = korder[p];
+    const int S = chunk_count(G * work[kt], C);
+    // running out of slots or cut-tile entries is not reached (see the
+    // bounds above); the tile would then be one chunk and its other
+    // positions idle
+    const bool cut = S > 1 && slot + S <= kSplitSlots && ci < kDkdvSlots;
+    for (int q = 0; q < S && c < ncmax; ++q, ++c)
+      cdesc[c] = cut ? make_int4(kt, q, S, slot) : (q == 0 ? make_int4(kt, 0, 1, -1) : make_int4(-1, 0, 0, 0));
+    if (S > 1) {
+      if (ci < kDkdvSlots) ktcut[ci] = cut ? make_int4(kt, S, slot, 0) : make_int4(-1, 0, 0, 0);
+      slot += S;
+      ++ci;
+    }
+  }
+  if (t == 1023) sums[0] = acc;
+  __syncthreads();
+  for (int i = sums[0].x + t; i < ncmax; i += blockDim.x) cdesc[i] = make_int4(-1, 0, 0, 0);
+  for (int i = sums[0].z + t; i < kDkdvSlots; i += blockDim.x) ktcut[i] = make_int4(-1, 0, 0, 0);
+}
+
+// Workgroup 0 orders the query tiles for the forward and dQ passes,
+// workgroup 1 plans the dK/dV chunks.
+__global__ __launch_bounds__(1024) void order_kernel(const int* __restrict__ qcount, int nq, int* __restrict__ qorder,
+                                                     const int* __restrict__ kwork, int nk, int G,
+                                                     int* __restrict__ korder, int4* __restrict__ cdesc, int ncmax,
+                                                     int4* __restrict__ ktcut) {
+  if (blockIdx.x == 0)
+    order_tiles(qcount, nq, qorder);
+  else
+    chunk_plan(kwork, nk, G, korder, cdesc, ncmax, ktcut);
 }
 
 // Stores 8 floats as elements [0, 8) of a caller row (one 16- or 32-byte
@@ -967,6 +1086,70 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------------
+// dK / dV epilogue of one 128-key tile, dK (pass 0) then dV (pass 1): the
+// waves holding that gradient (m = 1 holds dK', m = 0 dV) stage their 32 x DP
+// block in LDS as [key][d] float32, one of the four tile buffers per key
+// slice, then all waves write 16 keys each: dK rotated back (R(pos)^T) and
+// scaled, cached rows to dk_past / dv_past in float32 (added when acc_past),
+// padding rows skipped. Called by all eight waves with the buffers free.
+template <int DP, typename Tio>
+__device__ __forceinline__ void dkdv_epilogue(const f32x16* acc, bf16* qb0, bf16* qb1, bf16* ob0, bf16* ob1, int j0,
+                                              int hk, int T, int Lq, int Lp, int Hkv, float scale,
+                                              const float2* __restrict__ cs, Tio* __restrict__ dk,
+                                              Tio* __restrict__ dv, float* __restrict__ dk_past,
+                                              float* __restrict__ dv_past, int acc_past) {
+  constexpr int D = DP == 32 ? 16 : DP;
+  constexpr int NDB = DP / 32;
+  constexpr int SE = DP;  // f32 row stride: 32 rows x DP floats = one tile buffer
+  static_assert(32 * SE * 4 <= 64 * DP * 2, "a key slice's epilogue block must fit in one tile buffer");
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = w & 3, m = w >> 2;
+  const int lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  constexpr int half = D / 2;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (m == 1 - pass) {
+      float* ep = reinterpret_cast<float*>(ks < 2 ? (ks == 0 ? qb0 : qb1) : (ks == 2 ? ob0 : ob1));
+      const float mul = pass == 0 ? scale : 1.0f;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * lg + (i & 3);
+          ep[r * SE + 32 * b + lc] = acc[b][i] * mul;
+        }
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = 16 * w + rr;  // key row within the workgroup's 128
+      const int j = j0 + r;
+      if (j >= T) break;
+      if (j >= Lp && j < Lq) continue;  // padding after the cached rows
+      const bf16* eb = (r >> 5) < 2 ? ((r >> 5) == 0 ? qb0 : qb1) : ((r >> 5) == 2 ? ob0 : ob1);
+      const float* er = reinterpret_cast<const float*>(eb) + (r & 31) * SE;
+      if (j < Lp) {
+        // cached rows: their keys came in rotated, so dK is left unrotated
+        float* out = (pass == 0 ? dk_past : dv_past) + ((size_t)j * Hkv + hk) * D;
+        for (int c = lane; c < D; c += 64) out[c] = acc_past ? out[c] + er[c] : er[c];
+      } else if (pass == 0) {
+        Tio* out = dk + ((size_t)(j - Lq) * Hkv + hk) * D;
+        const float2* csr = cs + (size_t)j * half;
+        for (int kk = lane; kk < half; kk += 64) {
+          float y1, y2;
+          rope_rot_t(er[kk], er[kk + half], csr[kk], y1, y2);
+          out[kk] = from_f32<Tio>(y1);
+          out[kk + half] = from_f32<Tio>(y2);
+        }
+      } else {
+        Tio* out = dv + ((size_t)(j - Lq) * Hkv + hk) * D;
+        for (int c = lane; c < D; c += 64) out[c] = from_f32<Tio>(er[c]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Backward dK / dV. One workgroup owns 128 keys of one kv head and loops over
 // the 64-row query blocks those keys can see, for every query head of the
 // group. The visible queries of a key tile form the contiguous range
@@ -1075,20 +1258,19 @@ template <int DP, typename Tio>
 __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vr,
     const bf16* __restrict__ dor, const float* __restrict__ l2, const float* __restrict__ dd,
-    const int* __restrict__ sep, const int2* __restrict__ kmm, const int* __restrict__ korder,
-    const float2* __restrict__ cs, int T, int Lq, int Lp, int Tp, int Hq, int Hkv, int nkb, float sl2, float scale,
-    Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dk_past, float* __restrict__ dv_past,
-    int acc_past) {
+    const int* __restrict__ sep, const int2* __restrict__ kmm, const int4* __restrict__ cdesc, int ncmax,
+    float* __restrict__ kpart, const float2* __restrict__ cs, int T, int Lq, int Lp, int Tp,
+    int Hq, int Hkv, float sl2, float scale, Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dk_past,
+    float* __restrict__ dv_past, int acc_past) {
   // Key rows are those of the combined sequence: Lp cached rows (gradients to
   // dk_past / dv_past in float32, added to their contents when acc_past),
   // padding up to Lq, then the packed tokens (dk, dv); T = Lq + own tokens.
-  // Queries exist from row Lq on.
-  constexpr int D = DP == 32 ? 16 : DP;
+  // Queries exist from row Lq on. A workgroup runs one chunk of the work
+  // split (chunk_plan) for one kv head.
   constexpr int BQ = kBwdBQ;
   constexpr int KS = DP / 16;
   constexpr int NDB = DP / 32;
   constexpr int TILE = 64 * DP;
-  constexpr int SE = DP;  // epilogue f32 row stride: 32 rows x DP floats = one tile buffer
   __shared__ __attribute__((aligned(1024))) bf16 qb0[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 qb1[TILE];
   __shared__ __attribute__((aligned(1024))) bf16 ob0[TILE];
@@ -1101,9 +1283,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) bf16x8 xb[4 * 4 * 64];
 
   const int G = Hq / Hkv;
-  const int lid = xcd_remap(blockIdx.x, nkb * Hkv);
-  const int kt = korder[lid % nkb];
-  const int hk = lid / nkb;
+  const int lid = xcd_remap(blockIdx.x, ncmax * Hkv);
+  const int4 cd = cdesc[lid % ncmax];  // {tile, chunk, chunks of the tile, first partial-sum slot}
+  const int hk = lid / ncmax;
+  if (cd.x < 0) return;  // an unused chunk position (uniform over the workgroup)
+  const int kt = cd.x;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1135,11 +1319,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   const int2 mm = kmm[kt];
   const int qb_lo = max(j0, Lq) / BQ;
   const int nqb = max((mm.y + BQ - 1) / BQ - qb_lo, 0);
-  const int n_it = G * nqb;
+  // this chunk's iterations [it0, n_it) of the tile's G * nqb
+  const int it0 = (int)((long long)G * nqb * cd.y / cd.z);
+  const int n_it = (int)((long long)G * nqb * (cd.y + 1) / cd.z);
 
   // iteration it covers query head hk * G + it / nqb, block qb_lo + it % nqb;
   // (hh, qq) track that pair for the block being loaded next
-  int hh = 0, qq = 0;
+  int hh = nqb > 0 ? it0 / nqb : 0, qq = nqb > 0 ? it0 % nqb : 0;
   auto issue = [&](bf16* qs_, bf16* ds_, float* lsb, float* dlb) {
     const int h = hk * G + hh;
     const int i0 = (qb_lo + qq) * BQ;
@@ -1163,9 +1349,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
   // Two query blocks in LDS (the one computed, the one loaded), as separate
   // arrays and an unrolled pair of iterations so the compiler can tell them
   // apart.
-  if (n_it > 0) issue(qb0, ob0, lb0, db0);
-  int cq = 0;  // block index (within the head) of the block being computed
-  for (int it = 0; it < n_it; it += 2) {
+  int cq = qq;  // block index (within the head) of the block being computed
+  if (it0 < n_it) issue(qb0, ob0, lb0, db0);
+  for (int it = it0; it < n_it; it += 2) {
     {
       wait_dma();
       __syncthreads();
@@ -1182,53 +1368,53 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
     }
   }
 
-  // Epilogue, dK (pass 0) then dV (pass 1): the waves holding that gradient
-  // stage their 32 x DP block in LDS as [key][d] f32 (one tile buffer per key
-  // slice; the tile buffers are free now), then all waves write 16 keys each.
-  static_assert(32 * SE * 4 <= TILE * 2, "a key slice's epilogue block must fit in one tile buffer");
-  __syncthreads();
-  constexpr int half = D / 2;
+  if (cd.z > 1) {
+    // a chunk of a cut tile: its accumulators go to its partial-sum slot,
+    // laid out [slot][kv head][wave][register][lane]; dkdv_reduce_kernel
+    // adds the tile's slots and writes the gradients
+    float* mine = kpart + (((size_t)(cd.w + cd.y) * Hkv + hk) * kDkdvWaves + w) * (NDB * 16 * 64) + lane;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if (m == 1 - pass) {
-      float* ep = reinterpret_cast<float*>(ks < 2 ? (ks == 0 ? qb0 : qb1) : (ks == 2 ? ob0 : ob1));
-      const float mul = pass == 0 ? scale : 1.0f;
+    for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * lg + (i & 3);
-          ep[r * SE + 32 * b + lc] = acc[b][i] * mul;
-        }
-    }
-    __syncthreads();
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = 16 * w + rr;  // key row within the workgroup's 128
-      const int j = j0 + r;
-      if (j >= T) break;
-      if (j >= Lp && j < Lq) continue;  // padding after the cached rows
-      const bf16* eb = (r >> 5) < 2 ? ((r >> 5) == 0 ? qb0 : qb1) : ((r >> 5) == 2 ? ob0 : ob1);
-      const float* er = reinterpret_cast<const float*>(eb) + (r & 31) * SE;
-      if (j < Lp) {
-        // cached rows: their keys came in rotated, so dK is left unrotated
-        float* out = (pass == 0 ? dk_past : dv_past) + ((size_t)j * Hkv + hk) * D;
-        for (int c = lane; c < D; c += 64) out[c] = acc_past ? out[c] + er[c] : er[c];
-      } else if (pass == 0) {
-        Tio* out = dk + ((size_t)(j - Lq) * Hkv + hk) * D;
-        const float2* csr = cs + (size_t)j * half;
-        for (int kk = lane; kk < half; kk += 64) {
-          float y1, y2;
-          rope_rot_t(er[kk], er[kk + half], csr[kk], y1, y2);
-          out[kk] = from_f32<Tio>(y1);
-          out[kk + half] = from_f32<Tio>(y2);
-        }
-      } else {
-        Tio* out = dv + ((size_t)(j - Lq) * Hkv + hk) * D;
-        for (int c = lane; c < D; c += 64) out[c] = from_f32<Tio>(er[c]);
-      }
-    }
-    __syncthreads();
+      for (int i = 0; i < 16; ++i) mine[(16 * b + i) * 64] = acc[b][i];
+    return;
   }
+  __syncthreads();  // every wave is done with the tile buffers
+  dkdv_epilogue<DP, Tio>(acc, qb0, qb1, ob0, ob1, j0, hk, T, Lq, Lp, Hkv, scale, cs, dk, dv, dk_past, dv_past,
+                         acc_past);
+}
+
+// The cut tiles of the dK/dV work split: workgroup (i, kv head) adds the S
+// partial sums of cut tile i in slot order, each wave the slot blocks of its
+// own (key slice, role), and writes the tile's gradients.
+template <int DP, typename Tio>
+__global__ __launch_bounds__(64 * kDkdvWaves) void dkdv_reduce_kernel(
+    const int4* __restrict__ ktcut, const float* __restrict__ kpart, const float2* __restrict__ cs, int T, int Lq,
+    int Lp, int Hkv, float scale, Tio* __restrict__ dk, Tio* __restrict__ dv, float* __restrict__ dk_past,
+    float* __restrict__ dv_past, int acc_past) {
+  constexpr int NDB = DP / 32;
+  constexpr int TILE = 64 * DP;
+  __shared__ __attribute__((aligned(1024))) bf16 sb0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sb1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sb2[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sb3[TILE];
+  const int4 ct = ktcut[blockIdx.x % kDkdvSlots];  // {tile, chunks, first slot}
+  const int hk = blockIdx.x / kDkdvSlots;
+  if (ct.x < 0) return;  // uniform over the workgroup
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
+  for (int c = 0; c < ct.y; ++c) {
+    const float* src = kpart + (((size_t)(ct.z + c) * Hkv + hk) * kDkdvWaves + w) * (NDB * 16 * 64) + lane;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] += src[(16 * b + i) * 64];
+  }
+  dkdv_epilogue<DP, Tio>(acc, sb0, sb1, sb2, sb3, ct.x * kBwdBK, hk, T, Lq, Lp, Hkv, scale, cs, dk, dv, dk_past,
+                         dv_past, acc_past);
 }
 
 // ------------------------------------------------------------------------
@@ -1300,10 +1486,10 @@ __global__ __launch_bounds__(256) void gw_relay_kernel(const float* __restrict__
 // tokens; Tc = Lq + T rows in all, padded to Tp.
 struct AttnLayout {
   int T, Lp, Lq, Tc, Tp, Hq, Hkv, D, DP, nq, nk64, nk128;
-  int nsb;
+  int nsb, ncmax;
   size_t off_status, off_qr, off_kr, off_vr, off_sep, off_cs, off_kmm64, off_kmm128, off_sbmax, off_qcount, off_qfull,
       off_qorder;
-  size_t off_kwork, off_korder, off_dd, off_l2, off_dor, total;
+  size_t off_kwork, off_korder, off_cdesc, off_ktcut, off_dd, off_l2, off_dor, off_kpart, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1324,6 +1510,7 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   L.nk64 = (L.Tc + kFwdBK - 1) / kFwdBK;
   L.nk128 = (L.Tc + kBwdBK - 1) / kBwdBK;
   L.nsb = (L.nk64 + kSbTiles - 1) / kSbTiles;
+  L.ncmax = L.nk128 + kDkdvSlots;
   size_t o = 0;
   auto take = [&o](size_t bytes) {
     const size_t at = o;
@@ -1344,10 +1531,13 @@ AttnLayout make_layout(int T, int Lp, int Hq, int Hkv, int D, bool with_bwd) {
   L.off_qorder = take((size_t)L.nq * 4);
   L.off_kwork = take((size_t)L.nk128 * 4);
   L.off_korder = take((size_t)L.nk128 * 4);
+  L.off_cdesc = take((size_t)L.ncmax * 16);
+  L.off_ktcut = take((size_t)kDkdvSlots * 16);
   if (with_bwd) {
     L.off_dd = take((size_t)Hq * L.Tp * 4);
     L.off_l2 = take((size_t)Hq * L.Tp * 4);
     L.off_dor = take((size_t)Hq * L.Tp * L.DP * 2);
+    L.off_kpart = take((size_t)kSplitSlots * Hkv * kDkdvWaves * (L.DP / 2) * 64 * 4);
   }
   L.total = o;
   return L;
@@ -1412,7 +1602,8 @@ int run_prep(const AttnLayout& L, const void* q, const void* k, const void* v, c
                      at<const int>(ws, L.off_sbmax), L.Tc, L.Lq, L.nk64, at<int>(ws, L.off_qcount),
                      at<int>(ws, L.off_qfull));
   hipLaunchKernelGGL(order_kernel, dim3(2), dim3(1024), 0, st, at<const int>(ws, L.off_qcount), L.nq,
-                     at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, at<int>(ws, L.off_korder));
+                     at<int>(ws, L.off_qorder), at<const int>(ws, L.off_kwork), L.nk128, L.Hq / L.Hkv,
+                     at<int>(ws, L.off_korder), at<int4>(ws, L.off_cdesc), L.ncmax, at<int4>(ws, L.off_ktcut));
   return check_launch("prep");
 }
 
@@ -1441,12 +1632,17 @@ int run_bwd(const AttnLayout& L, const void* o, const float* lse, const void* do
                        L.Hkv, L.nq, L.nk64, sl2, scale, static_cast<Tio*>(dq));
   }
   ProfScope ps("attn_bwd_dkdv", st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.nk128 * L.Hkv), dim3(64 * kDkdvWaves), 0, st,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DP, Tio>), dim3(L.ncmax * L.Hkv), dim3(64 * kDkdvWaves), 0, st,
                      at<const bf16>(ws, L.off_qr), at<const bf16>(ws, L.off_kr), at<const bf16>(ws, L.off_vr),
                      at<const bf16>(ws, L.off_dor), at<const float>(ws, L.off_l2), at<const float>(ws, L.off_dd),
-                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm128), at<const int>(ws, L.off_korder),
-                     at<const float2>(ws, L.off_cs), L.Tc, L.Lq, L.Lp, L.Tp, L.Hq, L.Hkv, L.nk128, sl2, scale,
-                     static_cast<Tio*>(dk), static_cast<Tio*>(dv), past.dk, past.dv, past.accumulate);
+                     at<const int>(ws, L.off_sep), at<const int2>(ws, L.off_kmm128), at<const int4>(ws, L.off_cdesc),
+                     L.ncmax, at<float>(ws, L.off_kpart), at<const float2>(ws, L.off_cs), L.Tc, L.Lq, L.Lp, L.Tp,
+                     L.Hq, L.Hkv, sl2, scale, static_cast<Tio*>(dk), static_cast<Tio*>(dv), past.dk, past.dv,
+                     past.accumulate);
+  hipLaunchKernelGGL((dkdv_reduce_kernel<DP, Tio>), dim3(kDkdvSlots * L.Hkv), dim3(64 * kDkdvWaves), 0, st,
+                     at<const int4>(ws, L.off_ktcut), at<const float>(ws, L.off_kpart), at<const float2>(ws, L.off_cs),
+                     L.Tc, L.Lq, L.Lp, L.Hkv, scale, static_cast<Tio*>(dk), static_cast<Tio*>(dv), past.dk, past.dv,
+                     past.accumulate);
   return check_launch("tree_attn_bwd");
 }
 

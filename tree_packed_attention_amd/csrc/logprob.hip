@@ -523,9 +523,11 @@ int scratch_on(hipStream_t stream, const char* fn, void** out) {
       return fail(TA_EHIP, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(e));
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (cur != dev) hipSetDevice(cur);
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
     if (e != hipSuccess || p == nullptr)
       return fail(TA_EHIP, "%s: hipGetSymbolAddress of the scratch array: %s", fn, hipGetErrorString(e));
+    if (back != hipSuccess)
+      return fail(TA_EHIP, "%s: hipSetDevice(%d): %s", fn, cur, hipGetErrorString(back));
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];

@@ -1144,12 +1144,6 @@ __device__ __forceinline__ bf16x8 col8(const bf16* X, int ld, int c, int k0) {
   for (int s = 0; s < 8; ++s) v[s] = X[(k0 + s) * ld + c];
   return v;
 }
-__device__ __forceinline__ bf16x8 col8f(const float* X, int ld, int c, int k0) {
-  bf16x8 v;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) v[s] = (bf16)X[(k0 + s) * ld + c];
-  return v;
-}
 
 // A [R][C] row-major tile (global row stride gs, rows past rows_valid read
 // as zero) bound for LDS rows of stride ls: issue() starts all of this
