@@ -27,7 +27,7 @@
 //   ktcut [32] int4                      the cut tiles: {tile, chunks, first slot}
 //   dd, l2 [Hq][Tp] f32                  -rowsum(dO * O) and -lse / scale
 //   dor [Hq][Tp][DP] bf16                dO, head-major (written by dQ pass)
-//   kpart [64][Hkv][8][DP/2][64] f32     dK/dV partial sums of cut tiles
+//   kpart [64][Hkv][8][DP/8][64][4] f32  dK/dV partial sums of cut tiles
 //
 // Products use v_mfma_f32_32x32x16_bf16 with float32 accumulation. The
 // forward and dQ kernels work on S^T (keys x queries): each lane then owns
@@ -1370,13 +1370,14 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
 
   if (cd.z > 1) {
     // a chunk of a cut tile: its accumulators go to its partial-sum slot,
-    // laid out [slot][kv head][wave][register][lane]; dkdv_reduce_kernel
+    // laid out [slot][kv head][wave][register / 4][lane][4]; dkdv_reduce_kernel
     // adds the tile's slots and writes the gradients
-    float* mine = kpart + (((size_t)(cd.w + cd.y) * Hkv + hk) * kDkdvWaves + w) * (NDB * 16 * 64) + lane;
+    f32x4* mine = reinterpret_cast<f32x4*>(kpart) + (((size_t)(cd.w + cd.y) * Hkv + hk) * kDkdvWaves + w) * (NDB * 4 * 64) + lane;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mine[(16 * b + i) * 64] = acc[b][i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        mine[(4 * b + i4) * 64] = f32x4{acc[b][4 * i4], acc[b][4 * i4 + 1], acc[b][4 * i4 + 2], acc[b][4 * i4 + 3]};
     return;
   }
   __syncthreads();  // every wave is done with the tile buffers
@@ -1407,11 +1408,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void dkdv_reduce_kernel(
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
   for (int c = 0; c < ct.y; ++c) {
-    const float* src = kpart + (((size_t)(ct.z + c) * Hkv + hk) * kDkdvWaves + w) * (NDB * 16 * 64) + lane;
+    const f32x4* src =
+        reinterpret_cast<const f32x4*>(kpart) + (((size_t)(ct.z + c) * Hkv + hk) * kDkdvWaves + w) * (NDB * 4 * 64) + lane;
+    // all of the slot's loads first, then the adds
+    f32x4 t[NDB * 4];
+#pragma unroll
+    for (int q = 0; q < NDB * 4; ++q) t[q] = src[q * 64];
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][i] += src[(16 * b + i) * 64];
+      for (int i = 0; i < 16; ++i) acc[b][i] += t[4 * b + (i >> 2)][i & 3];
   }
   dkdv_epilogue<DP, Tio>(acc, sb0, sb1, sb2, sb3, ct.x * kBwdBK, hk, T, Lq, Lp, Hkv, scale, cs, dk, dv, dk_past,
                          dv_past, acc_past);
