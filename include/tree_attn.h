@@ -145,7 +145,10 @@ int tree_pack(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
  * workspace: device memory of at least tree_attn_workspace_bytes(...) bytes,
  * 256-byte aligned; contents are scratch between calls except under
  * TA_REUSE_PREP and the status word at its start (see
- * tree_attn_workspace_status).
+ * tree_attn_workspace_status). The size is O(T (Hq + Hkv) d) plus, with
+ * with_bwd, a fixed 64 x Hkv x max(d, 32) KiB of float32 partial sums
+ * for key tiles whose dK/dV work is split over several workgroups (64 MB at
+ * Hkv = 8, d = 128).
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_EHIP (launch failure).
  * ---------------------------------------------------------------------- */
 size_t tree_attn_workspace_bytes(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t with_bwd);
