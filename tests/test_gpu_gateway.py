@@ -147,6 +147,23 @@ def test_long_prompt_gateway_full_size_heads():
     _check(_gpu(s["parts"][0], s), _oracle(s["parts"][0], s), "long_prompt")
 
 
+def test_gateway_with_cut_key_tiles():
+    """A 1024-token prompt cached over a 2000-token chain (4 q / 1 kv head,
+    d = 128): each key tile of the cached rows carries 32 query blocks per
+    head (128 iterations), over the per-CU share of the dK/dV work (C = 66),
+    so dK_past / dV_past of those rows, and dK / dV of the chain's first
+    keys, come from the summed partials of cut tiles."""
+    prompt = list(range(1024))
+    seqs = [prompt + [20000 + j for j in range(2000)], prompt + [30000 + j for j in range(64)]]
+    par = np.asarray(OP.pack(seqs, None)["par"])
+    child = 1024
+    assert par[child] == 1023
+    print("\n[case] cut_gateway", flush=True)
+    s = _setup(seqs, None, 4, 1, 128, "bf16", 43, child)
+    assert s["sp"]["past_len"] == 1024 and len(s["parts"][0]["par"]) == 2000
+    _check(_gpu(s["parts"][0], s), _oracle(s["parts"][0], s), "cut_gateway")
+
+
 def test_two_children_accumulate_into_the_gateway():
     """Eq. 18: the second child's cached-row gradients add to the first's."""
     seqs, groups = workloads.random_forest(35, [600])
