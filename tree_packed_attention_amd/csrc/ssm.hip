@@ -739,23 +739,42 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
   const int hk = hv / (Hv / H);
   const int t0 = cstart[c], L = clen[c];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lg = lane >> 5, lc = lane & 31;
+  // every HBM read of the chunk is issued here, before any is used: k rows
+  // (thread: rows tid / (DK/8) + 256 i / (DK/8), 16 bytes each) and the v
+  // half of the right-hand side (rows r = tid % 64, columns 8 (wv + 4 i))
+  constexpr int NKL = kCh * (DK / 8) / 256;
+  constexpr int NVL = kCh * (DV / 8) / 256;
+  static_assert(kCh * (DK / 8) % 256 == 0 && kCh * (DV / 8) % 256 == 0, "whole rounds of the workgroup");
+  bf16x8 kl[NKL], vl[NVL];
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) {
+    const int idx = tid + 256 * i, r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+    kl[i] = r < L ? load8(k + ((size_t)(t0 + r) * H + hk) * DK + cc) : zero8();
+  }
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int idx = tid + 256 * i, r = idx % kCh, cg = 8 * (idx / kCh);
+    vl[i] = r < L ? load8(v + ((size_t)(t0 + r) * Hv + hv) * DV + cg) : zero8();
+  }
   if (wv == 0) {
     float gv = lane < L ? g[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
+    const float bv = lane < L ? beta[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(gv, o);
       if (lane >= o) gv += y;
     }
     gcs[lane] = gv;
-    bs[lane] = lane < L ? beta[(size_t)(t0 + lane) * Hv + hv] : 0.0f;
+    bs[lane] = bv;
     gcw[((size_t)hv * nc + c) * kCh + lane] = gv;
     const float glast = __shfl(gv, 63);  // g is zero past L, so lane 63 holds gc of the last row
     dec[lane] = lane < L ? expf(glast - gv) : 0.0f;
     egs[lane] = lane < L ? expf(gv) : 0.0f;
   }
-  for (int idx = tid; idx < kCh * (DK / 8); idx += 256) {
-    const int r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&ks[r][cc]) = r < L ? load8(k + ((size_t)(t0 + r) * H + hk) * DK + cc) : zero8();
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) {
+    const int idx = tid + 256 * i, r = idx / (DK / 8), cc = (idx % (DK / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&ks[r][cc]) = kl[i];
   }
   __syncthreads();
   // M (rows m > n only are read): waves 0-2 form the lower 32x32 blocks of k k^T
@@ -789,17 +808,17 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const Tin* __restrict__ k
   // right-hand side, transposed: rt[col][row] = beta v (col < DV), beta k e^gc.
   // Lanes take consecutive rows, 8 columns each (16-byte loads along a row),
   // so each transposed LDS store covers 64 contiguous bytes.
-  for (int idx = tid; idx < kCh * (NCOL / 8); idx += 256) {
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int idx = tid + 256 * i, r = idx % kCh, cg = 8 * (idx / kCh);
+    const float sc = bs[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rt[cg + e][r] = (bf16)((float)vl[i][e] * sc);
+  }
+  for (int idx = tid + kCh * (DV / 8); idx < kCh * (NCOL / 8); idx += 256) {
     const int r = idx % kCh, cg = 8 * (idx / kCh);
-    bf16x8 x8;
-    float sc;
-    if (cg < DV) {
-      x8 = r < L ? load8(v + ((size_t)(t0 + r) * Hv + hv) * DV + cg) : zero8();
-      sc = bs[r];
-    } else {
-      x8 = *reinterpret_cast<const bf16x8*>(&ks[r][cg - DV]);
-      sc = bs[r] * egs[r];
-    }
+    const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(&ks[r][cg - DV]);
+    const float sc = bs[r] * egs[r];
 #pragma unroll
     for (int e = 0; e < 8; ++e) rt[cg + e][r] = (bf16)((float)x8[e] * sc);
   }
@@ -1037,43 +1056,54 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(const Tio* __restrict__ q,
     for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
       for (int s = 0; s < 8; ++s) qs[a][s] = (bf16)((float)qop[a][s] * eg);
+    // all of this wave's h0 operands are requested before the first product
+    const bf16* hp = h0w + ((size_t)c * Hv + hv) * DV * DK;
+    bf16x8 hA[NDW][DK / 16];
 #pragma unroll
-    for (int bb = 0; bb < NDW; ++bb) {
-      const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
-      const bf16* hp = h0w + ((size_t)c * Hv + hv) * DV * DK;
+    for (int bb = 0; bb < NDW; ++bb)
 #pragma unroll
-      for (int a = 0; a < DK / 16; ++a) {
-        const bf16x8 A = load8(hp + cr_off<DK>(d, 16 * a + 8 * lg));
-        acc[bb] = mfma32x32x16(A, qs[a], acc[bb]);
-      }
-    }
+      for (int a = 0; a < DK / 16; ++a)
+        hA[bb][a] = load8(hp + cr_off<DK>(32 * (NDW * (wv >> 1) + bb) + lc, 16 * a + 8 * lg));
+#pragma unroll
+    for (int bb = 0; bb < NDW; ++bb)
+#pragma unroll
+      for (int a = 0; a < DK / 16; ++a) acc[bb] = mfma32x32x16(hA[bb][a], qs[a], acc[bb]);
   }
   // intra-chunk term; key blocks above the query block are fully masked
   for (int kb = 0; kb <= qb; ++kb) {
     const int j = 32 * kb + lc;
     const bool kok = j < L;
     const Tio* krow = k + ((size_t)(t0 + (kok ? j : 0)) * H + hk) * DK;
+    // the block's k rows, vn^T pieces and decays are requested together
+    bf16x8 kA[DK / 16];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a) kA[a] = kok ? load8(krow + 16 * a + 8 * lg) : zero8();
+    const bf16* vp = vnt + hc * DV * kCh;
+    bf16x4 vA[2][NDW][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int bb = 0; bb < NDW; ++bb) {
+        const int d = 32 * (NDW * (wv >> 1) + bb) + lc, a2 = 2 * kb + h2;
+        vA[h2][bb][0] = *reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 4 * lg));
+        vA[h2][bb][1] = *reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 8 + 4 * lg));
+      }
+    float gj[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gj[r] = gcc[32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3)];
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int a = 0; a < DK / 16; ++a) s = mfma32x32x16(kok ? load8(krow + 16 * a + 8 * lg) : zero8(), qop[a], s);
+    for (int a = 0; a < DK / 16; ++a) s = mfma32x32x16(kA[a], qop[a], s);
     bf16x8 pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jj = 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3);
-      pb[r >> 3][r & 7] = (bf16)((jj <= i && qok) ? s[r] * expf(gi - gcc[jj]) : 0.0f);
+      pb[r >> 3][r & 7] = (bf16)((jj <= i && qok) ? s[r] * expf(gi - gj[r]) : 0.0f);
     }
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int a2 = 2 * kb + h2;
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int bb = 0; bb < NDW; ++bb) {
-        const int d = 32 * (NDW * (wv >> 1) + bb) + lc;
-        const bf16* vp = vnt + hc * DV * kCh;
-        const bf16x8 A = cat(*reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 4 * lg)),
-                             *reinterpret_cast<const bf16x4*>(vp + cr_off<kCh>(d, 16 * a2 + 8 + 4 * lg)));
-        acc[bb] = mfma32x32x16(A, pb[h2], acc[bb]);
-      }
-    }
+      for (int bb = 0; bb < NDW; ++bb) acc[bb] = mfma32x32x16(cat(vA[h2][bb][0], vA[h2][bb][1]), pb[h2], acc[bb]);
   }
   if (qok) {
     Tio* orow = o + ((size_t)(t0 + i) * Hv + hv) * DV;
