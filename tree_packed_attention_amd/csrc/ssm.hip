@@ -1805,10 +1805,15 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     if (own_v) {
       const int e = 32 * cb + lc;
       const bf16* dvb = dvnt + hc * DV * kCh;
+      // the block's right-hand sides are requested before the first product
+      bf16x8 B[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a >= 2 * rb) B[a] = load8(dvb + cr_off<kCh>(e, 16 * a + 8 * lg));
       f32x16 acc = f32x16{};
-      for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
-                           load8(dvb + cr_off<kCh>(e, 16 * a + 8 * lg)), acc);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a >= 2 * rb) acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), B[a], acc);
       float pv[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -1832,10 +1837,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
     if (own_k) {
       const int d = 32 * cb + lc;
       const bf16* dwb = dwt + hc * DK * kCh;
+      bf16x8 B[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a >= 2 * rb) B[a] = load8(dwb + cr_off<kCh>(d, 16 * a + 8 * lg));
       f32x16 acc = f32x16{};
-      for (int a = 2 * rb; a < 4; ++a)
-        acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg),
-                           load8(dwb + cr_off<kCh>(d, 16 * a + 8 * lg)), acc);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a >= 2 * rb) acc = mfma32x32x16(row8(&sm.tt[0][0], kCh + 8, 32 * rb + lc, 16 * a + 8 * lg), B[a], acc);
       float pk[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -1913,8 +1922,12 @@ __global__ __launch_bounds__(512) void gdn_bwd_wy_kernel(
       const int idx = tid + 512 * it, j = idx / (DV / 8), e0 = 8 * (idx % (DV / 8));
       if (j < L) {
         Tio* o = dv + ((size_t)(t0 + j) * Hv + hv) * DV + e0;
-#pragma unroll
-        for (int q8 = 0; q8 < 8; ++q8) o[q8] = sm.dvs[j][e0 + q8];
+        if constexpr (sizeof(Tio) == 2) {
+          *reinterpret_cast<bf16x8*>(o) = *reinterpret_cast<const bf16x8*>(&sm.dvs[j][e0]);
+        } else {
+          reinterpret_cast<f32x4*>(o)[0] = reinterpret_cast<const f32x4*>(&sm.dvs[j][e0])[0];
+          reinterpret_cast<f32x4*>(o)[1] = reinterpret_cast<const f32x4*>(&sm.dvs[j][e0])[1];
+        }
       }
     }
     // dk += (G + G^T) k
