@@ -980,14 +980,17 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_state_kernel(
   } else {
     // the start state of p's first child chunk p + 1 is p's end state
     const bf16* hp = h0w + ((size_t)(p + 1) * Hv + hv) * DV * DK;
+    bf16x4 x[NB][4];  // every piece requested before any is converted
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(hp + cr_off<DK>(n, 32 * b + 8 * j + 4 * lg));
+      for (int j = 0; j < 4; ++j) x[b][j] = *reinterpret_cast<const bf16x4*>(hp + cr_off<DK>(n, 32 * b + 8 * j + 4 * lg));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[b][4 * j + e] = (float)x[e];
-      }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[b][4 * j + e] = (float)x[b][j][e];
   }
   const StateBuf<DK, DV> sb0{w0, k0, u0}, sb1{w1, k1, u1};
   auto gl_of = [&](int c) { return gcw[((size_t)hv * nc + c) * kCh + kCh - 1]; };
@@ -1449,14 +1452,18 @@ __global__ __launch_bounds__(64 * (DV / 32)) void gdn_bwd_state_kernel(
   auto add_children = [&](int c) {
     for (int x = child_off[c]; x < child_off[c + 1]; ++x) {
       const float* hp = dhead + (((size_t)child_chains[x] * Hv + hv) * DV + n) * DK;
+      // the child's whole gradient is requested before it is added
+      f32x4 v[NB][4];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(hp + 32 * b + 8 * j4 + 4 * lg);
+        for (int j4 = 0; j4 < 4; ++j4) v[b][j4] = *reinterpret_cast<const f32x4*>(hp + 32 * b + 8 * j4 + 4 * lg);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dh[b][4 * j4 + e] += v[e];
-        }
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dh[b][4 * j4 + e] += v[b][j4][e];
     }
   };
   const BStateBuf<DK> sb0{g0, q0, x0}, sb1{g1, q1, x1};
