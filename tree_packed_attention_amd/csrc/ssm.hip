@@ -1230,6 +1230,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
     lq.issue(q + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
     lk.issue(k + ((size_t)t0 * H + hk) * DK, (size_t)H * DK, tid, L);
     lw.issue(wp + hc * kCh * DK, DK, tid, kCh);
+    // dO rows (lanes over rows, 8 columns each), requested with the tiles
+    constexpr int NDL = kCh * (DV / 8) / 256;
+    bf16x8 dl[NDL];
+#pragma unroll
+    for (int it = 0; it < NDL; ++it) {
+      const int idx = tid + 256 * it, i = idx % kCh, e0 = 8 * (idx / kCh);
+      dl[it] = i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
+    }
     if (tid < kCh) {
       const float gv = gcw[hc * kCh + tid], gl = gcw[hc * kCh + kCh - 1];
       gcs[tid] = gv;
@@ -1239,15 +1247,13 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(const Tio* __restrict
     lq.commit(&qs[0][0], DK + 8, tid);
     lk.commit(&ks[0][0], DK + 8, tid);
     lw.commit(&ws_[0][0], DK + 8, tid);
-  }
-  // dO^T into LDS (lanes over rows, so each transposed LDS store covers 64
-  // contiguous bytes)
+    // dO^T into LDS (each transposed LDS store covers 64 contiguous bytes)
 #pragma unroll
-  for (int it = 0; it < kCh * (DV / 8) / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx % kCh, e0 = 8 * (idx / kCh);
-    const bf16x8 d8 = i < L ? load8(dout + ((size_t)(t0 + i) * Hv + hv) * DV + e0) : zero8();
+    for (int it = 0; it < NDL; ++it) {
+      const int idx = tid + 256 * it, i = idx % kCh, e0 = 8 * (idx / kCh);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dT[e0 + s][i] = d8[s];
+      for (int s = 0; s < 8; ++s) dT[e0 + s][i] = dl[it][s];
+    }
   }
   __syncthreads();
   // transposed outputs, 16 bytes per lane, eight lanes per 128-byte row:
