@@ -983,17 +983,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   bf16x8 qop[KS], dop[KS];
   float dval = 0.0f;
   {
+    // every load of the row is issued before any is used
     const bf16* qb = qr + ((size_t)h * Tp + qrow) * DP + 8 * lg;
     bf16* dob = dor + ((size_t)h * Tp + qrow) * DP + 8 * lg;
     const size_t roff = ((size_t)(qok ? own : 0) * Hq + h) * D;
+    bf16x8 ov[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qop[s] = load8(qb + 16 * s);
       dop[s] = load_row8(dout + roff, qok, 16 * s + 8 * lg, D);
-      *reinterpret_cast<bf16x8*>(dob + 16 * s) = dop[s];
-      const bf16x8 ov = load_row8(o + roff, qok, 16 * s + 8 * lg, D);
+      ov[s] = load_row8(o + roff, qok, 16 * s + 8 * lg, D);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dval += (float)dop[s][e] * (float)ov[e];
+    for (int s = 0; s < KS; ++s) {
+      *reinterpret_cast<bf16x8*>(dob + 16 * s) = dop[s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dval += (float)dop[s][e] * (float)ov[s][e];
     }
   }
   dval += __shfl_xor(dval, 32);
