@@ -139,6 +139,61 @@ def test_invalid_entries_and_forward_only():
     assert dz2 is None and np.max(np.abs(host(logp2) - lp[valid])) == 0
 
 
+# Row sizes on both sides of the 256 entries the row kernel keeps in LDS:
+# rows up to 256 entries take the LDS entry tables, larger rows (1500 is also
+# more than one entry per thread) the general path; targets repeat in a row.
+WIDE_COUNTS = [0, 1, 255, 256, 257, 1500, 3, 0]
+
+
+def _wide_rows(seed):
+    rng = np.random.default_rng(seed)
+    src = np.concatenate([np.full(c, r) for r, c in enumerate(WIDE_COUNTS)])
+    tgt = rng.integers(0, 300, src.size)
+    perm = rng.permutation(src.size)
+    return src[perm], tgt[perm], rng
+
+
+@pytest.mark.parametrize("V,dtype", [(4096, "bf16"), (2052, "f32")])
+def test_wide_rows_both_paths(V, dtype):
+    R = len(WIDE_COUNTS)
+    src, tgt, rng = _wide_rows(V)
+    w = rng.random(src.size).astype(np.float32)
+    z = workloads.logits_input(R, V, dtype, 7) * 3
+    logp, lse, loss, dz = _run(z, src, tgt, w, gs=0.75)
+    r_logp, r_lse, r_loss, r_dz = OL.logprob(z.double().numpy(), src, tgt, w, grad_scale=0.75)
+    assert np.max(np.abs(host(logp) - r_logp)) <= (1e-3 if dtype == "f32" else 2e-2)
+    assert np.max(np.abs(host(lse) - r_lse)) <= 2e-2
+    assert abs(float(loss) - r_loss) <= 1e-4 * max(1.0, abs(r_loss))
+    d = host(dz)
+    for r in range(R):  # every row, both paths, element by element, relative to the row's scale
+        # (W_r p reaches tens here: float32 rounding of lse and of the sums)
+        tol = (2e-5 if dtype == "f32" else 2e-2) * max(1.0, np.max(np.abs(r_dz[r])))
+        assert np.max(np.abs(d[r] - r_dz[r])) <= tol, r
+    assert np.all(d[[0, R - 1]] == 0)
+    again = _run(z, src, tgt, w, gs=0.75)
+    for x, y in zip((logp, lse, loss, dz), again):
+        assert torch.equal(x, y)
+
+
+def test_wide_rows_policy_loss():
+    V, R = 4096, len(WIDE_COUNTS)
+    src, tgt, rng = _wide_rows(5)
+    M = src.size
+    w = (rng.random(M) + 0.1).astype(np.float32)
+    adv, ratio, mask = workloads.policy_inputs(M, 11)
+    z = workloads.logits_input(R, V, "f32", 8) * 3
+    zd = z.double().numpy()
+    old = _old_logp(zd, src, tgt, ratio)
+    logp, lse, loss, dz = _run_ppo(z, src, tgt, w, adv, old, mask, gs=1.25)
+    r_logp, r_lse, r_loss, r_dz, coef = OL.clipped_policy_loss(zd, src, tgt, w, adv, old, mask, EPS, EPS, 1.25)
+    assert np.any(coef == 0) and np.any(coef != 0)
+    assert np.max(np.abs(host(logp) - r_logp)) <= 1e-3
+    assert abs(float(loss) - r_loss) <= 1e-4 * max(1.0, abs(r_loss))
+    d = host(dz)
+    for r in range(R):
+        assert np.max(np.abs(d[r] - r_dz[r])) <= 1e-4 * max(1.0, np.max(np.abs(r_dz[r]))), r
+
+
 def test_bitwise_deterministic():
     R, V, M = 300, 4096, 3000
     rng = np.random.default_rng(1)

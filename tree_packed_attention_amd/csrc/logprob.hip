@@ -226,7 +226,61 @@ __device__ void row_corrections(const T* __restrict__ row, int beg, int n, const
   }
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Cache policy of the streamed row reads and gradient writes (nontemporal).
+constexpr int kNt = 2;
+// Raw buffer resource over [p, p + bytes): accesses past the end read zeros
+// and drop stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// Between passes over the row: the compiler would otherwise keep each pass's
+// float conversions of the packed row for the next pass, twice the registers
+// of the row, and spill them.
+template <typename V, int N>
+__device__ __forceinline__ void keep_packed(V (&x)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+v"(x[k]));
+}
+
+// Workgroup barrier that orders LDS only: global loads still in flight stay
+// in flight (__syncthreads waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// block_reduce with LDS-only barriers (same order, same result).
+template <typename Tv, typename Op>
+__device__ Tv block_reduce_lds(Tv v, Op op, Tv* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o));
+  const int wv = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  lds_barrier();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  lds_barrier();
+  Tv r = red[0];
+  for (int i = 1; i < nw; ++i) r = op(r, red[i]);
+  return r;
+}
+
+// Entries of one row that the register kernel keeps in LDS; a row with more
+// takes the general path (ids rank-sorted through global memory).
+constexpr int kEntCap = 256;
+
 // Row kernel with the row held in registers: NV 16-byte vectors per thread.
+// Vector vi of the row (EPV logits) sits in thread vi % kRowThreads, slot
+// vi / kRowThreads.
+//
+// Rows with at most kEntCap entries: the entry ids are requested before the
+// row and rank-sorted in LDS while it is in flight; each entry's target,
+// weight and logit are requested once the row is in and arrive during the
+// reductions. The corrected gradient of a target column is stored by the
+// thread that stored the column's vector, after it, so the row needs no
+// second pass and the workgroup never waits for its own stores. Sums run in
+// the same order as on the general path (sorted entry order), so both give
+// the same bits.
 template <typename T, int NV>
 __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
@@ -234,54 +288,186 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
   typedef typename Vec16<T>::type vec;
   constexpr int EPV = Vec16<T>::N;
+  constexpr int MAPW = (NV * kRowThreads + 31) / 32;
   __shared__ float red[16];
+  __shared__ unsigned int vmap[MAPW];  // bit vi: vector vi holds a target
+  __shared__ int e_id[kEntCap];        // entry ids in CSR order
+  __shared__ int e_t[kEntCap];         // the rest in sorted entry order: target column
+  __shared__ float e_z[kEntCap];       // logit at the target
+  __shared__ float e_c[kEntCap];       // coefficient c_m
+  __shared__ float e_tot[kEntCap];     // sum of c over the entries aiming at the same target
+  __shared__ unsigned char e_first[kEntCap];  // first entry (in sorted order) aiming at its target
   const int64_t r = blockIdx.x;
   const int beg = ptr[r], n = ptr[r + 1] - beg;
   if (n == 0 && !need_all_rows) return;
   const T* row = logits + r * V;
   const int64_t nvec = V / EPV;
+  const int tid = threadIdx.x;
   vec x[NV];
+  if (n > kEntCap) {
+    // general path
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      if (vi < nvec) {
+        x[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(row) + vi);  // read once: streamed
+#pragma unroll
+        for (int s = 0; s < EPV; ++s) mx = fmaxf(mx, to_f32(x[k][s]));
+      }
+    }
+    mx = block_reduce(mx, MaxOp(), red);
+    float se = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      if (vi < nvec) {
+#pragma unroll
+        for (int s = 0; s < EPV; ++s) se += __builtin_amdgcn_exp2f((to_f32(x[k][s]) - mx) * kLog2e);
+      }
+    }
+    se = block_reduce(se, SumOp(), red);
+    const float lse = mx + logf(se);
+    if (row_lse != nullptr && tid == 0) row_lse[r] = lse;
+    float W = 0.0f;
+    row_entries(row, beg, n, ids, sorted, tgt, er, lse, logp, red, &W);
+    if (dlogits == nullptr) return;
+    T* drow = dlogits + r * V;
+    const float sw = gs * W;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      if (vi < nvec) {
+        vec g;
+#pragma unroll
+        for (int s = 0; s < EPV; ++s)
+          g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
+        __builtin_nontemporal_store(g, reinterpret_cast<vec*>(drow) + vi);  // written once: streamed
+      }
+    }
+    __syncthreads();
+    row_corrections(row, beg, n, sorted, tgt, er.coefs(), lse, W, gs, drow);
+    return;
+  }
+
+  // the entry's id first, so that its load returns ahead of the row's
+  // Buffer loads: a lane past the end reads zeros without a memory access,
+  // so every thread issues the same loads, none behind a branch, and the
+  // compiler's waits count exactly the loads issued before the awaited one.
+  // The range check covers the per-lane offset, which therefore carries the
+  // whole offset (the uniform operand stays 0).
+  const bool ent = tid < n;
+  const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(ids + beg, 4 * n), 4 * tid, 0, 0);
+  for (int i = tid; i < MAPW; i += kRowThreads) vmap[i] = 0u;
+  // this thread's vectors are tid + kRowThreads k for k < nk (nvec < 2^31)
+  const int nk = (int)((nvec - tid + kRowThreads - 1) / kRowThreads);
+  const __amdgpu_buffer_rsrc_t rrow = buf_rsrc(row, (int)(16 * nvec));
+  int off = 16 * tid;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)  // read once: streamed
+    x[k] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(rrow, off + 16 * kRowThreads * k, 0, kNt));
+  if (ent) e_id[tid] = id;
+  lds_barrier();
+  // rank among the row's ids (all distinct) = sorted position; the entry's
+  // target, weight and policy inputs are requested behind the row
+  int rank = 0, t = 0, mk = 1;
+  float wv = 0.0f, av = 0.0f, ov = 0.0f;
+  if (ent) {
+    for (int f = 0; f < n; ++f) rank += e_id[f] < id;
+    t = tgt[id];
+    wv = er.w[id];
+    if (er.adv) {
+      av = er.adv[id];
+      ov = er.old[id];
+    }
+  }
   float mx = -__builtin_inff();
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
-    if (vi < nvec) {
-      x[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(row) + vi);  // read once: streamed
+    if (k < nk) {
 #pragma unroll
       for (int s = 0; s < EPV; ++s) mx = fmaxf(mx, to_f32(x[k][s]));
     }
   }
-  mx = block_reduce(mx, MaxOp(), red);
+  mx = block_reduce_lds(mx, MaxOp(), red);
+  // the logit at the target (just read, so served by the caches) and the
+  // mask (tested where it is loaded) arrive during the exponentials
+  float z = 0.0f;
+  if (ent) {
+    z = to_f32(row[t]);
+    if (er.adv && er.mask != nullptr) mk = er.mask[id];
+    e_t[rank] = t;
+    const int tv = t / EPV;
+    atomicOr(&vmap[tv >> 5], 1u << (tv & 31));
+  }
+  keep_packed(x);
   float se = 0.0f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
-    if (vi < nvec) {
+    if (k < nk) {
 #pragma unroll
       for (int s = 0; s < EPV; ++s) se += __builtin_amdgcn_exp2f((to_f32(x[k][s]) - mx) * kLog2e);
     }
   }
-  se = block_reduce(se, SumOp(), red);
+  se = block_reduce_lds(se, SumOp(), red);  // its barriers also publish e_t and vmap
   const float lse = mx + logf(se);
-  if (row_lse != nullptr && threadIdx.x == 0) row_lse[r] = lse;
-  float W = 0.0f;
-  row_entries(row, beg, n, ids, sorted, tgt, er, lse, logp, red, &W);
+  if (row_lse != nullptr && tid == 0) row_lse[r] = lse;
+  // logp and the coefficient of each entry (weighted log-likelihood: c = w)
+  if (ent) {
+    const float lp = z - lse;
+    logp[id] = lp;
+    float c = wv;
+    if (er.adv) {
+      bool unclipped;
+      const float ratio = policy_ratio(lp, ov);
+      policy_term(ratio, av, er.lo, er.hi, &unclipped);
+      c = (unclipped && mk != 0) ? c * av * ratio : 0.0f;
+      er.coef[id] = c;
+    }
+    e_c[rank] = c;
+    e_z[rank] = z;
+  }
+  lds_barrier();
+  const float W = block_reduce_lds(tid < n ? e_c[tid] : 0.0f, SumOp(), red);  // sorted entry order
   if (dlogits == nullptr) return;
+  if (tid < n) {
+    const int te = e_t[tid];
+    bool first = true;
+    for (int f = 0; f < tid; ++f) first = first && (e_t[f] != te);
+    float tot = 0.0f;
+    if (first)
+      for (int f = tid; f < n; ++f)
+        if (e_t[f] == te) tot += e_c[f];
+    e_tot[tid] = tot;
+    e_first[tid] = first;
+  }
   T* drow = dlogits + r * V;
+  const __amdgpu_buffer_rsrc_t rd = buf_rsrc(drow, (int)(16 * nvec));
   const float sw = gs * W;
+  keep_packed(x);
+  asm volatile("" : "+v"(off));  // offsets recomputed here, not kept from the loads
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int64_t vi = threadIdx.x + (int64_t)kRowThreads * k;
-    if (vi < nvec) {
-      vec g;
+    vec g;
 #pragma unroll
-      for (int s = 0; s < EPV; ++s)
-        g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
-      __builtin_nontemporal_store(g, reinterpret_cast<vec*>(drow) + vi);  // written once: streamed
+    for (int s = 0; s < EPV; ++s) g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
+    // written once: streamed; a store past the end is dropped
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, g), rd, off + 16 * kRowThreads * k, 0, kNt);
+  }
+  lds_barrier();  // e_tot, e_first
+  // target columns: s (W_r p_t - sum of the c aiming at t), written by the
+  // thread that stored the column's vector above, so this store lands last
+  for (int k = 0; k < nk; ++k) {
+    const int vi = tid + kRowThreads * k;
+    if (!((vmap[vi >> 5] >> (vi & 31)) & 1u)) continue;
+    for (int e = 0; e < n; ++e) {
+      const int te = e_t[e];
+      if (e_first[e] && te / EPV == vi) {
+        const float p = __builtin_amdgcn_exp2f((e_z[e] - lse) * kLog2e);
+        drow[te] = from_f32<T>(gs * (W * p) - gs * e_tot[e]);
+      }
     }
   }
-  __syncthreads();
-  row_corrections(row, beg, n, sorted, tgt, er.coefs(), lse, W, gs, drow);
 }
 
 // Row kernel for any V and alignment: streams the row twice (the second
