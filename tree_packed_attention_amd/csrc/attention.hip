@@ -1172,18 +1172,11 @@ __device__ __forceinline__ void dkdv_epilogue(const f32x16* acc, bf16* qb0, bf16
 // no atomics, so results are reproducible.
 constexpr int kDkdvWaves = 8;
 
-template <int DP>
-__device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const float* rowv, bool full, int m,
-                                          int rel_lo, int rel_hi, int lg, const SwzAddr<DP>& ad, float sl2,
-                                          const bf16x8* op, bf16x8* xch, f32x16* acc) {
-  constexpr int KS = DP / 16;
-  constexpr int NDB = DP / 32;
-  sched_hint();
-  // role 0: x = S - lse/scale = Q' K'^T + rowv (rowv holds -lse/scale);
-  // role 1: x = dP - D = dO V^T + rowv (rowv holds -D). The accumulators
-  // start at the per-row value, read from LDS straight into them.
-  // C register i of block mb <-> query row 32mb + 16(i/8) + 8lg + 4((i/4)%2) + i%4; lane <-> key.
-  f32x16 x[2];
+// role 0: x = S - lse/scale = Q' K'^T + rowv (rowv holds -lse/scale);
+// role 1: x = dP - D = dO V^T + rowv (rowv holds -D). The accumulators
+// start at the per-row value, read from LDS straight into them.
+// C register i of block mb <-> query row 32mb + 16(i/8) + 8lg + 4((i/4)%2) + i%4; lane <-> key.
+__device__ __forceinline__ void dkdv_rows(const float* rowv, int lg, f32x16* x) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -1194,6 +1187,15 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
       x[mb][4 * q4 + 2] = v.z;
       x[mb][4 * q4 + 3] = v.w;
     }
+}
+
+template <int DP>
+__device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, f32x16* x, bool full, int m, int rel_lo,
+                                          int rel_hi, int lg, const SwzAddr<DP>& ad, float sl2, const bf16x8* op,
+                                          bf16x8* xch, f32x16* acc) {
+  constexpr int KS = DP / 16;
+  constexpr int NDB = DP / 32;
+  sched_hint();
   // role 0's products and softmax go first on the SIMD
   if (m == 0) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
@@ -1229,7 +1231,9 @@ __device__ __forceinline__ void dkdv_tile(const bf16* xs, const bf16* ys, const 
     // waits for
     __builtin_amdgcn_s_setprio(0);
   }
-  __syncthreads();
+  // the P hand-over orders LDS only: the next block's copies stay in flight
+  // (__syncthreads would wait for them here)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (m == 1) {
     // dS = P (dP - D), P from the partner
 #pragma unroll
@@ -1345,30 +1349,36 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
       ++hh;
     }
   };
-  auto tile = [&](int cq, const bf16* qs_, const bf16* ds_, const float* lsb, const float* dlb) {
+  auto tile = [&](int cq, const bf16* qs_, const bf16* ds_, f32x16* x) {
     const int i0 = (qb_lo + cq) * BQ;
     const bool full = (j0 + kBwdBK - 1 <= i0) && (mm.x >= min(i0 + BQ, T));
-    dkdv_tile<DP>(m == 0 ? qs_ : ds_, m == 0 ? ds_ : qs_, m == 0 ? lsb : dlb, full, m, key - i0, myse - i0, lg, ad,
-                  sl2, op, xch, acc);
+    dkdv_tile<DP>(m == 0 ? qs_ : ds_, m == 0 ? ds_ : qs_, x, full, m, key - i0, myse - i0, lg, ad, sl2, op, xch, acc);
   };
   // Two query blocks in LDS (the one computed, the one loaded), as separate
   // arrays and an unrolled pair of iterations so the compiler can tell them
   // apart.
   int cq = qq;  // block index (within the head) of the block being computed
   if (it0 < n_it) issue(qb0, ob0, lb0, db0);
+  // The per-row values are read before the next block's copies are issued:
+  // an LDS read right after the issue would make the compiler wait for the
+  // copies (it cannot tell the buffers apart).
   for (int it = it0; it < n_it; it += 2) {
     {
       wait_dma();
       __syncthreads();
+      f32x16 x[2];
+      dkdv_rows(m == 0 ? lb0 : db0, lg, x);
       if (it + 1 < n_it) issue(qb1, ob1, lb1, db1);
-      tile(cq, qb0, ob0, lb0, db0);
+      tile(cq, qb0, ob0, x);
       if (++cq == nqb) cq = 0;
     }
     if (it + 1 < n_it) {
       wait_dma();
       __syncthreads();
+      f32x16 x[2];
+      dkdv_rows(m == 0 ? lb1 : db1, lg, x);
       if (it + 2 < n_it) issue(qb0, ob0, lb0, db0);
-      tile(cq, qb1, ob1, lb1, db1);
+      tile(cq, qb1, ob1, x);
       if (++cq == nqb) cq = 0;
     }
   }
