@@ -50,6 +50,9 @@
 
 #include "profile.h"
 #include "ta_device.h"
+#ifndef TA_DMA_ASM
+#define TA_DMA_ASM 1
+#endif
 #include "ta_lds.h"
 #include "ta_error.h"
 #include "tree_attn.h"
@@ -806,6 +809,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void attn_fwd_kernel
 
   const bf16* kg = kr + (size_t)hk * Tp * DP;
   const bf16* vg = vr + (size_t)hk * Tp * DP;
+  // The Q' operands are waited for before the loop: the compiler does not see
+  // the tile copies (inline assembly), and a wait for these loads placed at
+  // their first use inside the loop would also drain the copies in flight.
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qop[nb][s]));
 
   // this wave's own rows [r0, r1): a key tile can be empty or full for them
   // even when it is partial for the whole query tile
@@ -1320,6 +1330,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void attn_bwd_dkdv_kernel(
     const bf16* ob = (m == 0 ? kr : vr) + ((size_t)hk * Tp + key) * DP + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KS; ++s) op[s] = load8(ob + 16 * s);
+    // waited for here, not at their first use inside the loop, where the
+    // wait would also drain the tile copies in flight (the compiler does
+    // not see them)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(op[s]));
   }
   f32x16 acc[NDB];
 #pragma unroll

@@ -27,6 +27,33 @@ __device__ __forceinline__ int toff(int row, int col) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void glb_void;
 
+#if TA_DMA_ASM
+// The copies are issued as inline assembly. The compiler models an LDS copy
+// in flight as an unordered event on the counter LDS reads share, so with
+// the builtin every LDS operand wait behind a copy becomes a full wait (no
+// read-ahead at all while the next tile is being copied). Written this way
+// the compiler does not see the copies: the kernels that use them wait for
+// them themselves (s_waitcnt vmcnt(0), then a barrier, before a copied tile
+// is read, and a barrier after the last read of a buffer before it is
+// refilled). The instruction writes no register; m0 holds the LDS address
+// and is set in the same statement (one wait state before its use).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// Each lane copies 16 bytes from g to (wave-uniform) dst + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(dst))
+               : "memory", "m0");
+}
+// Each lane copies 4 bytes from g to (wave-uniform) dst + 4 * lane.
+__device__ __forceinline__ void dma4(const void* g, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(dst))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+#else
 // Each lane copies 16 bytes from g to (wave-uniform) dst + 16 * lane.
 __device__ __forceinline__ void dma16(const void* g, void* dst) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 16, 0, 0);
@@ -35,6 +62,7 @@ __device__ __forceinline__ void dma16(const void* g, void* dst) {
 __device__ __forceinline__ void dma4(const void* g, void* dst) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)dst, 4, 0, 0);
 }
+#endif
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Copies 64 head-major rows [row0 + rowmap(r)] of a [*][DP] bf16 array into a
