@@ -23,11 +23,12 @@
  *   - Device tensors are contiguous and token-major: q, o, dout, dq are
  *     [T][Hq][d]; k, v, dk, dv are [T][Hkv][d]; lse is [Hq][T] float32.
  *     Query head h uses kv head h / (Hq / Hkv).
- *   - The library keeps no state besides the thread-local error string and
- *     the opt-in, process-wide kernel timing table (tree_attn_profile_*,
- *     the one piece of shared state; while it is enabled the library creates
- *     HIP events inside its calls): calls on different streams with separate
- *     workspaces may run concurrently.
+ *   - The library keeps no state besides the thread-local error string, the
+ *     opt-in, process-wide kernel timing table (tree_attn_profile_*; while it
+ *     is enabled the library creates HIP events inside its calls) and the
+ *     per-device entry table of tree_logprob_noalloc: calls on different
+ *     streams with separate workspaces may run concurrently (calls of
+ *     tree_logprob_noalloc that overlap on one device may not).
  */
 #ifndef TREE_ATTN_H
 #define TREE_ATTN_H
