@@ -10,7 +10,9 @@ Also reported on the same line: the host packer's time (not in the step), a
 partition-boundary leg (tree 0 unsplit vs split after its prompt, the child
 partitions through the gateway entry points),
 the tile classification, tree_logprob on 16384 bf16 rows x 151936 vocab with
-every row referenced 3 times (its own timed leg, HBM GB/s), per-kernel HIP
+every row referenced 3 times (its own timed leg, HBM GB/s) and in unique form
+with the packer's weights g/K on the random agentic tree (32768 rows x 32000
+vocab), per-kernel HIP
 event timings, the roofline of the dominant kernel and the CPU oracle timed
 on a bounded sample.
 
@@ -648,6 +650,33 @@ def main():
         print(f"[bench] tree_logprob {lp['ms']:.3f} ms, {lp['gbps']:.0f} GB/s; clipped policy loss "
               f"{lp['policy_loss']['ms']:.3f} ms", flush=True)
         del z
+        # the per-token weights g/K of the random agentic tree in unique form:
+        # one entry per token with a parent (M = T - 1 per tree), row = the
+        # parent, target = the token, weight = the packer's g/K
+        aseqs, agroups = workloads.sequences("agentic")
+        ap = ta.tree_pack(aseqs, agroups)
+        at = np.nonzero(ap["parent"] >= 0)[0]
+        Ra, Va = ap["T"], 32000
+        za = workloads.logits_input(Ra, Va, "bf16", 4, device=dev)
+        sa_t = torch.as_tensor(ap["parent"][at], device=dev)
+        ta_t = torch.as_tensor(ap["ids"][at], device=dev)
+        wa_t = torch.as_tensor(ap["weight"][at], device=dev)
+        aws = torch.empty(ta.library().tree_logprob_workspace_bytes(Ra, len(at)), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            ta.tree_logprob(za, sa_t, ta_t, wa_t, workspace=aws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_lp):
+            ta.tree_logprob(za, sa_t, ta_t, wa_t, workspace=aws)
+        torch.cuda.synchronize()
+        ua_dt = (time.perf_counter() - t0) / n_lp
+        alg_u = 2.0 * Ra * Va * 2 + 12.0 * len(at) + 4.0 * Ra
+        lp["unique_agentic"] = {"workload": f"random agentic tree (T={Ra}), unique form M={len(at)}, weights g/K, "
+                                            f"{Ra} bf16 rows x {Va} vocab, fused fwd+bwd",
+                                "ms": round(ua_dt * 1e3, 4), "gbps": round(alg_u / ua_dt / 1e9, 1)}
+        print(f"[bench] tree_logprob unique form (agentic tree) {lp['unique_agentic']['ms']:.3f} ms, "
+              f"{lp['unique_agentic']['gbps']:.0f} GB/s", flush=True)
+        del za
 
     gw = None
     if not args.no_gateway:
