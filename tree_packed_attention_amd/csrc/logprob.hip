@@ -270,8 +270,9 @@ __device__ Tv block_reduce_lds(Tv v, Op op, Tv* red) {
 constexpr int kEntCap = 256;
 
 // Row kernel with the row held in registers: NV 16-byte vectors per thread.
-// Vector vi of the row (EPV logits) sits in thread vi % kRowThreads, slot
-// vi / kRowThreads.
+// Vector vi of the row (EPV logits) sits in thread vi % TPB, slot vi / TPB.
+// TPB threads per row: 1024 for long rows, 256 for rows of at most 4096
+// vectors, so that several rows (and their reductions) are in flight per CU.
 //
 // Rows with at most kEntCap entries: the entry ids are requested before the
 // row and rank-sorted in LDS while it is in flight; each entry's target,
@@ -281,14 +282,15 @@ constexpr int kEntCap = 256;
 // second pass and the workgroup never waits for its own stores. Sums run in
 // the same order as on the general path (sorted entry order), so both give
 // the same bits.
-template <typename T, int NV>
-__global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
+template <typename T, int NV, int TPB>
+__global__ __launch_bounds__(TPB) void lp_row_reg_kernel(
     const T* __restrict__ logits, int64_t V, const int* __restrict__ ptr, const int* __restrict__ ids,
     int* __restrict__ sorted, const int* __restrict__ tgt, EntryRule er, float* __restrict__ logp,
     float* __restrict__ row_lse, T* __restrict__ dlogits, float gs, int need_all_rows) {
+  static_assert(TPB >= kEntCap && TPB <= 1024, "one thread per entry of a short row");
   typedef typename Vec16<T>::type vec;
   constexpr int EPV = Vec16<T>::N;
-  constexpr int MAPW = (NV * kRowThreads + 31) / 32;
+  constexpr int MAPW = (NV * TPB + 31) / 32;
   __shared__ float red[16];
   __shared__ unsigned int vmap[MAPW];  // bit vi: vector vi holds a target
   __shared__ int e_id[kEntCap];        // entry ids in CSR order
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     float mx = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      const int64_t vi = tid + (int64_t)TPB * k;
       if (vi < nvec) {
         x[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(row) + vi);  // read once: streamed
 #pragma unroll
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     float se = 0.0f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      const int64_t vi = tid + (int64_t)TPB * k;
       if (vi < nvec) {
 #pragma unroll
         for (int s = 0; s < EPV; ++s) se += __builtin_amdgcn_exp2f((to_f32(x[k][s]) - mx) * kLog2e);
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
     const float sw = gs * W;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      const int64_t vi = tid + (int64_t)kRowThreads * k;
+      const int64_t vi = tid + (int64_t)TPB * k;
       if (vi < nvec) {
         vec g;
 #pragma unroll
@@ -358,14 +360,14 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
   // whole offset (the uniform operand stays 0).
   const bool ent = tid < n;
   const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(ids + beg, 4 * n), 4 * tid, 0, 0);
-  for (int i = tid; i < MAPW; i += kRowThreads) vmap[i] = 0u;
-  // this thread's vectors are tid + kRowThreads k for k < nk (nvec < 2^31)
-  const int nk = (int)((nvec - tid + kRowThreads - 1) / kRowThreads);
+  for (int i = tid; i < MAPW; i += TPB) vmap[i] = 0u;
+  // this thread's vectors are tid + TPB k for k < nk (nvec < 2^31)
+  const int nk = (int)((nvec - tid + TPB - 1) / TPB);
   const __amdgpu_buffer_rsrc_t rrow = buf_rsrc(row, (int)(16 * nvec));
   int off = 16 * tid;
 #pragma unroll
   for (int k = 0; k < NV; ++k)  // read once: streamed
-    x[k] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(rrow, off + 16 * kRowThreads * k, 0, kNt));
+    x[k] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(rrow, off + 16 * TPB * k, 0, kNt));
   if (ent) e_id[tid] = id;
   lds_barrier();
   // rank among the row's ids (all distinct) = sorted position; the entry's
@@ -452,13 +454,13 @@ __global__ __launch_bounds__(kRowThreads) void lp_row_reg_kernel(
 #pragma unroll
     for (int s = 0; s < EPV; ++s) g[s] = from_f32<T>(sw * __builtin_amdgcn_exp2f((to_f32(x[k][s]) - lse) * kLog2e));
     // written once: streamed; a store past the end is dropped
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, g), rd, off + 16 * kRowThreads * k, 0, kNt);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, g), rd, off + 16 * TPB * k, 0, kNt);
   }
   lds_barrier();  // e_tot, e_first
   // target columns: s (W_r p_t - sum of the c aiming at t), written by the
   // thread that stored the column's vector above, so this store lands last
   for (int k = 0; k < nk; ++k) {
-    const int vi = tid + kRowThreads * k;
+    const int vi = tid + TPB * k;
     if (!((vmap[vi >> 5] >> (vi & 31)) & 1u)) continue;
     for (int e = 0; e < n; ++e) {
       const int te = e_t[e];
@@ -559,10 +561,10 @@ LpLayout lp_layout(int64_t R, int64_t M) {
   return L;
 }
 
-template <typename T, int NV>
+template <typename T, int NV, int TPB = kRowThreads>
 void launch_reg(int64_t R, const void* logits, int64_t V, char* ws, const LpLayout& L, const int* tgt, const EntryRule& w,
                 float* logp, float* row_lse, void* dlogits, float gs, int need_all, hipStream_t st) {
-  hipLaunchKernelGGL((lp_row_reg_kernel<T, NV>), dim3((unsigned)R), dim3(kRowThreads), 0, st,
+  hipLaunchKernelGGL((lp_row_reg_kernel<T, NV, TPB>), dim3((unsigned)R), dim3(TPB), 0, st,
                      static_cast<const T*>(logits), V, reinterpret_cast<const int*>(ws + L.off_ptr),
                      reinterpret_cast<const int*>(ws + L.off_ids), reinterpret_cast<int*>(ws + L.off_sorted), tgt, w,
                      logp, row_lse, static_cast<T*>(dlogits), gs, need_all);
@@ -576,10 +578,13 @@ void launch_rows(int64_t R, const void* logits, int64_t V, char* ws, const LpLay
   const bool aligned = (V * (int64_t)sizeof(T)) % 16 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
                        (dlogits == nullptr || reinterpret_cast<uintptr_t>(dlogits) % 16 == 0);
   const int64_t nvec_per_thread = (V / EPV + kRowThreads - 1) / kRowThreads;
+  const int64_t nv256 = (V / EPV + 255) / 256;  // vectors per thread at 256 threads per row
+  if (aligned && nv256 <= 16) {
+    if (nv256 <= 4) return launch_reg<T, 4, 256>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    if (nv256 <= 8) return launch_reg<T, 8, 256>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+    return launch_reg<T, 16, 256>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
+  }
   if (aligned && nvec_per_thread <= 20) {
-    if (nvec_per_thread <= 1) return launch_reg<T, 1>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
-    if (nvec_per_thread <= 2) return launch_reg<T, 2>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
-    if (nvec_per_thread <= 4) return launch_reg<T, 4>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
     if (nvec_per_thread <= 8) return launch_reg<T, 8>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
     if (nvec_per_thread <= 12) return launch_reg<T, 12>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
     if (nvec_per_thread <= 16) return launch_reg<T, 16>(R, logits, V, ws, L, tgt, w, logp, row_lse, dlogits, gs, need_all, st);
