@@ -159,8 +159,22 @@ __device__ __forceinline__ bool conv_tile_is_chain(const int (*anc)[kConvMaxK], 
 }
 
 // weights of channels c0..c0+7 in tap order m (tap m multiplies the m-th ancestor)
+// With K = 4 and a 16-byte aligned w, the 8 channels' taps are 32
+// consecutive floats, read as eight 16-byte loads: per-element loads touch a
+// different cache line in every lane and kept the texture unit busy.
 template <int KM>
 __device__ __forceinline__ void conv_weights(const float* __restrict__ w, int c0, int K, float (*wr)[8]) {
+  if (KM >= 4 && K == 4 && (reinterpret_cast<uintptr_t>(w) & 15) == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + e) * 4);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wr[m][e] = f[3 - m];
+#pragma unroll
+      for (int m = 4; m < KM; ++m) wr[m][e] = 0.0f;
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < KM; ++m)
 #pragma unroll
