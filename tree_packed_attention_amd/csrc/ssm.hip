@@ -103,6 +103,14 @@ __device__ __forceinline__ float sigmoidf(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
 }
 
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight (__syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- tree conv
 
 constexpr int kConvThreads = 256;
@@ -229,6 +237,24 @@ struct ConvTile {
         rows[r].zero();
     }
   }
+  // The same rows without branches: a row outside [0, T) is read from a
+  // clamped row and zeroed by fix_edges once it has arrived. Every thread
+  // then issues the same loads, so a wait for a load issued before them
+  // (the window's parents) leaves them in flight.
+  __device__ __forceinline__ void load_all(const Tio* __restrict__ x, int t0, int T, int C, int c0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int t = min(max(t0 - (KM - 1) + r, 0), T - 1);
+      rows[r].load(x + (size_t)t * C + c0);
+    }
+  }
+  __device__ __forceinline__ void fix_edges(int t0, int T) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int t = t0 - (KM - 1) + r;
+      if (t < 0 || t >= T) rows[r].zero();
+    }
+  }
   // a_i += sum over taps of w_m x_{t-m}, for a tile whose every tap is on a
   // chain (the m-th ancestor of t is t - m): all inputs are in the tile
   __device__ __forceinline__ void chain_taps(int i, int K, const float (*wr)[8], float* a) const {
@@ -261,24 +287,53 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(const Tio* __res
                                                                 const float* __restrict__ bias,
                                                                 const int* __restrict__ par, int T, int C, int K,
                                                                 int act, Tio* __restrict__ y) {
+  constexpr int NWIN = kConvTB + kConvMaxK - 1;  // tokens whose parents are staged in LDS
+  static_assert(NWIN <= 64, "the window's parents are loaded and walked by wave 0");
   __shared__ int anc[kConvTB][kConvMaxK];
-  __shared__ int pl[kConvTB + kConvMaxK - 1];
+  __shared__ int pl[NWIN];
+  __shared__ int chain_all;
   const int t0 = blockIdx.x * kConvTB;
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
   const bool cok = c0 < C;
-  // rows, weights and bias are all in flight while the ancestor table forms
+  const int cl = cok ? c0 : C - 8;  // in-bounds channels for the threads past C (their results are dropped)
+  // The window's parents are requested first and the rows, weights and bias
+  // after them, all unconditionally: waiting for the parents leaves the rest
+  // in flight through the ancestor walk.
+  const int base = t0 - (kConvMaxK - 1);
+  const int tw = base + (int)threadIdx.x;
+  const int pv = par[min(max(tw, 0), T - 1)];
   ConvTile<Tio, KM> tile;
   float wr[KM][8], br[8];
-  if (cok) {
-    tile.load(x, t0, T, C, c0);
-    conv_weights<KM>(w, c0, K, wr);
+  tile.load_all(x, t0, T, C, cl);
+  conv_weights<KM>(w, cl, K, wr);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) br[e] = bias ? bias[c0 + e] : 0.0f;
+  for (int e = 0; e < 8; ++e) br[e] = bias ? bias[cl + e] : 0.0f;
+  if (threadIdx.x < NWIN) pl[threadIdx.x] = (tw >= 0 && tw < T) ? sane_parent(pv, tw) : -1;
+  lds_barrier();
+  // one thread per token lists its ancestors (HBM only where a walk leaves
+  // the window) and checks that every tap lies on a chain
+  if (threadIdx.x < 64) {
+    bool ok = true;
+    if ((int)threadIdx.x < kConvTB) {
+      const int i = threadIdx.x;
+      int s = t0 + i < T ? t0 + i : -1;
+      ok = t0 + i < T;
+#pragma unroll
+      for (int m = 0; m < kConvMaxK; ++m) {
+        if (m < K) {
+          anc[i][m] = s;
+          ok = ok && s == t0 + i - m;
+          if (s >= 0) s = s >= base ? pl[s - base] : sane_parent(par[s], s);
+        }
+      }
+    }
+    const bool all = __all(ok);
+    if (threadIdx.x == 0) chain_all = all ? 1 : 0;
   }
-  conv_ancestors<kConvTB>(par, t0, T, K, anc, pl);
-  __syncthreads();
-  const bool chain = conv_tile_is_chain(anc, t0, kConvTB, T, K);
+  lds_barrier();
+  const bool chain = chain_all != 0;
   if (!cok) return;
+  tile.fix_edges(t0, T);
   if (chain) {
 #pragma unroll
     for (int i = 0; i < kConvTB; ++i) {
