@@ -153,7 +153,9 @@ def _wide_rows(seed):
     return src[perm], tgt[perm], rng
 
 
-@pytest.mark.parametrize("V,dtype", [(4096, "bf16"), (2052, "f32")])
+# 4096 / 2052: 256 threads per row; 32768: the largest row at 256 threads (16
+# vectors each); 40000: 1024 threads per row
+@pytest.mark.parametrize("V,dtype", [(4096, "bf16"), (2052, "f32"), (32768, "bf16"), (40000, "bf16")])
 def test_wide_rows_both_paths(V, dtype):
     R = len(WIDE_COUNTS)
     src, tgt, rng = _wide_rows(V)
