@@ -480,16 +480,26 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
   __shared__ int dlist[kConvTB][kConvMaxDesc];
   __shared__ int dcount[kConvTB];
   __shared__ int pw[NWIN], sw[NWIN];
+  __shared__ int chain_all;
+  static_assert(NWIN <= 64 && kConvTB <= 64, "the window is staged and walked by wave 0");
   const int t0 = blockIdx.x * kConvTB;
   const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  const int cl = c0 < C ? c0 : C - 8;  // in-bounds channels for the threads past C (their results are dropped)
+  // The window's pos / se first, then (unconditionally, from clamped rows)
+  // the g rows a chain tile needs: waiting for the window leaves the g rows
+  // in flight through the walk, whose barriers order LDS only.
+  const int tw = min(t0 + (int)threadIdx.x, T - 1);
+  const int pv = pos[tw], sv = se[tw];
+  ConvTile<Tio, KM> gt;  // gt.rows[r] = g_{t0 + r}
+  gt.load_all(gbuf, t0 + KM - 1, T, C, cl);
   float wr[KM][8];
-  if (c0 < C) conv_weights<KM>(w, c0, K, wr);
-  for (int r = threadIdx.x; r < NWIN; r += blockDim.x) {
-    const int t = t0 + r;
-    pw[r] = t < T ? pos[t] : 0;
-    sw[r] = t < T ? se[t] : 0;
+  conv_weights<KM>(w, cl, K, wr);
+  if (threadIdx.x < NWIN) {
+    const bool in = t0 + (int)threadIdx.x < T;
+    pw[threadIdx.x] = in ? pv : 0;
+    sw[threadIdx.x] = in ? sv : 0;
   }
-  __syncthreads();
+  lds_barrier();
   // the walk reads LDS inside the window and HBM past it
   auto pos_at = [&](int t) { return t - t0 < NWIN ? pw[t - t0] : pos[t]; };
   auto se_at = [&](int t) { return t - t0 < NWIN ? sw[t - t0] : se[t]; };
@@ -519,17 +529,23 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_dx_kernel(const Tio* __
   // chain tile: every token j has exactly the descendants j + 1 .. j + K - 1
   // (depths 1 .. K - 1) within K - 1 levels, so dx_j = sum_m w_m g_{j+m}
   // from a tile of g rows loaded up front
-  bool ch = true;
-  if (threadIdx.x < kConvTB) {
-    const int i = threadIdx.x, j = t0 + i;
-    ch = j < T && dcount[i] == K - 1;
-    for (int q = 0; q < K - 1 && ch; ++q) ch = dlist[i][q] == (((j + q + 1) << 3) | (q + 1));
+  // (the walk's threads are wave 0's: its own dlist / dcount writes are seen
+  // in order, and the other waves wait at the barrier below)
+  if (threadIdx.x < 64) {
+    bool ch = true;
+    if ((int)threadIdx.x < kConvTB) {
+      const int i = threadIdx.x, j = t0 + i;
+      ch = j < T && dcount[i] == K - 1;
+      for (int q = 0; q < K - 1 && ch; ++q) ch = dlist[i][q] == (((j + q + 1) << 3) | (q + 1));
+    }
+    const bool all = __all(ch);
+    if (threadIdx.x == 0) chain_all = all ? 1 : 0;
   }
-  const bool chain = __syncthreads_and(ch) != 0;
+  lds_barrier();
+  const bool chain = chain_all != 0;
   if (c0 >= C) return;
   if (chain) {
-    ConvTile<Tio, KM> gt;  // gt.rows[r] = g_{t0 + r}
-    gt.load(gbuf, t0 + KM - 1, T, C, c0);
+    gt.fix_edges(t0 + KM - 1, T);
 #pragma unroll
     for (int i = 0; i < kConvTB; ++i) {
       float acc[8];
