@@ -97,8 +97,9 @@ def test_agentic_unique_form_weights():
 
 def test_large_vocab_repeated_rows_full_size():
     """16384 bf16 rows x 151936 vocab, every row referenced 3 times (M = 49152,
-    w = 1/3). Loss over all rows (row lse from the oracle, in chunks); logp,
-    lse and dlogits on sampled rows."""
+    w = 1/3). Loss over all rows (row lse from the oracle, in chunks); logp
+    and lse of every row; dlogits of every row at the columns no entry
+    targets, and in full (target corrections included) on sampled rows."""
     R, V = 16384, 151936
     src, tgt, w = workloads.repeated_rows_entries(R, V, 3, 5)
     z = workloads.logits_input(R, V, "bf16", 5, device="cuda")
@@ -120,6 +121,20 @@ def test_large_vocab_repeated_rows_full_size():
                                np.array([remap[int(x)] for x in src[sel]]), tgt[sel], w[sel])
     d = host(dz[torch.as_tensor(rows, device="cuda")])
     assert np.linalg.norm(d - r_dz) / np.linalg.norm(r_dz) <= 5e-2
+    # every row, every column that no entry targets: dlogits = W_r p = W_r exp(z - lse_r)
+    # with the oracle's lse (W_r = sum of the row's weights), to bf16 rounding
+    W = np.bincount(src, weights=w.astype(np.float64), minlength=R)
+    src_t = torch.as_tensor(src.astype(np.int64), device="cuda")
+    tgt_t = torch.as_tensor(tgt.astype(np.int64), device="cuda")
+    for a in range(0, R, 512):
+        b = min(a + 512, R)
+        lse_c = torch.as_tensor(r_lse[a:b], device="cuda", dtype=torch.float64)
+        W_c = torch.as_tensor(W[a:b], device="cuda", dtype=torch.float64)
+        exp = (W_c[:, None] * torch.exp(z[a:b].double() - lse_c[:, None])).float()
+        diff = (dz[a:b].float() - exp).abs()
+        m = (src_t >= a) & (src_t < b)
+        diff[src_t[m] - a, tgt_t[m]] = 0.0  # target columns: checked on the sampled rows above
+        assert bool((diff <= 1e-2 * exp + 1e-7).all()), a
 
 
 def test_invalid_entries_and_forward_only():
